@@ -1,0 +1,408 @@
+"""CPU oracle for the Hilbert-ordered Top-p block router and block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. The GPU library never calls it, and the
+two share no code.
+
+What it computes follows the FVAttn pages (the alanhou.org explainer of FVAttn,
+sections "Core Mechanism" and "Key Concepts"; the xllm-io review of FVAttn,
+sections 三 "技术架构" Stage 1, 核心公式 Eq. 1-2, 3.1 and the SASA steps of 五
+"代码实现分析"). Where the pages leave a step open the plainest reading is taken;
+each is named where it is used:
+
+  * Hilbert order (review 3.1): tokens of the (T, Y, X) latent grid are sorted by
+    their index on a 3-D Hilbert curve over the enclosing 2^m cube (cells outside
+    the grid are skipped), using Skilling's transform (J. Skilling, "Programming
+    the Hilbert curve", AIP Conf. Proc. 707, 2004) with axes (t, y, x), most
+    significant bit first. The sorted sequence is cut into blocks of b tokens;
+    the last block may be partial.
+  * Block summaries: the arithmetic mean of each block's q (and k) rows.
+  * Block scores s_ij = qbar_i . kbar_j / sqrt(d), softmax over key blocks j.
+  * Top-p (explainer, "Top-p Routing with Safety Floor"): the fewest blocks, in
+    descending probability (ties: smaller block id first), whose cumulative
+    probability reaches p (CDF >= p); p >= 1 keeps every block.
+  * Top-k floor: count' = max(count, min(k, nb)), taking the next blocks of the
+    same importance order.
+  * Eq. 1: L_h = mean over query blocks of the retained count.
+  * Slack fill (one-GPU reading of SASA): E = floor(beta * sum count') extra
+    blocks; repeatedly raise the lightest tile (ties: lowest tile id; full tiles
+    skipped) by the next block of its own importance order.
+  * LPT queue (one-GPU reading of RLB): tiles sorted by retained count,
+    descending, ties by ascending tile id.
+  * Attention: exact softmax(Q K_R^T / sqrt(d)) V_R over the tokens of the
+    retained key blocks R of each query block.
+
+Precision: routing decisions are integers decided by floating point, so the
+oracle takes them in the same precision as the GPU library: block means as the
+float64 mean of the rows rounded to float32; scores as a float64 dot product
+divided by sqrt(d) and rounded to float32; softmax, cumulative sums and the p
+comparison in float64. Attention is computed in float64.
+
+Parity pins: every function here is checked in tests/test_oracle_*.py against
+properties the pages or the mathematics fix (closed forms, brute force, library
+special cases); see the header of each test file.
+"""
+from __future__ import annotations
+
+import heapq
+import math
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# Hilbert order
+# --------------------------------------------------------------------------
+
+
+def hilbert_bits(*extent: int) -> int:
+    """Bits per axis m of the enclosing 2^m cube: m = max(1, ceil(log2(max extent)))."""
+    biggest = max(extent)
+    m = 1
+    while (1 << m) < biggest:
+        m += 1
+    return m
+
+
+def hilbert_index(coords: np.ndarray, m: int) -> np.ndarray:
+    """Hilbert index of each cell (rows of `coords`, one column per axis) on the 2^m cube.
+
+    Skilling's axes-to-index direction: undo the per-level reflections and axis
+    exchanges from the top bit down, Gray-encode across the axes, then read the
+    transposed bits out most-significant first, axis 0 first within each level.
+    """
+    coords = np.asarray(coords, dtype=np.int64)
+    n = coords.shape[1]
+    x = [coords[:, i].copy() for i in range(n)]
+    q = 1 << (m - 1)
+    while q > 1:
+        low = q - 1
+        for i in range(n):
+            on = (x[i] & q) != 0
+            if i == 0:
+                x[0] = np.where(on, x[0] ^ low, x[0])
+                continue
+            swap = (x[0] ^ x[i]) & low
+            new0 = np.where(on, x[0] ^ low, x[0] ^ swap)
+            newi = np.where(on, x[i], x[i] ^ swap)
+            x[0], x[i] = new0, newi
+        q >>= 1
+    for i in range(1, n):
+        x[i] = x[i] ^ x[i - 1]
+    flip = np.zeros_like(x[0])
+    q = 1 << (m - 1)
+    while q > 1:
+        flip = np.where((x[n - 1] & q) != 0, flip ^ (q - 1), flip)
+        q >>= 1
+    for i in range(n):
+        x[i] = x[i] ^ flip
+    index = np.zeros_like(x[0])
+    for level in range(m - 1, -1, -1):
+        for i in range(n):
+            index = (index << 1) | ((x[i] >> level) & 1)
+    return index
+
+
+def hilbert_perm(T: int, Y: int, X: int):
+    """perm[r] = row-major index (t*Y + y)*X + x of the r-th grid cell in Hilbert order.
+
+    Returns (perm, inv) as int64 arrays, inv = perm^-1.
+    """
+    m = hilbert_bits(T, Y, X)
+    t, y, x = np.meshgrid(np.arange(T), np.arange(Y), np.arange(X), indexing="ij")
+    cells = np.stack([t.ravel(), y.ravel(), x.ravel()], axis=1)
+    idx = hilbert_index(cells, m)
+    perm = np.argsort(idx, kind="stable")
+    assert len(np.unique(idx)) == len(idx)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size)
+    return perm.astype(np.int64), inv.astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# Blocks and block summaries
+# --------------------------------------------------------------------------
+
+
+def block_sizes(N: int, b: int) -> np.ndarray:
+    """True token count n_j of each of the ceil(N/b) consecutive blocks (last may be partial)."""
+    nb = -(-N // b)
+    starts = np.arange(nb) * b
+    return np.minimum(b, N - starts).astype(np.int64)
+
+
+def to_hilbert(x: np.ndarray, perm: np.ndarray) -> np.ndarray:
+    """[B, N, H, d] grid order -> [B, H, N, d] in Hilbert token order."""
+    return np.ascontiguousarray(np.transpose(x[:, perm], (0, 2, 1, 3)))
+
+
+def block_means(xh: np.ndarray, b: int) -> np.ndarray:
+    """Mean of each block's rows: [B, H, N, d] -> float32 [B, H, nb, d].
+
+    The sum is taken in float64 (exact for bf16 rows), divided by the true
+    token count in float64 and rounded once to float32.
+    """
+    B, H, N, d = xh.shape
+    sizes = block_sizes(N, b)
+    out = np.empty((B, H, sizes.size, d), dtype=np.float32)
+    for j, n in enumerate(sizes):
+        seg = xh[:, :, j * b: j * b + n, :].astype(np.float64)
+        out[:, :, j, :] = (seg.sum(axis=2) / np.float64(n)).astype(np.float32)
+    return out
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
+    """s_ij = qbar_i . kbar_j / sqrt(d) per head, float64 products and sums, rounded to float32.
+
+    qbar, kbar: [..., nb, d] float32. Returns float32 [..., nb, nb].
+    """
+    d = qbar.shape[-1]
+    q64 = qbar.astype(np.float64)
+    k64 = kbar.astype(np.float64)
+    s = np.matmul(q64, np.swapaxes(k64, -1, -2)) / math.sqrt(d)
+    return s.astype(np.float32)
+
+
+def block_softmax(s: np.ndarray) -> np.ndarray:
+    """Row softmax over key blocks in float64: exp(s - max) / sum."""
+    s64 = s.astype(np.float64)
+    e = np.exp(s64 - s64.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# Top-p with the Top-k floor
+# --------------------------------------------------------------------------
+
+
+@dataclass
+class RowRouting:
+    order: np.ndarray     # [nb] block ids, probability descending, ties by smaller id
+    cdf: np.ndarray       # [nb] float64 running sums of P along `order`
+    count_topp: int       # c: fewest blocks reaching p
+    count: int            # c' after the floor
+
+
+def importance_order(P: np.ndarray) -> np.ndarray:
+    """Block ids sorted by probability descending, ties broken by the smaller block id.
+
+    Works on the last axis of P (any leading shape).
+    """
+    ids = np.broadcast_to(np.arange(P.shape[-1]), P.shape)
+    return np.lexsort((ids, -P), axis=-1)
+
+
+def topp_count(cdf: np.ndarray, p: float) -> np.ndarray:
+    """c = smallest r (1-based) with cdf_r >= p; nb when p >= 1 or when no prefix reaches p."""
+    nb = cdf.shape[-1]
+    if p >= 1.0:
+        return np.full(cdf.shape[:-1], nb, dtype=np.int64)
+    reached = cdf >= p
+    first = np.argmax(reached, axis=-1) + 1
+    return np.where(reached.any(axis=-1), first, nb).astype(np.int64)
+
+
+def floor_count(c: np.ndarray, k_floor: int, nb: int) -> np.ndarray:
+    """count' = max(c, min(k, nb))."""
+    return np.maximum(c, min(k_floor, nb)).astype(np.int64)
+
+
+def route_row(s_row: np.ndarray, p: float, k_floor: int) -> RowRouting:
+    """Top-p + floor for one query block's score row (plain, one row at a time)."""
+    P = block_softmax(s_row[None, :])[0]
+    order = importance_order(P)
+    cdf = np.cumsum(P[order])
+    c = int(topp_count(cdf[None, :], p)[0])
+    return RowRouting(order, cdf, c, int(floor_count(np.array(c), k_floor, P.size)))
+
+
+@dataclass
+class Routing:
+    """Routing of a whole [B, H] problem."""
+
+    nb: int
+    sizes: np.ndarray          # [nb] true token count per block
+    scores: np.ndarray         # float32 [B, H, nb, nb]
+    P: np.ndarray              # float64 [B, H, nb, nb]
+    order: np.ndarray          # int64 [B, H, nb, nb] importance order per tile
+    cdf: np.ndarray            # float64 [B, H, nb, nb] along `order`
+    count_topp: np.ndarray     # int64 [B, H, nb]
+    counts: np.ndarray         # int64 [B, H, nb] after floor (and slack fill, if applied)
+
+    def retained(self, b: int, h: int, i: int) -> np.ndarray:
+        """Ascending ids of the retained key blocks of tile (b, h, i)."""
+        return np.sort(self.order[b, h, i, : self.counts[b, h, i]])
+
+
+def route(qh: np.ndarray, kh: np.ndarray, block: int, p: float, k_floor: int) -> Routing:
+    """Stage-1 routing on Hilbert-ordered q, k of shape [B, H, N, d] (float32 values)."""
+    B, H, N, d = qh.shape
+    sizes = block_sizes(N, block)
+    nb = sizes.size
+    qbar = block_means(qh, block)
+    kbar = block_means(kh, block)
+    s = block_scores(qbar, kbar)
+    P = block_softmax(s)
+    order = importance_order(P)
+    cdf = np.cumsum(np.take_along_axis(P, order, axis=-1), axis=-1)
+    c = topp_count(cdf, p)
+    return Routing(nb, sizes, s, P, order, cdf, c, floor_count(c, k_floor, nb))
+
+
+# --------------------------------------------------------------------------
+# Eq. 1 workloads, Eq. 2 imbalance
+# --------------------------------------------------------------------------
+
+
+def workloads(counts: np.ndarray):
+    """work_h = sum_i count'_{h,i} (exact); L_h = work_h / nb (float32 division)."""
+    nb = counts.shape[-1]
+    work = counts.sum(axis=-1).astype(np.int64)
+    L = (work.astype(np.float32) / np.float32(nb)).astype(np.float32)
+    return work, L
+
+
+def imbalance(loads: Sequence[float]) -> float:
+    """Eq. 2: rho = max_r L_r / mean_r L_r."""
+    loads = np.asarray(loads, dtype=np.float64)
+    return float(loads.max() / loads.mean())
+
+
+# --------------------------------------------------------------------------
+# Slack fill (one-GPU reading of SASA)
+# --------------------------------------------------------------------------
+
+
+def slack_budget(counts: np.ndarray, beta: float) -> int:
+    """E = floor(beta * sum count'), in float64."""
+    return int(math.floor(np.float64(beta) * np.float64(int(counts.sum()))))
+
+
+def slack_fill(counts: np.ndarray, beta: float) -> np.ndarray:
+    """Heap loop: E times, raise the tile with the smallest (count, tile id) among tiles below nb.
+
+    counts: any shape whose last axis is the nb query blocks of a head; tile id
+    is the flat row-major index. Returns the new counts (same shape). Each raise
+    appends the tile's next block in its own importance order, so the retained
+    set stays a prefix of that order.
+    """
+    nb = counts.shape[-1]
+    flat = counts.reshape(-1).astype(np.int64).copy()
+    E = slack_budget(counts, beta)
+    heap = [(int(c), t) for t, c in enumerate(flat) if c < nb]
+    heapq.heapify(heap)
+    for _ in range(E):
+        if not heap:
+            break
+        c, t = heapq.heappop(heap)
+        flat[t] = c + 1
+        if c + 1 < nb:
+            heapq.heappush(heap, (c + 1, t))
+    return flat.reshape(counts.shape)
+
+
+def slack_fill_level(counts: np.ndarray, beta: float) -> np.ndarray:
+    """Closed form of the heap loop: a water level lambda plus a remainder by tile id."""
+    nb = counts.shape[-1]
+    flat = counts.reshape(-1).astype(np.int64)
+    E = slack_budget(counts, beta)
+
+    def need(lam):
+        return int(np.maximum(0, np.minimum(lam, nb) - flat).sum())
+
+    lo, hi = 0, nb
+    while lo < hi:  # largest lam in [0, nb] with need(lam) <= E
+        mid = (lo + hi + 1) // 2
+        if need(mid) <= E:
+            lo = mid
+        else:
+            hi = mid - 1
+    lam = lo
+    out = np.maximum(flat, lam)
+    rest = E - need(lam)
+    if lam < nb and rest > 0:
+        at_level = np.nonzero(out == lam)[0]
+        out[at_level[:rest]] += 1
+    return out.reshape(counts.shape)
+
+
+# --------------------------------------------------------------------------
+# LPT tile queue and list scheduling
+# --------------------------------------------------------------------------
+
+
+def lpt_queue(counts: np.ndarray) -> np.ndarray:
+    """Tile ids (flat row-major) by retained count descending, ties by ascending tile id."""
+    flat = counts.reshape(-1)
+    ids = np.arange(flat.size)
+    return np.lexsort((ids, -flat)).astype(np.int64)
+
+
+def list_schedule(costs: Sequence[float], order: Sequence[int], workers: int):
+    """Greedy list scheduling: each next item goes to the earliest-free worker (ties: lowest id).
+
+    Returns (per-worker loads, makespan).
+    """
+    heap = [(0.0, w) for w in range(workers)]
+    loads = np.zeros(workers)
+    for t in order:
+        free, w = heapq.heappop(heap)
+        loads[w] += costs[t]
+        heapq.heappush(heap, (free + costs[t], w))
+    return loads, float(loads.max())
+
+
+# --------------------------------------------------------------------------
+# Block-sparse attention
+# --------------------------------------------------------------------------
+
+
+def attention_tile(qh_bh: np.ndarray, kh_bh: np.ndarray, vh_bh: np.ndarray,
+                   block: int, i: int, kv_blocks: Sequence[int]) -> np.ndarray:
+    """Output rows of query block i over the tokens of the given key blocks (float64).
+
+    qh_bh, kh_bh, vh_bh: [N, d] one head's rows in Hilbert order.
+    Returns [n_i, d].
+    """
+    N, d = qh_bh.shape
+    rows = slice(i * block, min((i + 1) * block, N))
+    keys = np.concatenate([np.arange(j * block, min((j + 1) * block, N)) for j in kv_blocks])
+    q = qh_bh[rows].astype(np.float64)
+    k = kh_bh[keys].astype(np.float64)
+    v = vh_bh[keys].astype(np.float64)
+    s = q @ k.T / math.sqrt(d)
+    s -= s.max(axis=1, keepdims=True)
+    w = np.exp(s)
+    w /= w.sum(axis=1, keepdims=True)
+    return w @ v
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, perm: np.ndarray, block: int,
+              retained: Optional[callable] = None) -> np.ndarray:
+    """Block-sparse attention in grid order: [B, N, H, d] in, float64 [B, N, H, d] out.
+
+    retained(b, h, i) gives the key-block ids of tile (b, h, i); None means every block.
+    """
+    B, N, H, d = q.shape
+    qh, kh, vh = to_hilbert(q, perm), to_hilbert(k, perm), to_hilbert(v, perm)
+    nb = -(-N // block)
+    out = np.zeros((B, N, H, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                blocks = range(nb) if retained is None else retained(b, h, i)
+                rows = perm[i * block: min((i + 1) * block, N)]
+                out[b, rows, h, :] = attention_tile(qh[b, h], kh[b, h], vh[b, h], block, i, blocks)
+    return out
+
+
+def retained_flops(sizes: np.ndarray, d: int, tiles) -> float:
+    """F_ret = sum over tiles and retained blocks of 4 * n_i * n_j * d (true token counts).
+
+    tiles: iterable of (i, retained block ids) pairs.
+    """
+    total = 0
+    for i, blocks in tiles:
+        total += 4 * int(sizes[i]) * int(sizes[np.asarray(blocks, dtype=np.int64)].sum()) * d
+    return float(total)
