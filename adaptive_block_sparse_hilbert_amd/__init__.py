@@ -1,0 +1,250 @@
+"""Python binding of libabsh.so: the Hilbert-ordered Top-p block router and block-sparse attention for MI355X.
+
+This module only marshals arguments: it takes torch tensors (for device memory
+and the current stream), checks their shapes and dtypes, and passes raw
+pointers to the C ABI declared in include/absh.h. Every step of the path runs in
+the library's HIP kernels. If libabsh.so is missing, importing the binding still
+works but the first call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libabsh.so")
+
+ABSH_BF16, ABSH_F32 = 0, 1
+ABSH_ROWS, ABSH_VT = 0, 1
+
+EXPORTED = (
+    "absh_version", "absh_status_string", "absh_last_error", "absh_create", "absh_destroy", "absh_dims",
+    "absh_perm", "absh_perm_copy", "absh_permute", "absh_unpermute", "absh_pool", "absh_block_scores",
+    "absh_route_workspace_bytes", "absh_route", "absh_sparse_attn",
+)
+
+
+class AbshError(RuntimeError):
+    """A non-OK status from the library; .status holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class RouteOpts(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_double), ("k_floor", ctypes.c_int32), ("slack_frac", ctypes.c_double),
+                ("lpt", ctypes.c_int32), ("order_depth", ctypes.c_int32)]
+
+
+class Lists(ctypes.Structure):
+    _fields_ = [("counts", ctypes.c_void_p), ("kv_idx", ctypes.c_void_p), ("order", ctypes.c_void_p),
+                ("work", ctypes.c_void_p), ("L", ctypes.c_void_p), ("queue", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libabsh.so (built in-tree by build.py); raises if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "absh_version": ([], i),
+        "absh_status_string": ([i], ctypes.c_char_p),
+        "absh_last_error": ([], ctypes.c_char_p),
+        "absh_create": ([ctypes.POINTER(vp), i, i, i, i, i, vp], i),
+        "absh_destroy": ([vp], i),
+        "absh_dims": ([vp, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)], i),
+        "absh_perm": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp)], i),
+        "absh_perm_copy": ([vp, vp, vp, vp], i),
+        "absh_permute": ([vp, vp, i, vp, i, i, i, i, vp], i),
+        "absh_unpermute": ([vp, vp, vp, i, i, i, vp], i),
+        "absh_pool": ([vp, vp, vp, i, i, i, vp], i),
+        "absh_block_scores": ([vp, vp, vp, vp, i, i, i, vp], i),
+        "absh_route_workspace_bytes": ([vp, i, i, i], sz),
+        "absh_route": ([vp, vp, vp, i, i, i, ctypes.POINTER(RouteOpts), ctypes.POINTER(Lists), vp, sz, vp], i),
+        "absh_sparse_attn": ([vp, vp, vp, vp, i, i, i, ctypes.POINTER(Lists), vp, vp], i),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise AbshError(status, f"{L.absh_status_string(status).decode()}: {L.absh_last_error().decode()}")
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+class Context:
+    """One (T, Y, X) grid and block size on one device; owns the Hilbert permutation."""
+
+    def __init__(self, T: int, Y: int, X: int, block: int, device: int = 0, stream=None):
+        self._h = ctypes.c_void_p()
+        s = _stream(stream) if stream is not None else ctypes.c_void_p(0)
+        _check(lib().absh_create(ctypes.byref(self._h), T, Y, X, block, device, s))
+        self.T, self.Y, self.X, self.block, self.device = T, Y, X, block, device
+        N, nb, n_pad = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        _check(lib().absh_dims(self._h, ctypes.byref(N), ctypes.byref(nb), ctypes.byref(n_pad)))
+        self.N, self.nb, self.n_pad = N.value, nb.value, n_pad.value
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    def close(self) -> None:
+        if self._h:
+            _check(lib().absh_destroy(self._h))
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            if self._h and _lib is not None:
+                _lib.absh_destroy(self._h)
+        except Exception:
+            pass
+
+
+def create(T: int, Y: int, X: int, block: int, device: int = 0, stream=None) -> Context:
+    return Context(T, Y, X, block, device, stream)
+
+
+def _dev(ctx: Context):
+    import torch
+    return torch.device("cuda", ctx.device)
+
+
+def perm_copy(ctx: Context, stream=None):
+    """(perm, inv) as int32 device tensors (copies of the context's arrays)."""
+    import torch
+    perm = torch.empty(ctx.N, dtype=torch.int32, device=_dev(ctx))
+    inv = torch.empty(ctx.N, dtype=torch.int32, device=_dev(ctx))
+    _check(lib().absh_perm_copy(ctx.handle, _ptr(perm), _ptr(inv), _stream(stream)))
+    return perm, inv
+
+
+def permute(ctx: Context, x, layout: int = ABSH_ROWS, out=None, stream=None):
+    """x [B, N, H, d] (bf16 or f32, grid order) -> bf16 Hilbert-order tensor in `layout`."""
+    import torch
+    B, N, H, d = x.shape
+    assert N == ctx.N and x.is_contiguous() and x.dtype in (torch.bfloat16, torch.float32)
+    xt = ABSH_F32 if x.dtype == torch.float32 else ABSH_BF16
+    if out is None:
+        shape = (B, H, ctx.n_pad, d) if layout == ABSH_ROWS else (B, H, ctx.nb, d, ctx.block)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=x.device)
+    _check(lib().absh_permute(ctx.handle, _ptr(x), xt, _ptr(out), B, H, d, layout, _stream(stream)))
+    return out
+
+
+def unpermute(ctx: Context, oh, out=None, stream=None):
+    """oh [B, H, n_pad, d] bf16 (Hilbert order) -> o [B, N, H, d] bf16 (grid order)."""
+    import torch
+    B, H, n_pad, d = oh.shape
+    assert n_pad == ctx.n_pad and oh.dtype == torch.bfloat16 and oh.is_contiguous()
+    if out is None:
+        out = torch.empty((B, ctx.N, H, d), dtype=torch.bfloat16, device=oh.device)
+    _check(lib().absh_unpermute(ctx.handle, _ptr(oh), _ptr(out), B, H, d, _stream(stream)))
+    return out
+
+
+def pool(ctx: Context, xh, out=None, stream=None):
+    """Block means of a Hilbert-order tensor [B, H, n_pad, d] -> float32 [B, H, nb, d]."""
+    import torch
+    B, H, n_pad, d = xh.shape
+    if out is None:
+        out = torch.empty((B, H, ctx.nb, d), dtype=torch.float32, device=xh.device)
+    _check(lib().absh_pool(ctx.handle, _ptr(xh), _ptr(out), B, H, d, _stream(stream)))
+    return out
+
+
+def block_scores(ctx: Context, qbar, kbar, out=None, stream=None):
+    """float32 block scores [B, H, nb, nb] from block means."""
+    import torch
+    B, H, nb, d = qbar.shape
+    if out is None:
+        out = torch.empty((B, H, nb, nb), dtype=torch.float32, device=qbar.device)
+    _check(lib().absh_block_scores(ctx.handle, _ptr(qbar), _ptr(kbar), _ptr(out), B, H, d, _stream(stream)))
+    return out
+
+
+@dataclass
+class Routing:
+    counts: object   # int32 [B, H, nb]
+    kv_idx: object   # int32 [B, H, nb, nb]
+    order: Optional[object]  # int32 [B, H, nb, depth] or None
+    work: object     # int32 [B, H]
+    L: object        # float32 [B, H]
+    queue: object    # int32 [B*H*nb]
+
+    def lists(self) -> Lists:
+        return Lists(self.counts.data_ptr(), self.kv_idx.data_ptr(),
+                     self.order.data_ptr() if self.order is not None else 0,
+                     self.work.data_ptr(), self.L.data_ptr(), self.queue.data_ptr())
+
+
+def route_workspace_bytes(ctx: Context, B: int, H: int, d: int) -> int:
+    return int(lib().absh_route_workspace_bytes(ctx.handle, B, H, d))
+
+
+def alloc_routing(ctx: Context, B: int, H: int, order_depth: int = 0) -> Routing:
+    import torch
+    dev = _dev(ctx)
+    nb = ctx.nb
+    return Routing(
+        counts=torch.empty((B, H, nb), dtype=torch.int32, device=dev),
+        kv_idx=torch.empty((B, H, nb, nb), dtype=torch.int32, device=dev),
+        order=torch.empty((B, H, nb, order_depth), dtype=torch.int32, device=dev) if order_depth else None,
+        work=torch.empty((B, H), dtype=torch.int32, device=dev),
+        L=torch.empty((B, H), dtype=torch.float32, device=dev),
+        queue=torch.empty((B * H * nb,), dtype=torch.int32, device=dev),
+    )
+
+
+def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0, lpt: bool = True,
+          order_depth: int = 0, out: Optional[Routing] = None, workspace=None, stream=None) -> Routing:
+    """Stage-1 routing of Hilbert-order qh, kh [B, H, n_pad, d] bf16 -> Routing (device tensors)."""
+    import torch
+    B, H, n_pad, d = qh.shape
+    if out is None:
+        out = alloc_routing(ctx, B, H, order_depth)
+    need = route_workspace_bytes(ctx, B, H, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=qh.device)
+    opts = RouteOpts(float(p), int(k_floor), float(slack_frac), int(bool(lpt)), int(order_depth))
+    lists = out.lists()
+    _check(lib().absh_route(ctx.handle, _ptr(qh), _ptr(kh), B, H, d, ctypes.byref(opts), ctypes.byref(lists),
+                            _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return out
+
+
+def sparse_attn(ctx: Context, qh, kh, vt, routing: Optional[Routing] = None, out=None, stream=None):
+    """Block-sparse attention (routing=None: dense) -> oh [B, H, n_pad, d] bf16 in Hilbert order."""
+    import torch
+    B, H, n_pad, d = qh.shape
+    if out is None:
+        out = torch.empty_like(qh)
+    lists = routing.lists() if routing is not None else None
+    _check(lib().absh_sparse_attn(ctx.handle, _ptr(qh), _ptr(kh), _ptr(vt), B, H, d,
+                                  ctypes.byref(lists) if lists is not None else None, _ptr(out), _stream(stream)))
+    return out

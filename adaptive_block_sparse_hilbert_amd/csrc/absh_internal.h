@@ -1,0 +1,65 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/absh.h"
+
+struct absh_ctx {
+  int T, Y, X, block;
+  int N, nb, n_pad;
+  int m;        // bits per axis of the enclosing Hilbert cube
+  int device;
+  int32_t* perm;  // [N] grid index of the r-th token in Hilbert order
+  int32_t* inv;   // [N] Hilbert position of grid token n
+};
+
+namespace absh {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+// Round a float to bfloat16, nearest-even (inputs are finite).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Launchers (each returns hipGetLastError() of its launches).
+int hilbert_chunks(int m);
+hipError_t launch_hilbert_perm(const absh_ctx* c, int32_t* chunk_counts, int chunks, hipStream_t s);
+hipError_t launch_permute(const absh_ctx* c, const void* x, int x_is_f32, void* xh, int B, int H, int d,
+                          int layout_vt, hipStream_t s);
+hipError_t launch_unpermute(const absh_ctx* c, const void* oh, void* o, int B, int H, int d, hipStream_t s);
+hipError_t launch_pool(const absh_ctx* c, const void* xh, float* xbar, int B, int H, int d, hipStream_t s);
+hipError_t launch_scores(const absh_ctx* c, const float* qbar, const float* kbar, float* S, int BH, int d,
+                         hipStream_t s);
+
+struct RouteBuffers {
+  const float* S;     // [tiles][nb] block scores
+  int32_t* counts;
+  int32_t* kv_idx;
+  int32_t* order;
+  int32_t* work;
+  float* L;
+  int32_t* queue;
+  int32_t* target;      // [tiles] slack-fill target counts
+  int64_t* slack_info;  // [4] lambda, remainder, E, total
+  int32_t* chunk_hist;  // [chunks][nb + 1]
+  int32_t* rank;        // [tiles]
+};
+hipError_t launch_select(const absh_ctx* c, const RouteBuffers& rb, int tiles, double p, int k_floor,
+                         int order_depth, int reselect, hipStream_t s);
+hipError_t launch_slack_plan(const absh_ctx* c, const RouteBuffers& rb, int tiles, double beta, hipStream_t s);
+hipError_t launch_workload(const absh_ctx* c, const RouteBuffers& rb, int BH, hipStream_t s);
+hipError_t launch_queue(const absh_ctx* c, const RouteBuffers& rb, int tiles, int lpt, hipStream_t s);
+int queue_chunks(int tiles);
+
+hipError_t launch_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B,
+                            int H, int d, const int32_t* queue, const int32_t* counts, const int32_t* kv_idx,
+                            hipStream_t s);
+
+}  // namespace absh

@@ -1,0 +1,327 @@
+// C ABI of the library: argument validation (always before any HIP call),
+// workspace layout, and the launch sequence of each entry point on the caller's
+// stream. See include/absh.h for the contract of every function.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "absh_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+absh_status fail(absh_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+absh_status hip_fail(hipError_t e, const char* where) {
+  return fail(ABSH_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define ABSH_HIP(call, where)                     \
+  do {                                            \
+    hipError_t e_ = (call);                       \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxNb = 2048;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+absh_status use_device(const absh_ctx* c) {
+  int cur = -1;
+  ABSH_HIP(hipGetDevice(&cur), "hipGetDevice");
+  if (cur != c->device) ABSH_HIP(hipSetDevice(c->device), "hipSetDevice");
+  return ABSH_OK;
+}
+
+absh_status check_ctx(const absh_ctx* c) {
+  if (!c) return fail(ABSH_EINVAL, "ctx is NULL");
+  return ABSH_OK;
+}
+
+absh_status check_shape(const absh_ctx* c, int B, int H, int d) {
+  if (B < 1 || H < 1) return fail(ABSH_EINVAL, "B and H must be >= 1 (got B=%d H=%d)", B, H);
+  if (d != 64 && d != 128) return fail(ABSH_EUNSUPPORTED, "head dim %d not built (64 or 128)", d);
+  const double rows = (double)B * H * c->n_pad * d;
+  if (rows >= 9.0e18) return fail(ABSH_EINVAL, "tensor too large");
+  if ((double)B * H * c->nb >= 2147483647.0) return fail(ABSH_EINVAL, "B*H*nb must fit in int32");
+  return ABSH_OK;
+}
+
+// Byte offsets of the route workspace regions.
+struct WsLayout {
+  size_t qbar, kbar, S, target, info, chunk_hist, rank, total;
+};
+
+WsLayout ws_layout(const absh_ctx* c, int B, int H, int d) {
+  const size_t tiles = (size_t)B * H * c->nb;
+  WsLayout w;
+  size_t off = 0;
+  w.qbar = off; off = align_up(off + tiles * d * sizeof(float));
+  w.kbar = off; off = align_up(off + tiles * d * sizeof(float));
+  w.S = off; off = align_up(off + tiles * c->nb * sizeof(float));
+  w.target = off; off = align_up(off + tiles * sizeof(int32_t));
+  w.info = off; off = align_up(off + 4 * sizeof(int64_t));
+  w.chunk_hist = off; off = align_up(off + (size_t)absh::queue_chunks((int)tiles) * (c->nb + 1) * sizeof(int32_t));
+  w.rank = off; off = align_up(off + tiles * sizeof(int32_t));
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int absh_version(void) { return 100; }
+
+const char* absh_status_string(int status) {
+  switch (status) {
+    case ABSH_OK: return "ABSH_OK";
+    case ABSH_EINVAL: return "ABSH_EINVAL";
+    case ABSH_EUNSUPPORTED: return "ABSH_EUNSUPPORTED";
+    case ABSH_EWORKSPACE: return "ABSH_EWORKSPACE";
+    case ABSH_ENODEV: return "ABSH_ENODEV";
+    case ABSH_EHIP: return "ABSH_EHIP";
+    default: return "ABSH_UNKNOWN";
+  }
+}
+
+const char* absh_last_error(void) { return g_last_error.c_str(); }
+
+absh_status absh_create(absh_ctx** out, int T, int Y, int X, int block, int device, void* stream) {
+  g_last_error.clear();
+  if (!out) return fail(ABSH_EINVAL, "ctx output pointer is NULL");
+  *out = nullptr;
+  if (T < 1 || Y < 1 || X < 1) return fail(ABSH_EINVAL, "grid extents must be >= 1 (got %d x %d x %d)", T, Y, X);
+  if (block != 16 && block != 64 && block != 128)
+    return fail(ABSH_EUNSUPPORTED, "block size %d not built (16, 64 or 128)", block);
+  const long long N = (long long)T * Y * X;
+  if (N > (1LL << 30)) return fail(ABSH_EINVAL, "grid too large (%lld tokens)", N);
+  int m = 1;
+  while ((1 << m) < T || (1 << m) < Y || (1 << m) < X) ++m;
+  if (m > 10) return fail(ABSH_EINVAL, "grid extent above 1024 along an axis");
+  if (device < 0) return fail(ABSH_EINVAL, "device index %d < 0", device);
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) {
+    (void)hipGetLastError();
+    return fail(ABSH_ENODEV, "no HIP device available");
+  }
+  if (device >= ndev) return fail(ABSH_ENODEV, "device %d does not exist (%d present)", device, ndev);
+  ABSH_HIP(hipSetDevice(device), "hipSetDevice");
+
+  absh_ctx* c = new (std::nothrow) absh_ctx();
+  if (!c) return fail(ABSH_EINVAL, "out of host memory");
+  c->T = T; c->Y = Y; c->X = X; c->block = block;
+  c->N = (int)N;
+  c->nb = (int)((N + block - 1) / block);
+  c->n_pad = c->nb * block;
+  c->m = m;
+  c->device = device;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int chunks = absh::hilbert_chunks(m);
+  int32_t* chunk_counts = nullptr;
+  hipError_t e = hipMalloc(&c->perm, sizeof(int32_t) * N);
+  if (e == hipSuccess) e = hipMalloc(&c->inv, sizeof(int32_t) * N);
+  if (e == hipSuccess) e = hipMalloc(&chunk_counts, sizeof(int32_t) * chunks);
+  if (e == hipSuccess) e = absh::launch_hilbert_perm(c, chunk_counts, chunks, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (chunk_counts) (void)hipFree(chunk_counts);
+  if (e != hipSuccess) {
+    absh_status st = hip_fail(e, "absh_create");
+    if (c->perm) (void)hipFree(c->perm);
+    if (c->inv) (void)hipFree(c->inv);
+    delete c;
+    return st;
+  }
+  *out = c;
+  return ABSH_OK;
+}
+
+absh_status absh_destroy(absh_ctx* c) {
+  g_last_error.clear();
+  if (!c) return ABSH_OK;
+  absh_status st = use_device(c);
+  if (st == ABSH_OK) {
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) st = hip_fail(e, "absh_destroy");
+  }
+  if (c->perm) (void)hipFree(c->perm);
+  if (c->inv) (void)hipFree(c->inv);
+  delete c;
+  return st;
+}
+
+absh_status absh_dims(const absh_ctx* c, int* N, int* nb, int* n_pad) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (N) *N = c->N;
+  if (nb) *nb = c->nb;
+  if (n_pad) *n_pad = c->n_pad;
+  return ABSH_OK;
+}
+
+absh_status absh_perm(const absh_ctx* c, const int32_t** perm, const int32_t** inv) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (perm) *perm = c->perm;
+  if (inv) *inv = c->inv;
+  return ABSH_OK;
+}
+
+absh_status absh_perm_copy(const absh_ctx* c, int32_t* perm_dst, int32_t* inv_dst, void* stream) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (absh_status st = use_device(c)) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t bytes = sizeof(int32_t) * c->N;
+  if (perm_dst) ABSH_HIP(hipMemcpyAsync(perm_dst, c->perm, bytes, hipMemcpyDeviceToDevice, s), "absh_perm_copy");
+  if (inv_dst) ABSH_HIP(hipMemcpyAsync(inv_dst, c->inv, bytes, hipMemcpyDeviceToDevice, s), "absh_perm_copy");
+  return ABSH_OK;
+}
+
+absh_status absh_permute(absh_ctx* c, const void* x, absh_dtype xt, void* xh, int B, int H, int d,
+                         absh_layout layout, void* stream) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (absh_status st = check_shape(c, B, H, d)) return st;
+  if (!x || !xh) return fail(ABSH_EINVAL, "x or xh is NULL");
+  if (xt != ABSH_BF16 && xt != ABSH_F32) return fail(ABSH_EINVAL, "unknown dtype %d", (int)xt);
+  if (layout != ABSH_ROWS && layout != ABSH_VT) return fail(ABSH_EINVAL, "unknown layout %d", (int)layout);
+  if (!aligned16(x) || !aligned16(xh)) return fail(ABSH_EINVAL, "x and xh must be 16-byte aligned");
+  if (absh_status st = use_device(c)) return st;
+  ABSH_HIP(absh::launch_permute(c, x, xt == ABSH_F32, xh, B, H, d, layout == ABSH_VT,
+                                reinterpret_cast<hipStream_t>(stream)),
+           "absh_permute");
+  return ABSH_OK;
+}
+
+absh_status absh_unpermute(absh_ctx* c, const void* oh, void* o, int B, int H, int d, void* stream) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (absh_status st = check_shape(c, B, H, d)) return st;
+  if (!oh || !o) return fail(ABSH_EINVAL, "oh or o is NULL");
+  if (!aligned16(oh) || !aligned16(o)) return fail(ABSH_EINVAL, "oh and o must be 16-byte aligned");
+  if (absh_status st = use_device(c)) return st;
+  ABSH_HIP(absh::launch_unpermute(c, oh, o, B, H, d, reinterpret_cast<hipStream_t>(stream)), "absh_unpermute");
+  return ABSH_OK;
+}
+
+absh_status absh_pool(absh_ctx* c, const void* xh, float* xbar, int B, int H, int d, void* stream) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (absh_status st = check_shape(c, B, H, d)) return st;
+  if (!xh || !xbar) return fail(ABSH_EINVAL, "xh or xbar is NULL");
+  if (absh_status st = use_device(c)) return st;
+  ABSH_HIP(absh::launch_pool(c, xh, xbar, B, H, d, reinterpret_cast<hipStream_t>(stream)), "absh_pool");
+  return ABSH_OK;
+}
+
+absh_status absh_block_scores(absh_ctx* c, const float* qbar, const float* kbar, float* s, int B, int H, int d,
+                              void* stream) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (absh_status st = check_shape(c, B, H, d)) return st;
+  if (!qbar || !kbar || !s) return fail(ABSH_EINVAL, "qbar, kbar or s is NULL");
+  if (!aligned16(qbar) || !aligned16(kbar)) return fail(ABSH_EINVAL, "qbar and kbar must be 16-byte aligned");
+  if (absh_status st = use_device(c)) return st;
+  ABSH_HIP(absh::launch_scores(c, qbar, kbar, s, B * H, d, reinterpret_cast<hipStream_t>(stream)),
+           "absh_block_scores");
+  return ABSH_OK;
+}
+
+size_t absh_route_workspace_bytes(const absh_ctx* c, int B, int H, int d) {
+  if (!c || B < 1 || H < 1 || d < 1) return 0;
+  return ws_layout(c, B, H, d).total;
+}
+
+absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H, int d,
+                       const absh_route_opts* opts, const absh_lists* out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (absh_status st = check_shape(c, B, H, d)) return st;
+  if (!qh || !kh) return fail(ABSH_EINVAL, "qh or kh is NULL");
+  if (!opts || !out) return fail(ABSH_EINVAL, "opts or out is NULL");
+  if (!(opts->p > 0.0 && opts->p <= 1.0)) return fail(ABSH_EINVAL, "p must lie in (0, 1] (got %g)", opts->p);
+  if (opts->k_floor < 0) return fail(ABSH_EINVAL, "k_floor must be >= 0 (got %d)", opts->k_floor);
+  if (!(opts->slack_frac >= 0.0 && opts->slack_frac < 1.0))
+    return fail(ABSH_EINVAL, "slack_frac must lie in [0, 1) (got %g)", opts->slack_frac);
+  if (opts->order_depth < 0 || opts->order_depth > 64)
+    return fail(ABSH_EINVAL, "order_depth must lie in [0, 64] (got %d)", opts->order_depth);
+  if (!out->counts || !out->kv_idx || !out->work || !out->L || !out->queue)
+    return fail(ABSH_EINVAL, "counts, kv_idx, work, L and queue must be non-NULL");
+  if (opts->order_depth > 0 && !out->order) return fail(ABSH_EINVAL, "order is NULL but order_depth > 0");
+  if (c->nb > kMaxNb) return fail(ABSH_EUNSUPPORTED, "nb = %d above the router's %d", c->nb, kMaxNb);
+  const WsLayout w = ws_layout(c, B, H, d);
+  if (!ws) return fail(ABSH_EWORKSPACE, "workspace is NULL (%zu bytes needed)", w.total);
+  if (ws_bytes < w.total) return fail(ABSH_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, w.total);
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+    return fail(ABSH_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+  if (absh_status st = use_device(c)) return st;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = reinterpret_cast<char*>(ws);
+  float* qbar = reinterpret_cast<float*>(base + w.qbar);
+  float* kbar = reinterpret_cast<float*>(base + w.kbar);
+  absh::RouteBuffers rb;
+  rb.S = reinterpret_cast<float*>(base + w.S);
+  rb.counts = out->counts;
+  rb.kv_idx = out->kv_idx;
+  rb.order = out->order;
+  rb.work = out->work;
+  rb.L = out->L;
+  rb.queue = out->queue;
+  rb.target = reinterpret_cast<int32_t*>(base + w.target);
+  rb.slack_info = reinterpret_cast<int64_t*>(base + w.info);
+  rb.chunk_hist = reinterpret_cast<int32_t*>(base + w.chunk_hist);
+  rb.rank = reinterpret_cast<int32_t*>(base + w.rank);
+  const int tiles = B * H * c->nb;
+
+  ABSH_HIP(absh::launch_pool(c, qh, qbar, B, H, d, s), "absh_route: pool q");
+  ABSH_HIP(absh::launch_pool(c, kh, kbar, B, H, d, s), "absh_route: pool k");
+  ABSH_HIP(absh::launch_scores(c, qbar, kbar, const_cast<float*>(rb.S), B * H, d, s), "absh_route: scores");
+  ABSH_HIP(absh::launch_select(c, rb, tiles, opts->p, opts->k_floor, opts->order_depth, 0, s),
+           "absh_route: select");
+  if (opts->slack_frac > 0.0) {
+    ABSH_HIP(absh::launch_slack_plan(c, rb, tiles, opts->slack_frac, s), "absh_route: slack plan");
+    ABSH_HIP(absh::launch_select(c, rb, tiles, opts->p, opts->k_floor, 0, 1, s), "absh_route: slack fill");
+  }
+  ABSH_HIP(absh::launch_workload(c, rb, B * H, s), "absh_route: workload");
+  ABSH_HIP(absh::launch_queue(c, rb, tiles, opts->lpt != 0, s), "absh_route: queue");
+  return ABSH_OK;
+}
+
+absh_status absh_sparse_attn(absh_ctx* c, const void* qh, const void* kh, const void* vt, int B, int H, int d,
+                             const absh_lists* lists, void* oh, void* stream) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (absh_status st = check_shape(c, B, H, d)) return st;
+  if (!qh || !kh || !vt || !oh) return fail(ABSH_EINVAL, "qh, kh, vt or oh is NULL");
+  if (!aligned16(qh) || !aligned16(kh) || !aligned16(vt) || !aligned16(oh))
+    return fail(ABSH_EINVAL, "qh, kh, vt and oh must be 16-byte aligned");
+  if (lists && (!lists->counts || !lists->kv_idx || !lists->queue))
+    return fail(ABSH_EINVAL, "lists needs counts, kv_idx and queue");
+  if (absh_status st = use_device(c)) return st;
+  ABSH_HIP(absh::launch_attention(c, qh, kh, vt, oh, B, H, d, lists ? lists->queue : nullptr,
+                                  lists ? lists->counts : nullptr, lists ? lists->kv_idx : nullptr,
+                                  reinterpret_cast<hipStream_t>(stream)),
+           "absh_sparse_attn");
+  return ABSH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+// Gather between grid order and Hilbert order (the reordering half of the
+// xllm-io review's Stage 1, "Hilbert curve block reordering").
+//
+// All three kernels move whole 16-byte pieces of rows, so every wave reads and
+// writes contiguous runs of at least d*2 bytes (one token's row of one head).
+#include "absh_internal.h"
+
+namespace absh {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct alignas(16) Pack8 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Pack8 load8(const void* base, size_t elem, int is_f32) {
+  Pack8 out;
+  if (is_f32) {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
+    const float4 a = p[0], b = p[1];
+    out.w[0] = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
+    out.w[1] = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
+    out.w[2] = (uint32_t)f32_to_bf16(b.x) | ((uint32_t)f32_to_bf16(b.y) << 16);
+    out.w[3] = (uint32_t)f32_to_bf16(b.z) | ((uint32_t)f32_to_bf16(b.w) << 16);
+  } else {
+    out = *reinterpret_cast<const Pack8*>(reinterpret_cast<const bf16_t*>(base) + elem);
+  }
+  return out;
+}
+
+// xh[b, h, r, :] = x[b, perm[r], h, :] for r < N, zero for N <= r < n_pad.
+// One thread per 8 output elements; consecutive threads cover one row, then the
+// next Hilbert position of the same head.
+__global__ __launch_bounds__(kThreads) void gather_rows(const void* __restrict__ x, int is_f32,
+                                                        bf16_t* __restrict__ xh, const int32_t* __restrict__ perm,
+                                                        int N, int n_pad, int H, int d, uint64_t pieces) {
+  const uint64_t id = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (id >= pieces) return;
+  const int per_row = d >> 3;
+  const int e = (int)(id % per_row);
+  const uint64_t row = id / per_row;          // (b*H + h)*n_pad + r
+  const int r = (int)(row % n_pad);
+  const uint64_t bh = row / n_pad;
+  const int h = (int)(bh % H);
+  const uint64_t b = bh / H;
+  Pack8 v = {{0u, 0u, 0u, 0u}};
+  if (r < N) v = load8(x, ((b * N + perm[r]) * H + h) * d + (size_t)e * 8, is_f32);
+  *reinterpret_cast<Pack8*>(xh + row * d + (size_t)e * 8) = v;
+}
+
+// vt[b, h, j, c, k] = x[b, perm[j*blk + k], h, c]: one workgroup per (b, h, j)
+// stages the block's rows in LDS and writes them back transposed.
+template <int D, int BLK>
+__global__ __launch_bounds__(kThreads) void gather_vt(const void* __restrict__ x, int is_f32,
+                                                      bf16_t* __restrict__ vt, const int32_t* __restrict__ perm,
+                                                      int N, int nb, int H) {
+  constexpr int kStride = BLK + 2;  // keys per LDS row (+2 breaks bank aliasing of the column writes)
+  __shared__ bf16_t tile[D * kStride];
+  const int j = blockIdx.x % nb;
+  const uint64_t bh = blockIdx.x / nb;
+  const int h = (int)(bh % H);
+  const uint64_t b = bh / H;
+  // Load: piece p = (key k, 8 channels starting at c8*8).
+  for (int p = threadIdx.x; p < BLK * (D / 8); p += kThreads) {
+    const int k = p / (D / 8);
+    const int c8 = p % (D / 8);
+    const int r = j * BLK + k;
+    Pack8 v = {{0u, 0u, 0u, 0u}};
+    if (r < N) v = load8(x, ((b * N + perm[r]) * H + h) * D + (size_t)c8 * 8, is_f32);
+    const bf16_t* vv = reinterpret_cast<const bf16_t*>(&v);
+    for (int q = 0; q < 8; ++q) tile[(c8 * 8 + q) * kStride + k] = vv[q];
+  }
+  __syncthreads();
+  // Store: piece p = (channel c, 8 keys starting at k8*8).
+  bf16_t* out = vt + (bh * nb + j) * (size_t)(D * BLK);
+  for (int p = threadIdx.x; p < D * (BLK / 8); p += kThreads) {
+    const int c = p / (BLK / 8);
+    const int k8 = p % (BLK / 8);
+    Pack8 v;
+    bf16_t* vv = reinterpret_cast<bf16_t*>(&v);
+    for (int q = 0; q < 8; ++q) vv[q] = tile[c * kStride + k8 * 8 + q];
+    *reinterpret_cast<Pack8*>(out + (size_t)c * BLK + k8 * 8) = v;
+  }
+}
+
+// o[b, n, h, :] = oh[b, h, inv[n], :]: one thread per 8 output elements.
+__global__ __launch_bounds__(kThreads) void scatter_rows(const bf16_t* __restrict__ oh, bf16_t* __restrict__ o,
+                                                         const int32_t* __restrict__ inv, int N, int n_pad, int H,
+                                                         int d, uint64_t pieces) {
+  const uint64_t id = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (id >= pieces) return;
+  const int per_row = d >> 3;
+  const int e = (int)(id % per_row);
+  const uint64_t row = id / per_row;  // (b*N + n)*H + h
+  const int h = (int)(row % H);
+  const uint64_t bn = row / H;
+  const int n = (int)(bn % N);
+  const uint64_t b = bn / N;
+  const Pack8 v = *reinterpret_cast<const Pack8*>(oh + ((b * H + h) * n_pad + inv[n]) * d + (size_t)e * 8);
+  *reinterpret_cast<Pack8*>(o + row * d + (size_t)e * 8) = v;
+}
+
+template <int D, int BLK>
+void launch_vt(const void* x, int is_f32, bf16_t* vt, const int32_t* perm, int N, int nb, int H, int B,
+               hipStream_t s) {
+  gather_vt<D, BLK><<<(unsigned)((uint64_t)B * H * nb), kThreads, 0, s>>>(x, is_f32, vt, perm, N, nb, H);
+}
+
+}  // namespace
+
+hipError_t launch_permute(const absh_ctx* c, const void* x, int x_is_f32, void* xh, int B, int H, int d,
+                          int layout_vt, hipStream_t s) {
+  bf16_t* out = reinterpret_cast<bf16_t*>(xh);
+  if (!layout_vt) {
+    const uint64_t pieces = (uint64_t)B * H * c->n_pad * (d / 8);
+    const unsigned grid = (unsigned)((pieces + kThreads - 1) / kThreads);
+    gather_rows<<<grid, kThreads, 0, s>>>(x, x_is_f32, out, c->perm, c->N, c->n_pad, H, d, pieces);
+    return hipGetLastError();
+  }
+#define ABSH_VT_CASE(DD, BB)                                                  \
+  if (d == DD && c->block == BB) {                                            \
+    launch_vt<DD, BB>(x, x_is_f32, out, c->perm, c->N, c->nb, H, B, s);       \
+    return hipGetLastError();                                                 \
+  }
+  ABSH_VT_CASE(64, 16)
+  ABSH_VT_CASE(64, 64)
+  ABSH_VT_CASE(64, 128)
+  ABSH_VT_CASE(128, 16)
+  ABSH_VT_CASE(128, 64)
+  ABSH_VT_CASE(128, 128)
+#undef ABSH_VT_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_unpermute(const absh_ctx* c, const void* oh, void* o, int B, int H, int d, hipStream_t s) {
+  const uint64_t pieces = (uint64_t)B * c->N * H * (d / 8);
+  const unsigned grid = (unsigned)((pieces + kThreads - 1) / kThreads);
+  scatter_rows<<<grid, kThreads, 0, s>>>(reinterpret_cast<const bf16_t*>(oh), reinterpret_cast<bf16_t*>(o), c->inv,
+                                         c->N, c->n_pad, H, d, pieces);
+  return hipGetLastError();
+}
+
+}  // namespace absh

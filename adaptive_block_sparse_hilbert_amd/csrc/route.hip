@@ -1,0 +1,502 @@
+// Stage-1 routing kernels (xllm-io review of FVAttn, section 三 Stage 1 and 3.1;
+// alanhou.org explainer of FVAttn, "Key Concepts": Top-p with a Top-k floor),
+// the Eq. 1 workloads, and the one-GPU runtime stages: a slack fill over tiles
+// (the review's SASA steps, read for one GPU) and a longest-first tile queue
+// (the review's RLB, read for one GPU).
+//
+// Precision: a routing decision is an integer decided by floating point, so it
+// is taken in a precision the checker can reproduce exactly: block means are
+// float64 sums of bf16 rows (exact) divided in float64 and rounded to float32;
+// scores are float64 dot products rounded to float32; the softmax, cumulative
+// sums and the comparison with p are float64.
+#include <math.h>
+
+#include "absh_internal.h"
+
+namespace absh {
+namespace {
+
+// ------------------------------------------------------------------ pooling
+
+// xbar[bh, j, c] = (sum over the block's true rows of xh[bh, r, c]) / n_j.
+// One workgroup per (bh, j); one thread per channel.
+__global__ __launch_bounds__(128) void pool_kernel(const bf16_t* __restrict__ xh, float* __restrict__ xbar, int N,
+                                                   int n_pad, int nb, int blk, int d) {
+  const int j = blockIdx.x % nb;
+  const uint64_t bh = blockIdx.x / nb;
+  const int c = threadIdx.x;
+  if (c >= d) return;
+  const int r0 = j * blk;
+  const int n = min(blk, N - r0);
+  const bf16_t* src = xh + (bh * n_pad + r0) * d + c;
+  double acc = 0.0;
+  for (int r = 0; r < n; ++r) acc += (double)bf16_to_f32(src[(size_t)r * d]);
+  xbar[(bh * nb + j) * d + c] = __double2float_rn(acc / (double)n);
+}
+
+// ------------------------------------------------------------------ scores
+
+// S[bh, i, j] = float32( sum_c double(qbar[bh,i,c]) * double(kbar[bh,j,c]) / sqrt_d ).
+// 64 x 64 output tile per workgroup, 4 x 4 per thread, channels staged in LDS
+// sixteen at a time as float64.
+constexpr int kTile = 64;
+constexpr int kDepth = 16;
+
+__global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                                     float* __restrict__ S, int nb, int d, double sqrt_d,
+                                                     int tiles_per_side) {
+  __shared__ double qs[kDepth][kTile + 1];
+  __shared__ double ks[kDepth][kTile + 1];
+  const int per_head = tiles_per_side * tiles_per_side;
+  const uint64_t bh = blockIdx.x / per_head;
+  const int tile = blockIdx.x % per_head;
+  const int i0 = (tile / tiles_per_side) * kTile;
+  const int j0 = (tile % tiles_per_side) * kTile;
+  const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
+  const float* qb = qbar + bh * nb * (size_t)d;
+  const float* kb = kbar + bh * nb * (size_t)d;
+  double acc[4][4];
+  for (int a = 0; a < 4; ++a)
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  // loader: thread -> (row lr, 4 channels at lc)
+  const int lr = threadIdx.x / 4, lc = (threadIdx.x % 4) * 4;
+  for (int c0 = 0; c0 < d; c0 += kDepth) {
+    float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i0 + lr < nb) qv = *reinterpret_cast<const float4*>(qb + (size_t)(i0 + lr) * d + c0 + lc);
+    if (j0 + lr < nb) kv = *reinterpret_cast<const float4*>(kb + (size_t)(j0 + lr) * d + c0 + lc);
+    qs[lc + 0][lr] = qv.x; qs[lc + 1][lr] = qv.y; qs[lc + 2][lr] = qv.z; qs[lc + 3][lr] = qv.w;
+    ks[lc + 0][lr] = kv.x; ks[lc + 1][lr] = kv.y; ks[lc + 2][lr] = kv.z; ks[lc + 3][lr] = kv.w;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kDepth; ++c) {
+      double a[4], b[4];
+      for (int u = 0; u < 4; ++u) {
+        a[u] = qs[c][ty * 4 + u];
+        b[u] = ks[c][tx * 4 + u];
+      }
+      for (int u = 0; u < 4; ++u)
+        for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+    }
+    __syncthreads();
+  }
+  for (int u = 0; u < 4; ++u) {
+    const int i = i0 + ty * 4 + u;
+    if (i >= nb) continue;
+    for (int v = 0; v < 4; ++v) {
+      const int j = j0 + tx * 4 + v;
+      if (j < nb) S[(bh * nb + i) * (size_t)nb + j] = __double2float_rn(acc[u][v] / sqrt_d);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ Top-p select
+
+__device__ __forceinline__ double wave_sum(double v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t o = __shfl_xor(v, off);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+__device__ __forceinline__ uint64_t lanes_below(int lane) { return lane == 0 ? 0ull : (~0ull >> (64 - lane)); }
+
+// Monotone map of a finite float to uint32 (a < b  <=>  key(a) < key(b)).
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave per tile row. Lane l holds key blocks j = l + 64 t, t < J.
+//
+// The importance order is probability descending, ties by smaller id. A block's
+// probability is exp(s_j - max s) / Z, so for blocks of non-zero probability the
+// order is the order of the scores; blocks whose probability underflows to zero
+// all tie. Each block gets a 32-bit key, larger = more important: 0 for zero
+// probability, else ordered_bits(s_j) + 1. Equal keys then mean equal
+// probabilities, and ties resolve by block id exactly as in the definition.
+//
+// Top-p: the largest key tau whose upper set {key >= tau} carries mass >= p is
+// found bit by bit from the top; the count is #{key > tau} plus as many of the
+// tied blocks at tau (each of the same probability) as the running sum needs to
+// reach p. The floor then asks for count' = max(c, min(k, nb)) blocks, and the
+// retained set is the top count' blocks, found the same way by counting.
+template <int J>
+__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S, int nb, int tiles, double p,
+                                                     int k_floor, int order_depth, int reselect,
+                                                     const int32_t* __restrict__ target, int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ kv_idx, int32_t* __restrict__ order) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= tiles) return;
+  int want = 0;
+  if (reselect) {
+    want = target[row];
+    if (want <= counts[row]) return;
+  }
+  const float* srow = S + (size_t)row * nb;
+  float s[J];
+  bool valid[J];
+#pragma unroll
+  for (int t = 0; t < J; ++t) {
+    const int j = lane + 64 * t;
+    valid[t] = j < nb;
+    s[t] = valid[t] ? srow[j] : -INFINITY;
+  }
+  float smax = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < J; ++t) smax = fmaxf(smax, s[t]);
+  smax = wave_max(smax);
+  double P[J];
+  uint32_t key[J];
+  double z = 0.0;
+#pragma unroll
+  for (int t = 0; t < J; ++t) {
+    P[t] = valid[t] ? exp((double)s[t] - (double)smax) : 0.0;
+    z += P[t];
+  }
+  z = wave_sum(z);
+#pragma unroll
+  for (int t = 0; t < J; ++t) {
+    P[t] = P[t] / z;
+    key[t] = (valid[t] && P[t] != 0.0) ? ordered_bits(s[t]) + 1u : 0u;
+  }
+
+  if (!reselect) {
+    int c = nb;
+    if (p < 1.0) {
+      uint32_t tau = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = tau | (1u << bit);
+        double f = 0.0;
+#pragma unroll
+        for (int t = 0; t < J; ++t) f += (valid[t] && key[t] >= cand) ? P[t] : 0.0;
+        if (wave_sum(f) >= p) tau = cand;
+      }
+      double above = 0.0, at = 0.0, f_tau = 0.0;
+      int n_above = 0, n_at = 0;
+#pragma unroll
+      for (int t = 0; t < J; ++t) {
+        const bool gt = valid[t] && key[t] > tau;
+        const bool eq = valid[t] && key[t] == tau;
+        above += gt ? P[t] : 0.0;
+        at = eq ? P[t] : at;
+        f_tau += (gt || eq) ? P[t] : 0.0;
+        n_above += popc64(__ballot(gt));
+        n_at += popc64(__ballot(eq));
+      }
+      above = wave_sum(above);
+      f_tau = wave_sum(f_tau);
+      // every tied block has the same probability; take it from any lane holding one
+      const uint64_t holders = __ballot(at != 0.0);
+      const double tied = holders ? __shfl(at, __ffsll((long long)holders) - 1) : 0.0;
+      if (f_tau >= p) {
+        int m = 1;
+        double run = above + tied;
+        while (run < p && m < n_at) {
+          run += tied;
+          ++m;
+        }
+        c = n_above + m;
+      }
+    }
+    want = max(c, min(k_floor, nb));
+  }
+
+  // Top-`want` blocks by (key desc, id asc): count search on the key.
+  uint32_t tau = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int t = 0; t < J; ++t) cnt += popc64(__ballot(valid[t] && key[t] >= cand));
+    if (cnt >= want) tau = cand;
+  }
+  int n_above = 0;
+#pragma unroll
+  for (int t = 0; t < J; ++t) n_above += popc64(__ballot(valid[t] && key[t] > tau));
+  const int ties_needed = want - n_above;
+  int32_t* out = kv_idx + (size_t)row * nb;
+  int written = 0, ties_seen = 0;
+  const uint64_t below = lanes_below(lane);
+#pragma unroll
+  for (int t = 0; t < J; ++t) {
+    const bool gt = valid[t] && key[t] > tau;
+    const bool eq = valid[t] && key[t] == tau;
+    const uint64_t eq_mask = __ballot(eq);
+    const bool take = gt || (eq && ties_seen + popc64(eq_mask & below) < ties_needed);
+    const uint64_t take_mask = __ballot(take);
+    if (take) out[written + popc64(take_mask & below)] = lane + 64 * t;
+    written += popc64(take_mask);
+    ties_seen += popc64(eq_mask);
+  }
+  if (lane == 0) counts[row] = want;
+
+  // Importance-order prefix: repeated arg-max of (key, -id) over the blocks not yet taken.
+  if (!reselect && order_depth > 0) {
+    uint32_t taken = 0;
+    int32_t* ord = order + (size_t)row * order_depth;
+    for (int r = 0; r < order_depth; ++r) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int t = 0; t < J; ++t) {
+        if (valid[t] && !(taken & (1u << t))) {
+          const uint64_t cand = ((uint64_t)key[t] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * t));
+          best = cand > best ? cand : best;
+        }
+      }
+      best = wave_max_u64(best);
+      const int j = best ? (int)(0xFFFFFFFFu - (uint32_t)best) : -1;
+      if (j >= 0 && (j & 63) == lane) taken |= 1u << (j >> 6);
+      if (lane == 0) ord[r] = j;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ workloads (Eq. 1)
+
+__global__ __launch_bounds__(256) void workload_kernel(const int32_t* __restrict__ counts, int nb,
+                                                       int32_t* __restrict__ work, float* __restrict__ L) {
+  __shared__ int partial[4];
+  const int32_t* c = counts + (size_t)blockIdx.x * nb;
+  int sum = 0;
+  for (int i = threadIdx.x; i < nb; i += 256) sum += c[i];
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int w = partial[0] + partial[1] + partial[2] + partial[3];
+    work[blockIdx.x] = w;
+    L[blockIdx.x] = __fdiv_rn((float)w, (float)nb);
+  }
+}
+
+// ------------------------------------------------------------------ block-wide scans (1024 threads)
+
+template <typename T>
+__device__ T block_exclusive_scan(T v, T* buf, T& total) {
+  buf[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const T add = threadIdx.x >= (unsigned)off ? buf[threadIdx.x - off] : (T)0;
+    __syncthreads();
+    buf[threadIdx.x] += add;
+    __syncthreads();
+  }
+  const T incl = buf[threadIdx.x];
+  total = buf[1023];
+  __syncthreads();
+  return incl - v;
+}
+
+// ------------------------------------------------------------------ slack fill plan
+
+// One workgroup. E = floor(beta * sum counts) extra blocks; the water level is
+// the largest lambda with need(lambda) = sum_t max(0, lambda - c_t) <= E (tiles
+// at nb never rise); every tile at or below lambda rises to lambda, and the first
+// E - need(lambda) of them by tile id take one more. target[t] is the result.
+constexpr int kMaxBins = 2049;
+
+__global__ __launch_bounds__(1024) void slack_plan_kernel(const int32_t* __restrict__ counts, int tiles, int nb,
+                                                          double beta, int32_t* __restrict__ target,
+                                                          int64_t* __restrict__ info) {
+  __shared__ int32_t hist[kMaxBins];
+  __shared__ int64_t buf[1024];
+  __shared__ int64_t cnt_lt_s[kMaxBins + 1];
+  __shared__ int64_t sum_lt_s[kMaxBins + 1];
+  __shared__ int64_t lam_s, rest_s;
+  for (int b = threadIdx.x; b <= nb; b += 1024) hist[b] = 0;
+  __syncthreads();
+  for (int t = threadIdx.x; t < tiles; t += 1024) atomicAdd(&hist[counts[t]], 1);
+  __syncthreads();
+  // exclusive prefix over bins of hist[c] and c*hist[c]: each thread owns a run of bins
+  const int bins = nb + 1;
+  const int per = (bins + 1023) / 1024;
+  const int b0 = threadIdx.x * per;
+  int64_t my_cnt = 0, my_sum = 0;
+  for (int b = b0; b < min(bins, b0 + per); ++b) {
+    my_cnt += hist[b];
+    my_sum += (int64_t)b * hist[b];
+  }
+  int64_t tot_cnt, tot_sum;
+  int64_t run_cnt = block_exclusive_scan<int64_t>(my_cnt, buf, tot_cnt);
+  int64_t run_sum = block_exclusive_scan<int64_t>(my_sum, buf, tot_sum);
+  for (int b = b0; b < min(bins, b0 + per); ++b) {
+    cnt_lt_s[b] = run_cnt;
+    sum_lt_s[b] = run_sum;
+    run_cnt += hist[b];
+    run_sum += (int64_t)b * hist[b];
+  }
+  __syncthreads();
+  const int64_t E = (int64_t)floor(beta * (double)tot_sum);
+  // need(lambda) = lambda * #(c < lambda) - sum(c < lambda) is non-decreasing: count lambdas with need <= E
+  int64_t ok = 0;
+  for (int lam = threadIdx.x; lam <= nb; lam += 1024) ok += ((int64_t)lam * cnt_lt_s[lam] - sum_lt_s[lam]) <= E;
+  int64_t n_ok;
+  block_exclusive_scan<int64_t>(ok, buf, n_ok);
+  if (threadIdx.x == 0) {
+    const int64_t lam = n_ok - 1;
+    lam_s = lam;
+    rest_s = E - (lam * cnt_lt_s[lam] - sum_lt_s[lam]);
+    info[0] = lam;
+    info[1] = rest_s;
+    info[2] = E;
+    info[3] = tot_sum;
+  }
+  __syncthreads();
+  const int lam = (int)lam_s;
+  const int64_t rest = rest_s;
+  int64_t seen = 0;
+  for (int base = 0; base < tiles; base += 1024) {
+    const int t = base + threadIdx.x;
+    const int c = t < tiles ? counts[t] : nb;
+    const int64_t low = (lam < nb && c <= lam) ? 1 : 0;
+    int64_t chunk_total;
+    const int64_t rank = seen + block_exclusive_scan<int64_t>(low, buf, chunk_total);
+    if (t < tiles) target[t] = lam >= nb ? nb : (low ? lam + (rank < rest ? 1 : 0) : c);
+    seen += chunk_total;
+  }
+}
+
+// ------------------------------------------------------------------ tile queue
+
+constexpr int kQChunk = 256;
+
+__global__ __launch_bounds__(kQChunk) void queue_hist_kernel(const int32_t* __restrict__ counts, int tiles, int nb,
+                                                             int32_t* __restrict__ chunk_hist,
+                                                             int32_t* __restrict__ rank) {
+  __shared__ int32_t c[kQChunk];
+  __shared__ int32_t hist[kMaxBins];
+  const int t = blockIdx.x * kQChunk + threadIdx.x;
+  c[threadIdx.x] = t < tiles ? counts[t] : -1;
+  for (int b = threadIdx.x; b <= nb; b += kQChunk) hist[b] = 0;
+  __syncthreads();
+  if (t < tiles) {
+    const int mine = c[threadIdx.x];
+    int r = 0;
+    for (int u = 0; u < (int)threadIdx.x; ++u) r += c[u] == mine;
+    rank[t] = r;
+    atomicAdd(&hist[mine], 1);
+  }
+  __syncthreads();
+  int32_t* row = chunk_hist + (size_t)blockIdx.x * (nb + 1);
+  for (int b = threadIdx.x; b <= nb; b += kQChunk) row[b] = hist[b];
+}
+
+// Turn per-chunk histograms into output offsets: bins in descending count,
+// chunks (tile-id order) in ascending order within a bin. Thread u owns the
+// bin positions q = nb - b in [u * per, (u + 1) * per).
+__global__ __launch_bounds__(1024) void queue_scan_kernel(int32_t* __restrict__ chunk_hist, int chunks, int nb) {
+  __shared__ int64_t buf[1024];
+  __shared__ int64_t bin_total[kMaxBins];
+  const int bins = nb + 1;
+  const int per = (bins + 1023) / 1024;
+  const int q0 = threadIdx.x * per, q1 = min(bins, q0 + per);
+  int64_t my_total = 0;
+  for (int q = q0; q < q1; ++q) {
+    const int b = nb - q;
+    int64_t off = 0;
+    for (int ch = 0; ch < chunks; ++ch) {
+      int32_t* cell = chunk_hist + (size_t)ch * bins + b;
+      const int32_t v = *cell;
+      *cell = (int32_t)off;
+      off += v;
+    }
+    bin_total[b] = off;
+    my_total += off;
+  }
+  int64_t all;
+  int64_t base = block_exclusive_scan<int64_t>(my_total, buf, all);
+  for (int q = q0; q < q1; ++q) {
+    const int b = nb - q;
+    for (int ch = 0; ch < chunks; ++ch) chunk_hist[(size_t)ch * bins + b] += (int32_t)base;
+    base += bin_total[b];
+  }
+}
+
+__global__ __launch_bounds__(256) void queue_scatter_kernel(const int32_t* __restrict__ counts, int tiles, int nb,
+                                                            const int32_t* __restrict__ chunk_hist,
+                                                            const int32_t* __restrict__ rank,
+                                                            int32_t* __restrict__ queue) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= tiles) return;
+  const int ch = t / kQChunk;
+  queue[chunk_hist[(size_t)ch * (nb + 1) + counts[t]] + rank[t]] = t;
+}
+
+__global__ __launch_bounds__(256) void queue_identity_kernel(int tiles, int32_t* __restrict__ queue) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < tiles) queue[t] = t;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_pool(const absh_ctx* c, const void* xh, float* xbar, int B, int H, int d, hipStream_t s) {
+  pool_kernel<<<(unsigned)((uint64_t)B * H * c->nb), 128, 0, s>>>(reinterpret_cast<const bf16_t*>(xh), xbar, c->N,
+                                                                   c->n_pad, c->nb, c->block, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_scores(const absh_ctx* c, const float* qbar, const float* kbar, float* S, int BH, int d,
+                         hipStream_t s) {
+  const int side = (c->nb + kTile - 1) / kTile;
+  scores_kernel<<<(unsigned)((uint64_t)BH * side * side), 256, 0, s>>>(qbar, kbar, S, c->nb, d,
+                                                                        sqrt((double)d), side);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const absh_ctx* c, const RouteBuffers& rb, int tiles, double p, int k_floor,
+                         int order_depth, int reselect, hipStream_t s) {
+  const unsigned grid = (unsigned)((tiles + 3) / 4);
+  const int nb = c->nb;
+#define ABSH_SELECT(JJ)                                                                                  \
+  select_kernel<JJ><<<grid, 256, 0, s>>>(rb.S, nb, tiles, p, k_floor, order_depth, reselect, rb.target, \
+                                         rb.counts, rb.kv_idx, rb.order)
+  if (nb <= 64) ABSH_SELECT(1);
+  else if (nb <= 256) ABSH_SELECT(4);
+  else if (nb <= 512) ABSH_SELECT(8);
+  else if (nb <= 1024) ABSH_SELECT(16);
+  else if (nb <= 1280) ABSH_SELECT(20);
+  else if (nb <= 1536) ABSH_SELECT(24);
+  else if (nb <= 2048) ABSH_SELECT(32);
+  else return hipErrorInvalidValue;
+#undef ABSH_SELECT
+  return hipGetLastError();
+}
+
+hipError_t launch_slack_plan(const absh_ctx* c, const RouteBuffers& rb, int tiles, double beta, hipStream_t s) {
+  slack_plan_kernel<<<1, 1024, 0, s>>>(rb.counts, tiles, c->nb, beta, rb.target, rb.slack_info);
+  return hipGetLastError();
+}
+
+hipError_t launch_workload(const absh_ctx* c, const RouteBuffers& rb, int BH, hipStream_t s) {
+  workload_kernel<<<BH, 256, 0, s>>>(rb.counts, c->nb, rb.work, rb.L);
+  return hipGetLastError();
+}
+
+int queue_chunks(int tiles) { return (tiles + kQChunk - 1) / kQChunk; }
+
+hipError_t launch_queue(const absh_ctx* c, const RouteBuffers& rb, int tiles, int lpt, hipStream_t s) {
+  const unsigned grid = (unsigned)((tiles + 255) / 256);
+  if (!lpt) {
+    queue_identity_kernel<<<grid, 256, 0, s>>>(tiles, rb.queue);
+    return hipGetLastError();
+  }
+  const int chunks = queue_chunks(tiles);
+  queue_hist_kernel<<<chunks, kQChunk, 0, s>>>(rb.counts, tiles, c->nb, rb.chunk_hist, rb.rank);
+  queue_scan_kernel<<<1, 1024, 0, s>>>(rb.chunk_hist, chunks, c->nb);
+  queue_scatter_kernel<<<grid, 256, 0, s>>>(rb.counts, tiles, c->nb, rb.chunk_hist, rb.rank, rb.queue);
+  return hipGetLastError();
+}
+
+}  // namespace absh

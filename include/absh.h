@@ -1,0 +1,173 @@
+/*
+ * absh.h — C ABI of the Hilbert-ordered Top-p block router and block-sparse
+ * attention for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the sparse-routing frontend and block-sparse execution of FVAttn
+ * as described on the xllm-io review of FVAttn (section 三 "技术架构", Stage 1
+ * "Sparse Mask Routing" and "Block-Sparse Attention Execution"; section 3.1) and
+ * on the alanhou.org explainer of FVAttn ("Core Mechanism", layer 1; "Key
+ * Concepts", Top-p routing with a safety floor). The multi-GPU runtime stages
+ * (head migration, slack augmentation) appear here in their one-GPU form: a
+ * longest-processing-time-first tile queue and a slack fill over tiles.
+ *
+ * Conventions shared by every call
+ *  - All tensor, list and workspace pointers are DEVICE pointers on the context's
+ *    device unless stated otherwise; the caller owns them. The library owns only
+ *    the context and the Hilbert permutation inside it.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *    call except absh_create/absh_destroy only enqueues work on it: no host
+ *    synchronisation, no device allocation.
+ *  - Grid order: token n = (t*Y + y)*X + x of the (T, Y, X) latent grid; caller
+ *    tensors are [B, N, H, d], row-major.
+ *  - Hilbert order: the library's own tensors hold tokens sorted along a 3-D
+ *    Hilbert curve, in head-major form, with n_pad = nb*block rows per head;
+ *    rows N..n_pad-1 are zero. nb = ceil(N / block) blocks of `block` tokens;
+ *    block j holds Hilbert positions [j*block, min((j+1)*block, N)).
+ *  - A tile is one (batch b, head h, query block i); its id is (b*H + h)*nb + i.
+ *  - Arguments are validated on the host before any HIP call; a failure returns
+ *    ABSH_EINVAL / ABSH_EUNSUPPORTED / ABSH_EWORKSPACE and launches nothing.
+ *    HIP failures return ABSH_EHIP. absh_last_error() gives the detail of the
+ *    last failing call on this thread. Device faults surface at the caller's
+ *    next synchronisation. Inputs must be finite.
+ */
+#ifndef ABSH_H
+#define ABSH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ABSH_OK = 0,
+  ABSH_EINVAL = -1,       /* bad argument (null pointer, value out of range, shape mismatch) */
+  ABSH_EUNSUPPORTED = -2, /* valid but not built: head dim, block size or nb outside the kernels */
+  ABSH_EWORKSPACE = -3,   /* workspace smaller than absh_route_workspace_bytes() */
+  ABSH_ENODEV = -4,       /* no HIP device, or the device index does not exist */
+  ABSH_EHIP = -5          /* a HIP runtime call or a kernel launch failed */
+} absh_status;
+
+typedef enum { ABSH_BF16 = 0, ABSH_F32 = 1 } absh_dtype;
+
+/* Layout of a tensor in Hilbert order written by absh_permute. */
+typedef enum {
+  ABSH_ROWS = 0, /* [B, H, n_pad, d] bf16: one row of d per token (queries, keys, outputs) */
+  ABSH_VT = 1    /* [B, H, nb, d, block] bf16: each block transposed, keys fastest (values) */
+} absh_layout;
+
+typedef struct absh_ctx absh_ctx;
+
+/* Routing options (xllm-io review of FVAttn, section 五 "关键超参数": Top-p
+ * operating points 0.90 / 0.95; explainer "Key Concepts": the Top-k floor). */
+typedef struct {
+  double p;            /* Top-p threshold in (0, 1]; p == 1 keeps every block              */
+  int32_t k_floor;     /* Top-k safety floor, >= 0; clamped to nb                         */
+  double slack_frac;   /* slack-fill budget beta in [0, 1): E = floor(beta * sum counts)  */
+  int32_t lpt;         /* 1: queue in longest-first order; 0: queue = tile ids in order   */
+  int32_t order_depth; /* 0..64: length of the importance-order prefix written to `order` */
+} absh_route_opts;
+
+/* Routing outputs, all caller-allocated device buffers. nb, tiles = B*H*nb. */
+typedef struct {
+  int32_t* counts; /* [tiles] retained key blocks per tile (after floor and slack fill)        */
+  int32_t* kv_idx; /* [tiles][nb] row-padded; the first counts[t] entries, ascending block id  */
+  int32_t* order;  /* [tiles][order_depth] block ids, probability descending, ties by smaller
+                      id; -1 past nb. May be NULL when order_depth == 0                         */
+  int32_t* work;   /* [B*H] sum_i counts (the numerator of Eq. 1, exact)                        */
+  float* L;        /* [B*H] L_h = work / nb, float32 division (Eq. 1)                           */
+  int32_t* queue;  /* [tiles] execution order of the tiles for absh_sparse_attn                 */
+} absh_lists;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int absh_version(void);
+
+/* Human-readable name of a status code. Never NULL. */
+const char* absh_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). Valid
+ * until the next call into the library on this thread. */
+const char* absh_last_error(void);
+
+/* Create a context for one (T, Y, X) grid and block size on `device`.
+ * Builds the Hilbert permutation (xllm-io review of FVAttn, 3.1: blocks follow a
+ * Hilbert curve so that neighbouring tokens share blocks) on the device: every
+ * index of the enclosing 2^m cube is mapped to its cell, out-of-grid cells are
+ * dropped, and the survivors are ranked in index order. Synchronises `stream`
+ * once (set-up only). block must be 16, 64 or 128. On success *ctx owns device
+ * memory for perm and inv (2 * N int32). */
+absh_status absh_create(absh_ctx** ctx, int T, int Y, int X, int block, int device, void* stream);
+
+/* Release a context (synchronises the device first). NULL is accepted. */
+absh_status absh_destroy(absh_ctx* ctx);
+
+/* Host outputs: token count N, block count nb, padded rows per head n_pad. Any
+ * output pointer may be NULL. */
+absh_status absh_dims(const absh_ctx* ctx, int* N, int* nb, int* n_pad);
+
+/* Device pointers (owned by the context, valid until absh_destroy) to
+ * perm[r] = grid index of the r-th token in Hilbert order, and inv = perm^-1;
+ * both int32[N]. */
+absh_status absh_perm(const absh_ctx* ctx, const int32_t** perm, const int32_t** inv);
+
+/* Copy perm and inv (int32[N] each) into caller buffers (either may be NULL),
+ * asynchronously on `stream`. */
+absh_status absh_perm_copy(const absh_ctx* ctx, int32_t* perm_dst, int32_t* inv_dst, void* stream);
+
+/* Gather a grid-order tensor x [B, N, H, d] (bf16, or f32 rounded to bf16 to
+ * nearest-even) into Hilbert order, in the given layout, zero-filling pad rows.
+ * xh must hold B*H*n_pad*d bf16. d must be 64 or 128. */
+absh_status absh_permute(absh_ctx* ctx, const void* x, absh_dtype xt, void* xh, int B, int H, int d,
+                         absh_layout layout, void* stream);
+
+/* Scatter a Hilbert-order output oh [B, H, n_pad, d] bf16 back to grid order
+ * o [B, N, H, d] bf16 (pad rows are dropped). */
+absh_status absh_unpermute(absh_ctx* ctx, const void* oh, void* o, int B, int H, int d, void* stream);
+
+/* Block summaries: xbar[b, h, j, :] = mean of the rows of block j of xh
+ * ([B, H, n_pad, d] bf16), summed in float64, divided by the block's true token
+ * count in float64, rounded once to float32. xbar: float32 [B, H, nb, d]. */
+absh_status absh_pool(absh_ctx* ctx, const void* xh, float* xbar, int B, int H, int d, void* stream);
+
+/* Block scores s[b, h, i, j] = qbar_i . kbar_j / sqrt(d), products and sums in
+ * float64, rounded once to float32 (the routing-stage similarity of the xllm-io
+ * review's Stage 1). qbar, kbar: float32 [B, H, nb, d]; s: float32 [B, H, nb, nb]. */
+absh_status absh_block_scores(absh_ctx* ctx, const float* qbar, const float* kbar, float* s, int B, int H,
+                              int d, void* stream);
+
+/* Device workspace needed by absh_route for this shape, in bytes. */
+size_t absh_route_workspace_bytes(const absh_ctx* ctx, int B, int H, int d);
+
+/* Stage-1 routing (xllm-io review of FVAttn, Stage 1; explainer, "Key Concepts"):
+ * from Hilbert-order qh, kh ([B, H, n_pad, d] bf16, ABSH_ROWS):
+ *   block means -> float32 block scores -> softmax over key blocks (float64) ->
+ *   Top-p: the fewest blocks, by probability descending (ties: smaller id),
+ *   whose cumulative probability reaches p -> floor count' = max(c, min(k, nb))
+ *   -> optional slack fill of E = floor(beta * sum count') blocks raising the
+ *   lightest tiles along their own importance order -> Eq. 1 workloads
+ *   work_h and L_h -> the tile queue (longest first when opts->lpt).
+ * nb must be <= 2048. Writes every field of *out (order only if
+ * opts->order_depth > 0). ws must hold absh_route_workspace_bytes(); its
+ * contents are scratch. No host synchronisation. */
+absh_status absh_route(absh_ctx* ctx, const void* qh, const void* kh, int B, int H, int d,
+                       const absh_route_opts* opts, const absh_lists* out, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Block-sparse attention (xllm-io review of FVAttn, "Block-Sparse Attention
+ * Execution"): for every tile (b, h, i) in lists->queue order,
+ *   O_i = softmax(Q_i K_R^T / sqrt(d)) V_R
+ * over the tokens of its retained key blocks R (lists->kv_idx, ascending), with
+ * the pad keys of a partial last block masked. lists == NULL runs dense
+ * attention over every block with the same kernel. qh, kh: [B, H, n_pad, d]
+ * bf16 (ABSH_ROWS); vt: [B, H, nb, d, block] bf16 (ABSH_VT); oh: [B, H, n_pad, d]
+ * bf16 out (pad rows hold unspecified values). Scores and softmax in float32,
+ * probabilities rounded to bf16 for the value product, float32 accumulation. */
+absh_status absh_sparse_attn(absh_ctx* ctx, const void* qh, const void* kh, const void* vt, int B, int H,
+                             int d, const absh_lists* lists, void* oh, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ABSH_H */

@@ -1,0 +1,383 @@
+"""GPU parity: every step of the HIP path against the CPU oracle, through the C ABI.
+
+Bars (written here, per step):
+  * Hilbert perm, permutes, pooling, LPT queue, slack-fill counts: bit-exact;
+  * block scores: within one float32 ulp (float64 sums in a different order,
+    rounded once), at most a 1e-5 share of entries off;
+  * routing sets and counts: exact, except tiles excused by the rule in
+    routing_compare (threshold within 1e-5 of p, or a score tie within 5e-7);
+    work and L then follow exactly from the counts;
+  * attention on the GPU's own mask: max-abs <= 2e-2 and mean-abs <= 2e-3 against
+    the float64 oracle (bf16 inputs, bf16 probabilities in the value product);
+  * same-kernel invariants: p = 1 sparse == dense, LPT on == off, and two runs,
+    all bit-identical.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import adaptive_block_sparse_hilbert_amd as absh
+import workloads as W
+from oracle import absh_oracle as O
+from routing_compare import compare_routing
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+ATOL_MAX, ATOL_MEAN = 2e-2, 2e-3
+
+
+def to_dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def bf16_bits_of(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class Case:
+    """Inputs of one workload on the GPU and on the host (exact float32 of the bf16 values)."""
+
+    def __init__(self, w, seed=None):
+        self.w = w
+        d = W.generate(w, seed=seed)
+        self.bits = d
+        self.s = d["s"]
+        self.ctx = absh.create(w.T, w.Y, w.X, w.block)
+        self.q, self.k, self.v = (to_dev_bf16(d[n]) for n in ("q16", "k16", "v16"))
+        self.qh = absh.permute(self.ctx, self.q)
+        self.kh = absh.permute(self.ctx, self.k)
+        self.vt = absh.permute(self.ctx, self.v, layout=absh.ABSH_VT)
+        torch.cuda.synchronize()
+        self.perm, _ = O.hilbert_perm(w.T, w.Y, w.X)
+        self._routes = {}
+
+    def host(self, name):
+        return W.bf16_to_f32(self.bits[name + "16"])
+
+    @functools.cached_property
+    def hq(self):
+        return O.to_hilbert(self.host("q"), self.perm)
+
+    @functools.cached_property
+    def hk(self):
+        return O.to_hilbert(self.host("k"), self.perm)
+
+    @functools.cached_property
+    def hv(self):
+        return O.to_hilbert(self.host("v"), self.perm)
+
+    def oracle_route(self, p=None, k=None):
+        w = self.w
+        key = (w.p if p is None else p, w.k_floor if k is None else k)
+        if key not in self._routes:
+            self._routes[key] = O.route(self.hq, self.hk, w.block, *key)
+        R = self._routes[key]
+        return O.Routing(R.nb, R.sizes, R.scores, R.P, R.order, R.cdf, R.count_topp, R.counts.copy())
+
+
+@functools.lru_cache(maxsize=None)
+def case(index):
+    print(f"[gpu-parity] building case {W.workload(index).name}", flush=True)
+    return Case(W.workload(index))
+
+
+def check_lists_valid(r, nb):
+    """Host-side validity of lists and queue before any kernel consumes them."""
+    counts = r.counts.cpu().numpy()
+    kv = r.kv_idx.cpu().numpy()
+    queue = r.queue.cpu().numpy()
+    assert counts.min() >= 1 and counts.max() <= nb
+    assert np.array_equal(np.sort(queue), np.arange(queue.size))
+    flat_c = counts.reshape(-1)
+    flat_kv = kv.reshape(-1, nb)
+    for t in range(flat_c.size):
+        row = flat_kv[t, : flat_c[t]]
+        assert row.min() >= 0 and row.max() < nb and np.all(np.diff(row) > 0), f"tile {t} list invalid"
+    return counts, kv, queue
+
+
+# ---------------------------------------------------------------- Hilbert permutation
+
+@pytest.mark.parametrize("grid,block", [((4, 8, 8), 16), ((21, 30, 52), 64), ((21, 45, 80), 64),
+                                        ((126, 30, 52), 128), ((1, 1, 1), 16), ((3, 5, 7), 16),
+                                        ((2, 1, 9), 64), ((17, 2, 33), 128), ((64, 64, 64), 64)])
+def test_perm_matches_oracle(grid, block):
+    ctx = absh.create(*grid, block)
+    perm, inv = absh.perm_copy(ctx)
+    want, want_inv = O.hilbert_perm(*grid)
+    assert np.array_equal(perm.cpu().numpy(), want)
+    assert np.array_equal(inv.cpu().numpy(), want_inv)
+    N = grid[0] * grid[1] * grid[2]
+    assert (ctx.N, ctx.nb, ctx.n_pad) == (N, -(-N // block), -(-N // block) * block)
+
+
+# ---------------------------------------------------------------- permute / unpermute
+
+def test_permute_f32_rounds_to_nearest_even():
+    w = W.workload(0)
+    d = W.generate(w, want_fp32=True)
+    ctx = absh.create(w.T, w.Y, w.X, w.block)
+    x = torch.from_numpy(d["q32"]).to(DEV)
+    xh = absh.permute(ctx, x)
+    perm, _ = O.hilbert_perm(w.T, w.Y, w.X)
+    want = np.transpose(W.bf16_bits(d["q32"])[:, perm], (0, 2, 1, 3))
+    got = bf16_bits_of(xh)
+    assert np.array_equal(got[:, :, : w.N], want)
+    assert (got[:, :, w.N:] == 0).all()
+
+
+@pytest.mark.parametrize("index", [0, 1])
+def test_permute_rows_and_vt_bit_exact(index):
+    c = case(index)
+    w = c.w
+    want = np.transpose(c.bits["k16"][:, c.perm], (0, 2, 1, 3))
+    got = bf16_bits_of(c.kh)
+    assert np.array_equal(got[:, :, : w.N], want)
+    assert (got[:, :, w.N:] == 0).all()
+    vpad = np.zeros((w.B, w.H, w.nb * w.block, w.d), dtype=np.uint16)
+    vpad[:, :, : w.N] = np.transpose(c.bits["v16"][:, c.perm], (0, 2, 1, 3))
+    want_vt = vpad.reshape(w.B, w.H, w.nb, w.block, w.d).transpose(0, 1, 2, 4, 3)
+    assert np.array_equal(bf16_bits_of(c.vt).reshape(want_vt.shape), want_vt)
+
+
+@pytest.mark.parametrize("index", [0, 1])
+def test_unpermute_round_trip(index):
+    c = case(index)
+    back = absh.unpermute(c.ctx, c.qh)
+    assert torch.equal(back.view(torch.int16), c.q.view(torch.int16))
+
+
+# ---------------------------------------------------------------- pooling and scores
+
+@pytest.mark.parametrize("index", [0, 1, 2])
+def test_pool_bit_exact(index):
+    c = case(index)
+    got = absh.pool(c.ctx, c.kh).cpu().numpy()
+    want = O.block_means(c.hk, c.w.block)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("index", [0, 1, 2])
+def test_scores_within_one_ulp(index):
+    c = case(index)
+    qbar, kbar = absh.pool(c.ctx, c.qh), absh.pool(c.ctx, c.kh)
+    got = absh.block_scores(c.ctx, qbar, kbar).cpu().numpy()
+    want = O.block_scores(O.block_means(c.hq, c.w.block), O.block_means(c.hk, c.w.block))
+    ulp = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1
+    assert (ulp > 0).mean() <= 1e-5
+
+
+# ---------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("index,p", [(0, None), (1, None), (2, None), (4, 0.8), (4, 0.9), (4, 0.95)])
+def test_route_matches_oracle(index, p):
+    c = case(index)
+    w = c.w
+    p = w.p if p is None else p
+    r = absh.route(c.ctx, c.qh, c.kh, p, w.k_floor, lpt=True)
+    torch.cuda.synchronize()
+    counts, kv, queue = check_lists_valid(r, w.nb)
+    R = c.oracle_route(p=p)
+    excused, failures = compare_routing(R, counts, kv, p)
+    print(f"[route] {w.name} p={p}: density {counts.mean() / w.nb:.4f}, excused tiles {excused}")
+    assert not failures, failures[:5]
+    assert excused <= 0.01 * counts.size
+    work = r.work.cpu().numpy()
+    L = r.L.cpu().numpy()
+    assert np.array_equal(work, counts.sum(-1))
+    assert np.array_equal(L, (work.astype(np.float32) / np.float32(w.nb)).astype(np.float32))
+    assert (counts >= min(w.k_floor, w.nb)).all()
+    # LPT queue: exactly the oracle's order for these counts
+    assert np.array_equal(queue, O.lpt_queue(counts))
+    if excused == 0:
+        wo, Lo = O.workloads(R.counts)
+        assert np.array_equal(work, wo) and np.array_equal(L, Lo)
+
+
+def test_importance_order_prefix():
+    c = case(1)
+    w = c.w
+    r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, order_depth=16)
+    got = r.order.cpu().numpy()
+    R = c.oracle_route()
+    want = R.order[..., :16]
+    mism = np.argwhere((got != want).any(-1))
+    # a differing prefix is allowed only where the oracle's scores tie to the last bits
+    for b, h, i in mism:
+        k = int(np.argmax(got[b, h, i] != want[b, h, i]))
+        s = R.scores[b, h, i].astype(np.float64)
+        assert abs(s[got[b, h, i, k]] - s[want[b, h, i, k]]) <= 5e-7 * max(1.0, abs(s[want[b, h, i, k]]))
+    assert len(mism) <= 0.01 * got.shape[2] * w.H
+
+
+def test_order_prefix_past_nb_is_minus_one():
+    c = case(0)
+    r = absh.route(c.ctx, c.qh, c.kh, 0.9, 2, order_depth=20)
+    got = r.order.cpu().numpy()
+    assert (got[..., 16:] == -1).all()
+    assert all(sorted(row[:16].tolist()) == list(range(16)) for row in got.reshape(-1, 20))
+
+
+def test_slack_fill_matches_oracle():
+    c = case(3)
+    w = c.w
+    base = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=0.0, lpt=True)
+    filled = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, lpt=True)
+    torch.cuda.synchronize()
+    c0, _, _ = check_lists_valid(base, w.nb)
+    c1, kv1, q1 = check_lists_valid(filled, w.nb)
+    want = O.slack_fill(c0, w.slack_frac)
+    assert np.array_equal(c1, want)
+    added = int((c1 - c0).sum())
+    E = O.slack_budget(c0, w.slack_frac)
+    print(f"[slack] {w.name}: sum before {int(c0.sum())}, E {E}, added {added}")
+    assert added == min(E, int((w.nb - c0).sum()))
+    # the filled sets are the oracle's importance-order prefixes of the new counts
+    R = c.oracle_route()
+    R.counts = c1.astype(np.int64)
+    excused, failures = compare_routing(R, c1, kv1, w.p)
+    assert not failures, failures[:5]
+    assert np.array_equal(q1, O.lpt_queue(c1))
+    work = filled.work.cpu().numpy()
+    assert np.array_equal(work, c1.sum(-1))
+
+
+def test_route_deterministic():
+    c = case(1)
+    w = c.w
+    a = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, order_depth=8)
+    b = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, order_depth=8)
+    for x, y in ((a.counts, b.counts), (a.kv_idx, b.kv_idx), (a.order, b.order), (a.queue, b.queue)):
+        cnt = a.counts.reshape(-1)
+        if x is a.kv_idx:
+            xs, ys = x.reshape(cnt.numel(), -1), y.reshape(cnt.numel(), -1)
+            for t in range(cnt.numel()):
+                assert torch.equal(xs[t, : cnt[t]], ys[t, : cnt[t]])
+        else:
+            assert torch.equal(x, y)
+
+
+# ---------------------------------------------------------------- attention
+
+def attention_errors(c, r, tiles):
+    """Max / mean abs error of the GPU output rows of `tiles` against the oracle on the GPU's mask."""
+    w = c.w
+    oh = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r)
+    o = absh.unpermute(c.ctx, oh).float().cpu().numpy()
+    counts = r.counts.cpu().numpy().reshape(-1)
+    kv = r.kv_idx.cpu().numpy().reshape(counts.size, -1)
+    errs = []
+    for t in tiles:
+        bh, i = divmod(int(t), w.nb)
+        b, h = divmod(bh, w.H)
+        blocks = kv[t, : counts[t]]
+        ref = O.attention_tile(c.hq[b, h], c.hk[b, h], c.hv[b, h], w.block, i, blocks)
+        rows = c.perm[i * w.block: min((i + 1) * w.block, w.N)]
+        errs.append(np.abs(o[b, rows, h, :] - ref))
+    e = np.concatenate([x.ravel() for x in errs])
+    return e.max(), e.mean()
+
+
+def test_attention_tiny_all_tiles():
+    c = case(0)
+    w = c.w
+    r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor)
+    check_lists_valid(r, w.nb)
+    mx, mean = attention_errors(c, r, range(w.tiles))
+    print(f"[attn] tiny: max {mx:.3e} mean {mean:.3e}")
+    assert mx <= ATOL_MAX and mean <= ATOL_MEAN
+
+
+@pytest.mark.parametrize("index", [1, 2, 3, 4])
+def test_attention_sampled_tiles(index):
+    c = case(index)
+    w = c.w
+    r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, lpt=True)
+    counts, _, _ = check_lists_valid(r, w.nb)
+    rng = np.random.default_rng(100 + index)
+    flat = counts.reshape(-1)
+    # the heaviest tile, the last (partial) query block of a few heads, and random tiles
+    pick = {int(np.argmax(flat)), w.nb - 1, w.tiles - 1}
+    pick |= set(rng.choice(w.tiles, size=10, replace=False).tolist())
+    mx, mean = attention_errors(c, r, sorted(pick))
+    print(f"[attn] {w.name}: max {mx:.3e} mean {mean:.3e} over {len(pick)} tiles")
+    assert mx <= ATOL_MAX and mean <= ATOL_MEAN
+
+
+@pytest.mark.parametrize("index", [0, 1])
+def test_p_one_sparse_equals_dense(index):
+    c = case(index)
+    w = c.w
+    r = absh.route(c.ctx, c.qh, c.kh, 1.0, 0, lpt=True)
+    counts, kv, _ = check_lists_valid(r, w.nb)
+    assert (counts == w.nb).all()
+    sparse = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r)
+    dense = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, None)
+    torch.cuda.synchronize()
+    assert torch.equal(sparse.view(torch.int16), dense.view(torch.int16))
+
+
+def test_dense_matches_oracle_tiny():
+    c = case(0)
+    w = c.w
+    o = absh.unpermute(c.ctx, absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, None)).float().cpu().numpy()
+    ref = O.attention(c.host("q"), c.host("k"), c.host("v"), c.perm, w.block, None)
+    e = np.abs(o - ref)
+    assert e.max() <= ATOL_MAX and e.mean() <= ATOL_MEAN
+
+
+def test_lpt_on_off_and_repeat_bit_identical():
+    c = case(1)
+    w = c.w
+    a = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, lpt=True)
+    b = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, lpt=False)
+    check_lists_valid(a, w.nb)
+    check_lists_valid(b, w.nb)
+    assert np.array_equal(b.queue.cpu().numpy(), np.arange(w.tiles))
+    oa = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, a)
+    ob = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, b)
+    oc = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, a)
+    torch.cuda.synchronize()
+    rows = torch.arange(w.N, device=DEV)
+    assert torch.equal(oa[:, :, rows].view(torch.int16), ob[:, :, rows].view(torch.int16))
+    assert torch.equal(oa.view(torch.int16), oc.view(torch.int16))
+
+
+# ---------------------------------------------------------------- edge shapes
+
+@pytest.mark.parametrize("grid,block,d,H,B,p,k", [
+    ((1, 1, 1), 16, 64, 1, 1, 0.9, 2),      # one token, one partial block
+    ((2, 3, 5), 16, 64, 2, 2, 0.5, 0),      # N = 30 < 2 blocks, batch of 2
+    ((4, 4, 4), 64, 128, 3, 1, 0.7, 9),     # exactly one full block, floor above nb
+    ((5, 6, 7), 64, 128, 2, 1, 0.3, 1),     # ragged tail of 18
+    ((3, 9, 10), 128, 128, 2, 1, 0.99, 1),  # ragged tail with block 128
+    ((2, 8, 8), 16, 128, 2, 1, 0.05, 3),    # tiny p: the floor decides
+])
+def test_edge_shapes(grid, block, d, H, B, p, k):
+    T, Y, X = grid
+    N = T * Y * X
+    rng = np.random.default_rng(7)
+    q32 = rng.standard_normal((B, N, H, d)).astype(np.float32) * 2
+    k32 = rng.standard_normal((B, N, H, d)).astype(np.float32) * 2
+    v32 = rng.standard_normal((B, N, H, d)).astype(np.float32)
+    bits = [W.bf16_bits(a) for a in (q32, k32, v32)]
+    ctx = absh.create(T, Y, X, block)
+    qd, kd, vd = (to_dev_bf16(b) for b in bits)
+    qh, kh = absh.permute(ctx, qd), absh.permute(ctx, kd)
+    vt = absh.permute(ctx, vd, layout=absh.ABSH_VT)
+    r = absh.route(ctx, qh, kh, p, k, slack_frac=0.25, lpt=True)
+    counts, kv, _ = check_lists_valid(r, ctx.nb)
+    perm, _ = O.hilbert_perm(T, Y, X)
+    hq, hk, hv = (O.to_hilbert(W.bf16_to_f32(b), perm) for b in bits)
+    base = O.route(hq, hk, block, p, k)
+    want = O.slack_fill(base.counts, 0.25)
+    assert np.array_equal(counts, want)
+    o = absh.unpermute(ctx, absh.sparse_attn(ctx, qh, kh, vt, r)).float().cpu().numpy()
+    ref = O.attention(W.bf16_to_f32(bits[0]), W.bf16_to_f32(bits[1]), W.bf16_to_f32(bits[2]), perm, block,
+                      lambda b, h, i: kv[b, h, i, : counts[b, h, i]])
+    e = np.abs(o - ref)
+    assert e.max() <= ATOL_MAX and e.mean() <= ATOL_MEAN
