@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libabsh.so")
 
 ABSH_BF16, ABSH_F32 = 0, 1
 ABSH_ROWS, ABSH_VT = 0, 1
+SCHED_ORDER, SCHED_LPT, SCHED_XCD = 0, 1, 2
+SCHEDULES = {"order": SCHED_ORDER, "lpt": SCHED_LPT, "xcd": SCHED_XCD}
 
 EXPORTED = (
     "absh_version", "absh_status_string", "absh_last_error", "absh_create", "absh_destroy", "absh_dims",
@@ -36,12 +38,13 @@ class AbshError(RuntimeError):
 
 class RouteOpts(ctypes.Structure):
     _fields_ = [("p", ctypes.c_double), ("k_floor", ctypes.c_int32), ("slack_frac", ctypes.c_double),
-                ("lpt", ctypes.c_int32), ("order_depth", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("order_depth", ctypes.c_int32)]
 
 
 class Lists(ctypes.Structure):
     _fields_ = [("counts", ctypes.c_void_p), ("kv_idx", ctypes.c_void_p), ("order", ctypes.c_void_p),
-                ("work", ctypes.c_void_p), ("L", ctypes.c_void_p), ("queue", ctypes.c_void_p)]
+                ("work", ctypes.c_void_p), ("L", ctypes.c_void_p), ("queue", ctypes.c_void_p),
+                ("sched", ctypes.c_void_p)]
 
 
 _lib = None
@@ -151,10 +154,15 @@ def permute(ctx: Context, x, layout: int = ABSH_ROWS, out=None, stream=None):
     assert N == ctx.N and x.is_contiguous() and x.dtype in (torch.bfloat16, torch.float32)
     xt = ABSH_F32 if x.dtype == torch.float32 else ABSH_BF16
     if out is None:
-        shape = (B, H, ctx.n_pad, d) if layout == ABSH_ROWS else (B, H, ctx.nb, d, ctx.block)
+        shape = (B, H, ctx.n_pad, d) if layout == ABSH_ROWS else (B, H, ctx.nb, d, vt_keys(ctx.block))
         out = torch.empty(shape, dtype=torch.bfloat16, device=x.device)
     _check(lib().absh_permute(ctx.handle, _ptr(x), xt, _ptr(out), B, H, d, layout, _stream(stream)))
     return out
+
+
+def vt_keys(block: int) -> int:
+    """Keys per block in the ABSH_VT layout (blocks shorter than 32 keys are zero-padded)."""
+    return max(block, 32)
 
 
 def unpermute(ctx: Context, oh, out=None, stream=None):
@@ -196,11 +204,12 @@ class Routing:
     work: object     # int32 [B, H]
     L: object        # float32 [B, H]
     queue: object    # int32 [B*H*nb]
+    sched: object    # int32 [9] bounds of the per-XCD runs of the queue
 
     def lists(self) -> Lists:
         return Lists(self.counts.data_ptr(), self.kv_idx.data_ptr(),
                      self.order.data_ptr() if self.order is not None else 0,
-                     self.work.data_ptr(), self.L.data_ptr(), self.queue.data_ptr())
+                     self.work.data_ptr(), self.L.data_ptr(), self.queue.data_ptr(), self.sched.data_ptr())
 
 
 def route_workspace_bytes(ctx: Context, B: int, H: int, d: int) -> int:
@@ -218,12 +227,16 @@ def alloc_routing(ctx: Context, B: int, H: int, order_depth: int = 0) -> Routing
         work=torch.empty((B, H), dtype=torch.int32, device=dev),
         L=torch.empty((B, H), dtype=torch.float32, device=dev),
         queue=torch.empty((B * H * nb,), dtype=torch.int32, device=dev),
+        sched=torch.empty((9,), dtype=torch.int32, device=dev),
     )
 
 
-def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0, lpt: bool = True,
+def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0, schedule="lpt",
           order_depth: int = 0, out: Optional[Routing] = None, workspace=None, stream=None) -> Routing:
-    """Stage-1 routing of Hilbert-order qh, kh [B, H, n_pad, d] bf16 -> Routing (device tensors)."""
+    """Stage-1 routing of Hilbert-order qh, kh [B, H, n_pad, d] bf16 -> Routing (device tensors).
+
+    schedule: "order", "lpt" or "xcd" (or the SCHED_* integer).
+    """
     import torch
     B, H, n_pad, d = qh.shape
     if out is None:
@@ -231,7 +244,8 @@ def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0,
     need = route_workspace_bytes(ctx, B, H, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=qh.device)
-    opts = RouteOpts(float(p), int(k_floor), float(slack_frac), int(bool(lpt)), int(order_depth))
+    sched = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
+    opts = RouteOpts(float(p), int(k_floor), float(slack_frac), sched, int(order_depth))
     lists = out.lists()
     _check(lib().absh_route(ctx.handle, _ptr(qh), _ptr(kh), B, H, d, ctypes.byref(opts), ctypes.byref(lists),
                             _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream)))

@@ -11,13 +11,19 @@ struct absh_ctx {
   int N, nb, n_pad;
   int m;        // bits per axis of the enclosing Hilbert cube
   int device;
-  int32_t* perm;  // [N] grid index of the r-th token in Hilbert order
-  int32_t* inv;   // [N] Hilbert position of grid token n
+  int num_cus;        // compute units of the device (persistent launch size)
+  int32_t* perm;      // [N] grid index of the r-th token in Hilbert order
+  int32_t* inv;       // [N] Hilbert position of grid token n
+  int32_t* counters;  // [16] tile-pull counters of the attention kernel (zero between launches)
 };
 
 namespace absh {
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+// Keys per block in the block-transposed value layout: blocks shorter than one
+// 32-key MFMA step are padded with zero keys.
+__host__ __device__ constexpr int vt_keys(int block) { return block < 32 ? 32 : block; }
 
 // Round a float to bfloat16, nearest-even (inputs are finite).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
@@ -50,16 +56,18 @@ struct RouteBuffers {
   int64_t* slack_info;  // [4] lambda, remainder, E, total
   int32_t* chunk_hist;  // [chunks][nb + 1]
   int32_t* rank;        // [tiles]
+  int32_t* sched;       // [9] queue segment bounds, one segment per XCD
 };
 hipError_t launch_select(const absh_ctx* c, const RouteBuffers& rb, int tiles, double p, int k_floor,
                          int order_depth, int reselect, hipStream_t s);
 hipError_t launch_slack_plan(const absh_ctx* c, const RouteBuffers& rb, int tiles, double beta, hipStream_t s);
 hipError_t launch_workload(const absh_ctx* c, const RouteBuffers& rb, int BH, hipStream_t s);
 hipError_t launch_queue(const absh_ctx* c, const RouteBuffers& rb, int tiles, int lpt, hipStream_t s);
+hipError_t launch_segments(const absh_ctx* c, const RouteBuffers& rb, int BH, int balanced, hipStream_t s);
 int queue_chunks(int tiles);
 
 hipError_t launch_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B,
                             int H, int d, const int32_t* queue, const int32_t* counts, const int32_t* kv_idx,
-                            hipStream_t s);
+                            const int32_t* bounds, hipStream_t s);
 
 }  // namespace absh

@@ -135,8 +135,11 @@ absh_status absh_create(absh_ctx** out, int T, int Y, int X, int block, int devi
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int chunks = absh::hilbert_chunks(m);
   int32_t* chunk_counts = nullptr;
-  hipError_t e = hipMalloc(&c->perm, sizeof(int32_t) * N);
+  hipError_t e = hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e == hipSuccess) e = hipMalloc(&c->perm, sizeof(int32_t) * N);
   if (e == hipSuccess) e = hipMalloc(&c->inv, sizeof(int32_t) * N);
+  if (e == hipSuccess) e = hipMalloc(&c->counters, sizeof(int32_t) * 16);
+  if (e == hipSuccess) e = hipMemsetAsync(c->counters, 0, sizeof(int32_t) * 16, s);
   if (e == hipSuccess) e = hipMalloc(&chunk_counts, sizeof(int32_t) * chunks);
   if (e == hipSuccess) e = absh::launch_hilbert_perm(c, chunk_counts, chunks, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -145,6 +148,7 @@ absh_status absh_create(absh_ctx** out, int T, int Y, int X, int block, int devi
     absh_status st = hip_fail(e, "absh_create");
     if (c->perm) (void)hipFree(c->perm);
     if (c->inv) (void)hipFree(c->inv);
+    if (c->counters) (void)hipFree(c->counters);
     delete c;
     return st;
   }
@@ -162,6 +166,7 @@ absh_status absh_destroy(absh_ctx* c) {
   }
   if (c->perm) (void)hipFree(c->perm);
   if (c->inv) (void)hipFree(c->inv);
+  if (c->counters) (void)hipFree(c->counters);
   delete c;
   return st;
 }
@@ -263,8 +268,10 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
     return fail(ABSH_EINVAL, "slack_frac must lie in [0, 1) (got %g)", opts->slack_frac);
   if (opts->order_depth < 0 || opts->order_depth > 64)
     return fail(ABSH_EINVAL, "order_depth must lie in [0, 64] (got %d)", opts->order_depth);
-  if (!out->counts || !out->kv_idx || !out->work || !out->L || !out->queue)
-    return fail(ABSH_EINVAL, "counts, kv_idx, work, L and queue must be non-NULL");
+  if (opts->schedule < ABSH_SCHED_ORDER || opts->schedule > ABSH_SCHED_XCD)
+    return fail(ABSH_EINVAL, "unknown schedule %d", opts->schedule);
+  if (!out->counts || !out->kv_idx || !out->work || !out->L || !out->queue || !out->sched)
+    return fail(ABSH_EINVAL, "counts, kv_idx, work, L, queue and sched must be non-NULL");
   if (opts->order_depth > 0 && !out->order) return fail(ABSH_EINVAL, "order is NULL but order_depth > 0");
   if (c->nb > kMaxNb) return fail(ABSH_EUNSUPPORTED, "nb = %d above the router's %d", c->nb, kMaxNb);
   const WsLayout w = ws_layout(c, B, H, d);
@@ -290,6 +297,7 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
   rb.slack_info = reinterpret_cast<int64_t*>(base + w.info);
   rb.chunk_hist = reinterpret_cast<int32_t*>(base + w.chunk_hist);
   rb.rank = reinterpret_cast<int32_t*>(base + w.rank);
+  rb.sched = out->sched;
   const int tiles = B * H * c->nb;
 
   ABSH_HIP(absh::launch_pool(c, qh, qbar, B, H, d, s), "absh_route: pool q");
@@ -302,7 +310,8 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
     ABSH_HIP(absh::launch_select(c, rb, tiles, opts->p, opts->k_floor, 0, 1, s), "absh_route: slack fill");
   }
   ABSH_HIP(absh::launch_workload(c, rb, B * H, s), "absh_route: workload");
-  ABSH_HIP(absh::launch_queue(c, rb, tiles, opts->lpt != 0, s), "absh_route: queue");
+  ABSH_HIP(absh::launch_queue(c, rb, tiles, opts->schedule == ABSH_SCHED_LPT, s), "absh_route: queue");
+  ABSH_HIP(absh::launch_segments(c, rb, B * H, opts->schedule == ABSH_SCHED_XCD, s), "absh_route: segments");
   return ABSH_OK;
 }
 
@@ -314,12 +323,12 @@ absh_status absh_sparse_attn(absh_ctx* c, const void* qh, const void* kh, const 
   if (!qh || !kh || !vt || !oh) return fail(ABSH_EINVAL, "qh, kh, vt or oh is NULL");
   if (!aligned16(qh) || !aligned16(kh) || !aligned16(vt) || !aligned16(oh))
     return fail(ABSH_EINVAL, "qh, kh, vt and oh must be 16-byte aligned");
-  if (lists && (!lists->counts || !lists->kv_idx || !lists->queue))
-    return fail(ABSH_EINVAL, "lists needs counts, kv_idx and queue");
+  if (lists && (!lists->counts || !lists->kv_idx || !lists->queue || !lists->sched))
+    return fail(ABSH_EINVAL, "lists needs counts, kv_idx, queue and sched");
   if (absh_status st = use_device(c)) return st;
   ABSH_HIP(absh::launch_attention(c, qh, kh, vt, oh, B, H, d, lists ? lists->queue : nullptr,
                                   lists ? lists->counts : nullptr, lists ? lists->kv_idx : nullptr,
-                                  reinterpret_cast<hipStream_t>(stream)),
+                                  lists ? lists->sched : nullptr, reinterpret_cast<hipStream_t>(stream)),
            "absh_sparse_attn");
   return ABSH_OK;
 }

@@ -49,14 +49,20 @@ __global__ __launch_bounds__(kThreads) void gather_rows(const void* __restrict__
   *reinterpret_cast<Pack8*>(xh + row * d + (size_t)e * 8) = v;
 }
 
-// vt[b, h, j, c, k] = x[b, perm[j*blk + k], h, c]: one workgroup per (b, h, j)
-// stages the block's rows in LDS and writes them back transposed.
+// vt[b, h, j, c, k] = x[b, perm[j*blk + k], h, c] for k < blk, with KB = vt_keys(blk)
+// keys per block (keys blk..KB-1 and pad tokens are zero): one workgroup per
+// (b, h, j) stages the block's rows in LDS and writes them back transposed.
 template <int D, int BLK>
 __global__ __launch_bounds__(kThreads) void gather_vt(const void* __restrict__ x, int is_f32,
                                                       bf16_t* __restrict__ vt, const int32_t* __restrict__ perm,
                                                       int N, int nb, int H) {
-  constexpr int kStride = BLK + 2;  // keys per LDS row (+2 breaks bank aliasing of the column writes)
+  constexpr int KB = vt_keys(BLK);
+  constexpr int kStride = KB + 2;  // keys per LDS row (+2 breaks bank aliasing of the column writes)
   __shared__ bf16_t tile[D * kStride];
+  if (KB > BLK) {
+    for (int e = threadIdx.x; e < D * kStride; e += kThreads) tile[e] = 0;
+    __syncthreads();
+  }
   const int j = blockIdx.x % nb;
   const uint64_t bh = blockIdx.x / nb;
   const int h = (int)(bh % H);
@@ -73,14 +79,14 @@ __global__ __launch_bounds__(kThreads) void gather_vt(const void* __restrict__ x
   }
   __syncthreads();
   // Store: piece p = (channel c, 8 keys starting at k8*8).
-  bf16_t* out = vt + (bh * nb + j) * (size_t)(D * BLK);
-  for (int p = threadIdx.x; p < D * (BLK / 8); p += kThreads) {
-    const int c = p / (BLK / 8);
-    const int k8 = p % (BLK / 8);
+  bf16_t* out = vt + (bh * nb + j) * (size_t)(D * KB);
+  for (int p = threadIdx.x; p < D * (KB / 8); p += kThreads) {
+    const int c = p / (KB / 8);
+    const int k8 = p % (KB / 8);
     Pack8 v;
     bf16_t* vv = reinterpret_cast<bf16_t*>(&v);
     for (int q = 0; q < 8; ++q) vv[q] = tile[c * kStride + k8 * 8 + q];
-    *reinterpret_cast<Pack8*>(out + (size_t)c * BLK + k8 * 8) = v;
+    *reinterpret_cast<Pack8*>(out + (size_t)c * KB + k8 * 8) = v;
   }
 }
 

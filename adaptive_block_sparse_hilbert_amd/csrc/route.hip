@@ -437,6 +437,91 @@ __global__ __launch_bounds__(256) void queue_identity_kernel(int tiles, int32_t*
   if (t < tiles) queue[t] = t;
 }
 
+// ------------------------------------------------------------------ queue segments (one per XCD)
+
+constexpr int kSegments = 8;
+constexpr int kTileOverhead = 1;  // per-tile cost of the query load and output write, in key blocks
+
+// sched[0..8]: bounds of the eight queue segments the attention kernel pulls
+// from, one per XCD. balanced == 0: one segment holds the whole queue (plain list
+// scheduling in queue order). balanced != 0: the queue is the tile ids in order
+// and it is cut where the running cost sum (retained blocks + overhead) crosses
+// x/8 of the total, so each XCD gets a contiguous, equally heavy run of tiles
+// (whole heads where they fit): the one-GPU reading of the review's RLB, with
+// the XCDs (separate L2 caches) as the ranks.
+__global__ __launch_bounds__(1024) void segments_kernel(const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ work, int BH, int nb,
+                                                        int balanced, int32_t* __restrict__ sched) {
+  __shared__ int64_t buf[1024];
+  __shared__ int64_t target[kSegments + 1];
+  __shared__ int32_t head_of[kSegments + 1];
+  __shared__ int64_t base_of[kSegments + 1];
+  const int64_t tiles = (int64_t)BH * nb;
+  if (!balanced) {
+    if (threadIdx.x <= kSegments) sched[threadIdx.x] = threadIdx.x == 0 ? 0 : (int32_t)tiles;
+    return;
+  }
+  // total cost and the target of each inner bound
+  int64_t mine = 0;
+  for (int h = threadIdx.x; h < BH; h += 1024) mine += (int64_t)work[h] + (int64_t)nb * kTileOverhead;
+  int64_t total;
+  block_exclusive_scan<int64_t>(mine, buf, total);
+  if (threadIdx.x <= kSegments) {
+    target[threadIdx.x] = (total * threadIdx.x + kSegments - 1) / kSegments;
+    head_of[threadIdx.x] = BH;
+    base_of[threadIdx.x] = total;
+  }
+  __syncthreads();
+  // the head holding each target: exclusive prefix < target <= inclusive prefix
+  int64_t seen = 0;
+  for (int h0 = 0; h0 < BH; h0 += 1024) {
+    const int h = h0 + threadIdx.x;
+    const int64_t cost = h < BH ? (int64_t)work[h] + (int64_t)nb * kTileOverhead : 0;
+    int64_t chunk;
+    const int64_t excl = seen + block_exclusive_scan<int64_t>(cost, buf, chunk);
+    if (h < BH) {
+      for (int x = 1; x < kSegments; ++x)
+        if (excl < target[x] && target[x] <= excl + cost) {
+          head_of[x] = h;
+          base_of[x] = excl;
+        }
+    }
+    seen += chunk;
+    __syncthreads();
+  }
+  // within that head, the first tile whose preceding cost reaches the target
+  for (int x = 1; x < kSegments; ++x) {
+    const int h = head_of[x];
+    if (h >= BH) {  // target beyond the last head (cannot happen with counts >= 1)
+      if (threadIdx.x == 0) sched[x] = (int32_t)tiles;
+      continue;
+    }
+    int64_t run = base_of[x];
+    int found = nb;
+    for (int i0 = 0; i0 < nb; i0 += 1024) {
+      const int i = i0 + threadIdx.x;
+      const int64_t cost = i < nb ? (int64_t)counts[(size_t)h * nb + i] + kTileOverhead : 0;
+      int64_t chunk;
+      const int64_t before = run + block_exclusive_scan<int64_t>(cost, buf, chunk);
+      // smallest i with before >= target: count the i in this chunk with before < target
+      const int64_t below = (i < nb && before < target[x]) ? 1 : 0;
+      int64_t n_below;
+      block_exclusive_scan<int64_t>(below, buf, n_below);
+      if (n_below < (int64_t)min(1024, nb - i0)) {
+        found = i0 + (int)n_below;
+        break;
+      }
+      run += chunk;
+    }
+    if (threadIdx.x == 0) sched[x] = (int32_t)((int64_t)h * nb + found);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    sched[0] = 0;
+    sched[kSegments] = (int32_t)tiles;
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
@@ -485,6 +570,11 @@ hipError_t launch_workload(const absh_ctx* c, const RouteBuffers& rb, int BH, hi
 }
 
 int queue_chunks(int tiles) { return (tiles + kQChunk - 1) / kQChunk; }
+
+hipError_t launch_segments(const absh_ctx* c, const RouteBuffers& rb, int BH, int balanced, hipStream_t s) {
+  segments_kernel<<<1, 1024, 0, s>>>(rb.counts, rb.work, BH, c->nb, balanced, rb.sched);
+  return hipGetLastError();
+}
 
 hipError_t launch_queue(const absh_ctx* c, const RouteBuffers& rb, int tiles, int lpt, hipStream_t s) {
   const unsigned grid = (unsigned)((tiles + 255) / 256);

@@ -1,0 +1,263 @@
+"""Throughput of the Hilbert-ordered Top-p router + block-sparse attention on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input that is
+already resident in HBM:
+    permute q, k (rows) and v (block-transposed) into Hilbert order
+    -> route (block means, block scores, Top-p + floor [+ slack fill], Eq. 1, tile queue)
+    -> block-sparse attention over the retained blocks
+    -> unpermute the output back to grid order.
+The headline workload is 720p video at 40 heads (grid 21 x 45 x 80 = 75,600 tokens,
+d = 128, block 64, p = 0.9, k = 4, longest-first queue).
+
+value = retained FLOPs / step time, where retained FLOPs = sum over tiles and
+retained blocks of 4 * n_i * n_j * d with true token counts. Each stage is timed
+with HIP events on the stream its kernels run on; the attention kernel's own
+average duration gives the roofline figure against the bf16 MFMA peak.
+
+Prints one JSON line. Inputs are synthetic (see workloads/), data = "synthetic".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="720p-40h")
+    ap.add_argument("--p", type=float, default=None, help="override the workload's Top-p")
+    ap.add_argument("--schedule", default="xcd", choices=("order", "lpt", "xcd"),
+                    help="tile schedule of the attention kernel")
+    ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tiles", type=int, default=24, help="attention tiles in the oracle's timed sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the steps, run one plain device copy of this size (for counter scaling)")
+    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes of the attention kernel")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the path would shard by head across GPUs).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import adaptive_block_sparse_hilbert_amd as absh
+    import workloads as W
+
+    w = W.workload(args.workload)
+    p = w.p if args.p is None else args.p
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    data = W.generate(w)
+    to_dev = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to_dev(data["q16"]), to_dev(data["k16"]), to_dev(data["v16"])
+    gen_s = time.time() - t0
+    print(f"[bench] {w.name}: inputs ready in {gen_s:.1f}s", file=sys.stderr, flush=True)
+
+    ctx = absh.create(w.T, w.Y, w.X, w.block, device=0)
+    B, H, d = w.B, w.H, w.d
+    stream = torch.cuda.current_stream()
+    # every buffer of the step, allocated once
+    qh = torch.empty((B, H, ctx.n_pad, d), dtype=torch.bfloat16, device=dev)
+    kh = torch.empty_like(qh)
+    vt = torch.empty((B, H, ctx.nb, d, absh.vt_keys(w.block)), dtype=torch.bfloat16, device=dev)
+    oh = torch.empty_like(qh)
+    o = torch.empty_like(q)
+    routing = absh.alloc_routing(ctx, B, H)
+    ws = torch.empty(absh.route_workspace_bytes(ctx, B, H, d), dtype=torch.uint8, device=dev)
+
+    stages = ("permute", "route", "attn", "unpermute")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        absh.permute(ctx, q, out=qh)
+        absh.permute(ctx, k, out=kh)
+        absh.permute(ctx, v, layout=absh.ABSH_VT, out=vt)
+        if ev is not None:
+            ev[1].record(stream)
+        absh.route(ctx, qh, kh, p, w.k_floor, slack_frac=w.slack_frac, schedule=args.schedule, out=routing,
+                   workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+        absh.sparse_attn(ctx, qh, kh, vt, routing, out=oh)
+        if ev is not None:
+            ev[3].record(stream)
+        absh.unpermute(ctx, oh, out=o)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events])) for i, s in enumerate(stages)}
+    stage_min = {s: float(np.min([e[i].elapsed_time(e[i + 1]) for e in events])) for i, s in enumerate(stages)}
+
+    # retained work of this routing (identical every step: the path is deterministic)
+    counts = routing.counts.cpu().numpy().reshape(-1)
+    kv = routing.kv_idx.cpu().numpy().reshape(counts.size, ctx.nb)
+    sizes = np.minimum(w.block, w.N - np.arange(ctx.nb) * w.block).astype(np.int64)
+    # sum of n_j over each retained list: only the last block can be partial, and an
+    # ascending list holds it in its last slot
+    has_last = kv[np.arange(counts.size), counts - 1] == ctx.nb - 1
+    kv_tokens = counts.astype(np.int64) * w.block - has_last * (w.block - sizes[-1])
+    qi = np.tile(sizes, B * H)
+    f_ret = float(4.0 * d * np.sum(qi * kv_tokens))
+    density = float(counts.mean() / ctx.nb)
+
+    value = f_ret / (ms_per_step * 1e-3) / 1e12
+    attn_tflops = f_ret / (stage_ms["attn"] * 1e-3) / 1e12
+
+    dense_ms = None
+    if not args.no_dense:
+        absh.sparse_attn(ctx, qh, kh, vt, None, out=oh)
+        torch.cuda.synchronize()
+        de = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        times = []
+        for _ in range(args.dense_reps):
+            de[0].record(stream)
+            absh.sparse_attn(ctx, qh, kh, vt, None, out=oh)
+            de[1].record(stream)
+            torch.cuda.synchronize()
+            times.append(de[0].elapsed_time(de[1]))
+        dense_ms = float(np.mean(times))
+    n_all = float(4.0 * d * B * H * float(w.N) ** 2)
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("attn_bytes_per_launch")
+
+    roof = {
+        "bound": "mfma",
+        "kernel": "attn_kernel<128,64>",
+        "achieved": round(attn_tflops, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, p, data, args.cpu_tiles)
+
+    out = {
+        "metric": "effective bf16 TFLOP/s on retained blocks + speedup vs dense, 720p 40-head",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": B, "heads": H, "head_dim": d, "grid_t_y_x": [w.T, w.Y, w.X],
+            "tokens": w.N, "block": w.block, "blocks": ctx.nb, "p": p, "k_floor": w.k_floor,
+            "slack_frac": w.slack_frac, "schedule": args.schedule,
+        },
+        "density": round(density, 5),
+        "retained_tflop": round(f_ret / 1e12, 4),
+        "dense_tflop": round(n_all / 1e12, 4),
+        "stage_ms": {s: round(x, 4) for s, x in stage_ms.items()},
+        "stage_ms_min": {s: round(x, 4) for s, x in stage_min.items()},
+        "attn_effective_tflops": round(attn_tflops, 2),
+        "route_share_of_attn": round(stage_ms["route"] / stage_ms["attn"], 4),
+        "dense_attn_ms": None if dense_ms is None else round(dense_ms, 3),
+        "dense_tflops": None if dense_ms is None else round(n_all / (dense_ms * 1e-3) / 1e12, 2),
+        "speedup_vs_dense": None if dense_ms is None else round(dense_ms / stage_ms["attn"], 3),
+        "speedup_vs_dense_incl_route": None if dense_ms is None else
+        round(dense_ms / (stage_ms["attn"] + stage_ms["route"]), 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(w, p, data, n_tiles):
+    """The oracle on a bounded sample of the same workload, timed on the host cores.
+
+    Sample: head 0 of the workload. The oracle computes the Hilbert order, gathers
+    head 0's q, k, v, routes all of head 0's query blocks (block means, scores,
+    softmax, Top-p + floor), then runs attention for n_tiles query blocks of head 0
+    spread evenly over the head. Routing time is prorated to those tiles
+    (n_tiles / nb of it), so the figure is retained FLOPs of the sample tiles
+    divided by their share of the oracle's time.
+    """
+    import numpy as np
+    import threadpoolctl
+
+    import workloads as W
+    from oracle import absh_oracle as O
+
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    perm, _ = O.hilbert_perm(w.T, w.Y, w.X)
+    head = lambda name: W.bf16_to_f32(data[name + "16"][:, :, :1, :])
+    qh, kh, vh = (O.to_hilbert(head(n), perm) for n in ("q", "k", "v"))
+    R = O.route(qh, kh, w.block, p, w.k_floor)
+    t_route = time.perf_counter() - t0
+    nb = R.nb
+    tiles = np.linspace(0, nb - 1, n_tiles).round().astype(int)
+    t1 = time.perf_counter()
+    flops = 0.0
+    for i in tiles:
+        blocks = R.retained(0, 0, i)
+        O.attention_tile(qh[0, 0], kh[0, 0], vh[0, 0], w.block, i, blocks)
+        flops += 4.0 * w.d * R.sizes[i] * R.sizes[blocks].sum()
+    t_attn = time.perf_counter() - t1
+    t = t_attn + t_route * len(tiles) / nb
+    return {
+        "value": round(flops / t / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"head 0 of {w.name}: Hilbert order + full routing of its {nb} query blocks "
+                   f"({t_route:.2f} s, prorated to the sample), attention for {len(tiles)} query blocks "
+                   f"spread over the head ({t_attn:.2f} s); float64 NumPy"),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -24,6 +24,8 @@
  *    rows N..n_pad-1 are zero. nb = ceil(N / block) blocks of `block` tokens;
  *    block j holds Hilbert positions [j*block, min((j+1)*block, N)).
  *  - A tile is one (batch b, head h, query block i); its id is (b*H + h)*nb + i.
+ *  - Calls on one context must not overlap in time (the attention kernel's
+ *    tile counters live in the context); use one context per stream.
  *  - Arguments are validated on the host before any HIP call; a failure returns
  *    ABSH_EINVAL / ABSH_EUNSUPPORTED / ABSH_EWORKSPACE and launches nothing.
  *    HIP failures return ABSH_EHIP. absh_last_error() gives the detail of the
@@ -54,10 +56,21 @@ typedef enum { ABSH_BF16 = 0, ABSH_F32 = 1 } absh_dtype;
 /* Layout of a tensor in Hilbert order written by absh_permute. */
 typedef enum {
   ABSH_ROWS = 0, /* [B, H, n_pad, d] bf16: one row of d per token (queries, keys, outputs) */
-  ABSH_VT = 1    /* [B, H, nb, d, block] bf16: each block transposed, keys fastest (values) */
+  ABSH_VT = 1    /* [B, H, nb, d, KB] bf16, KB = max(block, 32): each block transposed, keys
+                    fastest, zero keys past `block` (values) */
 } absh_layout;
 
 typedef struct absh_ctx absh_ctx;
+
+/* Tile schedules for absh_sparse_attn (the one-GPU readings of the xllm-io
+ * review's runtime load balancing, section 三 Stage 2 and section 3.2). */
+typedef enum {
+  ABSH_SCHED_ORDER = 0, /* queue = tile ids in order, pulled by whichever CU is free          */
+  ABSH_SCHED_LPT = 1,   /* queue = tiles by retained count, longest first (ties: lower id)    */
+  ABSH_SCHED_XCD = 2    /* queue = tile ids in order, cut into eight runs of equal retained
+                           cost, one per XCD (L2 cache); an XCD whose run is done takes tiles
+                           from the next runs                                                  */
+} absh_schedule;
 
 /* Routing options (xllm-io review of FVAttn, section 五 "关键超参数": Top-p
  * operating points 0.90 / 0.95; explainer "Key Concepts": the Top-k floor). */
@@ -65,7 +78,7 @@ typedef struct {
   double p;            /* Top-p threshold in (0, 1]; p == 1 keeps every block              */
   int32_t k_floor;     /* Top-k safety floor, >= 0; clamped to nb                         */
   double slack_frac;   /* slack-fill budget beta in [0, 1): E = floor(beta * sum counts)  */
-  int32_t lpt;         /* 1: queue in longest-first order; 0: queue = tile ids in order   */
+  int32_t schedule;    /* an absh_schedule                                                */
   int32_t order_depth; /* 0..64: length of the importance-order prefix written to `order` */
 } absh_route_opts;
 
@@ -78,6 +91,7 @@ typedef struct {
   int32_t* work;   /* [B*H] sum_i counts (the numerator of Eq. 1, exact)                        */
   float* L;        /* [B*H] L_h = work / nb, float32 division (Eq. 1)                           */
   int32_t* queue;  /* [tiles] execution order of the tiles for absh_sparse_attn                 */
+  int32_t* sched;  /* [9] bounds of the eight queue runs, one per XCD (see absh_schedule)        */
 } absh_lists;
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -117,7 +131,9 @@ absh_status absh_perm_copy(const absh_ctx* ctx, int32_t* perm_dst, int32_t* inv_
 
 /* Gather a grid-order tensor x [B, N, H, d] (bf16, or f32 rounded to bf16 to
  * nearest-even) into Hilbert order, in the given layout, zero-filling pad rows.
- * xh must hold B*H*n_pad*d bf16. d must be 64 or 128. */
+ * ABSH_ROWS: xh holds B*H*n_pad*d bf16. ABSH_VT: xh holds B*H*nb*d*KB bf16 with
+ * KB = max(block, 32) keys per block (keys past `block` are zero). d must be 64
+ * or 128. */
 absh_status absh_permute(absh_ctx* ctx, const void* x, absh_dtype xt, void* xh, int B, int H, int d,
                          absh_layout layout, void* stream);
 
@@ -160,9 +176,12 @@ absh_status absh_route(absh_ctx* ctx, const void* qh, const void* kh, int B, int
  * over the tokens of its retained key blocks R (lists->kv_idx, ascending), with
  * the pad keys of a partial last block masked. lists == NULL runs dense
  * attention over every block with the same kernel. qh, kh: [B, H, n_pad, d]
- * bf16 (ABSH_ROWS); vt: [B, H, nb, d, block] bf16 (ABSH_VT); oh: [B, H, n_pad, d]
- * bf16 out (pad rows hold unspecified values). Scores and softmax in float32,
- * probabilities rounded to bf16 for the value product, float32 accumulation. */
+ * bf16 (ABSH_ROWS); vt: ABSH_VT layout; oh: [B, H, n_pad, d] bf16 out (pad rows
+ * hold unspecified values). Scores and softmax in float32, probabilities rounded
+ * to bf16 for the value product, float32 accumulation. Tiles are pulled by a
+ * persistent grid (one workgroup per CU slot) following lists->queue and
+ * lists->sched; dense mode splits the tiles evenly over the XCDs. Every tile is
+ * computed the same way whatever the schedule, so outputs do not depend on it. */
 absh_status absh_sparse_attn(absh_ctx* ctx, const void* qh, const void* kh, const void* vt, int B, int H,
                              int d, const absh_lists* lists, void* oh, void* stream);
 

@@ -139,7 +139,9 @@ def test_permute_rows_and_vt_bit_exact(index):
     assert (got[:, :, w.N:] == 0).all()
     vpad = np.zeros((w.B, w.H, w.nb * w.block, w.d), dtype=np.uint16)
     vpad[:, :, : w.N] = np.transpose(c.bits["v16"][:, c.perm], (0, 2, 1, 3))
-    want_vt = vpad.reshape(w.B, w.H, w.nb, w.block, w.d).transpose(0, 1, 2, 4, 3)
+    kb = absh.vt_keys(w.block)
+    want_vt = np.zeros((w.B, w.H, w.nb, w.d, kb), dtype=np.uint16)
+    want_vt[..., : w.block] = vpad.reshape(w.B, w.H, w.nb, w.block, w.d).transpose(0, 1, 2, 4, 3)
     assert np.array_equal(bf16_bits_of(c.vt).reshape(want_vt.shape), want_vt)
 
 
@@ -178,7 +180,7 @@ def test_route_matches_oracle(index, p):
     c = case(index)
     w = c.w
     p = w.p if p is None else p
-    r = absh.route(c.ctx, c.qh, c.kh, p, w.k_floor, lpt=True)
+    r = absh.route(c.ctx, c.qh, c.kh, p, w.k_floor, schedule="lpt")
     torch.cuda.synchronize()
     counts, kv, queue = check_lists_valid(r, w.nb)
     R = c.oracle_route(p=p)
@@ -191,8 +193,9 @@ def test_route_matches_oracle(index, p):
     assert np.array_equal(work, counts.sum(-1))
     assert np.array_equal(L, (work.astype(np.float32) / np.float32(w.nb)).astype(np.float32))
     assert (counts >= min(w.k_floor, w.nb)).all()
-    # LPT queue: exactly the oracle's order for these counts
+    # LPT queue: exactly the oracle's order for these counts; one run holds it all
     assert np.array_equal(queue, O.lpt_queue(counts))
+    assert r.sched.cpu().numpy().tolist() == [0] + [w.tiles] * 8
     if excused == 0:
         wo, Lo = O.workloads(R.counts)
         assert np.array_equal(work, wo) and np.array_equal(L, Lo)
@@ -225,8 +228,8 @@ def test_order_prefix_past_nb_is_minus_one():
 def test_slack_fill_matches_oracle():
     c = case(3)
     w = c.w
-    base = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=0.0, lpt=True)
-    filled = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, lpt=True)
+    base = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=0.0, schedule="lpt")
+    filled = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, schedule="lpt")
     torch.cuda.synchronize()
     c0, _, _ = check_lists_valid(base, w.nb)
     c1, kv1, q1 = check_lists_valid(filled, w.nb)
@@ -296,7 +299,7 @@ def test_attention_tiny_all_tiles():
 def test_attention_sampled_tiles(index):
     c = case(index)
     w = c.w
-    r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, lpt=True)
+    r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, schedule="lpt")
     counts, _, _ = check_lists_valid(r, w.nb)
     rng = np.random.default_rng(100 + index)
     flat = counts.reshape(-1)
@@ -312,7 +315,7 @@ def test_attention_sampled_tiles(index):
 def test_p_one_sparse_equals_dense(index):
     c = case(index)
     w = c.w
-    r = absh.route(c.ctx, c.qh, c.kh, 1.0, 0, lpt=True)
+    r = absh.route(c.ctx, c.qh, c.kh, 1.0, 0, schedule="lpt")
     counts, kv, _ = check_lists_valid(r, w.nb)
     assert (counts == w.nb).all()
     sparse = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r)
@@ -330,21 +333,41 @@ def test_dense_matches_oracle_tiny():
     assert e.max() <= ATOL_MAX and e.mean() <= ATOL_MEAN
 
 
-def test_lpt_on_off_and_repeat_bit_identical():
-    c = case(1)
+def expected_xcd_bounds(counts, overhead=1, segments=8):
+    """Cut the tile ids where the running cost (count + overhead) first reaches x/8 of the total."""
+    cost = counts.reshape(-1).astype(np.int64) + overhead
+    before = np.concatenate([[0], np.cumsum(cost)])[:-1]
+    total = int(cost.sum())
+    bounds = [0]
+    for x in range(1, segments):
+        target = -(-total * x // segments)
+        bounds.append(int(np.searchsorted(before, target, side="left")))
+    return bounds + [cost.size]
+
+
+@pytest.mark.parametrize("index", [1, 3])
+def test_schedules_bit_identical(index):
+    c = case(index)
     w = c.w
-    a = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, lpt=True)
-    b = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, lpt=False)
-    check_lists_valid(a, w.nb)
-    check_lists_valid(b, w.nb)
-    assert np.array_equal(b.queue.cpu().numpy(), np.arange(w.tiles))
-    oa = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, a)
-    ob = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, b)
-    oc = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, a)
+    outs = {}
+    for sched in ("order", "lpt", "xcd"):
+        r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, schedule=sched)
+        counts, _, queue = check_lists_valid(r, w.nb)
+        bounds = r.sched.cpu().numpy().tolist()
+        if sched == "order":
+            assert np.array_equal(queue, np.arange(w.tiles)) and bounds == [0] + [w.tiles] * 8
+        elif sched == "lpt":
+            assert np.array_equal(queue, O.lpt_queue(counts)) and bounds == [0] + [w.tiles] * 8
+        else:
+            assert np.array_equal(queue, np.arange(w.tiles))
+            assert bounds == expected_xcd_bounds(counts), (bounds, expected_xcd_bounds(counts))
+        outs[sched] = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r)
+        outs[sched + "2"] = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r)
     torch.cuda.synchronize()
     rows = torch.arange(w.N, device=DEV)
-    assert torch.equal(oa[:, :, rows].view(torch.int16), ob[:, :, rows].view(torch.int16))
-    assert torch.equal(oa.view(torch.int16), oc.view(torch.int16))
+    ref = outs["order"][:, :, rows].view(torch.int16)
+    for k, v in outs.items():
+        assert torch.equal(v[:, :, rows].view(torch.int16), ref), k
 
 
 # ---------------------------------------------------------------- edge shapes
@@ -369,7 +392,7 @@ def test_edge_shapes(grid, block, d, H, B, p, k):
     qd, kd, vd = (to_dev_bf16(b) for b in bits)
     qh, kh = absh.permute(ctx, qd), absh.permute(ctx, kd)
     vt = absh.permute(ctx, vd, layout=absh.ABSH_VT)
-    r = absh.route(ctx, qh, kh, p, k, slack_frac=0.25, lpt=True)
+    r = absh.route(ctx, qh, kh, p, k, slack_frac=0.25, schedule="lpt")
     counts, kv, _ = check_lists_valid(r, ctx.nb)
     perm, _ = O.hilbert_perm(T, Y, X)
     hq, hk, hv = (O.to_hilbert(W.bf16_to_f32(b), perm) for b in bits)
