@@ -44,7 +44,8 @@ class RouteOpts(ctypes.Structure):
 class Lists(ctypes.Structure):
     _fields_ = [("counts", ctypes.c_void_p), ("kv_idx", ctypes.c_void_p), ("order", ctypes.c_void_p),
                 ("work", ctypes.c_void_p), ("L", ctypes.c_void_p), ("queue", ctypes.c_void_p),
-                ("sched", ctypes.c_void_p)]
+                ("sched", ctypes.c_void_p), ("pairs", ctypes.c_void_p), ("pair_cnt", ctypes.c_void_p),
+                ("schedule", ctypes.c_int32)]
 
 
 _lib = None
@@ -204,12 +205,16 @@ class Routing:
     work: object     # int32 [B, H]
     L: object        # float32 [B, H]
     queue: object    # int32 [B*H*nb]
-    sched: object    # int32 [9] bounds of the per-XCD runs of the queue
+    sched: object    # int32 [10] bounds of the per-XCD runs of the work queue + unit kind
+    pairs: object    # int32 [B*H*npairs, nb] flagged union lists of query-block pairs
+    pair_cnt: object  # int32 [B*H*npairs]
+    schedule: int = -1  # the schedule absh_route made these lists for
 
     def lists(self) -> Lists:
         return Lists(self.counts.data_ptr(), self.kv_idx.data_ptr(),
                      self.order.data_ptr() if self.order is not None else 0,
-                     self.work.data_ptr(), self.L.data_ptr(), self.queue.data_ptr(), self.sched.data_ptr())
+                     self.work.data_ptr(), self.L.data_ptr(), self.queue.data_ptr(), self.sched.data_ptr(),
+                     self.pairs.data_ptr(), self.pair_cnt.data_ptr(), self.schedule)
 
 
 def route_workspace_bytes(ctx: Context, B: int, H: int, d: int) -> int:
@@ -227,7 +232,9 @@ def alloc_routing(ctx: Context, B: int, H: int, order_depth: int = 0) -> Routing
         work=torch.empty((B, H), dtype=torch.int32, device=dev),
         L=torch.empty((B, H), dtype=torch.float32, device=dev),
         queue=torch.empty((B * H * nb,), dtype=torch.int32, device=dev),
-        sched=torch.empty((9,), dtype=torch.int32, device=dev),
+        sched=torch.empty((10,), dtype=torch.int32, device=dev),
+        pairs=torch.empty((B * H * ((nb + 1) // 2), nb), dtype=torch.int32, device=dev),
+        pair_cnt=torch.empty((B * H * ((nb + 1) // 2),), dtype=torch.int32, device=dev),
     )
 
 
@@ -249,6 +256,7 @@ def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0,
     lists = out.lists()
     _check(lib().absh_route(ctx.handle, _ptr(qh), _ptr(kh), B, H, d, ctypes.byref(opts), ctypes.byref(lists),
                             _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    out.schedule = lists.schedule
     return out
 
 

@@ -56,18 +56,32 @@ struct RouteBuffers {
   int64_t* slack_info;  // [4] lambda, remainder, E, total
   int32_t* chunk_hist;  // [chunks][nb + 1]
   int32_t* rank;        // [tiles]
-  int32_t* sched;       // [9] queue segment bounds, one segment per XCD
+  int32_t* sched;       // [10] queue segment bounds (one segment per XCD) and the unit kind
+  uint32_t* pair_list;  // [units][nb] union lists of query-block pairs
+  int32_t* pair_cnt;    // [units]
 };
 hipError_t launch_select(const absh_ctx* c, const RouteBuffers& rb, int tiles, double p, int k_floor,
                          int order_depth, int reselect, hipStream_t s);
 hipError_t launch_slack_plan(const absh_ctx* c, const RouteBuffers& rb, int tiles, double beta, hipStream_t s);
 hipError_t launch_workload(const absh_ctx* c, const RouteBuffers& rb, int BH, hipStream_t s);
 hipError_t launch_queue(const absh_ctx* c, const RouteBuffers& rb, int tiles, int lpt, hipStream_t s);
-hipError_t launch_segments(const absh_ctx* c, const RouteBuffers& rb, int BH, int balanced, hipStream_t s);
+hipError_t launch_pairs(const absh_ctx* c, const RouteBuffers& rb, int BH, hipStream_t s);
+hipError_t launch_segments(const absh_ctx* c, const RouteBuffers& rb, int BH, int schedule, hipStream_t s);
 int queue_chunks(int tiles);
 
+// Work units of the attention kernel.
+enum UnitKind { kUnitSingle = 1, kUnitPair = 2 };
+
+struct AttnLists {
+  const int32_t* queue;      // single units: queue position -> tile
+  const int32_t* counts;     // [tiles]
+  const int32_t* kv_idx;     // [tiles][nb]
+  const uint32_t* pair_list;  // pair units: [units][nb] flagged union entries
+  const int32_t* pair_cnt;   // [units]
+  const int32_t* sched;      // [10] segment bounds + unit kind (read by the kernel)
+  int kind;                  // kUnitSingle or kUnitPair (host copy of sched[9])
+};
 hipError_t launch_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B,
-                            int H, int d, const int32_t* queue, const int32_t* counts, const int32_t* kv_idx,
-                            const int32_t* bounds, hipStream_t s);
+                            int H, int d, const AttnLists* lists, hipStream_t s);
 
 }  // namespace absh

@@ -3,16 +3,22 @@
 // each head attends only to its selected KV blocks), for gfx950.
 //
 // Persistent kernel: one workgroup per (CU, occupancy slot). A workgroup pulls
-// tiles (b, h, query block i) from the tile queue, one at a time, with an atomic
-// counter per segment of the queue. The queue is cut into eight segments, one per
-// XCD; a workgroup pulls from its own XCD's segment first and then steals from
-// the others in turn. With one segment holding every tile this is plain list
-// scheduling in queue order (the longest-first order when the queue is LPT);
-// with the eight-way cost-balanced split of the queue it keeps the tiles that run
-// together on one XCD (one L2) contiguous in Hilbert order, so they share K/V.
+// work units one at a time, with an atomic counter per segment of the unit
+// queue. The queue is cut into eight segments, one per XCD; a workgroup pulls
+// from its own XCD's segment first and then steals from the others in turn. With
+// one segment holding every unit this is plain list scheduling in queue order
+// (the longest-first order for the LPT queue); with the eight-way cost-balanced
+// split it keeps the units that run together on one XCD (one L2) contiguous in
+// Hilbert order, so they share K/V.
 //
-// Per tile, one wave per 16 query rows. For every retained key block j, in
-// ascending order:
+// A unit is either one tile (b, h, query block i), taken from the tile queue, or
+// a pair of neighbouring query blocks (2p, 2p+1) of one head that walk the union
+// of their retained lists together: each staged K/V block, and each K/V operand
+// fragment read from LDS, then serves both blocks, which halves the K/V traffic
+// per flop; a block retained by only one member skips the other's MFMAs.
+//
+// Per unit, one wave per 16 query rows of each member. For every key block j of
+// the unit's list, in ascending order:
 //   S^T = K_j Q_i^T         16x16x32 bf16 MFMA, fp32 accumulate
 //   online softmax          fp32, base-2 exponent, lazy rescale of O
 //   O^T += V_j^T P^T        16x16x32 bf16 MFMA, P rounded to bf16
@@ -32,6 +38,8 @@
 // LDS layout: rows are stored unpadded (the direct loads write 1 KB runs) and the
 // sixteen-byte chunks of a row are XOR-swizzled by a function of the row, chosen
 // so that the sixteen rows one quarter-wave reads land on distinct banks.
+#include <type_traits>
+
 #include "absh_internal.h"
 
 namespace absh {
@@ -41,6 +49,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSegments = 8;  // XCDs of an MI355X: one queue segment each
+constexpr uint32_t kInFirst = 1u << 30;   // list entry flag: the unit's first query block retains it
+constexpr uint32_t kInSecond = 1u << 31;  // list entry flag: the second query block retains it
+constexpr uint32_t kBlockMask = kInFirst - 1;
 
 template <int D, int BLK>
 struct Cfg {
@@ -103,11 +114,10 @@ __device__ __forceinline__ int pull(int32_t* counters, const int32_t* bounds, in
 }
 
 template <int D, int BLK>
-__global__ __launch_bounds__((Cfg<D, BLK>::THREADS)) void attn_kernel(
+__global__ __launch_bounds__((Cfg<D, BLK>::THREADS)) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(
     const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, const bf16_t* __restrict__ vt,
-    bf16_t* __restrict__ oh, const int32_t* __restrict__ queue, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ bounds, int32_t* __restrict__ counters,
-    int tiles, int nb, int n_pad, int N, float scale_log2) {
+    bf16_t* __restrict__ oh, AttnLists L, int32_t* __restrict__ counters, int units, int nb, int n_pad, int N,
+    float scale_log2) {
   using C = Cfg<D, BLK>;
   __shared__ __attribute__((aligned(1024))) char stage0[C::K_BYTES + C::V_BYTES];
   __shared__ __attribute__((aligned(1024))) char stage1[C::K_BYTES + C::V_BYTES];
@@ -119,6 +129,9 @@ __global__ __launch_bounds__((Cfg<D, BLK>::THREADS)) void attn_kernel(
   const int n = lane & 15;
   const int g = lane >> 4;
   const int xcd = blockIdx.x & (kSegments - 1);
+  const int npairs = (nb + 1) >> 1;
+  const bool dense = L.counts == nullptr;
+  const bool pairs = dense || L.kind == kUnitPair;
 
   if (BLK < C::KB) {  // padding keys of both stages stay zero: the loads never write them
     for (int e = tid * 4; e < C::K_BYTES + C::V_BYTES; e += C::THREADS * 4) {
@@ -154,23 +167,46 @@ __global__ __launch_bounds__((Cfg<D, BLK>::THREADS)) void attn_kernel(
 #pragma unroll
   for (int u = 0; u < C::KS; ++u) v_rd[u] = C::K_BYTES + n * C::V_ROW + (((4 * u + g) ^ v_swz<C::KB>(n)) * 16);
 
+  const int32_t* bounds = dense ? nullptr : L.sched;
   unsigned dead = 0;
-  if (tid == 0) s_next = pull(counters, bounds, tiles, xcd, dead);
+  if (tid == 0) s_next = pull(counters, bounds, units, xcd, dead);
   __syncthreads();
 
   for (;;) {
     // wave-uniform values (readfirstlane) so that queue and list reads are scalar loads
     const int pos = __builtin_amdgcn_readfirstlane(s_next);
     if (pos < 0) break;
-    const int tile = __builtin_amdgcn_readfirstlane(queue ? as_const(queue)[pos] : pos);
-    const int bh = tile / nb;
-    const int qb = tile - bh * nb;
-    const int cnt = counts ? as_const(counts)[tile] : nb;
-    const const_i32 list = counts ? as_const(kv_idx + (size_t)tile * nb) : nullptr;
+    int tile0, tile1, cnt;
+    const_i32 plain = nullptr;     // single unit: plain ascending block ids
+    const_i32 flagged = nullptr;   // pair unit: flagged union entries
+    if (pairs) {
+      const int bh = pos / npairs;
+      const int pr = pos - bh * npairs;
+      tile0 = bh * nb + 2 * pr;
+      tile1 = 2 * pr + 1 < nb ? tile0 + 1 : -1;
+      cnt = dense ? nb : as_const(L.pair_cnt)[pos];
+      if (!dense) flagged = as_const(reinterpret_cast<const int32_t*>(L.pair_list) + (size_t)pos * nb);
+    } else {
+      tile0 = __builtin_amdgcn_readfirstlane(as_const(L.queue)[pos]);
+      tile1 = -1;
+      cnt = as_const(L.counts)[tile0];
+      plain = as_const(L.kv_idx + (size_t)tile0 * nb);
+    }
+    const int bh = tile0 / nb;
+    const int qb0 = tile0 - bh * nb;
+    const bool two = tile1 >= 0;
+    const uint32_t both = two ? (kInFirst | kInSecond) : kInFirst;
+    // entry k of the unit's list: block id | membership flags
+    auto entry = [&](int k) __attribute__((always_inline)) -> uint32_t {
+      if (flagged) return (uint32_t)flagged[k];
+      if (plain) return (uint32_t)plain[k] | kInFirst;
+      return (uint32_t)k | both;
+    };
     const char* kbase = reinterpret_cast<const char*>(kh + (size_t)bh * n_pad * D);
     const char* vbase = reinterpret_cast<const char*>(vt + (size_t)bh * nb * D * C::KB);
 
-    auto issue = [&](char* st, int j) {
+    auto issue = [&](char* st, uint32_t e) __attribute__((always_inline)) {
+      const int j = (int)(e & kBlockMask);
       const char* ks = kbase + (size_t)j * BLK * C::K_ROW;
       const char* vs = vbase + (size_t)j * C::V_BYTES;
 #pragma unroll
@@ -180,110 +216,140 @@ __global__ __launch_bounds__((Cfg<D, BLK>::THREADS)) void attn_kernel(
         load_lds16(vs + v_src[u], st + C::K_BYTES + (wave * C::V_PER_WAVE + u) * 1024);
     };
 
-    // block ids: the current one, the next (whose loads are issued one block
+    // list entries: the current one, the next (whose loads are issued one block
     // ahead) and the one after (read one block ahead of its use)
-    int j_cur = list ? list[0] : 0;
-    int j_nxt = cnt > 1 ? (list ? list[1] : 1) : 0;
-    issue(stage0, j_cur);
-    // this lane's query row as the B operand of S^T = K Q^T: channels 32s + 8g .. +8
-    const int qrow = qb * BLK + wave * 16 + n;
-    const bf16_t* qsrc = qh + ((size_t)bh * n_pad + qrow) * D;
-    bf16x8 qf[C::DS];
+    uint32_t e_cur = entry(0);
+    uint32_t e_nxt = cnt > 1 ? entry(1) : 0u;
+    issue(stage0, e_cur);
+    // each member's query rows as the B operand of S^T = K Q^T: channels 32s + 8g .. +8
+    bf16x8 qf[2][C::DS];
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qsrc + 32 * s + 8 * g);
+    for (int m = 0; m < 2; ++m) {
+      if (m == 1 && !two) break;
+      const int qrow = (qb0 + m) * BLK + wave * 16 + n;
+      const bf16_t* qsrc = qh + ((size_t)bh * n_pad + qrow) * D;
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) qf[m][s] = *reinterpret_cast<const bf16x8*>(qsrc + 32 * s + 8 * g);
+    }
     __syncthreads();  // every thread has read s_next
-    if (tid == 0) s_next = pull(counters, bounds, tiles, xcd, dead);  // next tile, read after the loop
+    if (tid == 0) s_next = pull(counters, bounds, units, xcd, dead);  // next unit, read after the loop
     wait_vm0();
     __syncthreads();
 
-    f32x4 o[C::DT];
+    f32x4 o[2][C::DT];
+    float m_run[2], l_run[2];
 #pragma unroll
-    for (int t = 0; t < C::DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;  // running max of this lane's row, base-2 scaled
-    float l_run = 0.f;        // this lane's share of the row's running sum
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t) o[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run[m] = -INFINITY;  // running max of this lane's row, base-2 scaled
+      l_run[m] = 0.f;        // this lane's share of the row's running sum
+    }
 
-    auto block = [&](const char* cur, char* nxt, int it) {
-      const int j = j_cur;
-      const int j_after = it + 2 < cnt ? (list ? list[it + 2] : it + 2) : 0;
-      if (it + 1 < cnt) issue(nxt, j_nxt);
-      f32x4 sacc[C::KT];
+    // One key block for the members in `mask` (bit 0 first, bit 1 second).
+    auto block = [&](const char* cur, char* nxt, int it, auto members) __attribute__((always_inline)) {
+      constexpr int MASK = decltype(members)::value;
+      const int j = (int)(e_cur & kBlockMask);
+      const uint32_t e_after = it + 2 < cnt ? entry(it + 2) : 0u;
+      if (it + 1 < cnt) issue(nxt, e_nxt);
+      f32x4 sacc[2][C::KT];
 #pragma unroll
       for (int t = 0; t < C::KT; ++t) {
-        sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sacc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sacc[1][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int trow = 32 * (t >> 1) + 4 * (t & 1);  // lane-independent part of krow
 #pragma unroll
         for (int s = 0; s < C::DS; ++s) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(cur + k_rd[s] + trow * C::K_ROW);
-          sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], sacc[t], 0, 0, 0);
+          if (MASK & 1) sacc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][s], sacc[0][t], 0, 0, 0);
+          if (MASK & 2) sacc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][s], sacc[1][t], 0, 0, 0);
         }
       }
       // accumulator element r of tile t is key 32*(t/2) + 8g + 4*(t%2) + r of this block
       const int nj = min(BLK, N - j * BLK);
-      if (nj < C::KB) {
+      bf16x8 pf[2][C::KS];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (!((MASK >> m) & 1)) continue;
+        if (nj < C::KB) {
+#pragma unroll
+          for (int t = 0; t < C::KT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (32 * (t >> 1) + 8 * g + 4 * (t & 1) + r >= nj) sacc[m][t][r] = -INFINITY;
+        }
+        float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < C::KT; ++t)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (32 * (t >> 1) + 8 * g + 4 * (t & 1) + r >= nj) sacc[t][r] = -INFINITY;
-      }
-      float mx = -INFINITY;
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[m][t][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[m], mx * scale_log2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[m] - m_new);
+        float rowsum = 0.f;
 #pragma unroll
-      for (int t = 0; t < C::KT; ++t)
+        for (int u = 0; u < C::KS; ++u) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[t][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-
-      bf16x8 pf[C::KS];
-      float rowsum = 0.f;
-#pragma unroll
-      for (int u = 0; u < C::KS; ++u) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * u][r], scale_log2, -m_new));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * u + 1][r], scale_log2, -m_new));
-          rowsum += p0 + p1;
-          pf[u][r] = (__bf16)p0;
-          pf[u][4 + r] = (__bf16)p1;
+          for (int r = 0; r < 4; ++r) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[m][2 * u][r], scale_log2, -m_new));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[m][2 * u + 1][r], scale_log2, -m_new));
+            rowsum += p0 + p1;
+            pf[m][u][r] = (__bf16)p0;
+            pf[m][u][4 + r] = (__bf16)p1;
+          }
         }
-      }
-      l_run = l_run * alpha + rowsum;
-      if (__any(m_new != m_run)) {
+        l_run[m] = l_run[m] * alpha + rowsum;
+        if (__any(m_new != m_run[m])) {
 #pragma unroll
-        for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
+          for (int t = 0; t < C::DT; ++t) o[m][t] *= alpha;
+        }
+        m_run[m] = m_new;
       }
-      m_run = m_new;
 #pragma unroll
       for (int t = 0; t < C::DT; ++t) {
 #pragma unroll
         for (int u = 0; u < C::KS; ++u) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(cur + v_rd[u] + 16 * t * C::V_ROW);
-          o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[u], o[t], 0, 0, 0);
+          if (MASK & 1) o[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[0][u], o[0][t], 0, 0, 0);
+          if (MASK & 2) o[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[1][u], o[1][t], 0, 0, 0);
         }
       }
-      j_cur = j_nxt;
-      j_nxt = j_after;
+      e_cur = e_nxt;
+      e_nxt = e_after;
       wait_vm0();
       __syncthreads();
     };
+    auto step = [&](const char* cur, char* nxt, int it) __attribute__((always_inline)) {
+      const uint32_t f = e_cur & (kInFirst | kInSecond);
+      if (f == (kInFirst | kInSecond))
+        block(cur, nxt, it, std::integral_constant<int, 3>());
+      else if (f == kInFirst)
+        block(cur, nxt, it, std::integral_constant<int, 1>());
+      else
+        block(cur, nxt, it, std::integral_constant<int, 2>());
+    };
 
     for (int it = 0; it < cnt; it += 2) {
-      block(stage0, stage1, it);
-      if (it + 1 < cnt) block(stage1, stage0, it + 1);
+      step(stage0, stage1, it);
+      if (it + 1 < cnt) step(stage1, stage0, it + 1);
     }
 
-    float l = l_run + __shfl_xor(l_run, 16);
-    l += __shfl_xor(l, 32);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    bf16_t* orow = oh + ((size_t)bh * n_pad + qrow) * D;
 #pragma unroll
-    for (int t = 0; t < C::DT; ++t) {
-      uint2 w;
-      w.x = (uint32_t)f32_to_bf16(o[t][0] * inv) | ((uint32_t)f32_to_bf16(o[t][1] * inv) << 16);
-      w.y = (uint32_t)f32_to_bf16(o[t][2] * inv) | ((uint32_t)f32_to_bf16(o[t][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(orow + 16 * t + 4 * g) = w;
+    for (int m = 0; m < 2; ++m) {
+      if (m == 1 && !two) break;
+      float l = l_run[m] + __shfl_xor(l_run[m], 16);
+      l += __shfl_xor(l, 32);
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int qrow = (qb0 + m) * BLK + wave * 16 + n;
+      bf16_t* orow = oh + ((size_t)bh * n_pad + qrow) * D;
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t) {
+        uint2 w;
+        w.x = (uint32_t)f32_to_bf16(o[m][t][0] * inv) | ((uint32_t)f32_to_bf16(o[m][t][1] * inv) << 16);
+        w.y = (uint32_t)f32_to_bf16(o[m][t][2] * inv) | ((uint32_t)f32_to_bf16(o[m][t][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(orow + 16 * t + 4 * g) = w;
+      }
     }
   }
 
@@ -299,8 +365,7 @@ __global__ __launch_bounds__((Cfg<D, BLK>::THREADS)) void attn_kernel(
 
 template <int D, int BLK>
 hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B, int H,
-                  const int32_t* queue, const int32_t* counts, const int32_t* kv_idx, const int32_t* bounds,
-                  hipStream_t s) {
+                  const AttnLists* lists, hipStream_t s) {
   using C = Cfg<D, BLK>;
   static int per_cu = 0;  // resident workgroups per CU for this instantiation
   if (per_cu == 0) {
@@ -308,23 +373,23 @@ hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void*
     if (e != hipSuccess) return e;
     if (per_cu < 1) per_cu = 1;
   }
-  const int tiles = B * H * c->nb;
+  AttnLists L = lists ? *lists : AttnLists{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, kUnitPair};
+  const int npairs = (c->nb + 1) / 2;
+  const int units = (lists && L.kind == kUnitSingle) ? B * H * c->nb : B * H * npairs;
   const int grid = c->num_cus * per_cu;
   const float scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
   attn_kernel<D, BLK><<<grid, C::THREADS, 0, s>>>(
       reinterpret_cast<const bf16_t*>(qh), reinterpret_cast<const bf16_t*>(kh), reinterpret_cast<const bf16_t*>(vt),
-      reinterpret_cast<bf16_t*>(oh), queue, counts, kv_idx, bounds, c->counters, tiles, c->nb, c->n_pad, c->N,
-      scale_log2);
+      reinterpret_cast<bf16_t*>(oh), L, c->counters, units, c->nb, c->n_pad, c->N, scale_log2);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B,
-                            int H, int d, const int32_t* queue, const int32_t* counts, const int32_t* kv_idx,
-                            const int32_t* bounds, hipStream_t s) {
+                            int H, int d, const AttnLists* lists, hipStream_t s) {
 #define ABSH_ATTN(DD, BB) \
-  if (d == DD && c->block == BB) return launch<DD, BB>(c, qh, kh, vt, oh, B, H, queue, counts, kv_idx, bounds, s);
+  if (d == DD && c->block == BB) return launch<DD, BB>(c, qh, kh, vt, oh, B, H, lists, s);
   ABSH_ATTN(64, 16)
   ABSH_ATTN(64, 64)
   ABSH_ATTN(64, 128)

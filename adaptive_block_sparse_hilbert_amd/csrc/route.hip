@@ -437,89 +437,111 @@ __global__ __launch_bounds__(256) void queue_identity_kernel(int tiles, int32_t*
   if (t < tiles) queue[t] = t;
 }
 
+// ------------------------------------------------------------------ query-block pairs
+
+// One wave per pair unit u = (bh, p): query blocks 2p and 2p + 1 of head bh (the
+// second is absent when 2p + 1 == nb). Writes the ascending union of the two
+// retained lists, each entry j | (in first << 30) | (in second << 31), and its
+// length. Lane l owns block ids 32l .. 32l + 31 as two bitmaps in LDS.
+constexpr uint32_t kInFirst = 1u << 30;
+constexpr uint32_t kInSecond = 1u << 31;
+
+__global__ __launch_bounds__(256) void pair_merge_kernel(const int32_t* __restrict__ counts,
+                                                         const int32_t* __restrict__ kv_idx, int nb, int npairs,
+                                                         int units, uint32_t* __restrict__ pair_list,
+                                                         int32_t* __restrict__ pair_cnt) {
+  __shared__ uint32_t bits[4][2][64];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int u = blockIdx.x * 4 + w;
+  if (u >= units) return;
+  const int bh = u / npairs;
+  const int pr = u - bh * npairs;
+  const int64_t ta = (int64_t)bh * nb + 2 * pr;
+  const bool has_b = 2 * pr + 1 < nb;
+  bits[w][0][lane] = 0u;
+  bits[w][1][lane] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int ca = counts[ta];
+  for (int i = lane; i < ca; i += 64) {
+    const int j = kv_idx[ta * nb + i];
+    atomicOr(&bits[w][0][j >> 5], 1u << (j & 31));
+  }
+  if (has_b) {
+    const int cb = counts[ta + 1];
+    for (int i = lane; i < cb; i += 64) {
+      const int j = kv_idx[(ta + 1) * nb + i];
+      atomicOr(&bits[w][1][j >> 5], 1u << (j & 31));
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const uint32_t wa = bits[w][0][lane], wb = bits[w][1][lane], wu = wa | wb;
+  const int mine = __popc(wu);
+  int incl = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  int pos = incl - mine;
+  uint32_t* out = pair_list + (size_t)u * nb;
+  for (int k = 0; k < 32; ++k) {
+    if ((wu >> k) & 1u) {
+      const uint32_t j = (uint32_t)(lane * 32 + k);
+      out[pos++] = j | (((wa >> k) & 1u) ? kInFirst : 0u) | (((wb >> k) & 1u) ? kInSecond : 0u);
+    }
+  }
+  if (lane == 63) pair_cnt[u] = incl;
+}
+
 // ------------------------------------------------------------------ queue segments (one per XCD)
 
 constexpr int kSegments = 8;
-constexpr int kTileOverhead = 1;  // per-tile cost of the query load and output write, in key blocks
+constexpr int kUnitOverhead = 1;  // per-unit cost of the query loads and output writes, in key blocks
 
 // sched[0..8]: bounds of the eight queue segments the attention kernel pulls
-// from, one per XCD. balanced == 0: one segment holds the whole queue (plain list
-// scheduling in queue order). balanced != 0: the queue is the tile ids in order
-// and it is cut where the running cost sum (retained blocks + overhead) crosses
-// x/8 of the total, so each XCD gets a contiguous, equally heavy run of tiles
-// (whole heads where they fit): the one-GPU reading of the review's RLB, with
-// the XCDs (separate L2 caches) as the ranks.
-__global__ __launch_bounds__(1024) void segments_kernel(const int32_t* __restrict__ counts,
-                                                        const int32_t* __restrict__ work, int BH, int nb,
-                                                        int balanced, int32_t* __restrict__ sched) {
+// from, one per XCD, over `units` work units with costs cost[u] (retained key
+// blocks; NULL = all equal). balanced == 0: one segment holds every unit (plain
+// list scheduling in queue order). balanced != 0: the units, in order, are cut
+// where the running cost (cost + overhead) first reaches x/8 of the total, so
+// each XCD gets a contiguous, equally heavy run of neighbouring query blocks:
+// the one-GPU reading of the review's RLB with the XCDs (separate L2 caches) as
+// the ranks. sched[9] = the unit kind for the attention kernel.
+__global__ __launch_bounds__(1024) void segments_kernel(const int32_t* __restrict__ cost, int units, int balanced,
+                                                        int kind, int32_t* __restrict__ sched) {
   __shared__ int64_t buf[1024];
   __shared__ int64_t target[kSegments + 1];
-  __shared__ int32_t head_of[kSegments + 1];
-  __shared__ int64_t base_of[kSegments + 1];
-  const int64_t tiles = (int64_t)BH * nb;
+  __shared__ int32_t bound[kSegments + 1];
+  if (threadIdx.x == 0) sched[kSegments + 1] = kind;
   if (!balanced) {
-    if (threadIdx.x <= kSegments) sched[threadIdx.x] = threadIdx.x == 0 ? 0 : (int32_t)tiles;
+    if (threadIdx.x <= kSegments) sched[threadIdx.x] = threadIdx.x == 0 ? 0 : units;
     return;
   }
-  // total cost and the target of each inner bound
   int64_t mine = 0;
-  for (int h = threadIdx.x; h < BH; h += 1024) mine += (int64_t)work[h] + (int64_t)nb * kTileOverhead;
+  for (int u = threadIdx.x; u < units; u += 1024) mine += (int64_t)cost[u] + kUnitOverhead;
   int64_t total;
   block_exclusive_scan<int64_t>(mine, buf, total);
   if (threadIdx.x <= kSegments) {
     target[threadIdx.x] = (total * threadIdx.x + kSegments - 1) / kSegments;
-    head_of[threadIdx.x] = BH;
-    base_of[threadIdx.x] = total;
+    bound[threadIdx.x] = units;
   }
   __syncthreads();
-  // the head holding each target: exclusive prefix < target <= inclusive prefix
+  // bound x = the smallest u whose preceding cost reaches target x: the unit v
+  // with before(v) < target <= before(v) + cost(v) ends just before it
   int64_t seen = 0;
-  for (int h0 = 0; h0 < BH; h0 += 1024) {
-    const int h = h0 + threadIdx.x;
-    const int64_t cost = h < BH ? (int64_t)work[h] + (int64_t)nb * kTileOverhead : 0;
+  for (int u0 = 0; u0 < units; u0 += 1024) {
+    const int u = u0 + threadIdx.x;
+    const int64_t c = u < units ? (int64_t)cost[u] + kUnitOverhead : 0;
     int64_t chunk;
-    const int64_t excl = seen + block_exclusive_scan<int64_t>(cost, buf, chunk);
-    if (h < BH) {
+    const int64_t before = seen + block_exclusive_scan<int64_t>(c, buf, chunk);
+    if (u < units)
       for (int x = 1; x < kSegments; ++x)
-        if (excl < target[x] && target[x] <= excl + cost) {
-          head_of[x] = h;
-          base_of[x] = excl;
-        }
-    }
+        if (before < target[x] && target[x] <= before + c) bound[x] = u + 1;
     seen += chunk;
     __syncthreads();
   }
-  // within that head, the first tile whose preceding cost reaches the target
-  for (int x = 1; x < kSegments; ++x) {
-    const int h = head_of[x];
-    if (h >= BH) {  // target beyond the last head (cannot happen with counts >= 1)
-      if (threadIdx.x == 0) sched[x] = (int32_t)tiles;
-      continue;
-    }
-    int64_t run = base_of[x];
-    int found = nb;
-    for (int i0 = 0; i0 < nb; i0 += 1024) {
-      const int i = i0 + threadIdx.x;
-      const int64_t cost = i < nb ? (int64_t)counts[(size_t)h * nb + i] + kTileOverhead : 0;
-      int64_t chunk;
-      const int64_t before = run + block_exclusive_scan<int64_t>(cost, buf, chunk);
-      // smallest i with before >= target: count the i in this chunk with before < target
-      const int64_t below = (i < nb && before < target[x]) ? 1 : 0;
-      int64_t n_below;
-      block_exclusive_scan<int64_t>(below, buf, n_below);
-      if (n_below < (int64_t)min(1024, nb - i0)) {
-        found = i0 + (int)n_below;
-        break;
-      }
-      run += chunk;
-    }
-    if (threadIdx.x == 0) sched[x] = (int32_t)((int64_t)h * nb + found);
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    sched[0] = 0;
-    sched[kSegments] = (int32_t)tiles;
-  }
+  if (threadIdx.x <= kSegments) sched[threadIdx.x] = threadIdx.x == 0 ? 0 : bound[threadIdx.x];
 }
 
 }  // namespace
@@ -571,8 +593,20 @@ hipError_t launch_workload(const absh_ctx* c, const RouteBuffers& rb, int BH, hi
 
 int queue_chunks(int tiles) { return (tiles + kQChunk - 1) / kQChunk; }
 
-hipError_t launch_segments(const absh_ctx* c, const RouteBuffers& rb, int BH, int balanced, hipStream_t s) {
-  segments_kernel<<<1, 1024, 0, s>>>(rb.counts, rb.work, BH, c->nb, balanced, rb.sched);
+hipError_t launch_pairs(const absh_ctx* c, const RouteBuffers& rb, int BH, hipStream_t s) {
+  const int npairs = (c->nb + 1) / 2;
+  const int units = BH * npairs;
+  pair_merge_kernel<<<(units + 3) / 4, 256, 0, s>>>(rb.counts, rb.kv_idx, c->nb, npairs, units, rb.pair_list,
+                                                    rb.pair_cnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_segments(const absh_ctx* c, const RouteBuffers& rb, int BH, int schedule, hipStream_t s) {
+  const int npairs = (c->nb + 1) / 2;
+  if (schedule == ABSH_SCHED_LPT)
+    segments_kernel<<<1, 1024, 0, s>>>(rb.counts, BH * c->nb, 0, 1, rb.sched);
+  else
+    segments_kernel<<<1, 1024, 0, s>>>(rb.pair_cnt, BH * npairs, schedule == ABSH_SCHED_XCD, 2, rb.sched);
   return hipGetLastError();
 }
 

@@ -82,7 +82,8 @@ typedef struct {
   int32_t order_depth; /* 0..64: length of the importance-order prefix written to `order` */
 } absh_route_opts;
 
-/* Routing outputs, all caller-allocated device buffers. nb, tiles = B*H*nb. */
+/* Routing outputs, caller-allocated device buffers (plus one host field).
+ * nb, tiles = B*H*nb, npairs = ceil(nb / 2), pair units = B*H*npairs. */
 typedef struct {
   int32_t* counts; /* [tiles] retained key blocks per tile (after floor and slack fill)        */
   int32_t* kv_idx; /* [tiles][nb] row-padded; the first counts[t] entries, ascending block id  */
@@ -90,8 +91,15 @@ typedef struct {
                       id; -1 past nb. May be NULL when order_depth == 0                         */
   int32_t* work;   /* [B*H] sum_i counts (the numerator of Eq. 1, exact)                        */
   float* L;        /* [B*H] L_h = work / nb, float32 division (Eq. 1)                           */
-  int32_t* queue;  /* [tiles] execution order of the tiles for absh_sparse_attn                 */
-  int32_t* sched;  /* [9] bounds of the eight queue runs, one per XCD (see absh_schedule)        */
+  int32_t* queue;  /* [tiles] tiles by retained count (ABSH_SCHED_LPT) or in order (others)       */
+  int32_t* sched;  /* [10] bounds of the eight runs of the attention work queue, one per XCD,
+                      then the work-unit kind (see absh_sparse_attn)                             */
+  uint32_t* pairs; /* [pair units][nb] for ABSH_SCHED_ORDER / ABSH_SCHED_XCD (else unused, may be
+                      NULL): the ascending union of the retained lists of query blocks 2p and
+                      2p+1 of a head, entry = block id | (in 2p) << 30 | (in 2p+1) << 31          */
+  int32_t* pair_cnt; /* [pair units] length of each union list (same condition as pairs)        */
+  int32_t schedule;  /* HOST field, written by absh_route: the absh_schedule the lists were made
+                        for; absh_sparse_attn reads it                                           */
 } absh_lists;
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -167,8 +175,7 @@ size_t absh_route_workspace_bytes(const absh_ctx* ctx, int B, int H, int d);
  * opts->order_depth > 0). ws must hold absh_route_workspace_bytes(); its
  * contents are scratch. No host synchronisation. */
 absh_status absh_route(absh_ctx* ctx, const void* qh, const void* kh, int B, int H, int d,
-                       const absh_route_opts* opts, const absh_lists* out, void* ws, size_t ws_bytes,
-                       void* stream);
+                       const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Block-sparse attention (xllm-io review of FVAttn, "Block-Sparse Attention
  * Execution"): for every tile (b, h, i) in lists->queue order,
@@ -178,10 +185,14 @@ absh_status absh_route(absh_ctx* ctx, const void* qh, const void* kh, int B, int
  * attention over every block with the same kernel. qh, kh: [B, H, n_pad, d]
  * bf16 (ABSH_ROWS); vt: ABSH_VT layout; oh: [B, H, n_pad, d] bf16 out (pad rows
  * hold unspecified values). Scores and softmax in float32, probabilities rounded
- * to bf16 for the value product, float32 accumulation. Tiles are pulled by a
- * persistent grid (one workgroup per CU slot) following lists->queue and
- * lists->sched; dense mode splits the tiles evenly over the XCDs. Every tile is
- * computed the same way whatever the schedule, so outputs do not depend on it. */
+ * to bf16 for the value product, float32 accumulation. Work is pulled by a
+ * persistent grid (one workgroup per CU slot) following lists->sched. Under
+ * ABSH_SCHED_LPT a work unit is one tile, in lists->queue order; otherwise it is a
+ * pair of neighbouring query blocks walking the union of their lists
+ * (lists->pairs), so each staged K/V block serves both. Dense mode uses pairs
+ * split evenly over the XCDs. Every query row is computed the same way whatever
+ * the schedule (same blocks, same ascending order), so outputs do not depend on
+ * it. */
 absh_status absh_sparse_attn(absh_ctx* ctx, const void* qh, const void* kh, const void* vt, int B, int H,
                              int d, const absh_lists* lists, void* oh, void* stream);
 

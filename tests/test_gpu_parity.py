@@ -195,7 +195,7 @@ def test_route_matches_oracle(index, p):
     assert (counts >= min(w.k_floor, w.nb)).all()
     # LPT queue: exactly the oracle's order for these counts; one run holds it all
     assert np.array_equal(queue, O.lpt_queue(counts))
-    assert r.sched.cpu().numpy().tolist() == [0] + [w.tiles] * 8
+    assert r.sched.cpu().numpy().tolist() == [0] + [w.tiles] * 8 + [1]
     if excused == 0:
         wo, Lo = O.workloads(R.counts)
         assert np.array_equal(work, wo) and np.array_equal(L, Lo)
@@ -295,11 +295,11 @@ def test_attention_tiny_all_tiles():
     assert mx <= ATOL_MAX and mean <= ATOL_MEAN
 
 
-@pytest.mark.parametrize("index", [1, 2, 3, 4])
-def test_attention_sampled_tiles(index):
+@pytest.mark.parametrize("index,schedule", [(1, "xcd"), (2, "xcd"), (3, "xcd"), (4, "xcd"), (2, "lpt")])
+def test_attention_sampled_tiles(index, schedule):
     c = case(index)
     w = c.w
-    r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, schedule="lpt")
+    r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, schedule=schedule)
     counts, _, _ = check_lists_valid(r, w.nb)
     rng = np.random.default_rng(100 + index)
     flat = counts.reshape(-1)
@@ -333,9 +333,25 @@ def test_dense_matches_oracle_tiny():
     assert e.max() <= ATOL_MAX and e.mean() <= ATOL_MEAN
 
 
-def expected_xcd_bounds(counts, overhead=1, segments=8):
-    """Cut the tile ids where the running cost (count + overhead) first reaches x/8 of the total."""
-    cost = counts.reshape(-1).astype(np.int64) + overhead
+def expected_pairs(counts, kv, nb):
+    """Union lists of query blocks (2p, 2p+1) with membership flags, from the tile lists."""
+    B, H, _ = counts.shape
+    npairs = (nb + 1) // 2
+    lists, lens = [], []
+    for b in range(B):
+        for h in range(H):
+            for p in range(npairs):
+                a = set(kv[b, h, 2 * p, : counts[b, h, 2 * p]].tolist())
+                c = set(kv[b, h, 2 * p + 1, : counts[b, h, 2 * p + 1]].tolist()) if 2 * p + 1 < nb else set()
+                ent = [j | ((1 << 30) if j in a else 0) | ((1 << 31) if j in c else 0) for j in sorted(a | c)]
+                lists.append(np.array(ent, dtype=np.int64).astype(np.uint32))
+                lens.append(len(ent))
+    return lists, np.array(lens)
+
+
+def expected_xcd_bounds(cost, overhead=1, segments=8):
+    """Cut the units where the running cost (cost + overhead) first reaches x/8 of the total."""
+    cost = np.asarray(cost, dtype=np.int64) + overhead
     before = np.concatenate([[0], np.cumsum(cost)])[:-1]
     total = int(cost.sum())
     bounds = [0]
@@ -345,22 +361,31 @@ def expected_xcd_bounds(counts, overhead=1, segments=8):
     return bounds + [cost.size]
 
 
-@pytest.mark.parametrize("index", [1, 3])
+@pytest.mark.parametrize("index", [0, 1, 3])
 def test_schedules_bit_identical(index):
     c = case(index)
     w = c.w
+    npairs = (w.nb + 1) // 2
+    units = w.B * w.H * npairs
     outs = {}
     for sched in ("order", "lpt", "xcd"):
         r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, schedule=sched)
-        counts, _, queue = check_lists_valid(r, w.nb)
+        counts, kv, queue = check_lists_valid(r, w.nb)
         bounds = r.sched.cpu().numpy().tolist()
-        if sched == "order":
-            assert np.array_equal(queue, np.arange(w.tiles)) and bounds == [0] + [w.tiles] * 8
-        elif sched == "lpt":
-            assert np.array_equal(queue, O.lpt_queue(counts)) and bounds == [0] + [w.tiles] * 8
+        if sched == "lpt":
+            assert np.array_equal(queue, O.lpt_queue(counts)) and bounds == [0] + [w.tiles] * 8 + [1]
         else:
             assert np.array_equal(queue, np.arange(w.tiles))
-            assert bounds == expected_xcd_bounds(counts), (bounds, expected_xcd_bounds(counts))
+            want_lists, want_len = expected_pairs(counts, kv, w.nb)
+            got_len = r.pair_cnt.cpu().numpy()
+            got = r.pairs.cpu().numpy().view(np.uint32)
+            assert np.array_equal(got_len, want_len)
+            for u in range(units):
+                assert np.array_equal(got[u, : got_len[u]], want_lists[u]), u
+            if sched == "order":
+                assert bounds == [0] + [units] * 8 + [2]
+            else:
+                assert bounds == expected_xcd_bounds(got_len) + [2], (bounds, expected_xcd_bounds(got_len))
         outs[sched] = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r)
         outs[sched + "2"] = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r)
     torch.cuda.synchronize()
@@ -380,7 +405,8 @@ def test_schedules_bit_identical(index):
     ((3, 9, 10), 128, 128, 2, 1, 0.99, 1),  # ragged tail with block 128
     ((2, 8, 8), 16, 128, 2, 1, 0.05, 3),    # tiny p: the floor decides
 ])
-def test_edge_shapes(grid, block, d, H, B, p, k):
+@pytest.mark.parametrize("schedule", ["xcd", "lpt"])
+def test_edge_shapes(grid, block, d, H, B, p, k, schedule):
     T, Y, X = grid
     N = T * Y * X
     rng = np.random.default_rng(7)
@@ -392,7 +418,7 @@ def test_edge_shapes(grid, block, d, H, B, p, k):
     qd, kd, vd = (to_dev_bf16(b) for b in bits)
     qh, kh = absh.permute(ctx, qd), absh.permute(ctx, kd)
     vt = absh.permute(ctx, vd, layout=absh.ABSH_VT)
-    r = absh.route(ctx, qh, kh, p, k, slack_frac=0.25, schedule="lpt")
+    r = absh.route(ctx, qh, kh, p, k, slack_frac=0.25, schedule=schedule)
     counts, kv, _ = check_lists_valid(r, ctx.nb)
     perm, _ = O.hilbert_perm(T, Y, X)
     hq, hk, hv = (O.to_hilbert(W.bf16_to_f32(b), perm) for b in bits)
