@@ -24,7 +24,7 @@ SCHEDULES = {"order": SCHED_ORDER, "lpt": SCHED_LPT, "xcd": SCHED_XCD}
 EXPORTED = (
     "absh_version", "absh_status_string", "absh_last_error", "absh_create", "absh_destroy", "absh_dims",
     "absh_perm", "absh_perm_copy", "absh_permute", "absh_unpermute", "absh_pool", "absh_block_scores",
-    "absh_route_workspace_bytes", "absh_route", "absh_sparse_attn",
+    "absh_route_workspace_bytes", "absh_route", "absh_sparse_attn", "absh_lists_units",
 )
 
 
@@ -44,7 +44,7 @@ class RouteOpts(ctypes.Structure):
 class Lists(ctypes.Structure):
     _fields_ = [("counts", ctypes.c_void_p), ("kv_idx", ctypes.c_void_p), ("order", ctypes.c_void_p),
                 ("work", ctypes.c_void_p), ("L", ctypes.c_void_p), ("queue", ctypes.c_void_p),
-                ("sched", ctypes.c_void_p), ("pairs", ctypes.c_void_p), ("pair_cnt", ctypes.c_void_p),
+                ("sched", ctypes.c_void_p), ("unit_list", ctypes.c_void_p), ("unit_cnt", ctypes.c_void_p),
                 ("schedule", ctypes.c_int32)]
 
 
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         "absh_pool": ([vp, vp, vp, i, i, i, vp], i),
         "absh_block_scores": ([vp, vp, vp, vp, i, i, i, vp], i),
         "absh_route_workspace_bytes": ([vp, i, i, i], sz),
+        "absh_lists_units": ([vp, i, i, i], i),
         "absh_route": ([vp, vp, vp, i, i, i, ctypes.POINTER(RouteOpts), ctypes.POINTER(Lists), vp, sz, vp], i),
         "absh_sparse_attn": ([vp, vp, vp, vp, i, i, i, ctypes.POINTER(Lists), vp, vp], i),
     }
@@ -205,26 +206,34 @@ class Routing:
     work: object     # int32 [B, H]
     L: object        # float32 [B, H]
     queue: object    # int32 [B*H*nb]
-    sched: object    # int32 [10] bounds of the per-XCD runs of the work queue + unit kind
-    pairs: object    # int32 [B*H*npairs, nb] flagged union lists of query-block pairs
-    pair_cnt: object  # int32 [B*H*npairs]
+    sched: object    # int32 [10] bounds of the per-XCD runs of the work queue + query blocks per unit
+    unit_list: object  # int32 [units, nb] flagged union lists of query-block groups
+    unit_cnt: object   # int32 [units]
     schedule: int = -1  # the schedule absh_route made these lists for
 
     def lists(self) -> Lists:
         return Lists(self.counts.data_ptr(), self.kv_idx.data_ptr(),
                      self.order.data_ptr() if self.order is not None else 0,
                      self.work.data_ptr(), self.L.data_ptr(), self.queue.data_ptr(), self.sched.data_ptr(),
-                     self.pairs.data_ptr(), self.pair_cnt.data_ptr(), self.schedule)
+                     self.unit_list.data_ptr(), self.unit_cnt.data_ptr(), self.schedule)
 
 
 def route_workspace_bytes(ctx: Context, B: int, H: int, d: int) -> int:
     return int(lib().absh_route_workspace_bytes(ctx.handle, B, H, d))
 
 
+def lists_units(ctx: Context, B: int, H: int, schedule) -> int:
+    """Attention work units for this schedule (rows of Routing.unit_list)."""
+    sched = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
+    return int(lib().absh_lists_units(ctx.handle, B, H, sched))
+
+
 def alloc_routing(ctx: Context, B: int, H: int, order_depth: int = 0) -> Routing:
+    """Routing buffers sized for every schedule."""
     import torch
     dev = _dev(ctx)
     nb = ctx.nb
+    units = max(lists_units(ctx, B, H, "order"), 1)
     return Routing(
         counts=torch.empty((B, H, nb), dtype=torch.int32, device=dev),
         kv_idx=torch.empty((B, H, nb, nb), dtype=torch.int32, device=dev),
@@ -233,8 +242,8 @@ def alloc_routing(ctx: Context, B: int, H: int, order_depth: int = 0) -> Routing
         L=torch.empty((B, H), dtype=torch.float32, device=dev),
         queue=torch.empty((B * H * nb,), dtype=torch.int32, device=dev),
         sched=torch.empty((10,), dtype=torch.int32, device=dev),
-        pairs=torch.empty((B * H * ((nb + 1) // 2), nb), dtype=torch.int32, device=dev),
-        pair_cnt=torch.empty((B * H * ((nb + 1) // 2),), dtype=torch.int32, device=dev),
+        unit_list=torch.empty((units, nb), dtype=torch.int32, device=dev),
+        unit_cnt=torch.empty((units,), dtype=torch.int32, device=dev),
     )
 
 

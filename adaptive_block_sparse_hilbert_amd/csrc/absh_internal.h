@@ -56,30 +56,32 @@ struct RouteBuffers {
   int64_t* slack_info;  // [4] lambda, remainder, E, total
   int32_t* chunk_hist;  // [chunks][nb + 1]
   int32_t* rank;        // [tiles]
-  int32_t* sched;       // [10] queue segment bounds (one segment per XCD) and the unit kind
-  uint32_t* pair_list;  // [units][nb] union lists of query-block pairs
-  int32_t* pair_cnt;    // [units]
+  int32_t* sched;        // [10] queue segment bounds (one segment per XCD) and query blocks per unit
+  uint32_t* unit_list;   // [units][nb] union lists of query-block groups
+  int32_t* unit_cnt;     // [units]
 };
 hipError_t launch_select(const absh_ctx* c, const RouteBuffers& rb, int tiles, double p, int k_floor,
                          int order_depth, int reselect, hipStream_t s);
 hipError_t launch_slack_plan(const absh_ctx* c, const RouteBuffers& rb, int tiles, double beta, hipStream_t s);
 hipError_t launch_workload(const absh_ctx* c, const RouteBuffers& rb, int BH, hipStream_t s);
 hipError_t launch_queue(const absh_ctx* c, const RouteBuffers& rb, int tiles, int lpt, hipStream_t s);
-hipError_t launch_pairs(const absh_ctx* c, const RouteBuffers& rb, int BH, hipStream_t s);
+int unit_members(const absh_ctx* c, int schedule);  // query blocks per attention work unit
+int unit_count(const absh_ctx* c, int BH, int members);
+hipError_t launch_groups(const absh_ctx* c, const RouteBuffers& rb, int BH, int members, hipStream_t s);
 hipError_t launch_segments(const absh_ctx* c, const RouteBuffers& rb, int BH, int schedule, hipStream_t s);
 int queue_chunks(int tiles);
 
-// Work units of the attention kernel.
-enum UnitKind { kUnitSingle = 1, kUnitPair = 2 };
-
+// Work lists of the attention kernel. A unit is `members` neighbouring query
+// blocks of one head (1: a single tile taken from the queue; 2 or 4: a group
+// walking the union of its members' lists).
 struct AttnLists {
-  const int32_t* queue;      // single units: queue position -> tile
-  const int32_t* counts;     // [tiles]
-  const int32_t* kv_idx;     // [tiles][nb]
-  const uint32_t* pair_list;  // pair units: [units][nb] flagged union entries
-  const int32_t* pair_cnt;   // [units]
-  const int32_t* sched;      // [10] segment bounds + unit kind (read by the kernel)
-  int kind;                  // kUnitSingle or kUnitPair (host copy of sched[9])
+  const int32_t* queue;       // single units: queue position -> tile
+  const int32_t* counts;      // [tiles]
+  const int32_t* kv_idx;      // [tiles][nb]
+  const uint32_t* unit_list;  // group units: [units][nb] flagged union entries
+  const int32_t* unit_cnt;    // [units]
+  const int32_t* sched;       // [10] segment bounds + members (read by the kernel)
+  int members;                // host copy of sched[9]
 };
 hipError_t launch_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B,
                             int H, int d, const AttnLists* lists, hipStream_t s);

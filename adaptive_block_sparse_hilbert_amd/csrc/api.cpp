@@ -249,6 +249,11 @@ absh_status absh_block_scores(absh_ctx* c, const float* qbar, const float* kbar,
   return ABSH_OK;
 }
 
+int absh_lists_units(const absh_ctx* c, int B, int H, int schedule) {
+  if (!c || B < 1 || H < 1 || schedule < ABSH_SCHED_ORDER || schedule > ABSH_SCHED_XCD) return 0;
+  return absh::unit_count(c, B * H, absh::unit_members(c, schedule));
+}
+
 size_t absh_route_workspace_bytes(const absh_ctx* c, int B, int H, int d) {
   if (!c || B < 1 || H < 1 || d < 1) return 0;
   return ws_layout(c, B, H, d).total;
@@ -272,8 +277,8 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
   if (!out->counts || !out->kv_idx || !out->work || !out->L || !out->queue || !out->sched)
     return fail(ABSH_EINVAL, "counts, kv_idx, work, L, queue and sched must be non-NULL");
   if (opts->order_depth > 0 && !out->order) return fail(ABSH_EINVAL, "order is NULL but order_depth > 0");
-  if (opts->schedule != ABSH_SCHED_LPT && (!out->pairs || !out->pair_cnt))
-    return fail(ABSH_EINVAL, "pairs and pair_cnt must be non-NULL for this schedule");
+  if (opts->schedule != ABSH_SCHED_LPT && (!out->unit_list || !out->unit_cnt))
+    return fail(ABSH_EINVAL, "unit_list and unit_cnt must be non-NULL for this schedule");
   if (c->nb > kMaxNb) return fail(ABSH_EUNSUPPORTED, "nb = %d above the router's %d", c->nb, kMaxNb);
   const WsLayout w = ws_layout(c, B, H, d);
   if (!ws) return fail(ABSH_EWORKSPACE, "workspace is NULL (%zu bytes needed)", w.total);
@@ -299,8 +304,8 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
   rb.chunk_hist = reinterpret_cast<int32_t*>(base + w.chunk_hist);
   rb.rank = reinterpret_cast<int32_t*>(base + w.rank);
   rb.sched = out->sched;
-  rb.pair_list = out->pairs;
-  rb.pair_cnt = out->pair_cnt;
+  rb.unit_list = out->unit_list;
+  rb.unit_cnt = out->unit_cnt;
   const int tiles = B * H * c->nb;
 
   ABSH_HIP(absh::launch_pool(c, qh, qbar, B, H, d, s), "absh_route: pool q");
@@ -314,7 +319,8 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
   }
   ABSH_HIP(absh::launch_workload(c, rb, B * H, s), "absh_route: workload");
   ABSH_HIP(absh::launch_queue(c, rb, tiles, opts->schedule == ABSH_SCHED_LPT, s), "absh_route: queue");
-  if (opts->schedule != ABSH_SCHED_LPT) ABSH_HIP(absh::launch_pairs(c, rb, B * H, s), "absh_route: pairs");
+  if (opts->schedule != ABSH_SCHED_LPT)
+    ABSH_HIP(absh::launch_groups(c, rb, B * H, absh::unit_members(c, opts->schedule), s), "absh_route: groups");
   ABSH_HIP(absh::launch_segments(c, rb, B * H, opts->schedule, s), "absh_route: segments");
   out->schedule = opts->schedule;
   return ABSH_OK;
@@ -332,18 +338,18 @@ absh_status absh_sparse_attn(absh_ctx* c, const void* qh, const void* kh, const 
     return fail(ABSH_EINVAL, "lists needs counts, kv_idx, queue and sched");
   if (lists && (lists->schedule < ABSH_SCHED_ORDER || lists->schedule > ABSH_SCHED_XCD))
     return fail(ABSH_EINVAL, "lists->schedule %d is not a schedule (was absh_route run?)", lists->schedule);
-  if (lists && lists->schedule != ABSH_SCHED_LPT && (!lists->pairs || !lists->pair_cnt))
-    return fail(ABSH_EINVAL, "lists needs pairs and pair_cnt for this schedule");
+  if (lists && lists->schedule != ABSH_SCHED_LPT && (!lists->unit_list || !lists->unit_cnt))
+    return fail(ABSH_EINVAL, "lists needs unit_list and unit_cnt for this schedule");
   if (absh_status st = use_device(c)) return st;
   absh::AttnLists L{};
   if (lists) {
     L.queue = lists->queue;
     L.counts = lists->counts;
     L.kv_idx = lists->kv_idx;
-    L.pair_list = lists->pairs;
-    L.pair_cnt = lists->pair_cnt;
+    L.unit_list = lists->unit_list;
+    L.unit_cnt = lists->unit_cnt;
     L.sched = lists->sched;
-    L.kind = lists->schedule == ABSH_SCHED_LPT ? absh::kUnitSingle : absh::kUnitPair;
+    L.members = absh::unit_members(c, lists->schedule);
   }
   ABSH_HIP(absh::launch_attention(c, qh, kh, vt, oh, B, H, d, lists ? &L : nullptr,
                                   reinterpret_cast<hipStream_t>(stream)),

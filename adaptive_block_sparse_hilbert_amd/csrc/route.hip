@@ -437,62 +437,65 @@ __global__ __launch_bounds__(256) void queue_identity_kernel(int tiles, int32_t*
   if (t < tiles) queue[t] = t;
 }
 
-// ------------------------------------------------------------------ query-block pairs
+// ------------------------------------------------------------------ query-block groups
 
-// One wave per pair unit u = (bh, p): query blocks 2p and 2p + 1 of head bh (the
-// second is absent when 2p + 1 == nb). Writes the ascending union of the two
-// retained lists, each entry j | (in first << 30) | (in second << 31), and its
-// length. Lane l owns block ids 32l .. 32l + 31 as two bitmaps in LDS.
-constexpr uint32_t kInFirst = 1u << 30;
-constexpr uint32_t kInSecond = 1u << 31;
-
-__global__ __launch_bounds__(256) void pair_merge_kernel(const int32_t* __restrict__ counts,
-                                                         const int32_t* __restrict__ kv_idx, int nb, int npairs,
-                                                         int units, uint32_t* __restrict__ pair_list,
-                                                         int32_t* __restrict__ pair_cnt) {
-  __shared__ uint32_t bits[4][2][64];
+// One wave per group unit u = (bh, q): the M neighbouring query blocks qM .. qM+M-1
+// of head bh (those past nb are absent). Writes the ascending union of their
+// retained lists, each entry j | (member m retains j) << (28 + m), and its length.
+// Lane l owns block ids 32l .. 32l + 31 as M bitmaps in LDS.
+template <int M>
+__global__ __launch_bounds__(256) void group_merge_kernel(const int32_t* __restrict__ counts,
+                                                          const int32_t* __restrict__ kv_idx, int nb, int per_head,
+                                                          int units, uint32_t* __restrict__ unit_list,
+                                                          int32_t* __restrict__ unit_cnt) {
+  __shared__ uint32_t bits[4][M][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int u = blockIdx.x * 4 + w;
   if (u >= units) return;
-  const int bh = u / npairs;
-  const int pr = u - bh * npairs;
-  const int64_t ta = (int64_t)bh * nb + 2 * pr;
-  const bool has_b = 2 * pr + 1 < nb;
-  bits[w][0][lane] = 0u;
-  bits[w][1][lane] = 0u;
+  const int bh = u / per_head;
+  const int q = u - bh * per_head;
+#pragma unroll
+  for (int m = 0; m < M; ++m) bits[w][m][lane] = 0u;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const int ca = counts[ta];
-  for (int i = lane; i < ca; i += 64) {
-    const int j = kv_idx[ta * nb + i];
-    atomicOr(&bits[w][0][j >> 5], 1u << (j & 31));
-  }
-  if (has_b) {
-    const int cb = counts[ta + 1];
-    for (int i = lane; i < cb; i += 64) {
-      const int j = kv_idx[(ta + 1) * nb + i];
-      atomicOr(&bits[w][1][j >> 5], 1u << (j & 31));
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int qb = q * M + m;
+    if (qb >= nb) continue;
+    const int64_t t = (int64_t)bh * nb + qb;
+    const int c = counts[t];
+    for (int i = lane; i < c; i += 64) {
+      const int j = kv_idx[t * nb + i];
+      atomicOr(&bits[w][m][j >> 5], 1u << (j & 31));
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const uint32_t wa = bits[w][0][lane], wb = bits[w][1][lane], wu = wa | wb;
-  const int mine = __popc(wu);
+  uint32_t word[M];
+  uint32_t any = 0u;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    word[m] = bits[w][m][lane];
+    any |= word[m];
+  }
+  const int mine = __popc(any);
   int incl = mine;
   for (int off = 1; off < 64; off <<= 1) {
     const int o = __shfl_up(incl, off);
     if (lane >= off) incl += o;
   }
   int pos = incl - mine;
-  uint32_t* out = pair_list + (size_t)u * nb;
+  uint32_t* out = unit_list + (size_t)u * nb;
   for (int k = 0; k < 32; ++k) {
-    if ((wu >> k) & 1u) {
-      const uint32_t j = (uint32_t)(lane * 32 + k);
-      out[pos++] = j | (((wa >> k) & 1u) ? kInFirst : 0u) | (((wb >> k) & 1u) ? kInSecond : 0u);
+    if ((any >> k) & 1u) {
+      uint32_t e = (uint32_t)(lane * 32 + k);
+#pragma unroll
+      for (int m = 0; m < M; ++m) e |= ((word[m] >> k) & 1u) << (28 + m);
+      out[pos++] = e;
     }
   }
-  if (lane == 63) pair_cnt[u] = incl;
+  if (lane == 63) unit_cnt[u] = incl;
 }
 
 // ------------------------------------------------------------------ queue segments (one per XCD)
@@ -593,20 +596,33 @@ hipError_t launch_workload(const absh_ctx* c, const RouteBuffers& rb, int BH, hi
 
 int queue_chunks(int tiles) { return (tiles + kQChunk - 1) / kQChunk; }
 
-hipError_t launch_pairs(const absh_ctx* c, const RouteBuffers& rb, int BH, hipStream_t s) {
-  const int npairs = (c->nb + 1) / 2;
-  const int units = BH * npairs;
-  pair_merge_kernel<<<(units + 3) / 4, 256, 0, s>>>(rb.counts, rb.kv_idx, c->nb, npairs, units, rb.pair_list,
-                                                    rb.pair_cnt);
+int unit_members(const absh_ctx* c, int schedule) {
+  if (schedule == ABSH_SCHED_LPT) return 1;
+  return c->block >= 128 ? 2 : 4;
+}
+
+int unit_count(const absh_ctx* c, int BH, int members) { return BH * ((c->nb + members - 1) / members); }
+
+hipError_t launch_groups(const absh_ctx* c, const RouteBuffers& rb, int BH, int members, hipStream_t s) {
+  const int per_head = (c->nb + members - 1) / members;
+  const int units = BH * per_head;
+  const unsigned grid = (unsigned)((units + 3) / 4);
+  if (members == 2)
+    group_merge_kernel<2><<<grid, 256, 0, s>>>(rb.counts, rb.kv_idx, c->nb, per_head, units, rb.unit_list,
+                                                rb.unit_cnt);
+  else
+    group_merge_kernel<4><<<grid, 256, 0, s>>>(rb.counts, rb.kv_idx, c->nb, per_head, units, rb.unit_list,
+                                                rb.unit_cnt);
   return hipGetLastError();
 }
 
 hipError_t launch_segments(const absh_ctx* c, const RouteBuffers& rb, int BH, int schedule, hipStream_t s) {
-  const int npairs = (c->nb + 1) / 2;
-  if (schedule == ABSH_SCHED_LPT)
+  const int members = unit_members(c, schedule);
+  if (members == 1)
     segments_kernel<<<1, 1024, 0, s>>>(rb.counts, BH * c->nb, 0, 1, rb.sched);
   else
-    segments_kernel<<<1, 1024, 0, s>>>(rb.pair_cnt, BH * npairs, schedule == ABSH_SCHED_XCD, 2, rb.sched);
+    segments_kernel<<<1, 1024, 0, s>>>(rb.unit_cnt, unit_count(c, BH, members), schedule == ABSH_SCHED_XCD,
+                                       members, rb.sched);
   return hipGetLastError();
 }
 

@@ -83,7 +83,7 @@ typedef struct {
 } absh_route_opts;
 
 /* Routing outputs, caller-allocated device buffers (plus one host field).
- * nb, tiles = B*H*nb, npairs = ceil(nb / 2), pair units = B*H*npairs. */
+ * nb, tiles = B*H*nb. */
 typedef struct {
   int32_t* counts; /* [tiles] retained key blocks per tile (after floor and slack fill)        */
   int32_t* kv_idx; /* [tiles][nb] row-padded; the first counts[t] entries, ascending block id  */
@@ -93,11 +93,12 @@ typedef struct {
   float* L;        /* [B*H] L_h = work / nb, float32 division (Eq. 1)                           */
   int32_t* queue;  /* [tiles] tiles by retained count (ABSH_SCHED_LPT) or in order (others)       */
   int32_t* sched;  /* [10] bounds of the eight runs of the attention work queue, one per XCD,
-                      then the work-unit kind (see absh_sparse_attn)                             */
-  uint32_t* pairs; /* [pair units][nb] for ABSH_SCHED_ORDER / ABSH_SCHED_XCD (else unused, may be
-                      NULL): the ascending union of the retained lists of query blocks 2p and
-                      2p+1 of a head, entry = block id | (in 2p) << 30 | (in 2p+1) << 31          */
-  int32_t* pair_cnt; /* [pair units] length of each union list (same condition as pairs)        */
+                      then the query blocks per work unit (see absh_sparse_attn)                 */
+  uint32_t* unit_list; /* [units][nb] for ABSH_SCHED_ORDER / ABSH_SCHED_XCD (else unused, may be
+                      NULL; units = absh_lists_units()): the ascending union of the retained
+                      lists of the M neighbouring query blocks qM .. qM+M-1 of a head, entry =
+                      block id | (member m retains it) << (28 + m); M = 4 (block <= 64) or 2  */
+  int32_t* unit_cnt; /* [units] length of each union list (same condition as unit_list)         */
   int32_t schedule;  /* HOST field, written by absh_route: the absh_schedule the lists were made
                         for; absh_sparse_attn reads it                                           */
 } absh_lists;
@@ -160,6 +161,12 @@ absh_status absh_pool(absh_ctx* ctx, const void* xh, float* xbar, int B, int H, 
 absh_status absh_block_scores(absh_ctx* ctx, const float* qbar, const float* kbar, float* s, int B, int H,
                               int d, void* stream);
 
+/* Number of attention work units absh_route makes for this shape and schedule
+ * (the row count of absh_lists.unit_list): B*H*ceil(nb/M) with M query blocks per
+ * unit, M = 1 for ABSH_SCHED_LPT, else 4 (block <= 64) or 2 (block 128). 0 on a
+ * bad argument. */
+int absh_lists_units(const absh_ctx* ctx, int B, int H, int schedule);
+
 /* Device workspace needed by absh_route for this shape, in bytes. */
 size_t absh_route_workspace_bytes(const absh_ctx* ctx, int B, int H, int d);
 
@@ -188,9 +195,9 @@ absh_status absh_route(absh_ctx* ctx, const void* qh, const void* kh, int B, int
  * to bf16 for the value product, float32 accumulation. Work is pulled by a
  * persistent grid (one workgroup per CU slot) following lists->sched. Under
  * ABSH_SCHED_LPT a work unit is one tile, in lists->queue order; otherwise it is a
- * pair of neighbouring query blocks walking the union of their lists
- * (lists->pairs), so each staged K/V block serves both. Dense mode uses pairs
- * split evenly over the XCDs. Every query row is computed the same way whatever
+ * group of neighbouring query blocks walking the union of their lists
+ * (lists->unit_list), so each staged K/V block serves all of them. Dense mode
+ * uses groups split evenly over the XCDs. Every query row is computed the same way whatever
  * the schedule (same blocks, same ascending order), so outputs do not depend on
  * it. */
 absh_status absh_sparse_attn(absh_ctx* ctx, const void* qh, const void* kh, const void* vt, int B, int H,

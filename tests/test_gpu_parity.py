@@ -333,17 +333,18 @@ def test_dense_matches_oracle_tiny():
     assert e.max() <= ATOL_MAX and e.mean() <= ATOL_MEAN
 
 
-def expected_pairs(counts, kv, nb):
-    """Union lists of query blocks (2p, 2p+1) with membership flags, from the tile lists."""
+def expected_groups(counts, kv, nb, M):
+    """Union lists of the M query blocks qM .. qM+M-1 with membership flags, from the tile lists."""
     B, H, _ = counts.shape
-    npairs = (nb + 1) // 2
+    per_head = -(-nb // M)
     lists, lens = [], []
     for b in range(B):
         for h in range(H):
-            for p in range(npairs):
-                a = set(kv[b, h, 2 * p, : counts[b, h, 2 * p]].tolist())
-                c = set(kv[b, h, 2 * p + 1, : counts[b, h, 2 * p + 1]].tolist()) if 2 * p + 1 < nb else set()
-                ent = [j | ((1 << 30) if j in a else 0) | ((1 << 31) if j in c else 0) for j in sorted(a | c)]
+            for q in range(per_head):
+                sets = [set(kv[b, h, i, : counts[b, h, i]].tolist()) if i < nb else set()
+                        for i in range(q * M, q * M + M)]
+                allj = sorted(set().union(*sets))
+                ent = [j | sum((1 << (28 + m)) for m in range(M) if j in sets[m]) for j in allj]
                 lists.append(np.array(ent, dtype=np.int64).astype(np.uint32))
                 lens.append(len(ent))
     return lists, np.array(lens)
@@ -361,12 +362,14 @@ def expected_xcd_bounds(cost, overhead=1, segments=8):
     return bounds + [cost.size]
 
 
-@pytest.mark.parametrize("index", [0, 1, 3])
+@pytest.mark.parametrize("index", [0, 1, 3, 4])
 def test_schedules_bit_identical(index):
     c = case(index)
     w = c.w
-    npairs = (w.nb + 1) // 2
-    units = w.B * w.H * npairs
+    M = 2 if w.block >= 128 else 4
+    units = w.B * w.H * (-(-w.nb // M))
+    assert absh.lists_units(c.ctx, w.B, w.H, "xcd") == units
+    assert absh.lists_units(c.ctx, w.B, w.H, "lpt") == w.tiles
     outs = {}
     for sched in ("order", "lpt", "xcd"):
         r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, schedule=sched)
@@ -376,16 +379,16 @@ def test_schedules_bit_identical(index):
             assert np.array_equal(queue, O.lpt_queue(counts)) and bounds == [0] + [w.tiles] * 8 + [1]
         else:
             assert np.array_equal(queue, np.arange(w.tiles))
-            want_lists, want_len = expected_pairs(counts, kv, w.nb)
-            got_len = r.pair_cnt.cpu().numpy()
-            got = r.pairs.cpu().numpy().view(np.uint32)
+            want_lists, want_len = expected_groups(counts, kv, w.nb, M)
+            got_len = r.unit_cnt.cpu().numpy()[:units]
+            got = r.unit_list.cpu().numpy().view(np.uint32)
             assert np.array_equal(got_len, want_len)
             for u in range(units):
                 assert np.array_equal(got[u, : got_len[u]], want_lists[u]), u
             if sched == "order":
-                assert bounds == [0] + [units] * 8 + [2]
+                assert bounds == [0] + [units] * 8 + [M]
             else:
-                assert bounds == expected_xcd_bounds(got_len) + [2], (bounds, expected_xcd_bounds(got_len))
+                assert bounds == expected_xcd_bounds(got_len) + [M], (bounds, expected_xcd_bounds(got_len))
         outs[sched] = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r)
         outs[sched + "2"] = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r)
     torch.cuda.synchronize()
