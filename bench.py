@@ -44,10 +44,13 @@ def parse():
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tiles", type=int, default=24, help="attention tiles in the oracle's timed sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="host time budget of the oracle's attention sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the steps, run one plain device copy of this size (for counter scaling)")
-    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes of the attention kernel")
+    ap.add_argument("--traffic-profile", default=None,
+                    help="counter summary giving the attention kernel's HBM bytes per launch "
+                         "(default: profiles/attn_<workload>_hbm.md)")
     return ap.parse_args()
 
 
@@ -159,14 +162,12 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("attn_bytes_per_launch")
+    traffic = measured_traffic(args.traffic_profile or os.path.join(
+        ROOT, "profiles", "attn_" + w.name.replace("-", "") + "_hbm.md"), w.name, args.schedule)
 
     roof = {
         "bound": "mfma",
-        "kernel": "attn_kernel<128,64>",
+        "kernel": f"attn_kernel<{d},{w.block}>",
         "achieved": round(attn_tflops, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
@@ -176,7 +177,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, p, data, args.cpu_tiles)
+        cpu = cpu_baseline(w, p, data, args.cpu_seconds)
 
     out = {
         "metric": "effective bf16 TFLOP/s on retained blocks + speedup vs dense, 720p 40-head",
@@ -214,15 +215,42 @@ def main():
     print(json.dumps(out))
 
 
-def cpu_baseline(w, p, data, n_tiles):
+def measured_traffic(path, workload, schedule):
+    """HBM bytes per attention launch from a committed counter summary, or None.
+
+    The summary holds FETCH_SIZE + WRITE_SIZE of the attention kernel, scaled by a
+    plain-copy calibration, together with the sha256 of the kernel source it was
+    taken on. A figure taken on another source, workload or schedule is stale and
+    gives None.
+    """
+    import hashlib
+
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            m = line.strip().split(": ", 1)
+            if len(m) == 2:
+                fields[m[0]] = m[1]
+    src = os.path.join(ROOT, "adaptive_block_sparse_hilbert_amd", "csrc", "attn.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if (fields.get("attn_hip_sha256") != sha or fields.get("workload") != workload
+            or fields.get("schedule") != schedule or "hbm_bytes_per_launch" not in fields):
+        return None
+    return int(fields["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(w, p, data, budget_s):
     """The oracle on a bounded sample of the same workload, timed on the host cores.
 
     Sample: head 0 of the workload. The oracle computes the Hilbert order, gathers
     head 0's q, k, v, routes all of head 0's query blocks (block means, scores,
-    softmax, Top-p + floor), then runs attention for n_tiles query blocks of head 0
-    spread evenly over the head. Routing time is prorated to those tiles
-    (n_tiles / nb of it), so the figure is retained FLOPs of the sample tiles
-    divided by their share of the oracle's time.
+    softmax, Top-p + floor), then runs attention for query blocks of head 0 taken
+    in a fixed spread-out order until budget_s seconds of attention have run.
+    Routing time is prorated to the tiles done (n / nb of it), so the figure is the
+    retained FLOPs of the sample tiles divided by their share of the oracle's time.
     """
     import numpy as np
     import threadpoolctl
@@ -239,22 +267,25 @@ def cpu_baseline(w, p, data, n_tiles):
     R = O.route(qh, kh, w.block, p, w.k_floor)
     t_route = time.perf_counter() - t0
     nb = R.nb
-    tiles = np.linspace(0, nb - 1, n_tiles).round().astype(int)
+    order = np.argsort((np.arange(nb) * 0.6180339887) % 1.0, kind="stable")  # spread over the head
     t1 = time.perf_counter()
-    flops = 0.0
-    for i in tiles:
+    flops, done = 0.0, 0
+    for i in order:
         blocks = R.retained(0, 0, i)
         O.attention_tile(qh[0, 0], kh[0, 0], vh[0, 0], w.block, i, blocks)
         flops += 4.0 * w.d * R.sizes[i] * R.sizes[blocks].sum()
+        done += 1
+        if time.perf_counter() - t1 > budget_s:
+            break
     t_attn = time.perf_counter() - t1
-    t = t_attn + t_route * len(tiles) / nb
+    t = t_attn + t_route * done / nb
     return {
         "value": round(flops / t / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": (f"head 0 of {w.name}: Hilbert order + full routing of its {nb} query blocks "
-                   f"({t_route:.2f} s, prorated to the sample), attention for {len(tiles)} query blocks "
+                   f"({t_route:.2f} s, prorated to the sample), attention for {done} query blocks "
                    f"spread over the head ({t_attn:.2f} s); float64 NumPy"),
     }
 

@@ -1,0 +1,122 @@
+"""The C ABI without a GPU: the library loads, exports every function include/absh.h
+declares, and rejects bad arguments on the host before any HIP call (a machine
+without a device reports ABSH_ENODEV instead of crashing)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import adaptive_block_sparse_hilbert_amd as absh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "absh.h")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ENODEV, EHIP = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(absh_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(absh.LIB_PATH):
+        pytest.skip("libabsh.so not built")
+    return absh.lib()
+
+
+def test_every_declared_function_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(absh.EXPORTED)
+
+
+def test_version_and_status_strings(L):
+    assert L.absh_version() >= 100
+    for code, name in [(OK, b"ABSH_OK"), (EINVAL, b"ABSH_EINVAL"), (EUNSUPPORTED, b"ABSH_EUNSUPPORTED"),
+                       (EWORKSPACE, b"ABSH_EWORKSPACE"), (ENODEV, b"ABSH_ENODEV"), (EHIP, b"ABSH_EHIP")]:
+        assert L.absh_status_string(code) == name
+    assert L.absh_status_string(7) == b"ABSH_UNKNOWN"
+
+
+def create(L, *args):
+    h = ctypes.c_void_p()
+    st = L.absh_create(ctypes.byref(h), *args)
+    return st, h
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((0, 8, 8, 16, 0, None), EINVAL, b"grid extents"),
+    ((4, -1, 8, 16, 0, None), EINVAL, b"grid extents"),
+    ((4, 8, 8, 32, 0, None), EUNSUPPORTED, b"block size"),
+    ((4, 8, 8, 0, 0, None), EUNSUPPORTED, b"block size"),
+    ((2048, 2048, 2048, 64, 0, None), EINVAL, b"grid too large"),
+    ((4, 8, 2000, 64, 0, None), EINVAL, b"above 1024"),
+    ((4, 8, 8, 16, -1, None), EINVAL, b"device index"),
+])
+def test_create_rejects_bad_arguments_before_hip(L, args, status, msg):
+    st, h = create(L, *args)
+    assert st == status
+    assert msg in L.absh_last_error()
+    assert not h.value
+
+
+def test_create_null_out_pointer(L):
+    assert L.absh_create(None, 4, 8, 8, 16, 0, None) == EINVAL
+
+
+def test_create_without_device_is_enodev():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    L = absh.lib()
+    st, h = create(L, 4, 8, 8, 16, 0, None)
+    assert st == ENODEV and not h.value
+    assert b"no HIP device" in L.absh_last_error()
+
+
+def test_null_context_everywhere(L):
+    vp = ctypes.c_void_p
+    N, nb, npad = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert L.absh_dims(None, ctypes.byref(N), ctypes.byref(nb), ctypes.byref(npad)) == EINVAL
+    assert L.absh_perm(None, None, None) == EINVAL
+    assert L.absh_perm_copy(None, None, None, None) == EINVAL
+    assert L.absh_permute(None, vp(16), 0, vp(16), 1, 1, 64, 0, None) == EINVAL
+    assert L.absh_unpermute(None, vp(16), vp(16), 1, 1, 64, None) == EINVAL
+    assert L.absh_pool(None, vp(16), vp(16), 1, 1, 64, None) == EINVAL
+    assert L.absh_block_scores(None, vp(16), vp(16), vp(16), 1, 1, 64, None) == EINVAL
+    opts = absh.RouteOpts(0.9, 4, 0.0, 1, 0)
+    lists = absh.Lists()
+    assert L.absh_route(None, vp(16), vp(16), 1, 1, 64, ctypes.byref(opts), ctypes.byref(lists), vp(256),
+                        ctypes.c_size_t(1 << 20), None) == EINVAL
+    assert L.absh_sparse_attn(None, vp(16), vp(16), vp(16), 1, 1, 64, None, vp(16), None) == EINVAL
+    assert b"ctx is NULL" in L.absh_last_error()
+    assert L.absh_route_workspace_bytes(None, 1, 1, 64) == 0
+    assert L.absh_lists_units(None, 1, 1, 0) == 0
+    assert L.absh_destroy(None) == OK
+
+
+def test_last_error_is_thread_local(L):
+    import threading
+    assert L.absh_create(None, 4, 8, 8, 16, 0, None) == EINVAL
+    seen = []
+
+    def other():
+        seen.append(L.absh_last_error())
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen == [b""]
+    assert b"NULL" in L.absh_last_error()
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(absh, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(absh, "_lib", None)
+    with pytest.raises(ImportError):
+        absh.lib()
