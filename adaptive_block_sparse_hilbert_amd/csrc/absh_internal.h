@@ -85,5 +85,10 @@ struct AttnLists {
 };
 hipError_t launch_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B,
                             int H, int d, const AttnLists* lists, hipStream_t s);
+// Group units of 64- and 128-row query blocks (four and two members) run on the
+// union kernel; single tiles and other block sizes on the tile kernel.
+bool union_attention_supported(int d, int block, int members);
+hipError_t launch_union_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh,
+                                  int B, int H, int d, const AttnLists* lists, hipStream_t s);
 
 }  // namespace absh

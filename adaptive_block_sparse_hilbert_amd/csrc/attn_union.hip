@@ -1,0 +1,553 @@
+// Block-sparse attention for groups of neighbouring query blocks walking the
+// union of their retained lists (xllm-io review of FVAttn, "Block-Sparse
+// Attention Execution"; alanhou.org explainer, "Core Mechanism": each head
+// attends only to its selected KV blocks), for gfx950.
+//
+// Work unit: MEMBERS neighbouring query blocks of one head (four of 64 rows or two
+// of 128 rows, 256 query rows in all). The workgroup has eight waves and each
+// wave owns 32 query rows of one member. Every entry of the unit's union list is a
+// key block plus one flag per member; the workgroup stages the block's K and V^T
+// into LDS once, and only the waves whose member retains the block compute on it.
+// Waves that share a SIMD belong to different members, so when one skips a block
+// the other has the matrix core to itself.
+//
+// Keys are processed in steps of 64 (a 128-key block is two steps). Per step a
+// wave computes, with 32x32x16 bf16 MFMAs and fp32 accumulation:
+//   S^T = K Q^T                  two 32x32 tiles, D/16 k-steps each
+//   online softmax               fp32, base-2 exponent, lazy rescale of O
+//   O^T += V^T P^T               D/32 tiles, four k-steps, P rounded to bf16
+// The steps are software-pipelined inside each wave: while the exponentials of
+// step k run on the vector ALU, the matrix core computes S^T of step k + 1, and the
+// row maxima of step k + 1 are reduced while the value product of step k runs.
+//
+// Operand layouts (lane l, column c = l % 32, half g = l / 32). For a 32x32x16
+// MFMA the A operand of lane l is row c, k indices 8g..8g+7; the B operand is
+// column c, the same k indices; accumulator element r of lane l is row
+// 8(r/4) + 4g + r%4 of column c. In S^T the A rows of each 32-key tile are the
+// keys with bits 2 and 3 of the row index exchanged, which makes accumulator
+// element r hold key 16(r/8) + 8g + r%8: elements 8h..8h+7 of tile T are then
+// exactly the eight consecutive keys the lane supplies as B operand of the value
+// product for the 16-key step 2T + h. P never leaves registers.
+//
+// LDS: a ring of NS stages, each holding K (64 keys x D) and V^T (D x 64 keys) of
+// one step. Both are stored as 1 KB blocks, one per (32-row tile, 32-byte column
+// slice): block entry (g, c) at g * 512 + c * 16 holds 16 bytes of row c. A wave's
+// 16-byte reads then fall on 16 distinct bank groups per quarter wave, addresses
+// are one per-lane base plus immediates, and each block is written by exactly one
+// direct global-to-LDS load (16 bytes per lane, lane i at byte 16 i).
+#include <type_traits>
+
+#include "absh_internal.h"
+
+namespace absh {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kSegments = 8;    // XCDs of an MI355X: one queue segment each
+constexpr int kFlagShift = 28;  // union entry: block id | (member m retains it) << (28 + m)
+constexpr uint32_t kBlockMask = (1u << kFlagShift) - 1;
+constexpr float kLazy = 8.0f;   // base-2 headroom before a row's reference max moves
+constexpr int kStepKeys = 64;
+
+template <int D, int BLK>
+struct UCfg {
+  static constexpr int MEMBERS = BLK >= 128 ? 2 : 4;
+  static constexpr int WPM = BLK / 32;         // waves per member
+  static constexpr int TW = MEMBERS * WPM;     // waves per workgroup
+  static constexpr int THREADS = TW * 64;
+  static constexpr int HPB = BLK / kStepKeys;  // steps per key block
+  static constexpr int K_BYTES = kStepKeys * D * 2;
+  static constexpr int V_BYTES = D * kStepKeys * 2;
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int NS = (128 * 1024) / STAGE > 8 ? 8 : (128 * 1024) / STAGE;
+  static constexpr int DS = D / 16;            // k-steps of S^T
+  static constexpr int DT = D / 32;            // O^T tiles
+  static constexpr int K_SLICES = K_BYTES / 1024;
+  static constexpr int SLICES = STAGE / 1024;
+  static constexpr int LPS = SLICES / TW;      // direct loads per wave per stage
+  static constexpr int VT_ROW = BLK * 2;       // bytes per row of a V^T block in HBM
+  static_assert(TW == 8, "eight waves per workgroup");
+  static_assert(K_SLICES % TW == 0 && SLICES % TW == 0, "slices must tile the waves");
+  static_assert(NS >= 3, "the pipeline needs three stages");
+  static_assert((NS - 2) * LPS < 64, "vmcnt range");
+};
+
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, uint32_t wave_off,
+                                           char* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void __attribute__((address_space(3)))*)lds_dst, 16, lane_off,
+                                           wave_off, 0, 0);
+}
+
+constexpr int kRawBufferFlags = 0x00020000;  // raw buffer descriptor, 32-bit data format
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Wait until at most `later` stages of this wave's direct loads are in flight.
+template <int LPS, int NS>
+__device__ __forceinline__ void wait_stages(int later) {
+  if (NS > 7 && later >= 5) wait_vm<(NS > 7 ? 5 * LPS : 0)>();
+  else if (NS > 6 && later >= 4) wait_vm<(NS > 6 ? 4 * LPS : 0)>();
+  else if (NS > 5 && later >= 3) wait_vm<(NS > 5 ? 3 * LPS : 0)>();
+  else if (NS > 4 && later >= 2) wait_vm<(NS > 4 ? 2 * LPS : 0)>();
+  else if (later >= 1) wait_vm<LPS>();
+  else wait_vm<0>();
+}
+
+typedef const int32_t __attribute__((address_space(4)))* const_i32;
+__device__ __forceinline__ const_i32 as_const(const int32_t* p) { return (const_i32)p; }
+
+__device__ __forceinline__ int pull(int32_t* counters, const int32_t* bounds, int units, int xcd, unsigned& dead) {
+  for (int k = 0; k < kSegments; ++k) {
+    const int seg = (xcd + k) & (kSegments - 1);
+    if (dead & (1u << seg)) continue;
+    const int lo = bounds ? bounds[seg] : (int)((int64_t)units * seg / kSegments);
+    const int hi = bounds ? bounds[seg + 1] : (int)((int64_t)units * (seg + 1) / kSegments);
+    const int idx = atomicAdd(&counters[seg], 1);
+    if (lo + idx < hi) return lo + idx;
+    dead |= 1u << seg;
+  }
+  return -1;
+}
+
+// Maximum (sum) of a lane's value and the value of lane l ^ 32.
+__device__ __forceinline__ float max_across_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__((UCfg<D, BLK>::THREADS)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, const bf16_t* __restrict__ vt,
+                       bf16_t* __restrict__ oh, AttnLists L, int32_t* __restrict__ counters, int units, int nb,
+                       int n_pad, int N, float scale_log2) {
+  using C = UCfg<D, BLK>;
+  constexpr int NS = C::NS;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // One LDS variable per stage: distinct variables let the compiler see that the
+  // reads of one stage do not alias the direct loads in flight into another.
+  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st4[NS > 4 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st5[NS > 5 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st6[NS > 6 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st7[NS > 7 ? C::STAGE : 16];
+  auto stage_ptr = [&](int i) __attribute__((always_inline)) -> char* {
+    switch (i) {
+      case 0: return st0;
+      case 1: return st1;
+      case 2: return st2;
+      case 3: return st3;
+      case 4: return st4;
+      case 5: return st5;
+      case 6: return st6;
+      default: return st7;
+    }
+  };
+  __shared__ int s_next[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets per-wave branches be scalar
+  const int col = lane & 31;
+  const int g = lane >> 5;
+  const int member = wave / C::WPM;
+  const int rows0 = (wave % C::WPM) * 32;  // this wave's first row within its member's block
+  const int xcd = blockIdx.x & (kSegments - 1);
+  const bool dense = L.counts == nullptr;
+  const int per_head = (nb + C::MEMBERS - 1) / C::MEMBERS;
+
+  // direct loads: lane i of the load for block (tile, column slice) fetches row
+  // i % 32, 16-byte column i / 32 of that slice
+  const uint32_t k_lane = (uint32_t)(col * (2 * D) + g * 16);
+  const uint32_t v_lane = (uint32_t)(col * C::VT_ROW + g * 16);
+  // LDS reads: S^T row c of a tile is key kappa(c) (bits 2 and 3 exchanged)
+  const int kappa = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
+  const uint32_t k_rd = (uint32_t)(g * 512 + kappa * 16);
+  const uint32_t v_rd = (uint32_t)(C::K_BYTES + g * 512 + col * 16);
+
+  // The two waves of a SIMD (w and w + 4) run the same phases after each barrier.
+  // The first wins issue arbitration, so it runs its step as if alone while the
+  // second does its vector work under the first one's matrix phases.
+  if (wave < 4) __builtin_amdgcn_s_setprio(1);
+
+  const int32_t* bounds = dense ? nullptr : L.sched;
+  unsigned dead = 0;
+  if (tid == 0) s_next[0] = pull(counters, bounds, units, xcd, dead);
+
+  for (int parity = 0;; parity ^= 1) {
+    __syncthreads();  // s_next[parity] is published; every wave is done with the previous unit
+    const int pos = __builtin_amdgcn_readfirstlane(s_next[parity]);
+    if (pos < 0) break;
+    const int bh = pos / per_head;
+    const int qb0 = (pos - bh * per_head) * C::MEMBERS;
+    const int cnt = dense ? nb : as_const(L.unit_cnt)[pos];
+    const_i32 list = dense ? nullptr : as_const(reinterpret_cast<const int32_t*>(L.unit_list) + (size_t)pos * nb);
+    uint32_t present = 0;
+#pragma unroll
+    for (int m = 0; m < C::MEMBERS; ++m)
+      if (qb0 + m < nb) present |= 1u << (kFlagShift + m);
+    const int nsteps = cnt * C::HPB;
+    // union entry of step k (0 past the end)
+    auto entry = [&](int k) __attribute__((always_inline)) -> uint32_t {
+      if (k >= nsteps) return 0u;
+      const int e = C::HPB == 1 ? k : k / C::HPB;
+      return list ? (uint32_t)list[e] : ((uint32_t)e | present);
+    };
+    // keys of step k that exist (the last block of a head can be short)
+    auto valid_keys = [&](int k, uint32_t e) __attribute__((always_inline)) -> int {
+      const int j = (int)(e & kBlockMask);
+      const int half = C::HPB == 1 ? 0 : k % C::HPB;
+      return min(kStepKeys, N - j * BLK - half * kStepKeys);
+    };
+    auto mine = [&](int k, uint32_t e) __attribute__((always_inline)) -> bool {
+      return ((e >> (kFlagShift + member)) & 1u) && valid_keys(k, e) > 0;
+    };
+
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kh + (size_t)bh * n_pad * D), (short)0, n_pad * 2 * D, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vt + (size_t)bh * nb * D * BLK), (short)0, nb * D * C::VT_ROW, kRawBufferFlags);
+    // stage `stage` <- K and V^T of step k (union entry e)
+    auto issue = [&](int stage, int k, uint32_t e) __attribute__((always_inline)) {
+      const uint32_t j = e & kBlockMask;
+      const uint32_t half = C::HPB == 1 ? 0u : (uint32_t)(k % C::HPB);
+      char* st = stage_ptr(stage);
+#pragma unroll
+      for (int i = 0; i < C::LPS; ++i) {
+        const int sl = wave + C::TW * i;
+        if (i < C::K_SLICES / C::TW) {
+          const int T = sl / C::DS, s = sl % C::DS;
+          const uint32_t row = j * BLK + half * kStepKeys + 32 * T;
+          load_lds16(krs, k_lane, row * (2 * D) + 32 * s, st + sl * 1024);
+        } else {
+          const int v = sl - C::K_SLICES, t = v / 4, u = v % 4;
+          load_lds16(vrs, v_lane, j * (uint32_t)(D * C::VT_ROW) + (32 * t) * C::VT_ROW + half * 128 + 32 * u,
+                     st + sl * 1024);
+        }
+      }
+    };
+
+    // this wave's 32 query rows as the B operand of S^T = K Q^T
+    const bool have = (present >> (kFlagShift + member)) & 1u;
+    const int qrow = (qb0 + member) * BLK + rows0 + col;
+    bf16x8 qf[C::DS];
+    if (have) {
+      const bf16_t* qsrc = qh + ((size_t)bh * n_pad + qrow) * D + 8 * g;
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * s);
+    }
+
+    // ring prologue: steps 0 .. NS-2 in flight
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k)
+      if (k < nsteps) issue(k, k, entry(k));
+    if (tid == 0) s_next[parity ^ 1] = pull(counters, bounds, units, xcd, dead);
+
+    f32x16 o[C::DT];
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t) o[t] = f32x16{};
+    float l_run = 0.f;        // this lane's share of its row's sum of (bf16) probabilities
+    float m_run = -INFINITY;  // the row's reference max, base-2 scaled
+    f32x16 S[2];              // S^T of the step whose softmax comes next
+
+    // The reference max moves only when a row's step max exceeds it by more than
+    // kLazy (base 2): probabilities stay below 2^kLazy and O is rescaled rarely.
+    // The result is the same softmax.
+    auto rescale_to = [&](float m_blk) __attribute__((always_inline)) {
+      const float m_new = fmaxf(m_run, m_blk);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    };
+    auto rescale = [&](float m_blk) __attribute__((always_inline)) {
+      if (__any(m_blk > m_run + kLazy)) rescale_to(m_blk);
+    };
+    // probabilities of elements r0 .. r0 + n - 1 (n even) of S^T tile T, as bf16 into
+    // the B operand of 16-key value step 2T + r0 / 8, and their row sum
+    auto probs = [&](bf16x8 (&pf)[4], int T, int r0, int n) __attribute__((always_inline)) {
+      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int r = r0; r < r0 + n; r += 2) {
+        const int u = 2 * T + r / 8, i = r % 8;
+        pf[u][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[T][r], scale_log2, -m_run));
+        pf[u][i + 1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[T][r + 1], scale_log2, -m_run));
+        // row sum of the same bf16 probabilities that enter the value product
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[u][i], pf[u][i + 1]}, one2, l_run, false);
+      }
+    };
+    // masks element r of S^T tile T past `valid` keys: it is key 32 T + 16 (r / 8) + 8 g + r % 8
+    auto mask = [&](int T, int r, int valid) __attribute__((always_inline)) {
+      if (32 * T + 16 * (r / 8) + (r % 8) >= valid - 8 * g) S[T][r] = -INFINITY;
+    };
+
+    // One step as a hand-ordered instruction stream. The matrix instructions go
+    // in this order: value product of 16-key steps 0 and 1 (phase 0), S^T tile 0
+    // of the next step (phase 1), value product of 16-key steps 2 and 3 (phase 2),
+    // S^T tile 1 (phase 3). Each reads one 16-byte LDS fragment, fetched DIST
+    // instructions ahead. The vector work rides along: the probabilities of tile 0
+    // come first, those of tile 1 under phase 0, the row maxima of the new tile 0
+    // under phase 3. Scheduling barriers keep each group of one LDS read, one
+    // matrix instruction and its share of vector work in place.
+    constexpr int NPV = 2 * C::DT;  // value-product instructions per phase
+    constexpr int NQK = C::DS;      // S^T instructions per tile
+    constexpr int DIST = 3;
+    auto body = [&](auto pv_c, auto qk_c, auto masked_c, const char* kbase, const char* vbase, int valid)
+                    __attribute__((always_inline)) -> float {
+      constexpr bool DP = decltype(pv_c)::value;
+      constexpr bool DQ = decltype(qk_c)::value;
+      constexpr bool MK = decltype(masked_c)::value;
+      constexpr int P0 = DP ? NPV : 0, P1 = DQ ? NQK : 0;
+      constexpr int NOPS = 2 * (P0 + P1);
+      // op i -> LDS fragment address
+      auto frag = [&](int i) __attribute__((always_inline)) -> const bf16x8* {
+        const int ph = i < P0 ? 0 : i < P0 + P1 ? 1 : i < 2 * P0 + P1 ? 2 : 3;
+        const int j = ph == 0 ? i : ph == 1 ? i - P0 : ph == 2 ? i - P0 - P1 : i - 2 * P0 - P1;
+        if (ph == 0 || ph == 2) {
+          const int u = (ph == 0 ? 0 : 2) + j / C::DT, t = j % C::DT;
+          return reinterpret_cast<const bf16x8*>(vbase + (t * 4 + u) * 1024);
+        }
+        return reinterpret_cast<const bf16x8*>(kbase + ((ph == 1 ? 0 : 1) * C::DS + j) * 1024);
+      };
+      bf16x8 fr[DIST + 1];
+      bf16x8 pf[4];
+      float mx0 = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < DIST; ++i)
+        if (i < NOPS) fr[i] = *frag(i);
+      if (DP) probs(pf, 0, 0, 16);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NOPS; ++i) {
+        if (i + DIST < NOPS) fr[(i + DIST) % (DIST + 1)] = *frag(i + DIST);
+        const bf16x8 a = fr[i % (DIST + 1)];
+        const int ph = i < P0 ? 0 : i < P0 + P1 ? 1 : i < 2 * P0 + P1 ? 2 : 3;
+        const int j = ph == 0 ? i : ph == 1 ? i - P0 : ph == 2 ? i - P0 - P1 : i - 2 * P0 - P1;
+        if (ph == 0 || ph == 2) {
+          const int u = (ph == 0 ? 0 : 2) + j / C::DT, t = j % C::DT;
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[u], o[t], 0, 0, 0);
+        } else {
+          const int T = ph == 1 ? 0 : 1;
+          S[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[j], j == 0 ? f32x16{} : S[T], 0, 0, 0);
+        }
+        if (ph == 0) {
+          // probabilities of tile 1, spread over phase 0
+          constexpr int PER = P0 > 0 ? 16 / P0 : 16;
+          probs(pf, 1, j * PER, PER);
+        } else if (ph == 3) {
+          // row maxima of the new tile 0, spread over phase 3
+          constexpr int PER = P1 > 0 ? 16 / P1 : 16;
+#pragma unroll
+          for (int r = j * PER; r < j * PER + PER; ++r) {
+            if (MK) mask(0, r, valid);
+            mx0 = fmaxf(mx0, S[0][r]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (!DQ) return -INFINITY;
+      float mx = mx0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (MK) mask(1, r, valid);
+        mx = fmaxf(mx, S[1][r]);
+      }
+      return max_across_halves(mx) * scale_log2;
+    };
+    auto fused = [&](const char* kbase, const char* vbase, int valid, auto masked_c) __attribute__((always_inline))
+        -> float {
+      return body(T_(), T_(), masked_c, kbase, vbase, valid);
+    };
+    auto solo_pv = [&](const char* vbase) __attribute__((always_inline)) {
+      body(T_(), F_(), F_(), nullptr, vbase, kStepKeys);
+    };
+    auto solo_qk = [&](const char* kbase, int valid, auto masked_c) __attribute__((always_inline)) -> float {
+      return body(F_(), T_(), masked_c, kbase, nullptr, valid);
+    };
+
+    // step 0: S^T only
+    uint32_t e0 = entry(0), e1 = entry(1);
+    if (NS - 2 < nsteps - 1) wait_vm<(NS - 2) * C::LPS>();
+    else wait_vm<0>();  // fewer steps than stages: everything issued must land
+    __syncthreads();
+    {
+      const int vk = valid_keys(0, e0);
+      const float m = vk < kStepKeys ? solo_qk(st0 + k_rd, vk, T_()) : solo_qk(st0 + k_rd, vk, F_());
+      if (mine(0, e0)) rescale(m);
+    }
+    // the step's start: loads of step k + 1 landed, all waves done with step k - 1,
+    // stage of step k - 1 refilled with step k + NS - 1
+    auto step_start = [&](int k, int stage_refill) __attribute__((always_inline)) {
+      wait_stages<C::LPS, NS>(min(NS - 3, nsteps - 2 - k));
+      __syncthreads();
+      if (k + NS - 1 < nsteps) issue(stage_refill, k + NS - 1, entry(k + NS - 1));
+    };
+    // Steady state: step k with its stage known at compile time (the compiler can
+    // then tell its LDS reads from the direct loads in flight into the other
+    // stages) and S^T of step k + 1 unmasked. Every wave runs the whole step; a
+    // wave whose query block does not retain block k gets zero probabilities, and
+    // one that does not retain block k + 1 ignores its S^T. The step is straight-
+    // line code; it returns whether the reference max must move (in m_blk).
+    auto step_fast = [&](int k, auto stage_c, float& m_blk) __attribute__((always_inline)) -> bool {
+      constexpr int SG = decltype(stage_c)::value;
+      const uint32_t e2 = entry(k + 2);
+      step_start(k, (SG + NS - 1) % NS);
+      const bool now = mine(k, e0);
+      const bool next = mine(k + 1, e1);
+      // two straight-line parts, each skipped by a wave whose query block does
+      // not retain the block: softmax + value product of step k, S^T of step k + 1
+      if (now) body(T_(), F_(), F_(), nullptr, stage_ptr(SG) + v_rd, kStepKeys);
+      float m = -INFINITY;
+      if (next) m = body(F_(), T_(), F_(), stage_ptr((SG + 1) % NS) + k_rd, nullptr, kStepKeys);
+      e0 = e1;
+      e1 = e2;
+      m_blk = m;
+      return next && __any(m > m_run + kLazy);
+    };
+    // Steps next to a head's short last block: run-time stage, masking, and each
+    // wave skips the work of blocks its query block does not retain.
+    auto step_tail = [&](int k) __attribute__((always_inline)) {
+      const uint32_t e2 = entry(k + 2);
+      step_start(k, (k + NS - 1) % NS);
+      const char* vbase = stage_ptr(k % NS) + v_rd;
+      const char* kbase = stage_ptr((k + 1) % NS) + k_rd;
+      const bool now = mine(k, e0);
+      const bool next = k + 1 < nsteps && mine(k + 1, e1);
+      const int vk1 = next ? valid_keys(k + 1, e1) : kStepKeys;
+      float m_blk = -INFINITY;
+      if (now && next)
+        m_blk = vk1 < kStepKeys ? fused(kbase, vbase, vk1, T_()) : fused(kbase, vbase, vk1, F_());
+      else if (now)
+        solo_pv(vbase);
+      else if (next)
+        m_blk = vk1 < kStepKeys ? solo_qk(kbase, vk1, T_()) : solo_qk(kbase, vk1, F_());
+      if (next) rescale(m_blk);
+      e0 = e1;
+      e1 = e2;
+    };
+    // first step whose keys run short (the partial last block of a head), else nsteps
+    int first_masked = nsteps;
+    if (nsteps > 0) {
+      const int nj = N - (nb - 1) * BLK;  // keys of the head's last block
+      if (nj < BLK && (entry(nsteps - 1) & kBlockMask) == (uint32_t)(nb - 1))
+        first_masked = nsteps - C::HPB + nj / kStepKeys;
+    }
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1 % NS>;
+    using I2 = std::integral_constant<int, 2 % NS>;
+    using I3 = std::integral_constant<int, 3 % NS>;
+    using I4 = std::integral_constant<int, 4 % NS>;
+    using I5 = std::integral_constant<int, 5 % NS>;
+    using I6 = std::integral_constant<int, 6 % NS>;
+    using I7 = std::integral_constant<int, 7 % NS>;
+    const int kmain = first_masked - 1;  // steps before it compute unmasked S^T
+    int k = 0;
+    // The steady-state steps are unrolled by stage.
+    auto fast = [&](int k, auto stage_c) __attribute__((always_inline)) {
+      float m_blk;
+      if (step_fast(k, stage_c, m_blk)) rescale_to(m_blk);
+    };
+    while (k < kmain) {
+      fast(k, I0());
+      if (++k >= kmain) break;
+      fast(k, I1());
+      if (++k >= kmain) break;
+      fast(k, I2());
+      if (++k >= kmain) break;
+      fast(k, I3());
+      if (++k >= kmain) break;
+      if (NS > 4) {
+        fast(k, I4());
+        if (++k >= kmain) break;
+        fast(k, I5());
+        if (++k >= kmain) break;
+        fast(k, I6());
+        if (++k >= kmain) break;
+        fast(k, I7());
+        ++k;
+      }
+    }
+    for (; k < nsteps; ++k) step_tail(k);
+
+    if (have) {
+      const float l = sum_across_halves(l_run);
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      bf16_t* orow = oh + ((size_t)bh * n_pad + qrow) * D;
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 w;
+          w.x = (uint32_t)f32_to_bf16(o[t][4 * q] * inv) | ((uint32_t)f32_to_bf16(o[t][4 * q + 1] * inv) << 16);
+          w.y = (uint32_t)f32_to_bf16(o[t][4 * q + 2] * inv) | ((uint32_t)f32_to_bf16(o[t][4 * q + 3] * inv) << 16);
+          *reinterpret_cast<uint2*>(orow + 32 * t + 8 * q + 4 * g) = w;
+        }
+    }
+  }
+
+  // The last workgroup to finish resets the pull counters for the next launch.
+  if (tid == 0) {
+    __threadfence();
+    if (atomicAdd(&counters[kSegments], 1) == (int)gridDim.x - 1) {
+      for (int s = 0; s <= kSegments; ++s) atomicExch(&counters[s], 0);
+      __threadfence();
+    }
+  }
+}
+
+template <int D, int BLK>
+hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B, int H,
+                  const AttnLists& L, bool dense, hipStream_t s) {
+  using C = UCfg<D, BLK>;
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, union_attn_kernel<D, BLK>, C::THREADS, 0);
+    if (e != hipSuccess) return e;
+    if (per_cu < 1) per_cu = 1;
+  }
+  const int units = B * H * ((c->nb + C::MEMBERS - 1) / C::MEMBERS);
+  const int grid = c->num_cus * per_cu;
+  const float scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
+  AttnLists Lk = L;
+  if (dense) Lk = AttnLists{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, C::MEMBERS};
+  union_attn_kernel<D, BLK><<<grid, C::THREADS, 0, s>>>(
+      reinterpret_cast<const bf16_t*>(qh), reinterpret_cast<const bf16_t*>(kh), reinterpret_cast<const bf16_t*>(vt),
+      reinterpret_cast<bf16_t*>(oh), Lk, c->counters, units, c->nb, c->n_pad, c->N, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool union_attention_supported(int d, int block, int members) {
+  return (d == 64 || d == 128) && ((block == 64 && members == 4) || (block == 128 && members == 2));
+}
+
+hipError_t launch_union_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh,
+                                  int B, int H, int d, const AttnLists* lists, hipStream_t s) {
+  AttnLists L = lists ? *lists : AttnLists{};
+  const bool dense = lists == nullptr;
+#define ABSH_UNION(DD, BB) \
+  if (d == DD && c->block == BB) return launch<DD, BB>(c, qh, kh, vt, oh, B, H, L, dense, s);
+  ABSH_UNION(64, 64)
+  ABSH_UNION(64, 128)
+  ABSH_UNION(128, 64)
+  ABSH_UNION(128, 128)
+#undef ABSH_UNION
+  return hipErrorInvalidValue;
+}
+
+}  // namespace absh
