@@ -29,12 +29,17 @@
 // exactly the eight consecutive keys the lane supplies as B operand of the value
 // product for the 16-key step 2T + h. P never leaves registers.
 //
-// LDS: a ring of NS stages, each holding K (64 keys x D) and V^T (D x 64 keys) of
-// one step. Both are stored as 1 KB blocks, one per (32-row tile, 32-byte column
-// slice): block entry (g, c) at g * 512 + c * 16 holds 16 bytes of row c. A wave's
-// 16-byte reads then fall on 16 distinct bank groups per quarter wave, addresses
-// are one per-lane base plus immediates, and each block is written by exactly one
-// direct global-to-LDS load (16 bytes per lane, lane i at byte 16 i).
+// LDS: four slots for K (64 keys x D) and four for V^T (D x 64 keys), each slot
+// its own LDS variable. Both are stored as 1 KB blocks, one per (32-row tile,
+// 32-byte column slice): block entry (g, c) at g * 512 + c * 16 holds 16 bytes of
+// row c. A wave's 16-byte reads then fall on 16 distinct bank groups per quarter
+// wave, addresses are one per-lane base plus immediates, and each block is written
+// by exactly one direct global-to-LDS load (16 bytes per lane, lane i at 16 i).
+//
+// Steps go in pairs with one workgroup barrier per pair. Step k reads V^T of step
+// k and K of step k + 1, so a pair (k, k + 1) holds V^T of k, k + 1 and K of
+// k + 1, k + 2; at its barrier it issues V^T of k + 2, k + 3 and K of k + 3, k + 4
+// into the slots the previous pair released, to land before the next pair.
 #include <type_traits>
 
 #include "absh_internal.h"
@@ -61,18 +66,15 @@ struct UCfg {
   static constexpr int HPB = BLK / kStepKeys;  // steps per key block
   static constexpr int K_BYTES = kStepKeys * D * 2;
   static constexpr int V_BYTES = D * kStepKeys * 2;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int NS = (128 * 1024) / STAGE > 8 ? 8 : (128 * 1024) / STAGE;
   static constexpr int DS = D / 16;            // k-steps of S^T
   static constexpr int DT = D / 32;            // O^T tiles
   static constexpr int K_SLICES = K_BYTES / 1024;
-  static constexpr int SLICES = STAGE / 1024;
-  static constexpr int LPS = SLICES / TW;      // direct loads per wave per stage
+  static constexpr int V_SLICES = V_BYTES / 1024;
+  static constexpr int KPW = K_SLICES / TW;    // direct loads per wave per K slot
+  static constexpr int VPW = V_SLICES / TW;    // direct loads per wave per V^T slot
   static constexpr int VT_ROW = BLK * 2;       // bytes per row of a V^T block in HBM
   static_assert(TW == 8, "eight waves per workgroup");
-  static_assert(K_SLICES % TW == 0 && SLICES % TW == 0, "slices must tile the waves");
-  static_assert(NS >= 3, "the pipeline needs three stages");
-  static_assert((NS - 2) * LPS < 64, "vmcnt range");
+  static_assert(K_SLICES % TW == 0 && V_SLICES % TW == 0, "slices must tile the waves");
 };
 
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, uint32_t wave_off,
@@ -86,17 +88,6 @@ constexpr int kRawBufferFlags = 0x00020000;  // raw buffer descriptor, 32-bit da
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Wait until at most `later` stages of this wave's direct loads are in flight.
-template <int LPS, int NS>
-__device__ __forceinline__ void wait_stages(int later) {
-  if (NS > 7 && later >= 5) wait_vm<(NS > 7 ? 5 * LPS : 0)>();
-  else if (NS > 6 && later >= 4) wait_vm<(NS > 6 ? 4 * LPS : 0)>();
-  else if (NS > 5 && later >= 3) wait_vm<(NS > 5 ? 3 * LPS : 0)>();
-  else if (NS > 4 && later >= 2) wait_vm<(NS > 4 ? 2 * LPS : 0)>();
-  else if (later >= 1) wait_vm<LPS>();
-  else wait_vm<0>();
 }
 
 typedef const int32_t __attribute__((address_space(4)))* const_i32;
@@ -131,30 +122,25 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
                        bf16_t* __restrict__ oh, AttnLists L, int32_t* __restrict__ counters, int units, int nb,
                        int n_pad, int N, float scale_log2) {
   using C = UCfg<D, BLK>;
-  constexpr int NS = C::NS;
   using T_ = std::true_type;
   using F_ = std::false_type;
-  // One LDS variable per stage: distinct variables let the compiler see that the
-  // reads of one stage do not alias the direct loads in flight into another.
-  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st2[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? C::STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) char st4[NS > 4 ? C::STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) char st5[NS > 5 ? C::STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) char st6[NS > 6 ? C::STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) char st7[NS > 7 ? C::STAGE : 16];
-  auto stage_ptr = [&](int i) __attribute__((always_inline)) -> char* {
-    switch (i) {
-      case 0: return st0;
-      case 1: return st1;
-      case 2: return st2;
-      case 3: return st3;
-      case 4: return st4;
-      case 5: return st5;
-      case 6: return st6;
-      default: return st7;
-    }
+  // One LDS variable per slot: distinct variables let the compiler see that the
+  // reads of one slot do not alias the direct loads in flight into another.
+  __shared__ __attribute__((aligned(1024))) char ks0[C::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ks1[C::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ks2[C::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ks3[C::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vs0[C::V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vs1[C::V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vs2[C::V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vs3[C::V_BYTES];
+  auto kslot = [&](int i) __attribute__((always_inline)) -> char* {
+    i &= 3;
+    return i == 0 ? ks0 : i == 1 ? ks1 : i == 2 ? ks2 : ks3;
+  };
+  auto vslot = [&](int i) __attribute__((always_inline)) -> char* {
+    i &= 3;
+    return i == 0 ? vs0 : i == 1 ? vs1 : i == 2 ? vs2 : vs3;
   };
   __shared__ int s_next[2];
 
@@ -176,7 +162,7 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
   // LDS reads: S^T row c of a tile is key kappa(c) (bits 2 and 3 exchanged)
   const int kappa = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
   const uint32_t k_rd = (uint32_t)(g * 512 + kappa * 16);
-  const uint32_t v_rd = (uint32_t)(C::K_BYTES + g * 512 + col * 16);
+  const uint32_t v_rd = (uint32_t)(g * 512 + col * 16);
 
   // The two waves of a SIMD (w and w + 4) run the same phases after each barrier.
   // The first wins issue arbitration, so it runs its step as if alone while the
@@ -220,23 +206,27 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
         (void*)(kh + (size_t)bh * n_pad * D), (short)0, n_pad * 2 * D, kRawBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vt + (size_t)bh * nb * D * BLK), (short)0, nb * D * C::VT_ROW, kRawBufferFlags);
-    // stage `stage` <- K and V^T of step k (union entry e)
-    auto issue = [&](int stage, int k, uint32_t e) __attribute__((always_inline)) {
+    // K slot <- K of step k (union entry e); V^T slot <- V^T of step k
+    auto issue_k = [&](int slot, int k, uint32_t e) __attribute__((always_inline)) {
       const uint32_t j = e & kBlockMask;
       const uint32_t half = C::HPB == 1 ? 0u : (uint32_t)(k % C::HPB);
-      char* st = stage_ptr(stage);
+      char* st = kslot(slot);
 #pragma unroll
-      for (int i = 0; i < C::LPS; ++i) {
-        const int sl = wave + C::TW * i;
-        if (i < C::K_SLICES / C::TW) {
-          const int T = sl / C::DS, s = sl % C::DS;
-          const uint32_t row = j * BLK + half * kStepKeys + 32 * T;
-          load_lds16(krs, k_lane, row * (2 * D) + 32 * s, st + sl * 1024);
-        } else {
-          const int v = sl - C::K_SLICES, t = v / 4, u = v % 4;
-          load_lds16(vrs, v_lane, j * (uint32_t)(D * C::VT_ROW) + (32 * t) * C::VT_ROW + half * 128 + 32 * u,
-                     st + sl * 1024);
-        }
+      for (int i = 0; i < C::KPW; ++i) {
+        const int sl = wave + C::TW * i, T = sl / C::DS, s = sl % C::DS;
+        const uint32_t row = j * BLK + half * kStepKeys + 32 * T;
+        load_lds16(krs, k_lane, row * (2 * D) + 32 * s, st + sl * 1024);
+      }
+    };
+    auto issue_v = [&](int slot, int k, uint32_t e) __attribute__((always_inline)) {
+      const uint32_t j = e & kBlockMask;
+      const uint32_t half = C::HPB == 1 ? 0u : (uint32_t)(k % C::HPB);
+      char* st = vslot(slot);
+#pragma unroll
+      for (int i = 0; i < C::VPW; ++i) {
+        const int sl = wave + C::TW * i, t = sl / 4, u = sl % 4;
+        load_lds16(vrs, v_lane, j * (uint32_t)(D * C::VT_ROW) + (32 * t) * C::VT_ROW + half * 128 + 32 * u,
+                   st + sl * 1024);
       }
     };
 
@@ -250,10 +240,18 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
       for (int s = 0; s < C::DS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * s);
     }
 
-    // ring prologue: steps 0 .. NS-2 in flight
-#pragma unroll
-    for (int k = 0; k < NS - 1; ++k)
-      if (k < nsteps) issue(k, k, entry(k));
+    // entries of steps k .. k + 4
+    uint32_t e0 = entry(0), e1 = entry(1), e2 = entry(2), e3 = entry(3), e4 = entry(4);
+    // prologue: K of steps 0, 1, 2 and V^T of steps 0, 1
+    if (0 < nsteps) {
+      issue_k(0, 0, e0);
+      issue_v(0, 0, e0);
+    }
+    if (1 < nsteps) {
+      issue_k(1, 1, e1);
+      issue_v(1, 1, e1);
+    }
+    if (2 < nsteps) issue_k(2, 2, e2);
     if (tid == 0) s_next[parity ^ 1] = pull(counters, bounds, units, xcd, dead);
 
     f32x16 o[C::DT];
@@ -380,54 +378,53 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
     };
 
     // step 0: S^T only
-    uint32_t e0 = entry(0), e1 = entry(1);
-    if (NS - 2 < nsteps - 1) wait_vm<(NS - 2) * C::LPS>();
-    else wait_vm<0>();  // fewer steps than stages: everything issued must land
+    wait_vm<0>();
     __syncthreads();
     {
       const int vk = valid_keys(0, e0);
-      const float m = vk < kStepKeys ? solo_qk(st0 + k_rd, vk, T_()) : solo_qk(st0 + k_rd, vk, F_());
+      const float m = vk < kStepKeys ? solo_qk(ks0 + k_rd, vk, T_()) : solo_qk(ks0 + k_rd, vk, F_());
       if (mine(0, e0)) rescale(m);
     }
-    // the step's start: loads of step k + 1 landed, all waves done with step k - 1,
-    // stage of step k - 1 refilled with step k + NS - 1
-    auto step_start = [&](int k, int stage_refill) __attribute__((always_inline)) {
-      wait_stages<C::LPS, NS>(min(NS - 3, nsteps - 2 - k));
+    // Pair start (k even): everything issued at the previous pair has landed, all
+    // waves are done with steps k - 2 and k - 1, and their slots take V^T of
+    // k + 2, k + 3 and K of k + 3, k + 4.
+    auto pair_start = [&](int k) __attribute__((always_inline)) {
+      wait_vm<0>();
       __syncthreads();
-      if (k + NS - 1 < nsteps) issue(stage_refill, k + NS - 1, entry(k + NS - 1));
+      if (k + 2 < nsteps) issue_v(k + 2, k + 2, e2);
+      if (k + 3 < nsteps) {
+        issue_v(k + 3, k + 3, e3);
+        issue_k(k + 3, k + 3, e3);
+      }
+      if (k + 4 < nsteps) issue_k(k + 4, k + 4, e4);
     };
-    // Steady state: step k with its stage known at compile time (the compiler can
-    // then tell its LDS reads from the direct loads in flight into the other
-    // stages) and S^T of step k + 1 unmasked. Every wave runs the whole step; a
-    // wave whose query block does not retain block k gets zero probabilities, and
-    // one that does not retain block k + 1 ignores its S^T. The step is straight-
-    // line code; it returns whether the reference max must move (in m_blk).
-    auto step_fast = [&](int k, auto stage_c, float& m_blk) __attribute__((always_inline)) -> bool {
-      constexpr int SG = decltype(stage_c)::value;
-      const uint32_t e2 = entry(k + 2);
-      step_start(k, (SG + NS - 1) % NS);
-      const bool now = mine(k, e0);
-      const bool next = mine(k + 1, e1);
-      // two straight-line parts, each skipped by a wave whose query block does
-      // not retain the block: softmax + value product of step k, S^T of step k + 1
-      if (now) body(T_(), F_(), F_(), nullptr, stage_ptr(SG) + v_rd, kStepKeys);
-      float m = -INFINITY;
-      if (next) m = body(F_(), T_(), F_(), stage_ptr((SG + 1) % NS) + k_rd, nullptr, kStepKeys);
-      e0 = e1;
-      e1 = e2;
-      m_blk = m;
-      return next && __any(m > m_run + kLazy);
+    auto pair_end = [&](int k) __attribute__((always_inline)) {
+      e0 = e2;
+      e1 = e3;
+      e2 = e4;
+      e3 = entry(k + 5);
+      e4 = entry(k + 6);
     };
-    // Steps next to a head's short last block: run-time stage, masking, and each
-    // wave skips the work of blocks its query block does not retain.
-    auto step_tail = [&](int k) __attribute__((always_inline)) {
-      const uint32_t e2 = entry(k + 2);
-      step_start(k, (k + NS - 1) % NS);
-      const char* vbase = stage_ptr(k % NS) + v_rd;
-      const char* kbase = stage_ptr((k + 1) % NS) + k_rd;
-      const bool now = mine(k, e0);
-      const bool next = k + 1 < nsteps && mine(k + 1, e1);
-      const int vk1 = next ? valid_keys(k + 1, e1) : kStepKeys;
+    // Steady state: step k (slots known at compile time through the unrolling
+    // below, so the compiler need not wait for loads in flight into other slots)
+    // with S^T of step k + 1 unmasked. The step is two straight-line parts that a
+    // wave skips when its query block does not retain the block: softmax + value
+    // product of step k, then S^T of step k + 1.
+    auto step_fast = [&](int k, auto slot_c, uint32_t ek, uint32_t ek1) __attribute__((always_inline)) {
+      constexpr int SL = decltype(slot_c)::value;
+      if (mine(k, ek)) body(T_(), F_(), F_(), nullptr, vslot(SL) + v_rd, kStepKeys);
+      if (mine(k + 1, ek1)) {
+        const float m = body(F_(), T_(), F_(), kslot(SL + 1) + k_rd, nullptr, kStepKeys);
+        if (__any(m > m_run + kLazy)) rescale_to(m);
+      }
+    };
+    // Steps next to a head's short last block: run-time slots and masking.
+    auto step_tail = [&](int k, uint32_t ek, uint32_t ek1) __attribute__((always_inline)) {
+      const char* vbase = vslot(k) + v_rd;
+      const char* kbase = kslot(k + 1) + k_rd;
+      const bool now = mine(k, ek);
+      const bool next = k + 1 < nsteps && mine(k + 1, ek1);
+      const int vk1 = next ? valid_keys(k + 1, ek1) : kStepKeys;
       float m_blk = -INFINITY;
       if (now && next)
         m_blk = vk1 < kStepKeys ? fused(kbase, vbase, vk1, T_()) : fused(kbase, vbase, vk1, F_());
@@ -436,8 +433,6 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
       else if (next)
         m_blk = vk1 < kStepKeys ? solo_qk(kbase, vk1, T_()) : solo_qk(kbase, vk1, F_());
       if (next) rescale(m_blk);
-      e0 = e1;
-      e1 = e2;
     };
     // first step whose keys run short (the partial last block of a head), else nsteps
     int first_masked = nsteps;
@@ -447,41 +442,30 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
         first_masked = nsteps - C::HPB + nj / kStepKeys;
     }
     using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1 % NS>;
-    using I2 = std::integral_constant<int, 2 % NS>;
-    using I3 = std::integral_constant<int, 3 % NS>;
-    using I4 = std::integral_constant<int, 4 % NS>;
-    using I5 = std::integral_constant<int, 5 % NS>;
-    using I6 = std::integral_constant<int, 6 % NS>;
-    using I7 = std::integral_constant<int, 7 % NS>;
-    const int kmain = first_masked - 1;  // steps before it compute unmasked S^T
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    // pairs whose steps both compute unmasked S^T for their next step: k + 2 < first_masked
     int k = 0;
-    // The steady-state steps are unrolled by stage.
-    auto fast = [&](int k, auto stage_c) __attribute__((always_inline)) {
-      float m_blk;
-      if (step_fast(k, stage_c, m_blk)) rescale_to(m_blk);
-    };
-    while (k < kmain) {
-      fast(k, I0());
-      if (++k >= kmain) break;
-      fast(k, I1());
-      if (++k >= kmain) break;
-      fast(k, I2());
-      if (++k >= kmain) break;
-      fast(k, I3());
-      if (++k >= kmain) break;
-      if (NS > 4) {
-        fast(k, I4());
-        if (++k >= kmain) break;
-        fast(k, I5());
-        if (++k >= kmain) break;
-        fast(k, I6());
-        if (++k >= kmain) break;
-        fast(k, I7());
-        ++k;
-      }
+    while (k + 2 < first_masked) {
+      pair_start(k);
+      step_fast(k, I0(), e0, e1);
+      step_fast(k + 1, I1(), e1, e2);
+      pair_end(k);
+      k += 2;
+      if (k + 2 >= first_masked) break;
+      pair_start(k);
+      step_fast(k, I2(), e0, e1);
+      step_fast(k + 1, I3(), e1, e2);
+      pair_end(k);
+      k += 2;
     }
-    for (; k < nsteps; ++k) step_tail(k);
+    for (; k < nsteps; k += 2) {
+      pair_start(k);
+      step_tail(k, e0, e1);
+      if (k + 1 < nsteps) step_tail(k + 1, e1, e2);
+      pair_end(k);
+    }
 
     if (have) {
       const float l = sum_across_halves(l_run);
