@@ -167,7 +167,7 @@ def main():
 
     roof = {
         "bound": "mfma",
-        "kernel": f"attn_kernel<{d},{w.block}>",
+        "kernel": attention_kernel_name(d, w.block, 1 if args.schedule == "lpt" else (2 if w.block >= 128 else 4)),
         "achieved": round(attn_tflops, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
@@ -215,13 +215,24 @@ def main():
     print(json.dumps(out))
 
 
+def attention_kernel_name(d, block, members):
+    """Name of the kernel that runs the attention launch (as the profiler lists it).
+
+    Units of four 64-row or two 128-row query blocks at head dim 64 or 128 run on
+    the union kernel; any other shape runs on the general one.
+    """
+    if d in (64, 128) and (block, members) in ((64, 4), (128, 2)):
+        return f"union_attn_kernel<{d}, {block}>"
+    return f"attn_kernel<{d}, {block}>"
+
+
 def measured_traffic(path, workload, schedule):
     """HBM bytes per attention launch from a committed counter summary, or None.
 
     The summary holds FETCH_SIZE + WRITE_SIZE of the attention kernel, scaled by a
-    plain-copy calibration, together with the sha256 of the kernel source it was
-    taken on. A figure taken on another source, workload or schedule is stale and
-    gives None.
+    plain-copy calibration, together with the sha256 of the attention sources it
+    was taken on (attn.hip followed by attn_union.hip). A figure taken on another
+    source, workload or schedule is stale and gives None.
     """
     import hashlib
 
@@ -233,10 +244,11 @@ def measured_traffic(path, workload, schedule):
             m = line.strip().split(": ", 1)
             if len(m) == 2:
                 fields[m[0]] = m[1]
-    src = os.path.join(ROOT, "adaptive_block_sparse_hilbert_amd", "csrc", "attn.hip")
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if (fields.get("attn_hip_sha256") != sha or fields.get("workload") != workload
+    h = hashlib.sha256()
+    for name in ("attn.hip", "attn_union.hip"):
+        with open(os.path.join(ROOT, "adaptive_block_sparse_hilbert_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if (fields.get("attn_src_sha256") != h.hexdigest() or fields.get("workload") != workload
             or fields.get("schedule") != schedule or "hbm_bytes_per_launch" not in fields):
         return None
     return int(fields["hbm_bytes_per_launch"])
