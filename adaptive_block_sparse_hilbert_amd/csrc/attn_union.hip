@@ -30,11 +30,13 @@
 // product for the 16-key step 2T + h. P never leaves registers.
 //
 // LDS: four slots for K (64 keys x D) and four for V^T (D x 64 keys), each slot
-// its own LDS variable. Both are stored as 1 KB blocks, one per (32-row tile,
-// 32-byte column slice): block entry (g, c) at g * 512 + c * 16 holds 16 bytes of
-// row c. A wave's 16-byte reads then fall on 16 distinct bank groups per quarter
-// wave, addresses are one per-lane base plus immediates, and each block is written
-// by exactly one direct global-to-LDS load (16 bytes per lane, lane i at 16 i).
+// its own LDS variable. Both are stored as 1 KB blocks of 8 rows x 128 bytes (a
+// row's 128-byte chunk h, rows 8b .. 8b + 7): the 16-byte column c of row 8b + r
+// sits at (c ^ (b & 1)) * 128 + 16 r. Each block is written by exactly one direct
+// global-to-LDS load (16 bytes per lane, lane i at 16 i), whose lanes then cover
+// eight whole 128-byte lines of K or V^T in memory. A quarter wave's 16-byte reads
+// (16 consecutive rows of one column) fall on 16 distinct bank groups, and each
+// lane's read addresses are one per-lane base plus immediates.
 //
 // Steps go in pairs with one workgroup barrier per pair. Step k reads V^T of step
 // k and K of step k + 1, so a pair (k, k + 1) holds V^T of k, k + 1 and K of
@@ -74,6 +76,7 @@ struct UCfg {
   static constexpr int VPW = V_SLICES / TW;    // direct loads per wave per V^T slot
   static constexpr int VT_ROW = BLK * 2;       // bytes per row of a V^T block in HBM
   static_assert(TW == 8, "eight waves per workgroup");
+  static_assert(K_SLICES == 8 * KPW && V_SLICES == 8 * VPW, "wave w loads the blocks w + 8 i");
   static_assert(K_SLICES % TW == 0 && V_SLICES % TW == 0, "slices must tile the waves");
 };
 
@@ -155,14 +158,17 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
   const bool dense = L.counts == nullptr;
   const int per_head = (nb + C::MEMBERS - 1) / C::MEMBERS;
 
-  // direct loads: lane i of the load for block (tile, column slice) fetches row
-  // i % 32, 16-byte column i / 32 of that slice
-  const uint32_t k_lane = (uint32_t)(col * (2 * D) + g * 16);
-  const uint32_t v_lane = (uint32_t)(col * C::VT_ROW + g * 16);
-  // LDS reads: S^T row c of a tile is key kappa(c) (bits 2 and 3 exchanged)
+  // Direct loads: wave w loads the blocks w, w + 8, ... of a slot, all with row
+  // group b = w (K: blocks h * 8 + b; V^T: blocks b = w + 8 i, so b & 1 = w & 1).
+  // Lane i fetches row 8 b + i % 8, 16-byte column (i / 8) ^ (b & 1) of the chunk.
+  const uint32_t k_lane = (uint32_t)((lane % 8) * (2 * D) + ((lane / 8) ^ (wave & 1)) * 16);
+  const uint32_t v_lane = (uint32_t)((lane % 8) * C::VT_ROW + ((lane / 8) ^ (wave & 1)) * 16);
+  // LDS reads: S^T row c of a tile is key kappa(c) (bits 2 and 3 exchanged); the
+  // lane reads 16-byte column g (+ 2 per further k-step) of its row
   const int kappa = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
-  const uint32_t k_rd = (uint32_t)(g * 512 + kappa * 16);
-  const uint32_t v_rd = (uint32_t)(g * 512 + col * 16);
+  auto rd_base = [&](int row) { return (uint32_t)((row / 8) * 1024 + (g ^ ((row / 8) & 1)) * 128 + (row % 8) * 16); };
+  const uint32_t k_rd = rd_base(kappa);
+  const uint32_t v_rd = rd_base(col);
 
   // The two waves of a SIMD (w and w + 4) run the same phases after each barrier.
   // The first wins issue arbitration, so it runs its step as if alone while the
@@ -211,12 +217,9 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
       const uint32_t j = e & kBlockMask;
       const uint32_t half = C::HPB == 1 ? 0u : (uint32_t)(k % C::HPB);
       char* st = kslot(slot);
+      const uint32_t row = j * BLK + half * kStepKeys + 8 * wave;
 #pragma unroll
-      for (int i = 0; i < C::KPW; ++i) {
-        const int sl = wave + C::TW * i, T = sl / C::DS, s = sl % C::DS;
-        const uint32_t row = j * BLK + half * kStepKeys + 32 * T;
-        load_lds16(krs, k_lane, row * (2 * D) + 32 * s, st + sl * 1024);
-      }
+      for (int i = 0; i < C::KPW; ++i) load_lds16(krs, k_lane, row * (2 * D) + 128 * i, st + (wave + C::TW * i) * 1024);
     };
     auto issue_v = [&](int slot, int k, uint32_t e) __attribute__((always_inline)) {
       const uint32_t j = e & kBlockMask;
@@ -224,9 +227,8 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
       char* st = vslot(slot);
 #pragma unroll
       for (int i = 0; i < C::VPW; ++i) {
-        const int sl = wave + C::TW * i, t = sl / 4, u = sl % 4;
-        load_lds16(vrs, v_lane, j * (uint32_t)(D * C::VT_ROW) + (32 * t) * C::VT_ROW + half * 128 + 32 * u,
-                   st + sl * 1024);
+        const int n = wave + C::TW * i;  // block: V^T rows 8 n .. 8 n + 7
+        load_lds16(vrs, v_lane, j * (uint32_t)(D * C::VT_ROW) + (8 * n) * C::VT_ROW + half * 128, st + n * 1024);
       }
     };
 
@@ -317,9 +319,11 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
         const int j = ph == 0 ? i : ph == 1 ? i - P0 : ph == 2 ? i - P0 - P1 : i - 2 * P0 - P1;
         if (ph == 0 || ph == 2) {
           const int u = (ph == 0 ? 0 : 2) + j / C::DT, t = j % C::DT;
-          return reinterpret_cast<const bf16x8*>(vbase + (t * 4 + u) * 1024);
+          return reinterpret_cast<const bf16x8*>(vbase + t * 4096 + u * 256);
         }
-        return reinterpret_cast<const bf16x8*>(kbase + ((ph == 1 ? 0 : 1) * C::DS + j) * 1024);
+        // 32-key tile T, k-step j: chunk j / 4, row groups 4 T .. 4 T + 3
+        const int T = ph == 1 ? 0 : 1;
+        return reinterpret_cast<const bf16x8*>(kbase + ((j / 4) * 8 + 4 * T) * 1024 + (j % 4) * 256);
       };
       bf16x8 fr[DIST + 1];
       bf16x8 pf[4];
