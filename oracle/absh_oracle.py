@@ -29,6 +29,10 @@ each is named where it is used:
     skipped) by the next block of its own importance order.
   * LPT queue (one-GPU reading of RLB): tiles sorted by retained count,
     descending, ties by ascending tile id.
+  * Rank-level RLB and SASA (review Eq. 2, 5-10, 3.2, 3.3) with the eight XCDs
+    of one GPU as the ranks: contiguous head placement, the piecewise policy on
+    rho, an exhaustive search of a restricted one-send-one-receive migration
+    space, and per-rank slack budgets spent by water-filling the rank's tiles.
   * Attention: exact softmax(Q K_R^T / sqrt(d)) V_R over the tokens of the
     retained key blocks R of each query block.
 
@@ -45,6 +49,7 @@ special cases); see the header of each test file.
 from __future__ import annotations
 
 import heapq
+import itertools
 import math
 from dataclasses import dataclass
 from typing import List, Optional, Sequence
@@ -351,6 +356,180 @@ def list_schedule(costs: Sequence[float], order: Sequence[int], workers: int):
         loads[w] += costs[t]
         heapq.heappush(heap, (free + costs[t], w))
     return loads, float(loads.max())
+
+
+# --------------------------------------------------------------------------
+# Rank-level runtime stages with the eight XCDs of one GPU as the ranks
+# (review 核心公式 Eq. 1-2 and 5-10; 3.2 RLB; 3.3 SASA and its piecewise
+# policy; the RLB and SASA steps of 五; parameters of 五)
+# --------------------------------------------------------------------------
+
+RANKS = 8                     # XCDs of an MI355X, each with its own L2
+RLB_K1, RLB_K2 = 1.05, 1.10   # rho below k1: nothing; below k2: SASA only; else RLB, then SASA
+SASA_N1, SASA_N2 = 0.8, 0.07  # augmentation coefficient, trigger threshold
+MAX_PLANS = 1 << 26           # size limit of the enumerated migration space
+
+
+def rank_of_heads(BH: int, R: int = RANKS) -> np.ndarray:
+    """Initial placement: rank r holds the contiguous heads floor(r BH / R) .. floor((r+1) BH / R) - 1.
+
+    This is the head split of Ulysses sequence parallelism (review, 三 "技术架构").
+    """
+    owner = np.empty(BH, dtype=np.int64)
+    for r in range(R):
+        owner[r * BH // R:(r + 1) * BH // R] = r
+    return owner
+
+
+def rank_loads(work: np.ndarray, owner: np.ndarray, R: int = RANKS) -> np.ndarray:
+    """Eq. 1 at rank level, in retained blocks: W_r = sum of work_h over the heads rank r holds (int64).
+
+    L_r of Eq. 1 is W_r / nb; every ratio used below is the same in either unit.
+    """
+    W = np.zeros(R, dtype=np.int64)
+    np.add.at(W, owner, np.asarray(work, dtype=np.int64).reshape(-1))
+    return W
+
+
+def rank_policy(rho: float, k1: float = RLB_K1, k2: float = RLB_K2) -> str:
+    """Piecewise enabling (review 3.3): 'none' below k1, 'sasa' below k2, else 'rlb+sasa'."""
+    if rho < k1:
+        return "none"
+    return "sasa" if rho < k2 else "rlb+sasa"
+
+
+def rlb_options(work: np.ndarray, owner: np.ndarray, R: int = RANKS):
+    """The migration space searched by RLB, as options per sending rank.
+
+    Reading of S_20% (Eq. 6; "each rank migrates at most one local head", 五):
+    every rank above the mean load may send one of its heads to a rank below the
+    mean load, and each such rank receives at most one head; a rank does not both
+    send and receive. Returns (senders, options), where options[i] lists the
+    choices of senders[i] in enumeration order: None, then (head, receiver) with
+    heads ascending and, per head, receivers ascending.
+    """
+    W = rank_loads(work, owner, R)
+    total = int(W.sum())
+    senders = [r for r in range(R) if int(W[r]) * R > total]
+    receivers = [r for r in range(R) if int(W[r]) * R < total]
+    options = []
+    for r in senders:
+        heads = np.nonzero(owner == r)[0]
+        options.append([None] + [(int(h), int(l)) for h in heads for l in receivers])
+    return senders, options
+
+
+def rlb_plan(work: np.ndarray, owner: np.ndarray, R: int = RANKS):
+    """Eq. 5-6: the plan of least (max_r W_r^new, Var_r W_r^new), ties to the first in enumeration order.
+
+    The candidate plans are the product of the senders' options (the first sender
+    varies slowest) with distinct receivers. Var is compared through sum W^2, which
+    orders plans the same way because migration keeps the total. Returns
+    (new owner array, list of moves (head, from, to)).
+    """
+    work = np.asarray(work, dtype=np.int64).reshape(-1)
+    W = rank_loads(work, owner, R)
+    senders, options = rlb_options(work, owner, R)
+    n_plans = 1
+    for o in options:
+        n_plans *= len(o)
+    if n_plans > MAX_PLANS:
+        raise ValueError(f"migration space of {n_plans} plans is above the limit {MAX_PLANS}")
+    best_key, best = None, ()
+    for choice in itertools.product(*options):
+        moves = [(s, c) for s, c in zip(senders, choice) if c is not None]
+        dsts = [c[1] for _, c in moves]
+        if len(set(dsts)) != len(dsts):
+            continue
+        Wn = W.copy()
+        for s, (h, l) in moves:  # Eq. 5: L_r - L_{h_r} + L_{h_{sigma^-1(r)}}
+            Wn[s] -= work[h]
+            Wn[l] += work[h]
+        key = (int(Wn.max()), int((Wn * Wn).sum()))
+        if best_key is None or key < best_key:
+            best_key, best = key, tuple(moves)
+    new_owner = owner.copy()
+    for s, (h, l) in best:
+        new_owner[h] = l
+    return new_owner, [(h, s, l) for s, (h, l) in best]
+
+
+def sasa_budgets(W: np.ndarray, n1: float = SASA_N1, n2: float = SASA_N2) -> np.ndarray:
+    """Eq. 7-8 with the trigger: E_r = floor(n1 dW_r) if dW_r > n2 W_max, else 0, where dW_r = W_max - W_r.
+
+    In retained blocks (float64 arithmetic); n1 < 1 keeps E_r <= dW_r, so no rank
+    passes the current critical path (Eq. 10 with A = 0).
+    """
+    W = np.asarray(W, dtype=np.int64)
+    wmax = int(W.max())
+    E = np.zeros(W.size, dtype=np.int64)
+    for r in range(W.size):
+        dW = wmax - int(W[r])
+        if np.float64(dW) > np.float64(n2) * np.float64(wmax):
+            E[r] = int(math.floor(np.float64(n1) * np.float64(dW)))
+    return E
+
+
+def water_fill(flat: np.ndarray, nb: int, E: int) -> np.ndarray:
+    """Raise the lightest of the given counts E times by one (ties: lowest position; full ones skipped).
+
+    Closed form of that loop: the highest level lambda whose need sum max(0,
+    lambda - c) is at most E, then one more for the first E - need(lambda) counts
+    at the level, by position.
+    """
+    flat = np.asarray(flat, dtype=np.int64)
+
+    def need(lam):
+        return int(np.maximum(0, np.minimum(lam, nb) - flat).sum())
+
+    lo, hi = 0, nb
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if need(mid) <= E:
+            lo = mid
+        else:
+            hi = mid - 1
+    out = np.maximum(flat, lo)
+    rest = E - need(lo)
+    if lo < nb and rest > 0:
+        out[np.nonzero(out == lo)[0][:rest]] += 1
+    return out
+
+
+def rank_stage(counts: np.ndarray, R: int = RANKS, k1: float = RLB_K1, k2: float = RLB_K2,
+               n1: float = SASA_N1, n2: float = SASA_N2, policy: Optional[str] = None) -> dict:
+    """RLB then SASA over ranks, enabled by the piecewise policy on rho (or a forced policy).
+
+    counts: [B, H, nb] retained counts after Top-p and the floor. Returns the
+    initial and final head owners, the moves, the budgets E_r, the new counts
+    (each tile extended along its own importance order: SASA step 2b), rho before
+    migration, after migration and after augmentation, the policy taken, and the
+    head order of the per-rank queue segments (ranks ascending, heads ascending
+    within a rank) with the number of heads per rank.
+    """
+    B, H, nb = counts.shape
+    BH = B * H
+    flat = counts.reshape(BH, nb).astype(np.int64)
+    work = flat.sum(axis=1)
+    owner0 = rank_of_heads(BH, R)
+    W0 = rank_loads(work, owner0, R)
+    rho0 = imbalance(W0)
+    mode = rank_policy(rho0, k1, k2) if policy is None else policy
+    owner, moves = owner0.copy(), []
+    if mode == "rlb+sasa":
+        owner, moves = rlb_plan(work, owner0, R)
+    W1 = rank_loads(work, owner, R)
+    E = sasa_budgets(W1, n1, n2) if mode != "none" else np.zeros(R, dtype=np.int64)
+    new = flat.copy()
+    for r in range(R):
+        heads = np.nonzero(owner == r)[0]
+        if E[r] > 0 and heads.size:
+            new[heads] = water_fill(flat[heads].reshape(-1), nb, int(E[r])).reshape(heads.size, nb)
+    W2 = rank_loads(new.sum(axis=1), owner, R)
+    order = np.concatenate([np.nonzero(owner == r)[0] for r in range(R)]).astype(np.int64)
+    return dict(owner0=owner0, owner=owner, moves=moves, policy=mode, E=E, counts=new.reshape(B, H, nb),
+                W0=W0, W1=W1, W2=W2, rho0=rho0, rho_rlb=imbalance(W1), rho_final=imbalance(W2),
+                head_order=order, heads_per_rank=np.bincount(owner, minlength=R).astype(np.int64))
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,174 @@
+"""Pins of the oracle's rank-level stages: RLB head migration and SASA budgets over the eight XCDs.
+
+Fixed independently of the oracle's code by:
+  * placement: the contiguous head ranges of the Ulysses split cover every head
+    once, in order, with sizes that differ by at most one;
+  * Eq. 2: rho = max / mean of the rank loads, on worked cases;
+  * the piecewise policy at and around its thresholds k1 = 1.05, k2 = 1.10;
+  * RLB (Eq. 5-6): on small instances the plan's (max, variance) equals the
+    optimum found by enumerating every head-to-rank assignment, with loads
+    recomputed from scratch, that satisfies the restriction (each rank above the
+    mean gives at most one head to a distinct rank below the mean); the empty
+    plan is a candidate, so the maximum never rises; worked two-rank cases;
+  * SASA (Eq. 7-10): E_r <= n1 dW_r < dW_r, zero on the critical rank and at or
+    below the trigger n2 W_max; the fill equals an independent heap loop; after
+    the fill no rank exceeds the post-migration maximum (A = 0 in Eq. 10); counts
+    never drop, never pass nb, and policy 'none' changes nothing.
+The pages' reported imbalance (1.34 to 1.08 on Wan2.2 with 8 GPUs) needs their
+model and data: parity unpinned for those figures.
+"""
+import heapq
+import itertools
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from oracle import absh_oracle as O
+
+
+@pytest.mark.parametrize("BH,R", [(1, 8), (5, 8), (8, 8), (40, 8), (41, 8), (7, 3)])
+def test_contiguous_placement(BH, R):
+    owner = O.rank_of_heads(BH, R)
+    assert owner.shape == (BH,)
+    assert (np.diff(owner) >= 0).all()
+    sizes = np.bincount(owner, minlength=R)
+    assert sizes.sum() == BH and sizes.max() - sizes.min() <= 1
+
+
+def test_rho_worked_cases():
+    assert O.imbalance([1, 1, 1, 1]) == 1.0
+    assert O.imbalance([4, 2, 2, 0]) == 2.0            # max 4, mean 2
+    assert O.imbalance([3, 1]) == pytest.approx(1.5)  # max 3, mean 2
+    W = O.rank_loads(np.array([5, 1, 2, 2]), np.array([0, 0, 1, 1]), R=2)
+    assert list(W) == [6, 4]
+
+
+def test_policy_thresholds():
+    assert O.rank_policy(1.0) == "none"
+    assert O.rank_policy(1.0499) == "none"
+    assert O.rank_policy(1.05) == "sasa"
+    assert O.rank_policy(1.0999) == "sasa"
+    assert O.rank_policy(1.10) == "rlb+sasa"
+    assert O.rank_policy(1.34) == "rlb+sasa"
+
+
+def brute_force_best(work, owner, R):
+    """(max, var) of the best assignment in the restricted space, enumerating every owner vector."""
+    work = np.asarray(work, dtype=np.int64)
+    W0 = np.bincount(owner, weights=work, minlength=R)
+    mean = W0.sum() / R
+    best = None
+    for new in itertools.product(range(R), repeat=len(work)):
+        new = np.array(new)
+        moved = np.nonzero(new != owner)[0]
+        src, dst = owner[moved], new[moved]
+        if len(set(src.tolist())) != len(src) or len(set(dst.tolist())) != len(dst):
+            continue  # one head out and one head in per rank at most
+        if any(W0[s] <= mean for s in src) or any(W0[d] >= mean for d in dst):
+            continue  # senders above the mean, receivers below it
+        W = np.bincount(new, weights=work, minlength=R)
+        key = (W.max(), float(np.var(W)))
+        if best is None or key < best:
+            best = key
+    return best
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(2, 4), st.integers(2, 6), st.integers(0, 2 ** 31 - 1))
+def test_rlb_matches_brute_force(R, BH, seed):
+    rng = np.random.default_rng(seed)
+    work = rng.integers(1, 40, size=BH)
+    owner = O.rank_of_heads(BH, R)
+    new_owner, moves = O.rlb_plan(work, owner, R)
+    W0 = O.rank_loads(work, owner, R)
+    W = O.rank_loads(work, new_owner, R)
+    assert W.sum() == W0.sum() and W.max() <= W0.max()
+    for h, s, d in moves:
+        assert owner[h] == s and new_owner[h] == d and s != d
+    assert len({s for _, s, _ in moves}) == len(moves) == len({d for _, _, d in moves})
+    best = brute_force_best(work, owner, R)
+    assert W.max() == best[0]
+    assert float(np.var(W)) == pytest.approx(best[1], rel=0, abs=1e-9)
+
+
+def test_rlb_worked_two_ranks():
+    # rank 0 holds heads of work 6 and 4, rank 1 one head of work 2: moving the
+    # head of work 4 gives loads (6, 6); moving the head of work 6 gives (4, 8)
+    owner = np.array([0, 0, 1])
+    new_owner, moves = O.rlb_plan(np.array([6, 4, 2]), owner, R=2)
+    assert moves == [(1, 0, 1)] and list(O.rank_loads(np.array([6, 4, 2]), new_owner, 2)) == [6, 6]
+    # a single heavy head cannot help: moving it only moves the straggler
+    new_owner, moves = O.rlb_plan(np.array([10, 1]), np.array([0, 1]), R=2)
+    assert moves == [] and (new_owner == np.array([0, 1])).all()
+
+
+@settings(max_examples=100, deadline=None)
+@given(st.lists(st.integers(0, 5000), min_size=2, max_size=8))
+def test_sasa_budgets(W):
+    W = np.array(W, dtype=np.int64)
+    E = O.sasa_budgets(W)
+    wmax = W.max()
+    for r in range(W.size):
+        dW = wmax - W[r]
+        if dW > O.SASA_N2 * wmax:
+            assert E[r] == int(np.floor(O.SASA_N1 * dW)) and E[r] < dW
+        else:
+            assert E[r] == 0
+    assert (W + E <= wmax).all()
+
+
+def heap_fill(flat, nb, E):
+    heap = [(int(c), i) for i, c in enumerate(flat) if c < nb]
+    heapq.heapify(heap)
+    out = np.array(flat, dtype=np.int64)
+    for _ in range(E):
+        if not heap:
+            break
+        c, i = heapq.heappop(heap)
+        out[i] = c + 1
+        if c + 1 < nb:
+            heapq.heappush(heap, (c + 1, i))
+    return out
+
+
+@settings(max_examples=100, deadline=None)
+@given(st.integers(1, 40), st.integers(1, 60), st.integers(0, 400), st.integers(0, 2 ** 31 - 1))
+def test_water_fill_equals_heap(n, nb, E, seed):
+    flat = np.random.default_rng(seed).integers(1, nb + 1, size=n)
+    assert (O.water_fill(flat, nb, E) == heap_fill(flat, nb, E)).all()
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(8, 24), st.integers(4, 40), st.integers(0, 2 ** 31 - 1))
+def test_rank_stage_invariants(BH, nb, seed):
+    rng = np.random.default_rng(seed)
+    counts = rng.integers(1, nb + 1, size=(1, BH, nb))
+    heavy = rng.integers(0, BH, size=3)
+    counts[0, heavy] = nb  # a few dense heads make stragglers
+    st_ = O.rank_stage(counts)
+    new = st_["counts"]
+    assert (new >= counts).all() and (new <= nb).all()
+    assert st_["W2"].max() <= st_["W1"].max() <= st_["W0"].max()
+    added = O.rank_loads((new - counts).reshape(BH, nb).sum(axis=1), st_["owner"])
+    assert (added <= st_["E"]).all()
+    order = st_["head_order"]
+    assert sorted(order.tolist()) == list(range(BH))
+    assert (np.diff(st_["owner"][order]) >= 0).all()
+    assert list(st_["heads_per_rank"]) == list(np.bincount(st_["owner"], minlength=O.RANKS))
+    if st_["policy"] == "none":
+        assert (new == counts).all() and st_["moves"] == []
+    if st_["policy"] != "rlb+sasa":
+        assert st_["moves"] == []
+
+
+def test_forced_policies():
+    rng = np.random.default_rng(7)
+    counts = rng.integers(1, 20, size=(1, 16, 20))
+    counts[0, 14:] = 20
+    none = O.rank_stage(counts, policy="none")
+    sasa = O.rank_stage(counts, policy="sasa")
+    both = O.rank_stage(counts, policy="rlb+sasa")
+    assert (none["counts"] == counts).all() and none["rho_final"] == none["rho0"]
+    assert sasa["moves"] == [] and sasa["rho_final"] <= sasa["rho0"]
+    assert both["rho_rlb"] <= both["rho0"] and both["rho_final"] <= both["rho_rlb"]
