@@ -18,8 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libabsh.so")
 
 ABSH_BF16, ABSH_F32 = 0, 1
 ABSH_ROWS, ABSH_VT = 0, 1
-SCHED_ORDER, SCHED_LPT, SCHED_XCD = 0, 1, 2
-SCHEDULES = {"order": SCHED_ORDER, "lpt": SCHED_LPT, "xcd": SCHED_XCD}
+SCHED_ORDER, SCHED_LPT, SCHED_XCD, SCHED_RANKS = 0, 1, 2, 3
+SCHEDULES = {"order": SCHED_ORDER, "lpt": SCHED_LPT, "xcd": SCHED_XCD, "ranks": SCHED_RANKS}
+RANK_POLICIES = {"auto": -1, "none": 0, "sasa": 1, "rlb+sasa": 2}
+RANK_INFO = 64  # doubles in Routing.rank_info (layout in include/absh.h)
+# the review's parameters of the rank-level stages (section 五)
+RLB_K1, RLB_K2, SASA_N1, SASA_N2 = 1.05, 1.10, 0.8, 0.07
 
 EXPORTED = (
     "absh_version", "absh_status_string", "absh_last_error", "absh_create", "absh_destroy", "absh_dims",
@@ -38,14 +42,17 @@ class AbshError(RuntimeError):
 
 class RouteOpts(ctypes.Structure):
     _fields_ = [("p", ctypes.c_double), ("k_floor", ctypes.c_int32), ("slack_frac", ctypes.c_double),
-                ("schedule", ctypes.c_int32), ("order_depth", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("order_depth", ctypes.c_int32),
+                ("rank_policy", ctypes.c_int32), ("strict_ranks", ctypes.c_int32),
+                ("k1", ctypes.c_double), ("k2", ctypes.c_double), ("n1", ctypes.c_double), ("n2", ctypes.c_double)]
 
 
 class Lists(ctypes.Structure):
     _fields_ = [("counts", ctypes.c_void_p), ("kv_idx", ctypes.c_void_p), ("order", ctypes.c_void_p),
                 ("work", ctypes.c_void_p), ("L", ctypes.c_void_p), ("queue", ctypes.c_void_p),
                 ("sched", ctypes.c_void_p), ("unit_list", ctypes.c_void_p), ("unit_cnt", ctypes.c_void_p),
-                ("schedule", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("head_order", ctypes.c_void_p), ("rank_info", ctypes.c_void_p),
+                ("strict_ranks", ctypes.c_int32)]
 
 
 _lib = None
@@ -209,13 +216,17 @@ class Routing:
     sched: object    # int32 [10] bounds of the per-XCD runs of the work queue + query blocks per unit
     unit_list: object  # int32 [units, nb] flagged union lists of query-block groups
     unit_cnt: object   # int32 [units]
+    head_order: object  # int32 [B*H] heads by rank (schedule "ranks")
+    rank_info: object   # float64 [RANK_INFO] rank-stage report (schedule "ranks")
     schedule: int = -1  # the schedule absh_route made these lists for
+    strict_ranks: int = 0
 
     def lists(self) -> Lists:
         return Lists(self.counts.data_ptr(), self.kv_idx.data_ptr(),
                      self.order.data_ptr() if self.order is not None else 0,
                      self.work.data_ptr(), self.L.data_ptr(), self.queue.data_ptr(), self.sched.data_ptr(),
-                     self.unit_list.data_ptr(), self.unit_cnt.data_ptr(), self.schedule)
+                     self.unit_list.data_ptr(), self.unit_cnt.data_ptr(), self.schedule,
+                     self.head_order.data_ptr(), self.rank_info.data_ptr(), self.strict_ranks)
 
 
 def route_workspace_bytes(ctx: Context, B: int, H: int, d: int) -> int:
@@ -244,14 +255,20 @@ def alloc_routing(ctx: Context, B: int, H: int, order_depth: int = 0) -> Routing
         sched=torch.empty((10,), dtype=torch.int32, device=dev),
         unit_list=torch.empty((units, nb), dtype=torch.int32, device=dev),
         unit_cnt=torch.empty((units,), dtype=torch.int32, device=dev),
+        head_order=torch.empty((B * H,), dtype=torch.int32, device=dev),
+        rank_info=torch.zeros((RANK_INFO,), dtype=torch.float64, device=dev),
     )
 
 
 def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0, schedule="lpt",
-          order_depth: int = 0, out: Optional[Routing] = None, workspace=None, stream=None) -> Routing:
+          order_depth: int = 0, out: Optional[Routing] = None, workspace=None, stream=None,
+          rank_policy="auto", strict_ranks: bool = False, k1: float = RLB_K1, k2: float = RLB_K2,
+          n1: float = SASA_N1, n2: float = SASA_N2) -> Routing:
     """Stage-1 routing of Hilbert-order qh, kh [B, H, n_pad, d] bf16 -> Routing (device tensors).
 
-    schedule: "order", "lpt" or "xcd" (or the SCHED_* integer).
+    schedule: "order", "lpt", "xcd" or "ranks" (or the SCHED_* integer). The
+    rank_* and k/n arguments apply to "ranks" only: rank_policy "auto" (by rho),
+    "none", "sasa" or "rlb+sasa"; strict_ranks keeps each XCD on its own rank.
     """
     import torch
     B, H, n_pad, d = qh.shape
@@ -261,11 +278,14 @@ def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0,
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=qh.device)
     sched = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
-    opts = RouteOpts(float(p), int(k_floor), float(slack_frac), sched, int(order_depth))
+    policy = RANK_POLICIES[rank_policy] if isinstance(rank_policy, str) else int(rank_policy)
+    opts = RouteOpts(float(p), int(k_floor), float(slack_frac), sched, int(order_depth), policy,
+                     int(bool(strict_ranks)), float(k1), float(k2), float(n1), float(n2))
     lists = out.lists()
     _check(lib().absh_route(ctx.handle, _ptr(qh), _ptr(kh), B, H, d, ctypes.byref(opts), ctypes.byref(lists),
                             _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream)))
     out.schedule = lists.schedule
+    out.strict_ranks = lists.strict_ranks
     return out
 
 

@@ -59,6 +59,16 @@ struct RouteBuffers {
   int32_t* sched;        // [10] queue segment bounds (one segment per XCD) and query blocks per unit
   uint32_t* unit_list;   // [units][nb] union lists of query-block groups
   int32_t* unit_cnt;     // [units]
+  int32_t* owner;        // [B*H] rank of each head after migration (ABSH_SCHED_RANKS)
+  int32_t* head_order;   // [B*H] heads by rank, ascending within a rank (ABSH_SCHED_RANKS)
+  int64_t* budget;       // [8] SASA budgets E_r in retained blocks (ABSH_SCHED_RANKS)
+  double* rank_info;     // [kRankInfo] rank-stage report (ABSH_SCHED_RANKS)
+};
+// Rank-stage parameters (ABSH_SCHED_RANKS): policy -1 = piecewise on rho with
+// thresholds k1, k2; 0 = none; 1 = SASA only; 2 = RLB, then SASA.
+struct RankOpts {
+  int policy;
+  double k1, k2, n1, n2;
 };
 hipError_t launch_select(const absh_ctx* c, const RouteBuffers& rb, int tiles, double p, int k_floor,
                          int order_depth, int reselect, hipStream_t s);
@@ -70,6 +80,9 @@ int unit_count(const absh_ctx* c, int BH, int members);
 hipError_t launch_groups(const absh_ctx* c, const RouteBuffers& rb, int BH, int members, hipStream_t s);
 hipError_t launch_segments(const absh_ctx* c, const RouteBuffers& rb, int BH, int schedule, hipStream_t s);
 int queue_chunks(int tiles);
+hipError_t launch_rank_stage(const absh_ctx* c, const RouteBuffers& rb, int BH, const RankOpts& o, hipStream_t s);
+hipError_t launch_rank_fill(const absh_ctx* c, const RouteBuffers& rb, hipStream_t s);
+hipError_t launch_rank_final(const RouteBuffers& rb, int BH, hipStream_t s);
 
 // Work lists of the attention kernel. A unit is `members` neighbouring query
 // blocks of one head (1: a single tile taken from the queue; 2 or 4: a group
@@ -82,6 +95,8 @@ struct AttnLists {
   const int32_t* unit_cnt;    // [units]
   const int32_t* sched;       // [10] segment bounds + members (read by the kernel)
   int members;                // host copy of sched[9]
+  const int32_t* head_order;  // group units: segment position p / per_head -> head (NULL: identity)
+  int strict;                 // 1: a workgroup takes units from its own XCD's segment only
 };
 hipError_t launch_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B,
                             int H, int d, const AttnLists* lists, hipStream_t s);

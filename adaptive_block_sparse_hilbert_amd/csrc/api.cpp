@@ -65,7 +65,7 @@ absh_status check_shape(const absh_ctx* c, int B, int H, int d) {
 
 // Byte offsets of the route workspace regions.
 struct WsLayout {
-  size_t qbar, kbar, S, target, info, chunk_hist, rank, total;
+  size_t qbar, kbar, S, target, info, chunk_hist, rank, owner, budget, total;
 };
 
 WsLayout ws_layout(const absh_ctx* c, int B, int H, int d) {
@@ -79,6 +79,8 @@ WsLayout ws_layout(const absh_ctx* c, int B, int H, int d) {
   w.info = off; off = align_up(off + 4 * sizeof(int64_t));
   w.chunk_hist = off; off = align_up(off + (size_t)absh::queue_chunks((int)tiles) * (c->nb + 1) * sizeof(int32_t));
   w.rank = off; off = align_up(off + tiles * sizeof(int32_t));
+  w.owner = off; off = align_up(off + (size_t)B * H * sizeof(int32_t));
+  w.budget = off; off = align_up(off + 8 * sizeof(int64_t));
   w.total = off;
   return w;
 }
@@ -87,7 +89,7 @@ WsLayout ws_layout(const absh_ctx* c, int B, int H, int d) {
 
 extern "C" {
 
-int absh_version(void) { return 100; }
+int absh_version(void) { return 200; }
 
 const char* absh_status_string(int status) {
   switch (status) {
@@ -272,8 +274,21 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
     return fail(ABSH_EINVAL, "slack_frac must lie in [0, 1) (got %g)", opts->slack_frac);
   if (opts->order_depth < 0 || opts->order_depth > 64)
     return fail(ABSH_EINVAL, "order_depth must lie in [0, 64] (got %d)", opts->order_depth);
-  if (opts->schedule < ABSH_SCHED_ORDER || opts->schedule > ABSH_SCHED_XCD)
+  if (opts->schedule < ABSH_SCHED_ORDER || opts->schedule > ABSH_SCHED_RANKS)
     return fail(ABSH_EINVAL, "unknown schedule %d", opts->schedule);
+  const bool ranks = opts->schedule == ABSH_SCHED_RANKS;
+  if (ranks) {
+    if (opts->rank_policy < -1 || opts->rank_policy > 2)
+      return fail(ABSH_EINVAL, "rank_policy must be -1, 0, 1 or 2 (got %d)", opts->rank_policy);
+    if (opts->strict_ranks != 0 && opts->strict_ranks != 1)
+      return fail(ABSH_EINVAL, "strict_ranks must be 0 or 1 (got %d)", opts->strict_ranks);
+    if (!(opts->k1 > 0.0 && opts->k1 <= opts->k2))
+      return fail(ABSH_EINVAL, "need 0 < k1 <= k2 (got %g, %g)", opts->k1, opts->k2);
+    if (!(opts->n1 >= 0.0 && opts->n1 < 1.0) || !(opts->n2 >= 0.0))
+      return fail(ABSH_EINVAL, "need 0 <= n1 < 1 and n2 >= 0 (got %g, %g)", opts->n1, opts->n2);
+    if (!out->head_order || !out->rank_info)
+      return fail(ABSH_EINVAL, "head_order and rank_info must be non-NULL for ABSH_SCHED_RANKS");
+  }
   if (!out->counts || !out->kv_idx || !out->work || !out->L || !out->queue || !out->sched)
     return fail(ABSH_EINVAL, "counts, kv_idx, work, L, queue and sched must be non-NULL");
   if (opts->order_depth > 0 && !out->order) return fail(ABSH_EINVAL, "order is NULL but order_depth > 0");
@@ -306,6 +321,10 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
   rb.sched = out->sched;
   rb.unit_list = out->unit_list;
   rb.unit_cnt = out->unit_cnt;
+  rb.owner = reinterpret_cast<int32_t*>(base + w.owner);
+  rb.budget = reinterpret_cast<int64_t*>(base + w.budget);
+  rb.head_order = ranks ? out->head_order : nullptr;
+  rb.rank_info = ranks ? out->rank_info : nullptr;
   const int tiles = B * H * c->nb;
 
   ABSH_HIP(absh::launch_pool(c, qh, qbar, B, H, d, s), "absh_route: pool q");
@@ -318,11 +337,22 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
     ABSH_HIP(absh::launch_select(c, rb, tiles, opts->p, opts->k_floor, 0, 1, s), "absh_route: slack fill");
   }
   ABSH_HIP(absh::launch_workload(c, rb, B * H, s), "absh_route: workload");
+  if (ranks) {
+    // rank loads, policy, RLB plan, SASA budgets and the rank segments; then each
+    // rank's tiles are extended along their importance order, and loads redone
+    const absh::RankOpts ro{opts->rank_policy, opts->k1, opts->k2, opts->n1, opts->n2};
+    ABSH_HIP(absh::launch_rank_stage(c, rb, B * H, ro, s), "absh_route: rank plan");
+    ABSH_HIP(absh::launch_rank_fill(c, rb, s), "absh_route: rank fill");
+    ABSH_HIP(absh::launch_select(c, rb, tiles, opts->p, opts->k_floor, 0, 1, s), "absh_route: rank fill select");
+    ABSH_HIP(absh::launch_workload(c, rb, B * H, s), "absh_route: workload after fill");
+    ABSH_HIP(absh::launch_rank_final(rb, B * H, s), "absh_route: rank report");
+  }
   ABSH_HIP(absh::launch_queue(c, rb, tiles, opts->schedule == ABSH_SCHED_LPT, s), "absh_route: queue");
   if (opts->schedule != ABSH_SCHED_LPT)
     ABSH_HIP(absh::launch_groups(c, rb, B * H, absh::unit_members(c, opts->schedule), s), "absh_route: groups");
-  ABSH_HIP(absh::launch_segments(c, rb, B * H, opts->schedule, s), "absh_route: segments");
+  if (!ranks) ABSH_HIP(absh::launch_segments(c, rb, B * H, opts->schedule, s), "absh_route: segments");
   out->schedule = opts->schedule;
+  out->strict_ranks = ranks ? opts->strict_ranks : 0;
   return ABSH_OK;
 }
 
@@ -336,8 +366,10 @@ absh_status absh_sparse_attn(absh_ctx* c, const void* qh, const void* kh, const 
     return fail(ABSH_EINVAL, "qh, kh, vt and oh must be 16-byte aligned");
   if (lists && (!lists->counts || !lists->kv_idx || !lists->queue || !lists->sched))
     return fail(ABSH_EINVAL, "lists needs counts, kv_idx, queue and sched");
-  if (lists && (lists->schedule < ABSH_SCHED_ORDER || lists->schedule > ABSH_SCHED_XCD))
+  if (lists && (lists->schedule < ABSH_SCHED_ORDER || lists->schedule > ABSH_SCHED_RANKS))
     return fail(ABSH_EINVAL, "lists->schedule %d is not a schedule (was absh_route run?)", lists->schedule);
+  if (lists && lists->schedule == ABSH_SCHED_RANKS && !lists->head_order)
+    return fail(ABSH_EINVAL, "lists needs head_order for ABSH_SCHED_RANKS");
   if (lists && lists->schedule != ABSH_SCHED_LPT && (!lists->unit_list || !lists->unit_cnt))
     return fail(ABSH_EINVAL, "lists needs unit_list and unit_cnt for this schedule");
   if (absh_status st = use_device(c)) return st;
@@ -350,6 +382,10 @@ absh_status absh_sparse_attn(absh_ctx* c, const void* qh, const void* kh, const 
     L.unit_cnt = lists->unit_cnt;
     L.sched = lists->sched;
     L.members = absh::unit_members(c, lists->schedule);
+    if (lists->schedule == ABSH_SCHED_RANKS) {
+      L.head_order = lists->head_order;
+      L.strict = lists->strict_ranks ? 1 : 0;
+    }
   }
   ABSH_HIP(absh::launch_attention(c, qh, kh, vt, oh, B, H, d, lists ? &L : nullptr,
                                   reinterpret_cast<hipStream_t>(stream)),

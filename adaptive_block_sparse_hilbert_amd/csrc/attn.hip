@@ -144,8 +144,9 @@ __device__ __forceinline__ const_i32 as_const(const int32_t* p) { return (const_
 
 // Pull the next queue position for this workgroup (thread 0 only); -1 when
 // every segment is exhausted. `dead` remembers exhausted segments.
-__device__ __forceinline__ int pull(int32_t* counters, const int32_t* bounds, int units, int xcd, unsigned& dead) {
-  for (int k = 0; k < kSegments; ++k) {
+__device__ __forceinline__ int pull(int32_t* counters, const int32_t* bounds, int units, int xcd, unsigned& dead,
+                                    int strict) {
+  for (int k = 0; k < (strict ? 1 : kSegments); ++k) {
     const int seg = (xcd + k) & (kSegments - 1);
     if (dead & (1u << seg)) continue;
     const int lo = bounds ? bounds[seg] : (int)((int64_t)units * seg / kSegments);
@@ -215,7 +216,7 @@ void attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, c
 
   const int32_t* bounds = dense ? nullptr : L.sched;
   unsigned dead = 0;
-  if (tid == 0) s_next[0] = pull(counters, bounds, units, xcd, dead);
+  if (tid == 0) s_next[0] = pull(counters, bounds, units, xcd, dead, L.strict);
 
   for (int parity = 0;; parity ^= 1) {
     __syncthreads();  // s_next[parity] is published; every wave is done with the previous unit
@@ -232,10 +233,13 @@ void attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, c
       cnt = as_const(L.counts)[tile];
       plain = as_const(L.kv_idx + (size_t)tile * nb);
     } else {
-      bh = pos / per_head;
-      qb0 = (pos - bh * per_head) * members;
-      cnt = dense ? nb : as_const(L.unit_cnt)[pos];
-      if (!dense) flagged = as_const(reinterpret_cast<const int32_t*>(L.unit_list) + (size_t)pos * nb);
+      // segment position -> head (through head_order when the segments follow ranks) and unit
+      const int slot = pos / per_head;
+      bh = L.head_order ? __builtin_amdgcn_readfirstlane(as_const(L.head_order)[slot]) : slot;
+      const int unit = bh * per_head + (pos - slot * per_head);
+      qb0 = (pos - slot * per_head) * members;
+      cnt = dense ? nb : as_const(L.unit_cnt)[unit];
+      if (!dense) flagged = as_const(reinterpret_cast<const int32_t*>(L.unit_list) + (size_t)unit * nb);
     }
     // member m of the unit exists when it is below `members` and below nb
     uint32_t present = 0;
@@ -291,7 +295,7 @@ void attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, c
       if (k < cnt) issue(k, ent[k]);
     }
     uint32_t e_ahead = NS - 1 < cnt ? entry(NS - 1) : 0u;
-    if (tid == 0) s_next[parity ^ 1] = pull(counters, bounds, units, xcd, dead);  // the next unit
+    if (tid == 0) s_next[parity ^ 1] = pull(counters, bounds, units, xcd, dead, L.strict);  // the next unit
 
     f32x4 o[2][C::DT];
     float l_run[2];  // this lane's share of the row's running sum of (bf16) probabilities

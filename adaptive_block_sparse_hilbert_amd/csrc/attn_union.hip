@@ -96,8 +96,9 @@ __device__ __forceinline__ void wait_vm() {
 typedef const int32_t __attribute__((address_space(4)))* const_i32;
 __device__ __forceinline__ const_i32 as_const(const int32_t* p) { return (const_i32)p; }
 
-__device__ __forceinline__ int pull(int32_t* counters, const int32_t* bounds, int units, int xcd, unsigned& dead) {
-  for (int k = 0; k < kSegments; ++k) {
+__device__ __forceinline__ int pull(int32_t* counters, const int32_t* bounds, int units, int xcd, unsigned& dead,
+                                    int strict) {
+  for (int k = 0; k < (strict ? 1 : kSegments); ++k) {
     const int seg = (xcd + k) & (kSegments - 1);
     if (dead & (1u << seg)) continue;
     const int lo = bounds ? bounds[seg] : (int)((int64_t)units * seg / kSegments);
@@ -177,16 +178,19 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
 
   const int32_t* bounds = dense ? nullptr : L.sched;
   unsigned dead = 0;
-  if (tid == 0) s_next[0] = pull(counters, bounds, units, xcd, dead);
+  if (tid == 0) s_next[0] = pull(counters, bounds, units, xcd, dead, L.strict);
 
   for (int parity = 0;; parity ^= 1) {
     __syncthreads();  // s_next[parity] is published; every wave is done with the previous unit
     const int pos = __builtin_amdgcn_readfirstlane(s_next[parity]);
     if (pos < 0) break;
-    const int bh = pos / per_head;
-    const int qb0 = (pos - bh * per_head) * C::MEMBERS;
-    const int cnt = dense ? nb : as_const(L.unit_cnt)[pos];
-    const_i32 list = dense ? nullptr : as_const(reinterpret_cast<const int32_t*>(L.unit_list) + (size_t)pos * nb);
+    // segment position -> head (through head_order when the segments follow ranks) and unit
+    const int slot = pos / per_head;
+    const int bh = L.head_order ? __builtin_amdgcn_readfirstlane(as_const(L.head_order)[slot]) : slot;
+    const int unit = bh * per_head + (pos - slot * per_head);
+    const int qb0 = (pos - slot * per_head) * C::MEMBERS;
+    const int cnt = dense ? nb : as_const(L.unit_cnt)[unit];
+    const_i32 list = dense ? nullptr : as_const(reinterpret_cast<const int32_t*>(L.unit_list) + (size_t)unit * nb);
     uint32_t present = 0;
 #pragma unroll
     for (int m = 0; m < C::MEMBERS; ++m)
@@ -254,7 +258,7 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
       issue_v(1, 1, e1);
     }
     if (2 < nsteps) issue_k(2, 2, e2);
-    if (tid == 0) s_next[parity ^ 1] = pull(counters, bounds, units, xcd, dead);
+    if (tid == 0) s_next[parity ^ 1] = pull(counters, bounds, units, xcd, dead, L.strict);
 
     f32x16 o[C::DT];
 #pragma unroll

@@ -547,6 +547,261 @@ __global__ __launch_bounds__(1024) void segments_kernel(const int32_t* __restric
   if (threadIdx.x <= kSegments) sched[threadIdx.x] = threadIdx.x == 0 ? 0 : bound[threadIdx.x];
 }
 
+// ------------------------------------------------------------------ rank-level RLB and SASA
+
+// The eight XCDs as the ranks of the xllm-io review's runtime stages (核心公式
+// Eq. 1-2 and 5-10, 3.2 RLB, 3.3 SASA and its piecewise policy, parameters of
+// 五). Rank r first holds the contiguous heads floor(r BH / 8) ..
+// floor((r + 1) BH / 8) - 1 (the Ulysses head split). Loads are in retained
+// blocks, W_r = sum of work_h over the rank's heads; L_r of Eq. 1 is W_r / nb,
+// and every ratio below is the same in either unit.
+//
+// RLB searches, exhaustively, the plans in which every rank above the mean load
+// gives at most one of its heads to a distinct rank below the mean load (the
+// one-send-one-receive space with at most one head per rank); the plan of least
+// (max W^new, sum (W^new)^2) wins, ties to the first in enumeration order (the
+// first sender's option varies slowest; a sender's options are: none, then
+// (head, receiver) with heads ascending and receivers ascending per head). A
+// space above kMaxPlans combinations is not searched. SASA gives rank r the
+// budget E_r = floor(n1 dW_r) when dW_r = W_max - W_r exceeds n2 W_max (float64),
+// spent by water-filling the rank's tiles along their importance order.
+//
+// info (float64, kRankInfo entries): [0] rho before, [1] after migration, [2]
+// after augmentation; [3] policy taken (0 none, 1 SASA, 2 RLB + SASA); [4]
+// moves; [5..12] W before, [13..20] after migration, [21..28] after
+// augmentation; [29..36] E_r; [37..60] the moves as (head, from, to); [61]
+// combinations searched; [62] 1 if the space was too large to search.
+constexpr int kRanks = kSegments;
+constexpr int kMaxPlans = 1 << 26;
+
+__device__ double rank_rho(const int64_t* W) {
+  int64_t mx = W[0], sum = 0;
+  for (int r = 0; r < kRanks; ++r) {
+    mx = W[r] > mx ? W[r] : mx;
+    sum += W[r];
+  }
+  return (double)mx / ((double)sum / kRanks);
+}
+
+__global__ __launch_bounds__(1024) void rank_plan_kernel(const int32_t* __restrict__ work, int BH, int per_head,
+                                                         int members, int policy, double k1, double k2, double n1,
+                                                         double n2, int32_t* __restrict__ owner,
+                                                         int32_t* __restrict__ head_order,
+                                                         int64_t* __restrict__ budget, int32_t* __restrict__ sched,
+                                                         double* __restrict__ info) {
+  __shared__ int64_t W0[kRanks];
+  __shared__ int hlo[kRanks + 1];
+  __shared__ int snd[kRanks], rcv[kRanks], opt[kRanks];
+  __shared__ int n_snd, n_rcv, mode;
+  __shared__ int n_plans;
+  __shared__ int64_t red_max[1024], red_sq[1024];
+  __shared__ int red_idx[1024];
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    int64_t total = 0;
+    for (int r = 0; r <= kRanks; ++r) hlo[r] = (int)((int64_t)r * BH / kRanks);
+    for (int r = 0; r < kRanks; ++r) {
+      int64_t w = 0;
+      for (int h = hlo[r]; h < hlo[r + 1]; ++h) w += work[h];
+      W0[r] = w;
+      total += w;
+    }
+    const double rho = rank_rho(W0);
+    mode = policy >= 0 ? policy : (rho < k1 ? 0 : rho < k2 ? 1 : 2);
+    n_snd = n_rcv = 0;
+    int64_t space = 1;
+    if (mode == 2) {
+      for (int r = 0; r < kRanks; ++r) {
+        if (W0[r] * kRanks > total) snd[n_snd++] = r;
+        if (W0[r] * kRanks < total) rcv[n_rcv++] = r;
+      }
+      for (int i = 0; i < n_snd; ++i) {
+        opt[i] = 1 + (hlo[snd[i] + 1] - hlo[snd[i]]) * n_rcv;
+        space = space * opt[i] > (int64_t)kMaxPlans ? (int64_t)kMaxPlans + 1 : space * opt[i];
+      }
+    }
+    info[61] = (double)space;
+    info[62] = space > kMaxPlans ? 1.0 : 0.0;
+    if (space > kMaxPlans) n_snd = 0;  // not searched: no migration
+    int64_t np = 1;
+    for (int i = 0; i < n_snd; ++i) np *= opt[i];
+    n_plans = (int)np;
+    info[0] = rho;
+    info[3] = (double)mode;
+  }
+  __syncthreads();
+  // every plan p: decode the senders' choices, keep the least (max, sum of squares, p)
+  int64_t best_max = INT64_MAX, best_sq = INT64_MAX;
+  int best_p = INT32_MAX;
+  for (int p = tid; p < n_plans; p += 1024) {
+    int64_t w[kRanks];
+    for (int r = 0; r < kRanks; ++r) w[r] = W0[r];
+    unsigned used = 0;
+    bool ok = true;
+    int q = p;
+    for (int i = n_snd - 1; i >= 0; --i) {
+      const int c = q % opt[i];
+      q /= opt[i];
+      if (c == 0) continue;
+      const int h = hlo[snd[i]] + (c - 1) / n_rcv, dst = rcv[(c - 1) % n_rcv];
+      if (used & (1u << dst)) ok = false;
+      used |= 1u << dst;
+      w[snd[i]] -= work[h];
+      w[dst] += work[h];
+    }
+    if (!ok) continue;
+    int64_t mx = w[0], sq = 0;
+    for (int r = 0; r < kRanks; ++r) {
+      mx = w[r] > mx ? w[r] : mx;
+      sq += w[r] * w[r];
+    }
+    if (mx < best_max || (mx == best_max && (sq < best_sq || (sq == best_sq && p < best_p)))) {
+      best_max = mx;
+      best_sq = sq;
+      best_p = p;
+    }
+  }
+  red_max[tid] = best_max;
+  red_sq[tid] = best_sq;
+  red_idx[tid] = best_p;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (tid < off) {
+      const int o = tid + off;
+      if (red_max[o] < red_max[tid] ||
+          (red_max[o] == red_max[tid] &&
+           (red_sq[o] < red_sq[tid] || (red_sq[o] == red_sq[tid] && red_idx[o] < red_idx[tid])))) {
+        red_max[tid] = red_max[o];
+        red_sq[tid] = red_sq[o];
+        red_idx[tid] = red_idx[o];
+      }
+    }
+    __syncthreads();
+  }
+  if (tid != 0) return;
+  for (int r = 0; r < kRanks; ++r)
+    for (int h = hlo[r]; h < hlo[r + 1]; ++h) owner[h] = r;
+  int choice[kRanks];
+  int q = red_idx[0];
+  for (int i = n_snd - 1; i >= 0; --i) {
+    choice[i] = q % opt[i];
+    q /= opt[i];
+  }
+  int n_moves = 0;  // the moves in sender order
+  for (int i = 0; i < n_snd; ++i) {
+    if (choice[i] == 0) continue;
+    const int h = hlo[snd[i]] + (choice[i] - 1) / n_rcv, dst = rcv[(choice[i] - 1) % n_rcv];
+    owner[h] = dst;
+    info[37 + 3 * n_moves] = h;
+    info[38 + 3 * n_moves] = snd[i];
+    info[39 + 3 * n_moves] = dst;
+    ++n_moves;
+  }
+  int64_t W1[kRanks] = {};
+  for (int h = 0; h < BH; ++h) W1[owner[h]] += work[h];
+  int64_t wmax = 0;
+  for (int r = 0; r < kRanks; ++r) wmax = W1[r] > wmax ? W1[r] : wmax;
+  for (int r = 0; r < kRanks; ++r) {
+    const int64_t dW = wmax - W1[r];
+    int64_t e = 0;
+    if (mode > 0 && (double)dW > n2 * (double)wmax) e = (int64_t)floor(n1 * (double)dW);
+    budget[r] = e;
+    info[5 + r] = (double)W0[r];
+    info[13 + r] = (double)W1[r];
+    info[29 + r] = (double)e;
+  }
+  info[1] = rank_rho(W1);
+  info[4] = (double)n_moves;
+  // queue segments: the ranks' heads in rank order, ascending within a rank
+  int pos = 0;
+  for (int r = 0; r < kRanks; ++r) {
+    sched[r] = pos * per_head;
+    for (int h = 0; h < BH; ++h)
+      if (owner[h] == r) head_order[pos++] = h;
+  }
+  sched[kRanks] = pos * per_head;
+  sched[kRanks + 1] = members;
+}
+
+// SASA step 2 on rank r = blockIdx.x: raise the lightest of the rank's tiles E_r
+// times (ties: the lower position, positions running over the rank's heads in
+// head_order and over query blocks within a head; full tiles skipped), in closed
+// form as in slack_plan_kernel. target[t] = the new count of every tile.
+__global__ __launch_bounds__(1024) void rank_fill_kernel(const int32_t* __restrict__ counts,
+                                                         const int32_t* __restrict__ head_order,
+                                                         const int32_t* __restrict__ sched, int per_head, int nb,
+                                                         const int64_t* __restrict__ budget,
+                                                         int32_t* __restrict__ target) {
+  __shared__ int32_t hist[kMaxBins];
+  __shared__ int64_t buf[1024];
+  __shared__ int64_t cnt_lt_s[kMaxBins + 1];
+  __shared__ int64_t sum_lt_s[kMaxBins + 1];
+  __shared__ int64_t lam_s, rest_s;
+  const int r = blockIdx.x;
+  const int h0 = sched[r] / per_head, h1 = sched[r + 1] / per_head;
+  const int n = (h1 - h0) * nb;  // the rank's tiles, by position
+  auto tile = [&](int q) { return (size_t)head_order[h0 + q / nb] * nb + q % nb; };
+  const int64_t E = budget[r];
+  if (E == 0) {
+    for (int q = threadIdx.x; q < n; q += 1024) target[tile(q)] = counts[tile(q)];
+    return;
+  }
+  for (int b = threadIdx.x; b <= nb; b += 1024) hist[b] = 0;
+  __syncthreads();
+  for (int q = threadIdx.x; q < n; q += 1024) atomicAdd(&hist[counts[tile(q)]], 1);
+  __syncthreads();
+  const int bins = nb + 1;
+  const int per = (bins + 1023) / 1024;
+  const int b0 = threadIdx.x * per;
+  int64_t my_cnt = 0, my_sum = 0;
+  for (int b = b0; b < min(bins, b0 + per); ++b) {
+    my_cnt += hist[b];
+    my_sum += (int64_t)b * hist[b];
+  }
+  int64_t tot_cnt, tot_sum;
+  int64_t run_cnt = block_exclusive_scan<int64_t>(my_cnt, buf, tot_cnt);
+  int64_t run_sum = block_exclusive_scan<int64_t>(my_sum, buf, tot_sum);
+  for (int b = b0; b < min(bins, b0 + per); ++b) {
+    cnt_lt_s[b] = run_cnt;
+    sum_lt_s[b] = run_sum;
+    run_cnt += hist[b];
+    run_sum += (int64_t)b * hist[b];
+  }
+  __syncthreads();
+  int64_t ok = 0;
+  for (int lam = threadIdx.x; lam <= nb; lam += 1024) ok += ((int64_t)lam * cnt_lt_s[lam] - sum_lt_s[lam]) <= E;
+  int64_t n_ok;
+  block_exclusive_scan<int64_t>(ok, buf, n_ok);
+  if (threadIdx.x == 0) {
+    const int64_t lam = n_ok - 1;
+    lam_s = lam;
+    rest_s = E - (lam * cnt_lt_s[lam] - sum_lt_s[lam]);
+  }
+  __syncthreads();
+  const int lam = (int)lam_s;
+  const int64_t rest = rest_s;
+  int64_t seen = 0;
+  for (int base = 0; base < n; base += 1024) {
+    const int q = base + threadIdx.x;
+    const int c = q < n ? counts[tile(q)] : nb;
+    const int64_t low = (lam < nb && c <= lam) ? 1 : 0;
+    int64_t chunk_total;
+    const int64_t rank = seen + block_exclusive_scan<int64_t>(low, buf, chunk_total);
+    if (q < n) target[tile(q)] = lam >= nb ? nb : (low ? lam + (rank < rest ? 1 : 0) : c);
+    seen += chunk_total;
+  }
+}
+
+// rho and the rank loads after augmentation (info[2], info[21..28]).
+__global__ void rank_final_kernel(const int32_t* __restrict__ work, const int32_t* __restrict__ owner, int BH,
+                                  double* __restrict__ info) {
+  if (threadIdx.x != 0) return;
+  int64_t W[kRanks] = {};
+  for (int h = 0; h < BH; ++h) W[owner[h]] += work[h];
+  for (int r = 0; r < kRanks; ++r) info[21 + r] = (double)W[r];
+  info[2] = rank_rho(W);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
@@ -591,6 +846,27 @@ hipError_t launch_slack_plan(const absh_ctx* c, const RouteBuffers& rb, int tile
 
 hipError_t launch_workload(const absh_ctx* c, const RouteBuffers& rb, int BH, hipStream_t s) {
   workload_kernel<<<BH, 256, 0, s>>>(rb.counts, c->nb, rb.work, rb.L);
+  return hipGetLastError();
+}
+
+hipError_t launch_rank_stage(const absh_ctx* c, const RouteBuffers& rb, int BH, const RankOpts& o, hipStream_t s) {
+  const int members = unit_members(c, ABSH_SCHED_RANKS);
+  const int per_head = (c->nb + members - 1) / members;
+  rank_plan_kernel<<<1, 1024, 0, s>>>(rb.work, BH, per_head, members, o.policy, o.k1, o.k2, o.n1, o.n2, rb.owner,
+                                      rb.head_order, rb.budget, rb.sched, rb.rank_info);
+  return hipGetLastError();
+}
+
+hipError_t launch_rank_fill(const absh_ctx* c, const RouteBuffers& rb, hipStream_t s) {
+  const int members = unit_members(c, ABSH_SCHED_RANKS);
+  const int per_head = (c->nb + members - 1) / members;
+  rank_fill_kernel<<<kRanks, 1024, 0, s>>>(rb.counts, rb.head_order, rb.sched, per_head, c->nb, rb.budget,
+                                            rb.target);
+  return hipGetLastError();
+}
+
+hipError_t launch_rank_final(const RouteBuffers& rb, int BH, hipStream_t s) {
+  rank_final_kernel<<<1, 64, 0, s>>>(rb.work, rb.owner, BH, rb.rank_info);
   return hipGetLastError();
 }
 

@@ -67,9 +67,20 @@ typedef struct absh_ctx absh_ctx;
 typedef enum {
   ABSH_SCHED_ORDER = 0, /* queue = tile ids in order, pulled by whichever CU is free          */
   ABSH_SCHED_LPT = 1,   /* queue = tiles by retained count, longest first (ties: lower id)    */
-  ABSH_SCHED_XCD = 2    /* queue = tile ids in order, cut into eight runs of equal retained
+  ABSH_SCHED_XCD = 2,   /* queue = tile ids in order, cut into eight runs of equal retained
                            cost, one per XCD (L2 cache); an XCD whose run is done takes tiles
                            from the next runs                                                  */
+  ABSH_SCHED_RANKS = 3  /* the review's rank-level stages with the eight XCDs as the ranks
+                           (核心公式 Eq. 2, 5-10; 3.2 RLB; 3.3 SASA and its piecewise policy):
+                           XCD r runs the heads of rank r, which first holds the contiguous
+                           heads floor(r*B*H/8) .. floor((r+1)*B*H/8)-1; by the policy on
+                           rho = max/mean of the rank loads, RLB moves at most one head from
+                           each rank above the mean load to a distinct rank below it (the
+                           plan of least (max, variance) of the new loads, searched
+                           exhaustively), then SASA gives rank r E_r = floor(n1 * dW_r)
+                           extra blocks when dW_r = W_max - W_r > n2 * W_max, filling the
+                           rank's lightest tiles along their importance order. Work units are
+                           query-block groups as for ABSH_SCHED_XCD.                          */
 } absh_schedule;
 
 /* Routing options (xllm-io review of FVAttn, section 五 "关键超参数": Top-p
@@ -80,6 +91,13 @@ typedef struct {
   double slack_frac;   /* slack-fill budget beta in [0, 1): E = floor(beta * sum counts)  */
   int32_t schedule;    /* an absh_schedule                                                */
   int32_t order_depth; /* 0..64: length of the importance-order prefix written to `order` */
+  /* ABSH_SCHED_RANKS only (ignored otherwise): */
+  int32_t rank_policy;  /* -1: by rho (below k1 nothing, below k2 SASA only, else RLB then
+                           SASA); 0: nothing; 1: SASA only; 2: RLB then SASA                  */
+  int32_t strict_ranks; /* 1: an XCD takes work only from its own rank (as separate GPUs
+                           would); 0: an XCD that is done takes work from the other ranks     */
+  double k1, k2;        /* policy thresholds on rho, 0 < k1 <= k2 (the review's 1.05, 1.10)  */
+  double n1, n2;        /* SASA coefficient in [0, 1) and trigger >= 0 (0.8, 0.07)           */
 } absh_route_opts;
 
 /* Routing outputs, caller-allocated device buffers (plus one host field).
@@ -101,7 +119,21 @@ typedef struct {
   int32_t* unit_cnt; /* [units] length of each union list (same condition as unit_list)         */
   int32_t schedule;  /* HOST field, written by absh_route: the absh_schedule the lists were made
                         for; absh_sparse_attn reads it                                           */
+  int32_t* head_order; /* [B*H] ABSH_SCHED_RANKS: the heads by rank after migration (ranks
+                        ascending, heads ascending within a rank); the queue segment of rank r
+                        holds their work units in this order (else unused, may be NULL)          */
+  double* rank_info;   /* [ABSH_RANK_INFO] ABSH_SCHED_RANKS: [0] rho before, [1] after migration,
+                        [2] after augmentation; [3] policy taken (0 none, 1 SASA, 2 RLB + SASA);
+                        [4] number of moves; [5..12] rank loads W_r in retained blocks before,
+                        [13..20] after migration, [21..28] after augmentation; [29..36] E_r;
+                        [37..60] the moves as (head, from, to), in sender order; [61] plans
+                        searched; [62] 1 if the search space was too large (no migration)
+                        (else unused, may be NULL)                                               */
+  int32_t strict_ranks; /* HOST field, written by absh_route (opts->strict_ranks); absh_sparse_attn
+                        reads it                                                                 */
 } absh_lists;
+
+#define ABSH_RANK_INFO 64
 
 /* Library version as major*10000 + minor*100 + patch. */
 int absh_version(void);

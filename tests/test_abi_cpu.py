@@ -120,3 +120,30 @@ def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(absh, "_lib", None)
     with pytest.raises(ImportError):
         absh.lib()
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """The binding's ctypes structs have the C header's sizes and field offsets (compiled with gcc)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = tmp_path / "layout.c"
+    fields = {"absh_route_opts": [f for f, _ in absh.RouteOpts._fields_],
+              "absh_lists": [f for f, _ in absh.Lists._fields_]}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "absh.h"', "int main(void) {"]
+    for struct, names in fields.items():
+        lines.append(f'  printf("{struct} %zu\\n", sizeof({struct}));')
+        for n in names:
+            lines.append(f'  printf("{struct}.{n} %zu\\n", offsetof({struct}, {n}));')
+    lines += ["  return 0;", "}"]
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(root, "include"), str(src), "-o", str(exe)], check=True)
+    out = dict(line.rsplit(" ", 1) for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                              check=True).stdout.split("\n") if line)
+    for struct, cls in (("absh_route_opts", absh.RouteOpts), ("absh_lists", absh.Lists)):
+        assert int(out[struct]) == ctypes.sizeof(cls), struct
+        for n, _ in cls._fields_:
+            assert int(out[f"{struct}.{n}"]) == getattr(cls, n).offset, (struct, n)
