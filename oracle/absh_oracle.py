@@ -419,22 +419,28 @@ def rlb_options(work: np.ndarray, owner: np.ndarray, R: int = RANKS):
     return senders, options
 
 
+def rlb_space(work: np.ndarray, owner: np.ndarray, R: int = RANKS) -> int:
+    """Number of option combinations RLB enumerates (product of the senders' option counts)."""
+    n = 1
+    for o in rlb_options(work, owner, R)[1]:
+        n *= len(o)
+    return n
+
+
 def rlb_plan(work: np.ndarray, owner: np.ndarray, R: int = RANKS):
     """Eq. 5-6: the plan of least (max_r W_r^new, Var_r W_r^new), ties to the first in enumeration order.
 
     The candidate plans are the product of the senders' options (the first sender
     varies slowest) with distinct receivers. Var is compared through sum W^2, which
-    orders plans the same way because migration keeps the total. Returns
-    (new owner array, list of moves (head, from, to)).
+    orders plans the same way because migration keeps the total. A space of more
+    than MAX_PLANS combinations is not searched (no migration). Returns (new
+    owner array, list of moves (head, from, to)).
     """
     work = np.asarray(work, dtype=np.int64).reshape(-1)
     W = rank_loads(work, owner, R)
     senders, options = rlb_options(work, owner, R)
-    n_plans = 1
-    for o in options:
-        n_plans *= len(o)
-    if n_plans > MAX_PLANS:
-        raise ValueError(f"migration space of {n_plans} plans is above the limit {MAX_PLANS}")
+    if rlb_space(work, owner, R) > MAX_PLANS:  # too many to enumerate: no migration
+        return owner.copy(), []
     best_key, best = None, ()
     for choice in itertools.product(*options):
         moves = [(s, c) for s, c in zip(senders, choice) if c is not None]
