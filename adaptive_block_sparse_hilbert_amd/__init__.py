@@ -20,7 +20,7 @@ ABSH_BF16, ABSH_F32 = 0, 1
 ABSH_ROWS, ABSH_VT = 0, 1
 SCHED_ORDER, SCHED_LPT, SCHED_XCD, SCHED_RANKS = 0, 1, 2, 3
 SCHEDULES = {"order": SCHED_ORDER, "lpt": SCHED_LPT, "xcd": SCHED_XCD, "ranks": SCHED_RANKS}
-RANK_POLICIES = {"auto": -1, "none": 0, "sasa": 1, "rlb+sasa": 2}
+RANK_POLICIES = {"auto": -1, "none": 0, "sasa": 1, "rlb+sasa": 2, "rlb": 3}
 RANK_INFO = 64  # doubles in Routing.rank_info (layout in include/absh.h)
 # the review's parameters of the rank-level stages (section 五)
 RLB_K1, RLB_K2, SASA_N1, SASA_N2 = 1.05, 1.10, 0.8, 0.07

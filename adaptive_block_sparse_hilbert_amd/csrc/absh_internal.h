@@ -65,7 +65,7 @@ struct RouteBuffers {
   double* rank_info;     // [kRankInfo] rank-stage report (ABSH_SCHED_RANKS)
 };
 // Rank-stage parameters (ABSH_SCHED_RANKS): policy -1 = piecewise on rho with
-// thresholds k1, k2; 0 = none; 1 = SASA only; 2 = RLB, then SASA.
+// thresholds k1, k2; 0 = none; 1 = SASA only; 2 = RLB, then SASA; 3 = RLB only.
 struct RankOpts {
   int policy;
   double k1, k2, n1, n2;

@@ -278,8 +278,8 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
     return fail(ABSH_EINVAL, "unknown schedule %d", opts->schedule);
   const bool ranks = opts->schedule == ABSH_SCHED_RANKS;
   if (ranks) {
-    if (opts->rank_policy < -1 || opts->rank_policy > 2)
-      return fail(ABSH_EINVAL, "rank_policy must be -1, 0, 1 or 2 (got %d)", opts->rank_policy);
+    if (opts->rank_policy < -1 || opts->rank_policy > 3)
+      return fail(ABSH_EINVAL, "rank_policy must lie in -1 .. 3 (got %d)", opts->rank_policy);
     if (opts->strict_ranks != 0 && opts->strict_ranks != 1)
       return fail(ABSH_EINVAL, "strict_ranks must be 0 or 1 (got %d)", opts->strict_ranks);
     if (!(opts->k1 > 0.0 && opts->k1 <= opts->k2))

@@ -567,7 +567,7 @@ __global__ __launch_bounds__(1024) void segments_kernel(const int32_t* __restric
 // spent by water-filling the rank's tiles along their importance order.
 //
 // info (float64, kRankInfo entries): [0] rho before, [1] after migration, [2]
-// after augmentation; [3] policy taken (0 none, 1 SASA, 2 RLB + SASA); [4]
+// after augmentation; [3] policy taken (0 none, 1 SASA, 2 RLB + SASA, 3 RLB); [4]
 // moves; [5..12] W before, [13..20] after migration, [21..28] after
 // augmentation; [29..36] E_r; [37..60] the moves as (head, from, to); [61]
 // combinations searched; [62] 1 if the space was too large to search.
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(1024) void rank_plan_kernel(const int32_t* __restri
     mode = policy >= 0 ? policy : (rho < k1 ? 0 : rho < k2 ? 1 : 2);
     n_snd = n_rcv = 0;
     int64_t space = 1;
-    if (mode == 2) {
+    if (mode == 2 || mode == 3) {
       for (int r = 0; r < kRanks; ++r) {
         if (W0[r] * kRanks > total) snd[n_snd++] = r;
         if (W0[r] * kRanks < total) rcv[n_rcv++] = r;
@@ -704,7 +704,7 @@ __global__ __launch_bounds__(1024) void rank_plan_kernel(const int32_t* __restri
   for (int r = 0; r < kRanks; ++r) {
     const int64_t dW = wmax - W1[r];
     int64_t e = 0;
-    if (mode > 0 && (double)dW > n2 * (double)wmax) e = (int64_t)floor(n1 * (double)dW);
+    if ((mode == 1 || mode == 2) && (double)dW > n2 * (double)wmax) e = (int64_t)floor(n1 * (double)dW);
     budget[r] = e;
     info[5 + r] = (double)W0[r];
     info[13 + r] = (double)W1[r];

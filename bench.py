@@ -39,8 +39,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="720p-40h")
     ap.add_argument("--p", type=float, default=None, help="override the workload's Top-p")
-    ap.add_argument("--schedule", default="xcd", choices=("order", "lpt", "xcd"),
+    ap.add_argument("--schedule", default="xcd", choices=("order", "lpt", "xcd", "ranks"),
                     help="tile schedule of the attention kernel")
+    ap.add_argument("--rank-policy", default="auto", choices=("auto", "none", "sasa", "rlb+sasa", "rlb"),
+                    help="schedule 'ranks': RLB / SASA policy (auto: the piecewise policy on rho)")
+    ap.add_argument("--strict-ranks", action="store_true",
+                    help="schedule 'ranks': each XCD runs only its own rank's work (as separate GPUs would)")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -101,6 +105,7 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         absh.route(ctx, qh, kh, p, w.k_floor, slack_frac=w.slack_frac, schedule=args.schedule, out=routing,
+                   rank_policy=args.rank_policy, strict_ranks=args.strict_ranks,
                    workspace=ws)
         if ev is not None:
             ev[2].record(stream)
@@ -197,6 +202,7 @@ def main():
             "tokens": w.N, "block": w.block, "blocks": ctx.nb, "p": p, "k_floor": w.k_floor,
             "slack_frac": w.slack_frac, "schedule": args.schedule,
         },
+        "ranks": rank_report(routing, args) if args.schedule == "ranks" else None,
         "density": round(density, 5),
         "retained_tflop": round(f_ret / 1e12, 4),
         "dense_tflop": round(n_all / 1e12, 4),
@@ -213,6 +219,20 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def rank_report(routing, args):
+    """The rank stage's report (rho before / after migration / after augmentation, moves, budgets)."""
+    info = routing.rank_info.cpu().numpy()
+    return {
+        "policy_asked": args.rank_policy, "strict": bool(args.strict_ranks),
+        "policy_taken": ["none", "sasa", "rlb+sasa", "rlb"][int(info[3])],
+        "rho_before": round(float(info[0]), 4), "rho_after_rlb": round(float(info[1]), 4),
+        "rho_after_sasa": round(float(info[2]), 4),
+        "moves": [[int(x) for x in info[37 + 3 * i: 40 + 3 * i]] for i in range(int(info[4]))],
+        "rank_blocks_before": [int(x) for x in info[5:13]], "rank_blocks_after": [int(x) for x in info[21:29]],
+        "sasa_budgets": [int(x) for x in info[29:37]],
+    }
 
 
 def attention_kernel_name(d, block, members):

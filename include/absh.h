@@ -93,7 +93,7 @@ typedef struct {
   int32_t order_depth; /* 0..64: length of the importance-order prefix written to `order` */
   /* ABSH_SCHED_RANKS only (ignored otherwise): */
   int32_t rank_policy;  /* -1: by rho (below k1 nothing, below k2 SASA only, else RLB then
-                           SASA); 0: nothing; 1: SASA only; 2: RLB then SASA                  */
+                           SASA); 0: nothing; 1: SASA only; 2: RLB then SASA; 3: RLB only     */
   int32_t strict_ranks; /* 1: an XCD takes work only from its own rank (as separate GPUs
                            would); 0: an XCD that is done takes work from the other ranks     */
   double k1, k2;        /* policy thresholds on rho, 0 < k1 <= k2 (the review's 1.05, 1.10)  */
@@ -123,7 +123,7 @@ typedef struct {
                         ascending, heads ascending within a rank); the queue segment of rank r
                         holds their work units in this order (else unused, may be NULL)          */
   double* rank_info;   /* [ABSH_RANK_INFO] ABSH_SCHED_RANKS: [0] rho before, [1] after migration,
-                        [2] after augmentation; [3] policy taken (0 none, 1 SASA, 2 RLB + SASA);
+                        [2] after augmentation; [3] policy taken (0 none, 1 SASA, 2 RLB + SASA, 3 RLB);
                         [4] number of moves; [5..12] rank loads W_r in retained blocks before,
                         [13..20] after migration, [21..28] after augmentation; [29..36] E_r;
                         [37..60] the moves as (head, from, to), in sender order; [61] plans

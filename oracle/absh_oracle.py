@@ -504,7 +504,8 @@ def water_fill(flat: np.ndarray, nb: int, E: int) -> np.ndarray:
 
 def rank_stage(counts: np.ndarray, R: int = RANKS, k1: float = RLB_K1, k2: float = RLB_K2,
                n1: float = SASA_N1, n2: float = SASA_N2, policy: Optional[str] = None) -> dict:
-    """RLB then SASA over ranks, enabled by the piecewise policy on rho (or a forced policy).
+    """RLB then SASA over ranks, enabled by the piecewise policy on rho (or a forced policy:
+    'none', 'sasa', 'rlb+sasa', or 'rlb' for migration alone).
 
     counts: [B, H, nb] retained counts after Top-p and the floor. Returns the
     initial and final head owners, the moves, the budgets E_r, the new counts
@@ -522,10 +523,10 @@ def rank_stage(counts: np.ndarray, R: int = RANKS, k1: float = RLB_K1, k2: float
     rho0 = imbalance(W0)
     mode = rank_policy(rho0, k1, k2) if policy is None else policy
     owner, moves = owner0.copy(), []
-    if mode == "rlb+sasa":
+    if mode in ("rlb+sasa", "rlb"):
         owner, moves = rlb_plan(work, owner0, R)
     W1 = rank_loads(work, owner, R)
-    E = sasa_budgets(W1, n1, n2) if mode != "none" else np.zeros(R, dtype=np.int64)
+    E = sasa_budgets(W1, n1, n2) if mode in ("sasa", "rlb+sasa") else np.zeros(R, dtype=np.int64)
     new = flat.copy()
     for r in range(R):
         heads = np.nonzero(owner == r)[0]

@@ -28,13 +28,13 @@ pytestmark = pytest.mark.gpu
 def gpu_rank_report(r):
     info = r.rank_info.cpu().numpy()
     moves = [tuple(int(x) for x in info[37 + 3 * i: 40 + 3 * i]) for i in range(int(info[4]))]
-    return dict(rho0=info[0], rho_rlb=info[1], rho_final=info[2], policy=["none", "sasa", "rlb+sasa"][int(info[3])],
+    return dict(rho0=info[0], rho_rlb=info[1], rho_final=info[2], policy=["none", "sasa", "rlb+sasa", "rlb"][int(info[3])],
                 moves=moves, W0=info[5:13].astype(np.int64), W1=info[13:21].astype(np.int64),
                 W2=info[21:29].astype(np.int64), E=info[29:37].astype(np.int64), too_large=info[62])
 
 
 @pytest.mark.parametrize("index,policy", [(1, "auto"), (2, "auto"), (3, "auto"), (2, "rlb+sasa"), (3, "sasa"),
-                                          (1, "none")])
+                                          (3, "rlb"), (1, "none")])
 def test_rank_stage_matches_oracle(index, policy):
     c = case(index)
     w = c.w

@@ -172,3 +172,6 @@ def test_forced_policies():
     assert (none["counts"] == counts).all() and none["rho_final"] == none["rho0"]
     assert sasa["moves"] == [] and sasa["rho_final"] <= sasa["rho0"]
     assert both["rho_rlb"] <= both["rho0"] and both["rho_final"] <= both["rho_rlb"]
+    rlb = O.rank_stage(counts, policy="rlb")
+    assert (rlb["counts"] == counts).all() and (rlb["E"] == 0).all()
+    assert rlb["moves"] == both["moves"] and rlb["rho_final"] == both["rho_rlb"]
