@@ -29,6 +29,9 @@ each is named where it is used:
     skipped) by the next block of its own importance order.
   * LPT queue (one-GPU reading of RLB): tiles sorted by retained count,
     descending, ties by ascending tile id.
+  * Structured router (LVSA note): a local window over block ids plus every
+    stride-th key block as a global anchor, the anchors' offset rotating with
+    the diffusion step.
   * Rank-level RLB and SASA (review Eq. 2, 5-10, 3.2, 3.3) with the eight XCDs
     of one GPU as the ranks: contiguous head placement, the piecewise policy on
     rho, an exhaustive search of a restricted one-send-one-receive migration
@@ -356,6 +359,37 @@ def list_schedule(costs: Sequence[float], order: Sequence[int], workers: int):
         loads[w] += costs[t]
         heapq.heappush(heap, (free + costs[t], w))
     return loads, float(loads.max())
+
+
+# --------------------------------------------------------------------------
+# Structured router: local window plus rotating global anchors (LVSA note)
+# --------------------------------------------------------------------------
+
+
+def anchor_offset(stride: int, shift: int, step: int) -> int:
+    """Offset of the anchor blocks at diffusion step `step`: (step * shift) mod stride (0 without anchors)."""
+    return (step * shift) % stride if stride > 0 else 0
+
+
+def window_anchor_list(nb: int, i: int, window: int, stride: int, shift: int, step: int) -> np.ndarray:
+    """Key blocks of query block i, ascending: the local window |j - i| <= window plus the anchors.
+
+    Reading of the LVSA note ("a structured local window pattern with rotating
+    global anchors"): the window is over block ids, which in Hilbert order are
+    neighbours in (t, y, x); the anchors are every stride-th key block, starting
+    at anchor_offset(), so they shift with the diffusion step. stride = 0: no
+    anchors.
+    """
+    blocks = set(range(max(0, i - window), min(nb - 1, i + window) + 1))
+    if stride > 0:
+        blocks |= set(range(anchor_offset(stride, shift, step), nb, stride))
+    return np.array(sorted(blocks), dtype=np.int64)
+
+
+def window_anchor_counts(nb: int, window: int, stride: int, shift: int, step: int) -> np.ndarray:
+    """Retained count of every query block (the same for every head)."""
+    return np.array([window_anchor_list(nb, i, window, stride, shift, step).size for i in range(nb)],
+                    dtype=np.int64)
 
 
 # --------------------------------------------------------------------------
