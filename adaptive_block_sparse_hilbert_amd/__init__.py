@@ -22,6 +22,7 @@ SCHED_ORDER, SCHED_LPT, SCHED_XCD, SCHED_RANKS = 0, 1, 2, 3
 SCHEDULES = {"order": SCHED_ORDER, "lpt": SCHED_LPT, "xcd": SCHED_XCD, "ranks": SCHED_RANKS}
 RANK_POLICIES = {"auto": -1, "none": 0, "sasa": 1, "rlb+sasa": 2, "rlb": 3}
 RANK_INFO = 64  # doubles in Routing.rank_info (layout in include/absh.h)
+ROUTERS = {"topp": 0, "window-anchor": 1}
 # the review's parameters of the rank-level stages (section 五)
 RLB_K1, RLB_K2, SASA_N1, SASA_N2 = 1.05, 1.10, 0.8, 0.07
 
@@ -44,7 +45,9 @@ class RouteOpts(ctypes.Structure):
     _fields_ = [("p", ctypes.c_double), ("k_floor", ctypes.c_int32), ("slack_frac", ctypes.c_double),
                 ("schedule", ctypes.c_int32), ("order_depth", ctypes.c_int32),
                 ("rank_policy", ctypes.c_int32), ("strict_ranks", ctypes.c_int32),
-                ("k1", ctypes.c_double), ("k2", ctypes.c_double), ("n1", ctypes.c_double), ("n2", ctypes.c_double)]
+                ("k1", ctypes.c_double), ("k2", ctypes.c_double), ("n1", ctypes.c_double), ("n2", ctypes.c_double),
+                ("router", ctypes.c_int32), ("window", ctypes.c_int32), ("anchor_stride", ctypes.c_int32),
+                ("anchor_shift", ctypes.c_int32), ("step", ctypes.c_int32)]
 
 
 class Lists(ctypes.Structure):
@@ -263,12 +266,16 @@ def alloc_routing(ctx: Context, B: int, H: int, order_depth: int = 0) -> Routing
 def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0, schedule="lpt",
           order_depth: int = 0, out: Optional[Routing] = None, workspace=None, stream=None,
           rank_policy="auto", strict_ranks: bool = False, k1: float = RLB_K1, k2: float = RLB_K2,
-          n1: float = SASA_N1, n2: float = SASA_N2) -> Routing:
+          n1: float = SASA_N1, n2: float = SASA_N2, router="topp", window: int = 0, anchor_stride: int = 0,
+          anchor_shift: int = 0, step: int = 0) -> Routing:
     """Stage-1 routing of Hilbert-order qh, kh [B, H, n_pad, d] bf16 -> Routing (device tensors).
 
     schedule: "order", "lpt", "xcd" or "ranks" (or the SCHED_* integer). The
     rank_* and k/n arguments apply to "ranks" only: rank_policy "auto" (by rho),
-    "none", "sasa" or "rlb+sasa"; strict_ranks keeps each XCD on its own rank.
+    "none", "sasa", "rlb+sasa" or "rlb"; strict_ranks keeps each XCD on its own rank.
+    router "window-anchor" builds the structured lists (window, anchor_stride,
+    anchor_shift, step; see include/absh.h) instead of Top-p; qh and kh then only
+    give the shape.
     """
     import torch
     B, H, n_pad, d = qh.shape
@@ -280,7 +287,9 @@ def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0,
     sched = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
     policy = RANK_POLICIES[rank_policy] if isinstance(rank_policy, str) else int(rank_policy)
     opts = RouteOpts(float(p), int(k_floor), float(slack_frac), sched, int(order_depth), policy,
-                     int(bool(strict_ranks)), float(k1), float(k2), float(n1), float(n2))
+                     int(bool(strict_ranks)), float(k1), float(k2), float(n1), float(n2),
+                     ROUTERS[router] if isinstance(router, str) else int(router), int(window), int(anchor_stride),
+                     int(anchor_shift), int(step))
     lists = out.lists()
     _check(lib().absh_route(ctx.handle, _ptr(qh), _ptr(kh), B, H, d, ctypes.byref(opts), ctypes.byref(lists),
                             _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream)))

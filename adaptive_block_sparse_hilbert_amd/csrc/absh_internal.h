@@ -83,6 +83,8 @@ int queue_chunks(int tiles);
 hipError_t launch_rank_stage(const absh_ctx* c, const RouteBuffers& rb, int BH, const RankOpts& o, hipStream_t s);
 hipError_t launch_rank_fill(const absh_ctx* c, const RouteBuffers& rb, hipStream_t s);
 hipError_t launch_rank_final(const RouteBuffers& rb, int BH, hipStream_t s);
+hipError_t launch_window_anchor(const absh_ctx* c, const RouteBuffers& rb, int tiles, int window, int stride,
+                                int offset, hipStream_t s);
 
 // Work lists of the attention kernel. A unit is `members` neighbouring query
 // blocks of one head (1: a single tile taken from the queue; 2 or 4: a group

@@ -266,10 +266,22 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
   g_last_error.clear();
   if (absh_status st = check_ctx(c)) return st;
   if (absh_status st = check_shape(c, B, H, d)) return st;
-  if (!qh || !kh) return fail(ABSH_EINVAL, "qh or kh is NULL");
   if (!opts || !out) return fail(ABSH_EINVAL, "opts or out is NULL");
-  if (!(opts->p > 0.0 && opts->p <= 1.0)) return fail(ABSH_EINVAL, "p must lie in (0, 1] (got %g)", opts->p);
-  if (opts->k_floor < 0) return fail(ABSH_EINVAL, "k_floor must be >= 0 (got %d)", opts->k_floor);
+  if (opts->router != ABSH_ROUTER_TOPP && opts->router != ABSH_ROUTER_WINDOW_ANCHOR)
+    return fail(ABSH_EINVAL, "unknown router %d", opts->router);
+  const bool structured = opts->router == ABSH_ROUTER_WINDOW_ANCHOR;
+  if (structured) {
+    if (opts->window < 0 || opts->anchor_stride < 0 || opts->anchor_shift < 0 || opts->step < 0)
+      return fail(ABSH_EINVAL, "window, anchor_stride, anchor_shift and step must be >= 0");
+    if (opts->slack_frac != 0.0 || opts->order_depth != 0)
+      return fail(ABSH_EINVAL, "the window/anchor router takes no slack_frac and no order_depth");
+    if (opts->schedule == ABSH_SCHED_RANKS)
+      return fail(ABSH_EUNSUPPORTED, "the window/anchor router has no importance order for ABSH_SCHED_RANKS");
+  } else {
+    if (!qh || !kh) return fail(ABSH_EINVAL, "qh or kh is NULL");
+    if (!(opts->p > 0.0 && opts->p <= 1.0)) return fail(ABSH_EINVAL, "p must lie in (0, 1] (got %g)", opts->p);
+    if (opts->k_floor < 0) return fail(ABSH_EINVAL, "k_floor must be >= 0 (got %d)", opts->k_floor);
+  }
   if (!(opts->slack_frac >= 0.0 && opts->slack_frac < 1.0))
     return fail(ABSH_EINVAL, "slack_frac must lie in [0, 1) (got %g)", opts->slack_frac);
   if (opts->order_depth < 0 || opts->order_depth > 64)
@@ -327,11 +339,19 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
   rb.rank_info = ranks ? out->rank_info : nullptr;
   const int tiles = B * H * c->nb;
 
-  ABSH_HIP(absh::launch_pool(c, qh, qbar, B, H, d, s), "absh_route: pool q");
-  ABSH_HIP(absh::launch_pool(c, kh, kbar, B, H, d, s), "absh_route: pool k");
-  ABSH_HIP(absh::launch_scores(c, qbar, kbar, const_cast<float*>(rb.S), B * H, d, s), "absh_route: scores");
-  ABSH_HIP(absh::launch_select(c, rb, tiles, opts->p, opts->k_floor, opts->order_depth, 0, s),
-           "absh_route: select");
+  if (structured) {
+    const int offset = opts->anchor_stride > 0
+                           ? (int)(((int64_t)opts->step * opts->anchor_shift) % opts->anchor_stride)
+                           : 0;
+    ABSH_HIP(absh::launch_window_anchor(c, rb, tiles, opts->window, opts->anchor_stride, offset, s),
+             "absh_route: window/anchor lists");
+  } else {
+    ABSH_HIP(absh::launch_pool(c, qh, qbar, B, H, d, s), "absh_route: pool q");
+    ABSH_HIP(absh::launch_pool(c, kh, kbar, B, H, d, s), "absh_route: pool k");
+    ABSH_HIP(absh::launch_scores(c, qbar, kbar, const_cast<float*>(rb.S), B * H, d, s), "absh_route: scores");
+    ABSH_HIP(absh::launch_select(c, rb, tiles, opts->p, opts->k_floor, opts->order_depth, 0, s),
+             "absh_route: select");
+  }
   if (opts->slack_frac > 0.0) {
     ABSH_HIP(absh::launch_slack_plan(c, rb, tiles, opts->slack_frac, s), "absh_route: slack plan");
     ABSH_HIP(absh::launch_select(c, rb, tiles, opts->p, opts->k_floor, 0, 1, s), "absh_route: slack fill");

@@ -547,6 +547,33 @@ __global__ __launch_bounds__(1024) void segments_kernel(const int32_t* __restric
   if (threadIdx.x <= kSegments) sched[threadIdx.x] = threadIdx.x == 0 ? 0 : bound[threadIdx.x];
 }
 
+// ------------------------------------------------------------------ structured router
+
+// The LVSA note's block-sparse pattern (a structured local window plus global
+// anchor blocks that rotate with the diffusion step), in block ids: query block
+// i keeps the key blocks j with |j - i| <= window, and every key block with
+// j mod stride == offset (stride 0: none). The same for every head; one wave
+// per tile row writes the ascending list by ballot and prefix count.
+__global__ __launch_bounds__(256) void window_anchor_kernel(int nb, int tiles, int window, int stride, int offset,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ kv_idx) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= tiles) return;
+  const int i = row % nb;
+  const int lo = max(0, i - window), hi = min(nb - 1, i + window);
+  int32_t* out = kv_idx + (size_t)row * nb;
+  int n = 0;
+  for (int j0 = 0; j0 < nb; j0 += 64) {
+    const int j = j0 + lane;
+    const bool in = j < nb && ((j >= lo && j <= hi) || (stride > 0 && j % stride == offset));
+    const uint64_t mask = __ballot(in);
+    if (in) out[n + __popcll(mask & ((1ull << lane) - 1))] = j;
+    n += __popcll(mask);
+  }
+  if (lane == 0) counts[row] = n;
+}
+
 // ------------------------------------------------------------------ rank-level RLB and SASA
 
 // The eight XCDs as the ranks of the xllm-io review's runtime stages (核心公式
@@ -867,6 +894,13 @@ hipError_t launch_rank_fill(const absh_ctx* c, const RouteBuffers& rb, hipStream
 
 hipError_t launch_rank_final(const RouteBuffers& rb, int BH, hipStream_t s) {
   rank_final_kernel<<<1, 64, 0, s>>>(rb.work, rb.owner, BH, rb.rank_info);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_anchor(const absh_ctx* c, const RouteBuffers& rb, int tiles, int window, int stride,
+                                int offset, hipStream_t s) {
+  window_anchor_kernel<<<(unsigned)((tiles + 3) / 4), 256, 0, s>>>(c->nb, tiles, window, stride, offset, rb.counts,
+                                                                    rb.kv_idx);
   return hipGetLastError();
 }
 

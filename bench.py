@@ -45,6 +45,12 @@ def parse():
                     help="schedule 'ranks': RLB / SASA policy (auto: the piecewise policy on rho)")
     ap.add_argument("--strict-ranks", action="store_true",
                     help="schedule 'ranks': each XCD runs only its own rank's work (as separate GPUs would)")
+    ap.add_argument("--router", default="topp", choices=("topp", "window-anchor"),
+                    help="Top-p routing, or the structured local window + rotating anchors pattern")
+    ap.add_argument("--window", type=int, default=24, help="window-anchor router: blocks on each side")
+    ap.add_argument("--anchor-stride", type=int, default=32, help="window-anchor router: anchor spacing")
+    ap.add_argument("--anchor-shift", type=int, default=5, help="window-anchor router: offset advance per step")
+    ap.add_argument("--step", type=int, default=0, help="window-anchor router: diffusion step")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -104,8 +110,11 @@ def main():
         absh.permute(ctx, v, layout=absh.ABSH_VT, out=vt)
         if ev is not None:
             ev[1].record(stream)
-        absh.route(ctx, qh, kh, p, w.k_floor, slack_frac=w.slack_frac, schedule=args.schedule, out=routing,
-                   rank_policy=args.rank_policy, strict_ranks=args.strict_ranks,
+        absh.route(ctx, qh, kh, p, w.k_floor, slack_frac=w.slack_frac if args.router == "topp" else 0.0,
+                   schedule=args.schedule, out=routing,
+                   rank_policy=args.rank_policy, strict_ranks=args.strict_ranks, router=args.router,
+                   window=args.window, anchor_stride=args.anchor_stride, anchor_shift=args.anchor_shift,
+                   step=args.step,
                    workspace=ws)
         if ev is not None:
             ev[2].record(stream)
@@ -200,7 +209,9 @@ def main():
         "config": {
             "workload": w.name, "batch": B, "heads": H, "head_dim": d, "grid_t_y_x": [w.T, w.Y, w.X],
             "tokens": w.N, "block": w.block, "blocks": ctx.nb, "p": p, "k_floor": w.k_floor,
-            "slack_frac": w.slack_frac, "schedule": args.schedule,
+            "slack_frac": w.slack_frac, "schedule": args.schedule, "router": args.router,
+            **({"window": args.window, "anchor_stride": args.anchor_stride, "anchor_shift": args.anchor_shift,
+                "step": args.step} if args.router == "window-anchor" else {}),
         },
         "ranks": rank_report(routing, args) if args.schedule == "ranks" else None,
         "density": round(density, 5),

@@ -98,7 +98,22 @@ typedef struct {
                            would); 0: an XCD that is done takes work from the other ranks     */
   double k1, k2;        /* policy thresholds on rho, 0 < k1 <= k2 (the review's 1.05, 1.10)  */
   double n1, n2;        /* SASA coefficient in [0, 1) and trigger >= 0 (0.8, 0.07)           */
+  /* The router: ABSH_ROUTER_TOPP, or ABSH_ROUTER_WINDOW_ANCHOR, the structured
+   * pattern of the LVSA note (a local window plus global anchor blocks that
+   * rotate with the diffusion step): query block i keeps the key blocks j with
+   * |j - i| <= window and those with j mod anchor_stride == (step * anchor_shift)
+   * mod anchor_stride (anchor_stride 0: no anchors). It reads neither qh nor kh
+   * (both may be NULL); p and k_floor are not used; slack_frac and order_depth
+   * must be 0, and the schedule ABSH_SCHED_ORDER, _LPT or _XCD. */
+  int32_t router;
+  int32_t window;        /* >= 0, in blocks on each side                                     */
+  int32_t anchor_stride; /* >= 0                                                              */
+  int32_t anchor_shift;  /* >= 0: anchor offset advance per diffusion step                    */
+  int32_t step;          /* >= 0: the diffusion step                                          */
 } absh_route_opts;
+
+#define ABSH_ROUTER_TOPP 0
+#define ABSH_ROUTER_WINDOW_ANCHOR 1
 
 /* Routing outputs, caller-allocated device buffers (plus one host field).
  * nb, tiles = B*H*nb. */
