@@ -38,6 +38,11 @@ each is named where it is used:
     space, and per-rank slack budgets spent by water-filling the rank's tiles.
   * Attention: exact softmax(Q K_R^T / sqrt(d)) V_R over the tokens of the
     retained key blocks R of each query block.
+  * V quantization (review, "Block-Sparse Attention Execution" and 3.4): V is
+    stored in the OCP 8-bit E4M3 format with one power-of-two scale per head and
+    channel (the smallest that brings the channel's largest magnitude to 448 or
+    below); quantized attention is the exact attention above with V replaced by
+    its dequantized values.
 
 Precision: routing decisions are integers decided by floating point, so the
 oracle takes them in the same precision as the GPU library: block means as the
@@ -626,3 +631,122 @@ def retained_flops(sizes: np.ndarray, d: int, tiles) -> float:
     for i, blocks in tiles:
         total += 4 * int(sizes[i]) * int(sizes[np.asarray(blocks, dtype=np.int64)].sum()) * d
     return float(total)
+
+
+# --------------------------------------------------------------------------
+# V quantization: OCP FP8 E4M3 with a power-of-two scale per head and channel
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0        # largest finite E4M3 magnitude: 1.75 * 2^8
+E4M3_BIAS = 7
+E4M3_MIN_NORMAL = 2.0 ** -6
+E4M3_QUANTUM = 2.0 ** -9  # spacing of the subnormals (exponent field 0)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Codes of the OCP E4M3 format (sign, 4 exponent bits, bias 7, 3 mantissa bits,
+    no infinities, S.1111.111 is NaN) for finite x with |x| < 464, rounding to the
+    nearest value and ties to an even mantissa. Larger magnitudes raise.
+
+    Normal values (|x| >= 2^-6) are (1 + m/8) 2^E with exponent field E + 7; below
+    that the field is 0 and the value is m 2^-9. Rounding the mantissa up to 8
+    carries into the exponent field, which the code sum (E + 7) * 8 + m does by
+    itself, as does m = 8 in the subnormal range (the smallest normal, code 8).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if not np.isfinite(x).all():
+        raise ValueError("e4m3_encode: non-finite input")
+    a = np.abs(x)
+    if (a > 464.0).any():
+        raise ValueError("e4m3_encode: magnitude beyond the E4M3 range")
+    sub = a < E4M3_MIN_NORMAL
+    safe = np.where(sub, 1.0, a)
+    _, ex = np.frexp(safe)               # safe = f 2^ex with f in [0.5, 1)
+    E = ex.astype(np.int64) - 1          # safe = (1 + frac) 2^E
+    frac = np.ldexp(safe, -E) - 1.0      # exact: a power-of-two scaling
+    m_norm = np.rint(frac * 8.0).astype(np.int64)      # np.rint rounds half to even
+    m_sub = np.rint(np.ldexp(a, 9)).astype(np.int64)    # a / 2^-9, exact
+    code = np.where(sub, m_sub, (E + E4M3_BIAS) * 8 + m_norm)
+    if (code >= 0x7F).any():
+        raise ValueError("e4m3_encode: rounds past 448")
+    return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """Values of E4M3 codes as float64 (NaN for 0x7f and 0xff)."""
+    c = np.asarray(code, dtype=np.int64)
+    ef = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(ef == 0, np.ldexp(m.astype(np.float64), -9),
+                   np.ldexp(1.0 + m / 8.0, ef - E4M3_BIAS))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def v_scale_exponent(amax) -> np.ndarray:
+    """Smallest integer e with amax * 2^-e <= 448 (0 where amax is 0).
+
+    With amax = f 2^E, f in [0.5, 1): amax 2^-e <= 0.875 * 2^9 holds for
+    E - e <= 9 when f <= 0.875 and for E - e <= 8 otherwise.
+    """
+    amax = np.asarray(amax, dtype=np.float64)
+    f, E = np.frexp(amax)
+    e = np.where(f <= 0.875, E - 9, E - 8).astype(np.int64)
+    return np.where(amax > 0, e, 0)
+
+
+def quantize_v(v: np.ndarray):
+    """Per-channel E4M3 quantization of one head's values v [n, d].
+
+    Returns (codes uint8 [n, d], e int64 [d]): codes = E4M3(v * 2^-e) with e from
+    the channel's largest magnitude. The scaling by 2^-e is exact, so the only
+    rounding is the encoding.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    amax = np.abs(v).max(axis=0) if v.shape[0] else np.zeros(v.shape[1])
+    e = v_scale_exponent(amax)
+    return e4m3_encode(np.ldexp(v, -e[None, :])), e
+
+
+def dequantize_v(codes: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """v~ = E4M3 value of the code times 2^e, exactly (float64)."""
+    return np.ldexp(e4m3_decode(codes), np.asarray(e, dtype=np.int64)[None, :])
+
+
+def quantized_v(v: np.ndarray) -> np.ndarray:
+    """Grid-order [B, N, H, d] values replaced by their dequantized E4M3 values, each
+    (batch, head) with its own per-channel scales over all N tokens (float64)."""
+    v = np.asarray(v)
+    out = np.empty(v.shape, dtype=np.float64)
+    for b in range(v.shape[0]):
+        for h in range(v.shape[2]):
+            codes, e = quantize_v(v[b, :, h, :])
+            out[b, :, h, :] = dequantize_v(codes, e)
+    return out
+
+
+def attention_tile_spread(qh_bh: np.ndarray, kh_bh: np.ndarray, vh_bh: np.ndarray,
+                          block: int, i: int, kv_blocks: Sequence[int]):
+    """Output rows of query block i as in attention_tile, with two spreads of the
+    values around each output under the softmax weights w:
+      A1[r, c] = sum_j w_rj |v_jc - O_rc|,   A2[r, c] = sqrt(sum_j w_rj^2 (v_jc - O_rc)^2).
+    If every unnormalised weight P_j is replaced by P_j (1 + delta_j) with
+    |delta_j| <= u and the result renormalised, O moves by at most u / (1 - u) * A1;
+    for independent zero-mean delta_j of standard deviation s it moves by about
+    s * A2. Returns (O, A1, A2), each [n_i, d] float64.
+    """
+    N, d = qh_bh.shape
+    rows = slice(i * block, min((i + 1) * block, N))
+    keys = np.concatenate([np.arange(j * block, min((j + 1) * block, N)) for j in kv_blocks])
+    q = qh_bh[rows].astype(np.float64)
+    k = kh_bh[keys].astype(np.float64)
+    v = vh_bh[keys].astype(np.float64)
+    s = q @ k.T / math.sqrt(d)
+    s -= s.max(axis=1, keepdims=True)
+    w = np.exp(s)
+    w /= w.sum(axis=1, keepdims=True)
+    O = w @ v
+    dev = np.abs(v[None, :, :] - O[:, None, :])          # [n_i, keys, d]
+    A1 = np.einsum("rj,rjc->rc", w, dev)
+    A2 = np.sqrt(np.einsum("rj,rjc->rc", w * w, dev * dev))
+    return O, A1, A2
