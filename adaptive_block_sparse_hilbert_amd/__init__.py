@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libabsh.so")
 
 ABSH_BF16, ABSH_F32 = 0, 1
-ABSH_ROWS, ABSH_VT = 0, 1
+ABSH_ROWS, ABSH_VT, ABSH_VT8 = 0, 1, 2
 SCHED_ORDER, SCHED_LPT, SCHED_XCD, SCHED_RANKS = 0, 1, 2, 3
 SCHEDULES = {"order": SCHED_ORDER, "lpt": SCHED_LPT, "xcd": SCHED_XCD, "ranks": SCHED_RANKS}
 RANK_POLICIES = {"auto": -1, "none": 0, "sasa": 1, "rlb+sasa": 2, "rlb": 3}
@@ -29,7 +29,8 @@ RLB_K1, RLB_K2, SASA_N1, SASA_N2 = 1.05, 1.10, 0.8, 0.07
 EXPORTED = (
     "absh_version", "absh_status_string", "absh_last_error", "absh_create", "absh_destroy", "absh_dims",
     "absh_perm", "absh_perm_copy", "absh_permute", "absh_unpermute", "absh_pool", "absh_block_scores",
-    "absh_route_workspace_bytes", "absh_route", "absh_sparse_attn", "absh_lists_units",
+    "absh_route_workspace_bytes", "absh_route", "absh_sparse_attn", "absh_lists_units", "absh_quantize_v",
+    "absh_sparse_attn_v8",
 )
 
 
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         "absh_lists_units": ([vp, i, i, i], i),
         "absh_route": ([vp, vp, vp, i, i, i, ctypes.POINTER(RouteOpts), ctypes.POINTER(Lists), vp, sz, vp], i),
         "absh_sparse_attn": ([vp, vp, vp, vp, i, i, i, ctypes.POINTER(Lists), vp, vp], i),
+        "absh_quantize_v": ([vp, vp, i, i, i, vp, vp, vp], i),
+        "absh_sparse_attn_v8": ([vp, vp, vp, vp, vp, i, i, i, ctypes.POINTER(Lists), vp, vp], i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -307,4 +310,32 @@ def sparse_attn(ctx: Context, qh, kh, vt, routing: Optional[Routing] = None, out
     lists = routing.lists() if routing is not None else None
     _check(lib().absh_sparse_attn(ctx.handle, _ptr(qh), _ptr(kh), _ptr(vt), B, H, d,
                                   ctypes.byref(lists) if lists is not None else None, _ptr(out), _stream(stream)))
+    return out
+
+
+def quantize_v(ctx: Context, vh, out=None, scale=None, stream=None):
+    """vh [B, H, n_pad, d] bf16 (Hilbert order) -> (vt8, vscale): E4M3 codes in the
+    ABSH_VT8 layout, uint8 [B, H, n_pad / 64, 64 * d], and the per-channel
+    power-of-two scales, float32 [B, H, d]."""
+    import torch
+    B, H, n_pad, d = vh.shape
+    assert n_pad == ctx.n_pad and vh.dtype == torch.bfloat16 and vh.is_contiguous()
+    if out is None:
+        out = torch.empty((B, H, n_pad // 64, 64 * d), dtype=torch.uint8, device=vh.device)
+    if scale is None:
+        scale = torch.empty((B, H, d), dtype=torch.float32, device=vh.device)
+    _check(lib().absh_quantize_v(ctx.handle, _ptr(vh), B, H, d, _ptr(out), _ptr(scale), _stream(stream)))
+    return out, scale
+
+
+def sparse_attn_v8(ctx: Context, qh, kh, vt8, vscale, routing: Optional[Routing] = None, out=None, stream=None):
+    """sparse_attn with 8-bit values from quantize_v (routing=None: dense) -> oh [B, H, n_pad, d] bf16."""
+    import torch
+    B, H, n_pad, d = qh.shape
+    if out is None:
+        out = torch.empty_like(qh)
+    lists = routing.lists() if routing is not None else None
+    _check(lib().absh_sparse_attn_v8(ctx.handle, _ptr(qh), _ptr(kh), _ptr(vt8), _ptr(vscale), B, H, d,
+                                     ctypes.byref(lists) if lists is not None else None, _ptr(out),
+                                     _stream(stream)))
     return out

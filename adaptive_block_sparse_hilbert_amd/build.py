@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libabsh.so")
-SOURCES = ["hilbert.hip", "permute.hip", "route.hip", "attn.hip", "attn_union.hip", "api.cpp"]
+SOURCES = ["hilbert.hip", "permute.hip", "route.hip", "attn.hip", "attn_union.hip", "quant.hip", "api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

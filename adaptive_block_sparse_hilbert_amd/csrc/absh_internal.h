@@ -105,7 +105,13 @@ hipError_t launch_attention(const absh_ctx* c, const void* qh, const void* kh, c
 // Group units of 64- and 128-row query blocks (four and two members) run on the
 // union kernel; single tiles and other block sizes on the tile kernel.
 bool union_attention_supported(int d, int block, int members);
-hipError_t launch_union_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh,
-                                  int B, int H, int d, const AttnLists* lists, hipStream_t s);
+// vscale == NULL: vt in the bf16 ABSH_VT layout; else vt in the 8-bit ABSH_VT8
+// layout with per-channel scales vscale [B*H][d].
+hipError_t launch_union_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt,
+                                  const float* vscale, void* oh, int B, int H, int d, const AttnLists* lists,
+                                  hipStream_t s);
+// V quantization: vh [B*H][n_pad][d] bf16 -> vt8 (ABSH_VT8) and vscale [B*H][d].
+hipError_t launch_quantize_v(const absh_ctx* c, const void* vh, void* vt8, float* vscale, int BH, int d,
+                             hipStream_t s);
 
 }  // namespace absh

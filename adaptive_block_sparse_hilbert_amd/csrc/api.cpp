@@ -89,7 +89,7 @@ WsLayout ws_layout(const absh_ctx* c, int B, int H, int d) {
 
 extern "C" {
 
-int absh_version(void) { return 200; }
+int absh_version(void) { return 210; }
 
 const char* absh_status_string(int status) {
   switch (status) {
@@ -376,6 +376,40 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
   return ABSH_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation and kernel view of the lists of absh_sparse_attn / _v8.
+absh_status attn_lists(const absh_ctx* c, const absh_lists* lists, absh::AttnLists* L) {
+  *L = absh::AttnLists{};
+  if (!lists) return ABSH_OK;
+  if (!lists->counts || !lists->kv_idx || !lists->queue || !lists->sched)
+    return fail(ABSH_EINVAL, "lists needs counts, kv_idx, queue and sched");
+  if (lists->schedule < ABSH_SCHED_ORDER || lists->schedule > ABSH_SCHED_RANKS)
+    return fail(ABSH_EINVAL, "lists->schedule %d is not a schedule (was absh_route run?)", lists->schedule);
+  if (lists->schedule == ABSH_SCHED_RANKS && !lists->head_order)
+    return fail(ABSH_EINVAL, "lists needs head_order for ABSH_SCHED_RANKS");
+  if (lists->schedule != ABSH_SCHED_LPT && (!lists->unit_list || !lists->unit_cnt))
+    return fail(ABSH_EINVAL, "lists needs unit_list and unit_cnt for this schedule");
+  L->queue = lists->queue;
+  L->counts = lists->counts;
+  L->kv_idx = lists->kv_idx;
+  L->unit_list = lists->unit_list;
+  L->unit_cnt = lists->unit_cnt;
+  L->sched = lists->sched;
+  L->members = absh::unit_members(c, lists->schedule);
+  if (lists->schedule == ABSH_SCHED_RANKS) {
+    L->head_order = lists->head_order;
+    L->strict = lists->strict_ranks ? 1 : 0;
+  }
+  return ABSH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 absh_status absh_sparse_attn(absh_ctx* c, const void* qh, const void* kh, const void* vt, int B, int H, int d,
                              const absh_lists* lists, void* oh, void* stream) {
   g_last_error.clear();
@@ -384,32 +418,49 @@ absh_status absh_sparse_attn(absh_ctx* c, const void* qh, const void* kh, const 
   if (!qh || !kh || !vt || !oh) return fail(ABSH_EINVAL, "qh, kh, vt or oh is NULL");
   if (!aligned16(qh) || !aligned16(kh) || !aligned16(vt) || !aligned16(oh))
     return fail(ABSH_EINVAL, "qh, kh, vt and oh must be 16-byte aligned");
-  if (lists && (!lists->counts || !lists->kv_idx || !lists->queue || !lists->sched))
-    return fail(ABSH_EINVAL, "lists needs counts, kv_idx, queue and sched");
-  if (lists && (lists->schedule < ABSH_SCHED_ORDER || lists->schedule > ABSH_SCHED_RANKS))
-    return fail(ABSH_EINVAL, "lists->schedule %d is not a schedule (was absh_route run?)", lists->schedule);
-  if (lists && lists->schedule == ABSH_SCHED_RANKS && !lists->head_order)
-    return fail(ABSH_EINVAL, "lists needs head_order for ABSH_SCHED_RANKS");
-  if (lists && lists->schedule != ABSH_SCHED_LPT && (!lists->unit_list || !lists->unit_cnt))
-    return fail(ABSH_EINVAL, "lists needs unit_list and unit_cnt for this schedule");
+  absh::AttnLists L;
+  if (absh_status st = attn_lists(c, lists, &L)) return st;
   if (absh_status st = use_device(c)) return st;
-  absh::AttnLists L{};
-  if (lists) {
-    L.queue = lists->queue;
-    L.counts = lists->counts;
-    L.kv_idx = lists->kv_idx;
-    L.unit_list = lists->unit_list;
-    L.unit_cnt = lists->unit_cnt;
-    L.sched = lists->sched;
-    L.members = absh::unit_members(c, lists->schedule);
-    if (lists->schedule == ABSH_SCHED_RANKS) {
-      L.head_order = lists->head_order;
-      L.strict = lists->strict_ranks ? 1 : 0;
-    }
-  }
   ABSH_HIP(absh::launch_attention(c, qh, kh, vt, oh, B, H, d, lists ? &L : nullptr,
                                   reinterpret_cast<hipStream_t>(stream)),
            "absh_sparse_attn");
+  return ABSH_OK;
+}
+
+absh_status absh_quantize_v(absh_ctx* c, const void* vh, int B, int H, int d, void* vt8, float* vscale,
+                            void* stream) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (absh_status st = check_shape(c, B, H, d)) return st;
+  if (c->block != 64 && c->block != 128)
+    return fail(ABSH_EUNSUPPORTED, "8-bit values need block 64 or 128 (context has %d)", c->block);
+  if (!vh || !vt8 || !vscale) return fail(ABSH_EINVAL, "vh, vt8 or vscale is NULL");
+  if (!aligned16(vh) || !aligned16(vt8) || !aligned16(vscale))
+    return fail(ABSH_EINVAL, "vh, vt8 and vscale must be 16-byte aligned");
+  if ((double)B * H * (c->n_pad / 64) >= 2147483647.0) return fail(ABSH_EINVAL, "B*H*n_pad/64 must fit in int32");
+  if (absh_status st = use_device(c)) return st;
+  ABSH_HIP(absh::launch_quantize_v(c, vh, vt8, vscale, B * H, d, reinterpret_cast<hipStream_t>(stream)),
+           "absh_quantize_v");
+  return ABSH_OK;
+}
+
+absh_status absh_sparse_attn_v8(absh_ctx* c, const void* qh, const void* kh, const void* vt8, const float* vscale,
+                                int B, int H, int d, const absh_lists* lists, void* oh, void* stream) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (absh_status st = check_shape(c, B, H, d)) return st;
+  if (!qh || !kh || !vt8 || !vscale || !oh) return fail(ABSH_EINVAL, "qh, kh, vt8, vscale or oh is NULL");
+  if (!aligned16(qh) || !aligned16(kh) || !aligned16(vt8) || !aligned16(vscale) || !aligned16(oh))
+    return fail(ABSH_EINVAL, "qh, kh, vt8, vscale and oh must be 16-byte aligned");
+  absh::AttnLists L;
+  if (absh_status st = attn_lists(c, lists, &L)) return st;
+  const int members = lists ? L.members : (c->block >= 128 ? 2 : 4);
+  if (!absh::union_attention_supported(d, c->block, members))
+    return fail(ABSH_EUNSUPPORTED, "8-bit values need block 64 or 128 and a group schedule (not ABSH_SCHED_LPT)");
+  if (absh_status st = use_device(c)) return st;
+  ABSH_HIP(absh::launch_union_attention(c, qh, kh, vt8, vscale, oh, B, H, d, lists ? &L : nullptr,
+                                        reinterpret_cast<hipStream_t>(stream)),
+           "absh_sparse_attn_v8");
   return ABSH_OK;
 }
 

@@ -506,7 +506,7 @@ hipError_t launch_attention(const absh_ctx* c, const void* qh, const void* kh, c
                             int H, int d, const AttnLists* lists, hipStream_t s) {
   const int members = lists ? lists->members : (c->block >= 128 ? 2 : 4);
   if (union_attention_supported(d, c->block, members))
-    return launch_union_attention(c, qh, kh, vt, oh, B, H, d, lists, s);
+    return launch_union_attention(c, qh, kh, vt, nullptr, oh, B, H, d, lists, s);
 #define ABSH_ATTN(DD, BB) \
   if (d == DD && c->block == BB) return dispatch<DD, BB>(c, qh, kh, vt, oh, B, H, lists, s);
   ABSH_ATTN(64, 16)

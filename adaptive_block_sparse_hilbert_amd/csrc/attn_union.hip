@@ -20,6 +20,16 @@
 // step k run on the vector ALU, the matrix core computes S^T of step k + 1, and the
 // row maxima of step k + 1 are reduced while the value product of step k runs.
 //
+// With 8-bit values (the review's V quantization, ABSH_VT8 layout) the value
+// product of a step is one 32x32x64 fp8 MFMA per O^T tile: P is rounded to E4M3
+// (scaled so the row's reference maximum maps to at least 2^6 and nothing exceeds
+// 2^8), V^T comes in E4M3 with one power-of-two scale per channel, applied to
+// the output at the end. The row sum adds the same rounded probabilities. The
+// fp8 MFMA takes byte b of lane (column c, half g) as k index 32 g + b in both
+// operands, so byte 8 u + i of the P operand is element 8 (u % 2) + i of S^T tile
+// u / 2, i.e. the lane's 32 probabilities in register order, and the V^T image
+// stores the matching keys in the same byte positions.
+//
 // Operand layouts (lane l, column c = l % 32, half g = l / 32). For a 32x32x16
 // MFMA the A operand of lane l is row c, k indices 8g..8g+7; the B operand is
 // column c, the same k indices; accumulator element r of lane l is row
@@ -52,32 +62,37 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSegments = 8;    // XCDs of an MI355X: one queue segment each
 constexpr int kFlagShift = 28;  // union entry: block id | (member m retains it) << (28 + m)
 constexpr uint32_t kBlockMask = (1u << kFlagShift) - 1;
-constexpr float kLazy = 8.0f;   // base-2 headroom before a row's reference max moves
 constexpr int kStepKeys = 64;
 
-template <int D, int BLK>
+template <int D, int BLK, bool F8>
 struct UCfg {
+  // base-2 headroom before a row's reference max moves, and the base-2 offset of
+  // the probabilities: P = 2^(s - m + OFF) <= 2^(LAZY + OFF), at most 2^8 for E4M3
+  static constexpr float LAZY = F8 ? 2.0f : 8.0f;
+  static constexpr float OFF = F8 ? 6.0f : 0.0f;
   static constexpr int MEMBERS = BLK >= 128 ? 2 : 4;
   static constexpr int WPM = BLK / 32;         // waves per member
   static constexpr int TW = MEMBERS * WPM;     // waves per workgroup
   static constexpr int THREADS = TW * 64;
   static constexpr int HPB = BLK / kStepKeys;  // steps per key block
   static constexpr int K_BYTES = kStepKeys * D * 2;
-  static constexpr int V_BYTES = D * kStepKeys * 2;
+  static constexpr int V_BYTES = D * kStepKeys * (F8 ? 1 : 2);
   static constexpr int DS = D / 16;            // k-steps of S^T
   static constexpr int DT = D / 32;            // O^T tiles
   static constexpr int K_SLICES = K_BYTES / 1024;
   static constexpr int V_SLICES = V_BYTES / 1024;
   static constexpr int KPW = K_SLICES / TW;    // direct loads per wave per K slot
-  static constexpr int VPW = V_SLICES / TW;    // direct loads per wave per V^T slot
-  static constexpr int VT_ROW = BLK * 2;       // bytes per row of a V^T block in HBM
+  static constexpr int VPW = (V_SLICES + TW - 1) / TW;  // direct loads per wave per V^T slot
+  static constexpr int VT_ROW = BLK * 2;       // bytes per row of a bf16 V^T block in HBM
   static_assert(TW == 8, "eight waves per workgroup");
-  static_assert(K_SLICES == 8 * KPW && V_SLICES == 8 * VPW, "wave w loads the blocks w + 8 i");
-  static_assert(K_SLICES % TW == 0 && V_SLICES % TW == 0, "slices must tile the waves");
+  static_assert(K_SLICES == 8 * KPW, "wave w loads the K blocks w + 8 i");
+  static_assert(F8 ? V_SLICES <= 8 * VPW : V_SLICES == 8 * VPW, "wave w loads the V^T blocks w + 8 i");
 };
 
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, uint32_t wave_off,
@@ -120,12 +135,12 @@ __device__ __forceinline__ float sum_across_halves(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-template <int D, int BLK>
-__global__ __launch_bounds__((UCfg<D, BLK>::THREADS)) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, const bf16_t* __restrict__ vt,
-                       bf16_t* __restrict__ oh, AttnLists L, int32_t* __restrict__ counters, int units, int nb,
-                       int n_pad, int N, float scale_log2) {
-  using C = UCfg<D, BLK>;
+template <int D, int BLK, bool F8>
+__global__ __launch_bounds__((UCfg<D, BLK, F8>::THREADS)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, const char* __restrict__ vt,
+                       const float* __restrict__ vscale, bf16_t* __restrict__ oh, AttnLists L,
+                       int32_t* __restrict__ counters, int units, int nb, int n_pad, int N, float scale_log2) {
+  using C = UCfg<D, BLK, F8>;
   using T_ = std::true_type;
   using F_ = std::false_type;
   // One LDS variable per slot: distinct variables let the compiler see that the
@@ -163,13 +178,16 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
   // group b = w (K: blocks h * 8 + b; V^T: blocks b = w + 8 i, so b & 1 = w & 1).
   // Lane i fetches row 8 b + i % 8, 16-byte column (i / 8) ^ (b & 1) of the chunk.
   const uint32_t k_lane = (uint32_t)((lane % 8) * (2 * D) + ((lane / 8) ^ (wave & 1)) * 16);
-  const uint32_t v_lane = (uint32_t)((lane % 8) * C::VT_ROW + ((lane / 8) ^ (wave & 1)) * 16);
+  // (the 8-bit V^T image is stored as LDS wants it: lane i fetches bytes 16 i)
+  const uint32_t v_lane = F8 ? (uint32_t)(16 * lane) : (uint32_t)((lane % 8) * C::VT_ROW + ((lane / 8) ^ (wave & 1)) * 16);
   // LDS reads: S^T row c of a tile is key kappa(c) (bits 2 and 3 exchanged); the
   // lane reads 16-byte column g (+ 2 per further k-step) of its row
   const int kappa = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
   auto rd_base = [&](int row) { return (uint32_t)((row / 8) * 1024 + (g ^ ((row / 8) & 1)) * 128 + (row % 8) * 16); };
   const uint32_t k_rd = rd_base(kappa);
-  const uint32_t v_rd = rd_base(col);
+  // 8-bit V^T: channel c's 16 bytes of half g sit at 32 c + 16 (g ^ ((c >> 3) & 1)) of
+  // each of the two 32 D-byte regions
+  const uint32_t v_rd = F8 ? (uint32_t)(32 * col + 16 * (g ^ ((col >> 3) & 1))) : rd_base(col);
 
   // The two waves of a SIMD (w and w + 4) run the same phases after each barrier.
   // The first wins issue arbitration, so it runs its step as if alone while the
@@ -214,8 +232,9 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
 
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kh + (size_t)bh * n_pad * D), (short)0, n_pad * 2 * D, kRawBufferFlags);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vt + (size_t)bh * nb * D * BLK), (short)0, nb * D * C::VT_ROW, kRawBufferFlags);
+    const size_t v_head = F8 ? (size_t)n_pad * D : (size_t)nb * D * C::VT_ROW;  // bytes per head
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vt + (size_t)bh * v_head), (short)0, (int)v_head, kRawBufferFlags);
     // K slot <- K of step k (union entry e); V^T slot <- V^T of step k
     auto issue_k = [&](int slot, int k, uint32_t e) __attribute__((always_inline)) {
       const uint32_t j = e & kBlockMask;
@@ -231,8 +250,12 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
       char* st = vslot(slot);
 #pragma unroll
       for (int i = 0; i < C::VPW; ++i) {
-        const int n = wave + C::TW * i;  // block: V^T rows 8 n .. 8 n + 7
-        load_lds16(vrs, v_lane, j * (uint32_t)(D * C::VT_ROW) + (8 * n) * C::VT_ROW + half * 128, st + n * 1024);
+        const int n = wave + C::TW * i;  // block: V^T rows 8 n .. 8 n + 7 (bf16), bytes 1024 n .. of the image (fp8)
+        if (F8) {
+          if (n < C::V_SLICES) load_lds16(vrs, v_lane, (j * C::HPB + half) * (uint32_t)C::V_BYTES + 1024 * n, st + n * 1024);
+        } else {
+          load_lds16(vrs, v_lane, j * (uint32_t)(D * C::VT_ROW) + (8 * n) * C::VT_ROW + half * 128, st + n * 1024);
+        }
       }
     };
 
@@ -263,13 +286,13 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
     f32x16 o[C::DT];
 #pragma unroll
     for (int t = 0; t < C::DT; ++t) o[t] = f32x16{};
-    float l_run = 0.f;        // this lane's share of its row's sum of (bf16) probabilities
+    float l_run = 0.f;        // this lane's share of its row's sum of (rounded) probabilities
     float m_run = -INFINITY;  // the row's reference max, base-2 scaled
     f32x16 S[2];              // S^T of the step whose softmax comes next
 
     // The reference max moves only when a row's step max exceeds it by more than
-    // kLazy (base 2): probabilities stay below 2^kLazy and O is rescaled rarely.
-    // The result is the same softmax.
+    // LAZY (base 2): probabilities stay below 2^(LAZY + OFF) and O is rescaled
+    // rarely. The result is the same softmax.
     auto rescale_to = [&](float m_blk) __attribute__((always_inline)) {
       const float m_new = fmaxf(m_run, m_blk);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -279,7 +302,7 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
       m_run = m_new;
     };
     auto rescale = [&](float m_blk) __attribute__((always_inline)) {
-      if (__any(m_blk > m_run + kLazy)) rescale_to(m_blk);
+      if (__any(m_blk > m_run + C::LAZY)) rescale_to(m_blk);
     };
     // probabilities of elements r0 .. r0 + n - 1 (n even) of S^T tile T, as bf16 into
     // the B operand of 16-key value step 2T + r0 / 8, and their row sum
@@ -297,6 +320,44 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
     // masks element r of S^T tile T past `valid` keys: it is key 32 T + 16 (r / 8) + 8 g + r % 8
     auto mask = [&](int T, int r, int valid) __attribute__((always_inline)) {
       if (32 * T + 16 * (r / 8) + (r % 8) >= valid - 8 * g) S[T][r] = -INFINITY;
+    };
+    // 8-bit value product of one step: the 32 probabilities of both S^T tiles,
+    // rounded to E4M3 four to a register (tile T elements 4 w' .. 4 w' + 3 in
+    // register 4 T + w'), their row sum from the rounded values, then one fp8 MFMA
+    // per O^T tile, its V^T operand the 16 bytes at vbase + 1024 t of each region.
+    auto pv8 = [&](const char* vbase) __attribute__((always_inline)) {
+      // V^T operands one tile ahead of their MFMA (tile 0 under the exponentials)
+      auto frag = [&](int t) __attribute__((always_inline)) -> i32x8 {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(vbase + 1024 * t);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(vbase + 1024 * t + 32 * D);
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      i32x8 va = frag(0);
+      const float bias = C::OFF - m_run;
+      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+      i32x8 pf;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int T = w / 4, r = 4 * (w % 4);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(S[T][r], scale_log2, bias));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(S[T][r + 1], scale_log2, bias));
+        const float p2 = __builtin_amdgcn_exp2f(fmaf(S[T][r + 2], scale_log2, bias));
+        const float p3 = __builtin_amdgcn_exp2f(fmaf(S[T][r + 3], scale_log2, bias));
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, pk, true);
+        pf[w] = pk;
+        // E4M3 values are exact in bf16: the sum adds exactly what the MFMA multiplies
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pk, 1.0f, false), one2,
+                                                l_run, false);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pk, 1.0f, true), one2,
+                                                l_run, false);
+      }
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t) {
+        const i32x8 a = va;
+        if (t + 1 < C::DT) va = frag(t + 1);
+        o[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, o[t], 0, 0, 0, 0, 0, 0);
+      }
     };
 
     // One step as a hand-ordered instruction stream. The matrix instructions go
@@ -379,7 +440,10 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
       return body(T_(), T_(), masked_c, kbase, vbase, valid);
     };
     auto solo_pv = [&](const char* vbase) __attribute__((always_inline)) {
-      body(T_(), F_(), F_(), nullptr, vbase, kStepKeys);
+      if constexpr (F8)
+        pv8(vbase);
+      else
+        body(T_(), F_(), F_(), nullptr, vbase, kStepKeys);
     };
     auto solo_qk = [&](const char* kbase, int valid, auto masked_c) __attribute__((always_inline)) -> float {
       return body(F_(), T_(), masked_c, kbase, nullptr, valid);
@@ -420,10 +484,10 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
     // product of step k, then S^T of step k + 1.
     auto step_fast = [&](int k, auto slot_c, uint32_t ek, uint32_t ek1) __attribute__((always_inline)) {
       constexpr int SL = decltype(slot_c)::value;
-      if (mine(k, ek)) body(T_(), F_(), F_(), nullptr, vslot(SL) + v_rd, kStepKeys);
+      if (mine(k, ek)) solo_pv(vslot(SL) + v_rd);
       if (mine(k + 1, ek1)) {
         const float m = body(F_(), T_(), F_(), kslot(SL + 1) + k_rd, nullptr, kStepKeys);
-        if (__any(m > m_run + kLazy)) rescale_to(m);
+        if (__any(m > m_run + C::LAZY)) rescale_to(m);
       }
     };
     // Steps next to a head's short last block: run-time slots and masking.
@@ -434,7 +498,10 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
       const bool next = k + 1 < nsteps && mine(k + 1, ek1);
       const int vk1 = next ? valid_keys(k + 1, ek1) : kStepKeys;
       float m_blk = -INFINITY;
-      if (now && next)
+      if (now && next && F8) {
+        solo_pv(vbase);
+        m_blk = vk1 < kStepKeys ? solo_qk(kbase, vk1, T_()) : solo_qk(kbase, vk1, F_());
+      } else if (now && next)
         m_blk = vk1 < kStepKeys ? fused(kbase, vbase, vk1, T_()) : fused(kbase, vbase, vk1, F_());
       else if (now)
         solo_pv(vbase);
@@ -483,9 +550,18 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
       for (int t = 0; t < C::DT; ++t)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          // elements 4 q .. 4 q + 3 of tile t: channels 32 t + 8 q + 4 g + 0 .. 3
+          float sc[4] = {inv, inv, inv, inv};
+          if constexpr (F8) {
+            const float4 vs = *reinterpret_cast<const float4*>(vscale + (size_t)bh * D + 32 * t + 8 * q + 4 * g);
+            sc[0] *= vs.x;
+            sc[1] *= vs.y;
+            sc[2] *= vs.z;
+            sc[3] *= vs.w;
+          }
           uint2 w;
-          w.x = (uint32_t)f32_to_bf16(o[t][4 * q] * inv) | ((uint32_t)f32_to_bf16(o[t][4 * q + 1] * inv) << 16);
-          w.y = (uint32_t)f32_to_bf16(o[t][4 * q + 2] * inv) | ((uint32_t)f32_to_bf16(o[t][4 * q + 3] * inv) << 16);
+          w.x = (uint32_t)f32_to_bf16(o[t][4 * q] * sc[0]) | ((uint32_t)f32_to_bf16(o[t][4 * q + 1] * sc[1]) << 16);
+          w.y = (uint32_t)f32_to_bf16(o[t][4 * q + 2] * sc[2]) | ((uint32_t)f32_to_bf16(o[t][4 * q + 3] * sc[3]) << 16);
           *reinterpret_cast<uint2*>(orow + 32 * t + 8 * q + 4 * g) = w;
         }
     }
@@ -501,13 +577,14 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
   }
 }
 
-template <int D, int BLK>
-hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B, int H,
-                  const AttnLists& L, bool dense, hipStream_t s) {
-  using C = UCfg<D, BLK>;
+template <int D, int BLK, bool F8>
+hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void* vt, const float* vscale, void* oh,
+                  int B, int H, const AttnLists& L, bool dense, hipStream_t s) {
+  using C = UCfg<D, BLK, F8>;
   static int per_cu = 0;
   if (per_cu == 0) {
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, union_attn_kernel<D, BLK>, C::THREADS, 0);
+    hipError_t e =
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, union_attn_kernel<D, BLK, F8>, C::THREADS, 0);
     if (e != hipSuccess) return e;
     if (per_cu < 1) per_cu = 1;
   }
@@ -516,9 +593,9 @@ hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void*
   const float scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
   AttnLists Lk = L;
   if (dense) Lk = AttnLists{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, C::MEMBERS};
-  union_attn_kernel<D, BLK><<<grid, C::THREADS, 0, s>>>(
-      reinterpret_cast<const bf16_t*>(qh), reinterpret_cast<const bf16_t*>(kh), reinterpret_cast<const bf16_t*>(vt),
-      reinterpret_cast<bf16_t*>(oh), Lk, c->counters, units, c->nb, c->n_pad, c->N, scale_log2);
+  union_attn_kernel<D, BLK, F8><<<grid, C::THREADS, 0, s>>>(
+      reinterpret_cast<const bf16_t*>(qh), reinterpret_cast<const bf16_t*>(kh), reinterpret_cast<const char*>(vt),
+      vscale, reinterpret_cast<bf16_t*>(oh), Lk, c->counters, units, c->nb, c->n_pad, c->N, scale_log2);
   return hipGetLastError();
 }
 
@@ -528,12 +605,15 @@ bool union_attention_supported(int d, int block, int members) {
   return (d == 64 || d == 128) && ((block == 64 && members == 4) || (block == 128 && members == 2));
 }
 
-hipError_t launch_union_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh,
-                                  int B, int H, int d, const AttnLists* lists, hipStream_t s) {
+hipError_t launch_union_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt,
+                                  const float* vscale, void* oh, int B, int H, int d, const AttnLists* lists,
+                                  hipStream_t s) {
   AttnLists L = lists ? *lists : AttnLists{};
   const bool dense = lists == nullptr;
-#define ABSH_UNION(DD, BB) \
-  if (d == DD && c->block == BB) return launch<DD, BB>(c, qh, kh, vt, oh, B, H, L, dense, s);
+#define ABSH_UNION(DD, BB)                                                                              \
+  if (d == DD && c->block == BB)                                                                        \
+    return vscale ? launch<DD, BB, true>(c, qh, kh, vt, vscale, oh, B, H, L, dense, s)                  \
+                  : launch<DD, BB, false>(c, qh, kh, vt, nullptr, oh, B, H, L, dense, s);
   ABSH_UNION(64, 64)
   ABSH_UNION(64, 128)
   ABSH_UNION(128, 64)

@@ -14,6 +14,12 @@ retained blocks of 4 * n_i * n_j * d with true token counts. Each stage is timed
 with HIP events on the stream its kernels run on; the attention kernel's own
 average duration gives the roofline figure against the bf16 MFMA peak.
 
+--values fp8 runs the review's V quantization instead: v is permuted as rows and
+quantized to E4M3 with per-channel scales (its own stage), and the attention's
+value product runs on fp8 MFMAs. Half the retained FLOPs (Q K^T) stay bf16 and
+half (P V) are fp8, so the roofline peak is then 1 / (0.5 / 2.5 + 0.5 / 5.0)
+PFLOP/s = 3.33 PFLOP/s.
+
 Prints one JSON line. Inputs are synthetic (see workloads/), data = "synthetic".
 """
 from __future__ import annotations
@@ -29,6 +35,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+# half the attention's FLOPs on each: the time-weighted peak of bf16 Q K^T + fp8 P V
+PEAK_MIXED_TFLOPS = 1.0 / (0.5 / PEAK_BF16_TFLOPS + 0.5 / PEAK_FP8_TFLOPS)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -51,6 +60,8 @@ def parse():
     ap.add_argument("--anchor-stride", type=int, default=32, help="window-anchor router: anchor spacing")
     ap.add_argument("--anchor-shift", type=int, default=5, help="window-anchor router: offset advance per step")
     ap.add_argument("--step", type=int, default=0, help="window-anchor router: diffusion step")
+    ap.add_argument("--values", default="bf16", choices=("bf16", "fp8"),
+                    help="fp8: quantize V to E4M3 and run the value product on fp8 MFMAs")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -94,22 +105,41 @@ def main():
     # every buffer of the step, allocated once
     qh = torch.empty((B, H, ctx.n_pad, d), dtype=torch.bfloat16, device=dev)
     kh = torch.empty_like(qh)
-    vt = torch.empty((B, H, ctx.nb, d, absh.vt_keys(w.block)), dtype=torch.bfloat16, device=dev)
+    fp8 = args.values == "fp8"
+    if fp8:
+        vh = torch.empty_like(qh)
+        vt8 = torch.empty((B, H, ctx.n_pad // 64, 64 * d), dtype=torch.uint8, device=dev)
+        vscale = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    else:
+        vt = torch.empty((B, H, ctx.nb, d, absh.vt_keys(w.block)), dtype=torch.bfloat16, device=dev)
     oh = torch.empty_like(qh)
     o = torch.empty_like(q)
     routing = absh.alloc_routing(ctx, B, H)
     ws = torch.empty(absh.route_workspace_bytes(ctx, B, H, d), dtype=torch.uint8, device=dev)
 
-    stages = ("permute", "route", "attn", "unpermute")
+    stages = ("permute", "quantize", "route", "attn", "unpermute")
+
+    def attention(lists):
+        if fp8:
+            absh.sparse_attn_v8(ctx, qh, kh, vt8, vscale, lists, out=oh)
+        else:
+            absh.sparse_attn(ctx, qh, kh, vt, lists, out=oh)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         absh.permute(ctx, q, out=qh)
         absh.permute(ctx, k, out=kh)
-        absh.permute(ctx, v, layout=absh.ABSH_VT, out=vt)
+        if fp8:
+            absh.permute(ctx, v, out=vh)
+        else:
+            absh.permute(ctx, v, layout=absh.ABSH_VT, out=vt)
         if ev is not None:
             ev[1].record(stream)
+        if fp8:
+            absh.quantize_v(ctx, vh, out=vt8, scale=vscale)
+        if ev is not None:
+            ev[2].record(stream)
         absh.route(ctx, qh, kh, p, w.k_floor, slack_frac=w.slack_frac if args.router == "topp" else 0.0,
                    schedule=args.schedule, out=routing,
                    rank_policy=args.rank_policy, strict_ranks=args.strict_ranks, router=args.router,
@@ -117,19 +147,19 @@ def main():
                    step=args.step,
                    workspace=ws)
         if ev is not None:
-            ev[2].record(stream)
-        absh.sparse_attn(ctx, qh, kh, vt, routing, out=oh)
-        if ev is not None:
             ev[3].record(stream)
-        absh.unpermute(ctx, oh, out=o)
+        attention(routing)
         if ev is not None:
             ev[4].record(stream)
+        absh.unpermute(ctx, oh, out=o)
+        if ev is not None:
+            ev[5].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -157,13 +187,13 @@ def main():
 
     dense_ms = None
     if not args.no_dense:
-        absh.sparse_attn(ctx, qh, kh, vt, None, out=oh)
+        attention(None)
         torch.cuda.synchronize()
         de = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         times = []
         for _ in range(args.dense_reps):
             de[0].record(stream)
-            absh.sparse_attn(ctx, qh, kh, vt, None, out=oh)
+            attention(None)
             de[1].record(stream)
             torch.cuda.synchronize()
             times.append(de[0].elapsed_time(de[1]))
@@ -177,15 +207,18 @@ def main():
         torch.cuda.synchronize()
 
     traffic = measured_traffic(args.traffic_profile or os.path.join(
-        ROOT, "profiles", "attn_" + w.name.replace("-", "") + "_hbm.md"), w.name, args.schedule)
+        ROOT, "profiles", "attn_" + w.name.replace("-", "") + ("_fp8" if fp8 else "") + "_hbm.md"),
+        w.name, args.schedule, args.values)
 
+    peak = PEAK_MIXED_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     roof = {
         "bound": "mfma",
-        "kernel": attention_kernel_name(d, w.block, 1 if args.schedule == "lpt" else (2 if w.block >= 128 else 4)),
+        "kernel": attention_kernel_name(d, w.block, 1 if args.schedule == "lpt" else (2 if w.block >= 128 else 4),
+                                        fp8),
         "achieved": round(attn_tflops, 2),
-        "peak": PEAK_BF16_TFLOPS,
+        "peak": round(peak, 1),
         "unit": "TFLOP/s",
-        "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "frac": round(attn_tflops / peak, 4),
         "traffic": traffic,
     }
 
@@ -204,12 +237,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16+fp8" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": B, "heads": H, "head_dim": d, "grid_t_y_x": [w.T, w.Y, w.X],
             "tokens": w.N, "block": w.block, "blocks": ctx.nb, "p": p, "k_floor": w.k_floor,
-            "slack_frac": w.slack_frac, "schedule": args.schedule, "router": args.router,
+            "slack_frac": w.slack_frac, "schedule": args.schedule, "router": args.router, "values": args.values,
             **({"window": args.window, "anchor_stride": args.anchor_stride, "anchor_shift": args.anchor_shift,
                 "step": args.step} if args.router == "window-anchor" else {}),
         },
@@ -246,18 +279,19 @@ def rank_report(routing, args):
     }
 
 
-def attention_kernel_name(d, block, members):
+def attention_kernel_name(d, block, members, fp8=False):
     """Name of the kernel that runs the attention launch (as the profiler lists it).
 
     Units of four 64-row or two 128-row query blocks at head dim 64 or 128 run on
-    the union kernel; any other shape runs on the general one.
+    the union kernel (its last template argument: 8-bit values); any other shape
+    runs on the general one.
     """
     if d in (64, 128) and (block, members) in ((64, 4), (128, 2)):
-        return f"union_attn_kernel<{d}, {block}>"
+        return f"union_attn_kernel<{d}, {block}, {'true' if fp8 else 'false'}>"
     return f"attn_kernel<{d}, {block}>"
 
 
-def measured_traffic(path, workload, schedule):
+def measured_traffic(path, workload, schedule, values="bf16"):
     """HBM bytes per attention launch from a committed counter summary, or None.
 
     The summary holds FETCH_SIZE + WRITE_SIZE of the attention kernel, scaled by a
@@ -280,7 +314,8 @@ def measured_traffic(path, workload, schedule):
         with open(os.path.join(ROOT, "adaptive_block_sparse_hilbert_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     if (fields.get("attn_src_sha256") != h.hexdigest() or fields.get("workload") != workload
-            or fields.get("schedule") != schedule or "hbm_bytes_per_launch" not in fields):
+            or fields.get("schedule") != schedule or fields.get("values", "bf16") != values
+            or "hbm_bytes_per_launch" not in fields):
         return None
     return int(fields["hbm_bytes_per_launch"])
 

@@ -56,8 +56,13 @@ typedef enum { ABSH_BF16 = 0, ABSH_F32 = 1 } absh_dtype;
 /* Layout of a tensor in Hilbert order written by absh_permute. */
 typedef enum {
   ABSH_ROWS = 0, /* [B, H, n_pad, d] bf16: one row of d per token (queries, keys, outputs) */
-  ABSH_VT = 1    /* [B, H, nb, d, KB] bf16, KB = max(block, 32): each block transposed, keys
+  ABSH_VT = 1,   /* [B, H, nb, d, KB] bf16, KB = max(block, 32): each block transposed, keys
                     fastest, zero keys past `block` (values) */
+  ABSH_VT8 = 2   /* [B, H, n_pad / 64, 64 * d] bytes, written by absh_quantize_v (values in
+                    8-bit floating point): per 64-key step an image of 64*d bytes in which
+                    byte e*32*d + 32*c + 16*(g ^ ((c >> 3) & 1)) + 8*a + i holds channel c
+                    of key 32*e + 16*a + 8*g + i of the step (e, a, g in {0, 1}, i < 8),
+                    as an OCP FP8 E4M3 code of the value divided by the channel's scale */
 } absh_layout;
 
 typedef struct absh_ctx absh_ctx;
@@ -249,6 +254,31 @@ absh_status absh_route(absh_ctx* ctx, const void* qh, const void* kh, int B, int
  * it. */
 absh_status absh_sparse_attn(absh_ctx* ctx, const void* qh, const void* kh, const void* vt, int B, int H,
                              int d, const absh_lists* lists, void* oh, void* stream);
+
+/* V quantization (xllm-io review of FVAttn, "Block-Sparse Attention Execution"
+ * and section 3.4, which quantize V before the sparse attention): from
+ * Hilbert-order values vh ([B, H, n_pad, d] bf16, ABSH_ROWS) write
+ *   vscale[b, h, c] = 2^e, e the smallest integer with max_r |v[b, h, r, c]| * 2^-e <= 448
+ *                     (1 for an all-zero channel), float32 [B, H, d];
+ *   vt8 = E4M3 codes (OCP FP8: bias 7, largest 448, round to nearest, ties to
+ *         even) of v / vscale in the ABSH_VT8 layout, B*H*n_pad*d bytes.
+ * The division by a power of two is exact, so the encoding is the only rounding.
+ * block must be 64 or 128 (n_pad a multiple of 64); d 64 or 128. vscale's memory
+ * serves as scratch during the call. No host synchronisation. */
+absh_status absh_quantize_v(absh_ctx* ctx, const void* vh, int B, int H, int d, void* vt8, float* vscale,
+                            void* stream);
+
+/* absh_sparse_attn with 8-bit values: vt8 and vscale from absh_quantize_v, the
+ * rest as absh_sparse_attn. The value product runs in fp8 (E4M3) with float32
+ * accumulation: each probability, scaled by a power of two so that the row's
+ * reference maximum maps to at least 2^6 and none exceeds 2^8, is rounded to
+ * E4M3, and the row sum adds the same rounded values; the output is multiplied
+ * by the channel scales before its bf16 rounding. Scores and softmax as in
+ * absh_sparse_attn. Group schedules only (ABSH_SCHED_ORDER, _XCD, _RANKS, or
+ * lists == NULL for dense); block 64 or 128. ABSH_EUNSUPPORTED otherwise. */
+absh_status absh_sparse_attn_v8(absh_ctx* ctx, const void* qh, const void* kh, const void* vt8,
+                                const float* vscale, int B, int H, int d, const absh_lists* lists, void* oh,
+                                void* stream);
 
 #ifdef __cplusplus
 }

@@ -726,14 +726,18 @@ def quantized_v(v: np.ndarray) -> np.ndarray:
 
 
 def attention_tile_spread(qh_bh: np.ndarray, kh_bh: np.ndarray, vh_bh: np.ndarray,
-                          block: int, i: int, kv_blocks: Sequence[int]):
-    """Output rows of query block i as in attention_tile, with two spreads of the
-    values around each output under the softmax weights w:
-      A1[r, c] = sum_j w_rj |v_jc - O_rc|,   A2[r, c] = sqrt(sum_j w_rj^2 (v_jc - O_rc)^2).
+                          block: int, i: int, kv_blocks: Sequence[int], small: float = 0.0):
+    """Output rows of query block i as in attention_tile, with spreads of the values
+    around each output under the softmax weights w:
+      A1[r, c] = sum_j w_rj |v_jc - O_rc|,
+      A2[r, c] = sqrt(sum_j w_rj^2 (v_jc - O_rc)^2),
+      As[r, c] = sum over the keys j with w_rj <= small of |v_jc - O_rc|.
     If every unnormalised weight P_j is replaced by P_j (1 + delta_j) with
     |delta_j| <= u and the result renormalised, O moves by at most u / (1 - u) * A1;
     for independent zero-mean delta_j of standard deviation s it moves by about
-    s * A2. Returns (O, A1, A2), each [n_i, d] float64.
+    s * A2; an extra absolute change of at most a in each normalised weight at or
+    below `small` adds at most about a * As. Returns (O, A1, A2, As), each [n_i, d]
+    float64.
     """
     N, d = qh_bh.shape
     rows = slice(i * block, min((i + 1) * block, N))
@@ -746,7 +750,12 @@ def attention_tile_spread(qh_bh: np.ndarray, kh_bh: np.ndarray, vh_bh: np.ndarra
     w = np.exp(s)
     w /= w.sum(axis=1, keepdims=True)
     O = w @ v
-    dev = np.abs(v[None, :, :] - O[:, None, :])          # [n_i, keys, d]
-    A1 = np.einsum("rj,rjc->rc", w, dev)
-    A2 = np.sqrt(np.einsum("rj,rjc->rc", w * w, dev * dev))
-    return O, A1, A2
+    A1 = np.empty_like(O)
+    A2 = np.empty_like(O)
+    As = np.empty_like(O)
+    for r in range(O.shape[0]):                           # one query row at a time keeps memory small
+        dev = np.abs(v - O[r][None, :])                    # [keys, d]
+        A1[r] = w[r] @ dev
+        A2[r] = np.sqrt((w[r] * w[r]) @ (dev * dev))
+        As[r] = (w[r] <= small).astype(np.float64) @ dev
+    return O, A1, A2, As

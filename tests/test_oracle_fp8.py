@@ -133,7 +133,7 @@ def test_spread_bounds_weight_rounding():
     k = rng.standard_normal((N, d)) * 2
     v = rng.standard_normal((N, d)) + 3.0
     kv = [0, 2, 3]
-    O_, A1, A2 = O.attention_tile_spread(q, k, v, block, 1, kv)
+    O_, A1, A2, As = O.attention_tile_spread(q, k, v, block, 1, kv, small=0.02)
     assert np.allclose(O_, O.attention_tile(q, k, v, block, 1, kv), rtol=0, atol=1e-13)
     keys = np.concatenate([np.arange(j * block, (j + 1) * block) for j in kv])
     s = q[block:2 * block] @ k[keys].T / math.sqrt(d)
@@ -151,7 +151,19 @@ def test_spread_bounds_weight_rounding():
         Ot = (Pt @ v[keys][:, c]) / Pt.sum(axis=1)
         assert (np.abs(Ot - O_[:, c]) <= u / (1 - u) * A1[:, c] + 1e-12).all()
         assert (np.abs(Ot - O_[:, c]) >= 0.5 * u * A1[:, c]).all()   # the bound is within a factor ~2 of tight
+    # absolute changes of at most a in the normalised weights at or below `small`
+    a = 1e-3
+    w = P / P.sum(axis=1, keepdims=True)
+    for trial in range(50):
+        dw = np.where(w <= 0.02, rng.uniform(-a, a, w.shape), 0.0)
+        Ot = ((w + dw) @ v[keys]) / (w + dw).sum(axis=1, keepdims=True)
+        lo = 1 - a * (w <= 0.02).sum(axis=1, keepdims=True)     # the renormalisation
+        assert (np.abs(Ot - O_) <= a * As / lo + 1e-12).all()
     # a single key: no spread
-    one = O.attention_tile_spread(q[:1], k[:1], v[:1], 1, 0, [0])
-    assert (one[1] == 0).all() and (one[2] == 0).all()
+    one = O.attention_tile_spread(q[:1], k[:1], v[:1], 1, 0, [0], small=1.0)
+    assert (one[1] == 0).all() and (one[2] == 0).all() and (one[3] == 0).all()
     assert (A2 <= A1 + 1e-15).all()
+    # every key counted when small >= 1, none when small < min weight
+    full = O.attention_tile_spread(q, k, v, block, 1, kv, small=1.0)[3]
+    assert np.allclose(full, np.abs(v[keys][None, :, :] - O_[:, None, :]).sum(axis=1), rtol=1e-12, atol=0)
+    assert (O.attention_tile_spread(q, k, v, block, 1, kv, small=0.0)[3] == 0).all()
