@@ -19,34 +19,60 @@ namespace {
 // ------------------------------------------------------------------ pooling
 
 // xbar[bh, j, c] = (sum over the block's true rows of xh[bh, r, c]) / n_j.
-// One workgroup per (bh, j); one thread per channel.
-__global__ __launch_bounds__(128) void pool_kernel(const bf16_t* __restrict__ xh, float* __restrict__ xbar, int N,
-                                                   int n_pad, int nb, int blk, int d) {
+// One workgroup per (bh, j). Each thread reads 16-byte pieces (8 channels) of
+// every ROWS-th row and keeps eight float64 partial sums; the partials of a
+// channel are then added in LDS. Sums of bf16 values in float64 are exact for
+// any operands whose exponents lie within 45 binades of each other, so the
+// order of the additions does not change the result.
+constexpr int kPoolThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(const bf16_t* __restrict__ xh, float* __restrict__ xbar,
+                                                            int N, int n_pad, int nb, int blk) {
+  constexpr int PIECES = D / 8;
+  constexpr int ROWS = kPoolThreads / PIECES;
+  __shared__ double part[ROWS][D + 1];
   const int j = blockIdx.x % nb;
   const uint64_t bh = blockIdx.x / nb;
-  const int c = threadIdx.x;
-  if (c >= d) return;
-  const int r0 = j * blk;
-  const int n = min(blk, N - r0);
-  const bf16_t* src = xh + (bh * n_pad + r0) * d + c;
-  double acc = 0.0;
-  for (int r = 0; r < n; ++r) acc += (double)bf16_to_f32(src[(size_t)r * d]);
-  xbar[(bh * nb + j) * d + c] = __double2float_rn(acc / (double)n);
+  const int piece = threadIdx.x % PIECES;
+  const int r0 = threadIdx.x / PIECES;
+  const int n = min(blk, N - j * blk);
+  const bf16_t* src = xh + (bh * n_pad + (size_t)j * blk) * D + piece * 8;
+  double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+  for (int r = r0; r < n; r += ROWS) {
+    const uint4 w = *reinterpret_cast<const uint4*>(src + (size_t)r * D);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += (double)bf16_to_f32((bf16_t)(u[e] & 0xFFFFu));
+      acc[2 * e + 1] += (double)bf16_to_f32((bf16_t)(u[e] >> 16));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[r0][piece * 8 + e] = acc[e];
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += kPoolThreads) {
+    double sum = 0.0;
+    for (int r = 0; r < ROWS; ++r) sum += part[r][c];
+    xbar[(bh * nb + j) * D + c] = __double2float_rn(sum / (double)n);
+  }
 }
 
 // ------------------------------------------------------------------ scores
 
 // S[bh, i, j] = float32( sum_c double(qbar[bh,i,c]) * double(kbar[bh,j,c]) / sqrt_d ).
-// 64 x 64 output tile per workgroup, 4 x 4 per thread, channels staged in LDS
-// sixteen at a time as float64.
-constexpr int kTile = 64;
+// 128 x 128 output tile per workgroup, 8 x 8 per thread (rows ty + 16 u, columns
+// tx + 16 v), channels staged in LDS sixteen at a time as float64. Each float32
+// product is exact in float64; only the order of the additions is the kernel's.
+constexpr int kTile = 128;
 constexpr int kDepth = 16;
 
 __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                      float* __restrict__ S, int nb, int d, double sqrt_d,
                                                      int tiles_per_side) {
-  __shared__ double qs[kDepth][kTile + 1];
-  __shared__ double ks[kDepth][kTile + 1];
+  __shared__ double qs[kDepth][kTile];
+  __shared__ double ks[kDepth][kTile];
   const int per_head = tiles_per_side * tiles_per_side;
   const uint64_t bh = blockIdx.x / per_head;
   const int tile = blockIdx.x % per_head;
@@ -55,35 +81,55 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
   const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
   const float* qb = qbar + bh * nb * (size_t)d;
   const float* kb = kbar + bh * nb * (size_t)d;
-  double acc[4][4];
-  for (int a = 0; a < 4; ++a)
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-  // loader: thread -> (row lr, 4 channels at lc)
-  const int lr = threadIdx.x / 4, lc = (threadIdx.x % 4) * 4;
-  for (int c0 = 0; c0 < d; c0 += kDepth) {
-    float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i0 + lr < nb) qv = *reinterpret_cast<const float4*>(qb + (size_t)(i0 + lr) * d + c0 + lc);
-    if (j0 + lr < nb) kv = *reinterpret_cast<const float4*>(kb + (size_t)(j0 + lr) * d + c0 + lc);
-    qs[lc + 0][lr] = qv.x; qs[lc + 1][lr] = qv.y; qs[lc + 2][lr] = qv.z; qs[lc + 3][lr] = qv.w;
-    ks[lc + 0][lr] = kv.x; ks[lc + 1][lr] = kv.y; ks[lc + 2][lr] = kv.z; ks[lc + 3][lr] = kv.w;
-    __syncthreads();
+  double acc[8][8];
 #pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[a][b] = 0.0;
+  // loader: thread -> (row lr, 8 channels at lc)
+  const int lr = threadIdx.x / 2, lc = (threadIdx.x % 2) * 8;
+  for (int c0 = 0; c0 < d; c0 += kDepth) {
+    float4 q0 = make_float4(0.f, 0.f, 0.f, 0.f), q1 = q0, k0 = q0, k1 = q0;
+    if (i0 + lr < nb) {
+      const float4* p = reinterpret_cast<const float4*>(qb + (size_t)(i0 + lr) * d + c0 + lc);
+      q0 = p[0];
+      q1 = p[1];
+    }
+    if (j0 + lr < nb) {
+      const float4* p = reinterpret_cast<const float4*>(kb + (size_t)(j0 + lr) * d + c0 + lc);
+      k0 = p[0];
+      k1 = p[1];
+    }
+    const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qs[lc + e][lr] = qv[e];
+      ks[lc + e][lr] = kv[e];
+    }
+    __syncthreads();
+#pragma unroll 4
     for (int c = 0; c < kDepth; ++c) {
-      double a[4], b[4];
-      for (int u = 0; u < 4; ++u) {
-        a[u] = qs[c][ty * 4 + u];
-        b[u] = ks[c][tx * 4 + u];
+      double a[8], b[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a[u] = qs[c][ty + 16 * u];
+        b[u] = ks[c][tx + 16 * u];
       }
-      for (int u = 0; u < 4; ++u)
-        for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
     }
     __syncthreads();
   }
-  for (int u = 0; u < 4; ++u) {
-    const int i = i0 + ty * 4 + u;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = i0 + ty + 16 * u;
     if (i >= nb) continue;
-    for (int v = 0; v < 4; ++v) {
-      const int j = j0 + tx * 4 + v;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int j = j0 + tx + 16 * v;
       if (j < nb) S[(bh * nb + i) * (size_t)nb + j] = __double2float_rn(acc[u][v] / sqrt_d);
     }
   }
@@ -834,8 +880,14 @@ __global__ void rank_final_kernel(const int32_t* __restrict__ work, const int32_
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_pool(const absh_ctx* c, const void* xh, float* xbar, int B, int H, int d, hipStream_t s) {
-  pool_kernel<<<(unsigned)((uint64_t)B * H * c->nb), 128, 0, s>>>(reinterpret_cast<const bf16_t*>(xh), xbar, c->N,
-                                                                   c->n_pad, c->nb, c->block, d);
+  const unsigned grid = (unsigned)((uint64_t)B * H * c->nb);
+  const bf16_t* x = reinterpret_cast<const bf16_t*>(xh);
+  if (d == 64)
+    pool_kernel<64><<<grid, kPoolThreads, 0, s>>>(x, xbar, c->N, c->n_pad, c->nb, c->block);
+  else if (d == 128)
+    pool_kernel<128><<<grid, kPoolThreads, 0, s>>>(x, xbar, c->N, c->n_pad, c->nb, c->block);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
