@@ -204,3 +204,65 @@ def test_v8_constant_values():
     err = np.abs(o - want[:, None, :, :])
     print(f"[attn v8] constant values: max {err.max():.3e}", flush=True)
     assert (err <= 2.0 ** -8 * np.abs(want[:, None, :, :]) + 1e-6).all()
+
+
+@pytest.mark.parametrize("grid,block,d,H,B", [
+    ((1, 1, 1), 64, 64, 1, 1),       # one token: one partial block
+    ((2, 3, 37), 64, 64, 3, 2),      # d = 64, ragged tail of 30, batch of 2
+    ((4, 4, 4), 64, 128, 2, 1),      # exactly one full block
+    ((5, 6, 7), 64, 128, 2, 1),      # ragged tail of 18
+    ((3, 9, 10), 128, 128, 2, 1),    # block 128, tail of 14: the last block's second half is empty
+    ((2, 5, 13), 128, 64, 2, 2),     # block 128, d = 64, tail of 2
+])
+@pytest.mark.parametrize("schedule", ["xcd", "order", "dense"])
+def test_v8_edge_shapes(grid, block, d, H, B, schedule):
+    T, Y, X = grid
+    N = T * Y * X
+    rng = np.random.default_rng(11)
+    q32 = rng.standard_normal((B, N, H, d)).astype(np.float32) * 2
+    k32 = rng.standard_normal((B, N, H, d)).astype(np.float32) * 2
+    v32 = rng.standard_normal((B, N, H, d)).astype(np.float32) * rng.uniform(0.1, 4.0, d).astype(np.float32)
+    bits = [W.bf16_bits(a) for a in (q32, k32, v32)]
+    ctx = absh.create(T, Y, X, block)
+    qd, kd, vd = (torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(DEV) for b in bits)
+    qh, kh, vh = absh.permute(ctx, qd), absh.permute(ctx, kd), absh.permute(ctx, vd)
+    vt8, vscale = absh.quantize_v(ctx, vh)
+    r = None if schedule == "dense" else absh.route(ctx, qh, kh, 0.7, 2, schedule=schedule)
+    if r is not None:
+        counts, kv, _ = check_lists_valid(r, ctx.nb)
+    o = absh.unpermute(ctx, absh.sparse_attn_v8(ctx, qh, kh, vt8, vscale, r)).float().cpu().numpy()
+    perm, _ = O.hilbert_perm(T, Y, X)
+    hq, hk, hv = (O.to_hilbert(W.bf16_to_f32(b), perm) for b in bits)
+    nb = ctx.nb
+    for b in range(B):
+        for h in range(H):
+            codes, e = O.quantize_v(hv[b, h])
+            v8 = O.dequantize_v(codes, e)
+            for i in range(nb):
+                blocks = range(nb) if r is None else kv[b, h, i, : counts[b, h, i]]
+                ref, A1, A2, As = O.attention_tile_spread(hq[b, h], hk[b, h], v8, block, i, blocks, small=SMALL)
+                rows = perm[i * block: min((i + 1) * block, N)]
+                err = np.abs(o[b, rows, h, :] - ref)
+                bound = ATOL_MAX + U / (1 - U) * A1 + 2.0 ** -16 / (1 - U) * As
+                assert (err <= bound).all(), (b, h, i, float((err - bound).max()))
+                assert err.mean() <= ATOL_MEAN + (U * A2).mean()
+
+
+def test_v8_rejects_unsupported_shapes():
+    # block 16 has no 64-key steps; the longest-first schedule runs single tiles
+    ctx16 = absh.create(2, 3, 5, 16)
+    x = torch.zeros((1, 30, 1, 64), dtype=torch.bfloat16, device=DEV)
+    vh16 = absh.permute(ctx16, x)
+    with pytest.raises(absh.AbshError) as e:
+        absh.quantize_v(ctx16, vh16, out=torch.empty(64 * 64, dtype=torch.uint8, device=DEV),
+                        scale=torch.empty(64, dtype=torch.float32, device=DEV))
+    assert e.value.status == -2
+    ctx = absh.create(2, 3, 37, 64)
+    x = torch.randn((1, ctx.N, 1, 64), device=DEV).to(torch.bfloat16)
+    qh = absh.permute(ctx, x)
+    vt8, vscale = absh.quantize_v(ctx, qh)
+    r = absh.route(ctx, qh, qh, 0.9, 1, schedule="lpt")
+    with pytest.raises(absh.AbshError) as e:
+        absh.sparse_attn_v8(ctx, qh, qh, vt8, vscale, r)
+    assert e.value.status == -2
+    torch.cuda.synchronize()
