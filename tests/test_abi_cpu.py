@@ -150,3 +150,14 @@ def test_struct_layout_matches_header(tmp_path):
         assert int(out[struct]) == ctypes.sizeof(cls), struct
         for n, _ in cls._fields_:
             assert int(out[f"{struct}.{n}"]) == getattr(cls, n).offset, (struct, n)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asking for more exits with a message before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""
