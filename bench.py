@@ -6,7 +6,7 @@ already resident in HBM:
     -> route (block means, block scores, Top-p + floor [+ slack fill], Eq. 1, tile queue)
     -> block-sparse attention over the retained blocks
     -> unpermute the output back to grid order.
-The headline workload is 720p video at 40 heads (grid 21 x 45 x 80 = 75,600 tokens,
+The default workload is 720p video at 40 heads (grid 21 x 45 x 80 = 75,600 tokens,
 d = 128, block 64, p = 0.9, k = 4, longest-first queue).
 
 value = retained FLOPs / step time, where retained FLOPs = sum over tiles and
@@ -78,7 +78,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the path would shard by head across GPUs).", file=sys.stderr)
         sys.exit(2)
 
