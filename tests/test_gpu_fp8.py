@@ -266,3 +266,28 @@ def test_v8_rejects_unsupported_shapes():
         absh.sparse_attn_v8(ctx, qh, qh, vt8, vscale, r)
     assert e.value.status == -2
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("index,strict,policy", [(2, False, "auto"), (3, True, "auto"), (3, False, "rlb")])
+def test_attention_v8_rank_schedule(index, strict, policy):
+    # the rank schedule: segment positions map to heads through head_order (after migration)
+    c = case(index)
+    w = c.w
+    r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, schedule="ranks",
+                   strict_ranks=strict, rank_policy=policy)
+    counts, _, _ = check_lists_valid(r, w.nb)
+    rng = np.random.default_rng(330 + index)
+    flat = counts.reshape(-1)
+    pick = {int(np.argmax(flat)), w.nb - 1, w.tiles - 1} | set(rng.choice(w.tiles, size=5, replace=False).tolist())
+    fp8_attention_check(c, r, sorted(pick), f"{w.name} ranks strict={strict} {policy}")
+
+
+def test_attention_v8_window_anchor():
+    c = case(4)
+    w = c.w
+    r = absh.route(c.ctx, c.qh, c.kh, 0.9, 0, schedule="xcd", router="window-anchor", window=12,
+                   anchor_stride=24, anchor_shift=7, step=2)
+    check_lists_valid(r, w.nb)
+    rng = np.random.default_rng(340)
+    pick = {0, w.nb - 1, w.tiles - 1} | set(rng.choice(w.tiles, size=5, replace=False).tolist())
+    fp8_attention_check(c, r, sorted(pick), f"{w.name} window-anchor")
