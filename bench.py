@@ -169,6 +169,8 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events])) for i, s in enumerate(stages)}
     stage_min = {s: float(np.min([e[i].elapsed_time(e[i + 1]) for e in events])) for i, s in enumerate(stages)}
+    if not fp8:  # no quantization stage with bf16 values
+        del stage_ms["quantize"], stage_min["quantize"]
 
     # retained work of this routing (identical every step: the path is deterministic)
     counts = routing.counts.cpu().numpy().reshape(-1)
