@@ -70,7 +70,10 @@ import numpy as np
 
 
 def hilbert_bits(*extent: int) -> int:
-    """Bits per axis m of the enclosing 2^m cube: m = max(1, ceil(log2(max extent)))."""
+    """Bits per axis m of the enclosing 2^m cube: m = max(1, ceil(log2(max extent))).
+
+    Follows: xllm-io review, 3.1 (Hilbert block organisation); reading: the enclosing 2^m cube.
+    """
     biggest = max(extent)
     m = 1
     while (1 << m) < biggest:
@@ -119,6 +122,7 @@ def hilbert_index(coords: np.ndarray, m: int) -> np.ndarray:
 
 def hilbert_perm(T: int, Y: int, X: int):
     """perm[r] = row-major index (t*Y + y)*X + x of the r-th grid cell in Hilbert order.
+    Follows: xllm-io review, 3.1; alanhou.org explainer, "Core Mechanism", layer 1.
 
     Returns (perm, inv) as int64 arrays, inv = perm^-1.
     """
@@ -139,19 +143,26 @@ def hilbert_perm(T: int, Y: int, X: int):
 
 
 def block_sizes(N: int, b: int) -> np.ndarray:
-    """True token count n_j of each of the ceil(N/b) consecutive blocks (last may be partial)."""
+    """True token count n_j of each of the ceil(N/b) consecutive blocks (last may be partial).
+
+    Follows: xllm-io review, 3.1: consecutive blocks along the curve.
+    """
     nb = -(-N // b)
     starts = np.arange(nb) * b
     return np.minimum(b, N - starts).astype(np.int64)
 
 
 def to_hilbert(x: np.ndarray, perm: np.ndarray) -> np.ndarray:
-    """[B, N, H, d] grid order -> [B, H, N, d] in Hilbert token order."""
+    """[B, N, H, d] grid order -> [B, H, N, d] in Hilbert token order.
+
+    Follows: xllm-io review, 3.1.
+    """
     return np.ascontiguousarray(np.transpose(x[:, perm], (0, 2, 1, 3)))
 
 
 def block_means(xh: np.ndarray, b: int) -> np.ndarray:
     """Mean of each block's rows: [B, H, N, d] -> float32 [B, H, nb, d].
+    Follows: xllm-io review, 三 Stage 1 (block summaries); reading: the arithmetic mean.
 
     The sum is taken in float64 (exact for bf16 rows), divided by the true
     token count in float64 and rounded once to float32.
@@ -167,6 +178,7 @@ def block_means(xh: np.ndarray, b: int) -> np.ndarray:
 
 def block_scores(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
     """s_ij = qbar_i . kbar_j / sqrt(d) per head, float64 products and sums, rounded to float32.
+    Follows: xllm-io review, 三 Stage 1; alanhou.org explainer, "Key Concepts".
 
     qbar, kbar: [..., nb, d] float32. Returns float32 [..., nb, nb].
     """
@@ -178,7 +190,10 @@ def block_scores(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
 
 
 def block_softmax(s: np.ndarray) -> np.ndarray:
-    """Row softmax over key blocks in float64: exp(s - max) / sum."""
+    """Row softmax over key blocks in float64: exp(s - max) / sum.
+
+    Follows: alanhou.org explainer, "Key Concepts" (probabilities over key blocks).
+    """
     s64 = s.astype(np.float64)
     e = np.exp(s64 - s64.max(axis=-1, keepdims=True))
     return e / e.sum(axis=-1, keepdims=True)
@@ -199,6 +214,7 @@ class RowRouting:
 
 def importance_order(P: np.ndarray) -> np.ndarray:
     """Block ids sorted by probability descending, ties broken by the smaller block id.
+    Follows: alanhou.org explainer, "Top-p Routing with Safety Floor".
 
     Works on the last axis of P (any leading shape).
     """
@@ -207,7 +223,10 @@ def importance_order(P: np.ndarray) -> np.ndarray:
 
 
 def topp_count(cdf: np.ndarray, p: float) -> np.ndarray:
-    """c = smallest r (1-based) with cdf_r >= p; nb when p >= 1 or when no prefix reaches p."""
+    """c = smallest r (1-based) with cdf_r >= p; nb when p >= 1 or when no prefix reaches p.
+
+    Follows: alanhou.org explainer, "Top-p Routing with Safety Floor".
+    """
     nb = cdf.shape[-1]
     if p >= 1.0:
         return np.full(cdf.shape[:-1], nb, dtype=np.int64)
@@ -217,12 +236,18 @@ def topp_count(cdf: np.ndarray, p: float) -> np.ndarray:
 
 
 def floor_count(c: np.ndarray, k_floor: int, nb: int) -> np.ndarray:
-    """count' = max(c, min(k, nb))."""
+    """count' = max(c, min(k, nb)).
+
+    Follows: alanhou.org explainer, "Top-p Routing with Safety Floor" (the Top-k floor).
+    """
     return np.maximum(c, min(k_floor, nb)).astype(np.int64)
 
 
 def route_row(s_row: np.ndarray, p: float, k_floor: int) -> RowRouting:
-    """Top-p + floor for one query block's score row (plain, one row at a time)."""
+    """Top-p + floor for one query block's score row (plain, one row at a time).
+
+    Follows: xllm-io review, 三 Stage 1; alanhou.org explainer, "Key Concepts".
+    """
     P = block_softmax(s_row[None, :])[0]
     order = importance_order(P)
     cdf = np.cumsum(P[order])
@@ -249,7 +274,10 @@ class Routing:
 
 
 def route(qh: np.ndarray, kh: np.ndarray, block: int, p: float, k_floor: int) -> Routing:
-    """Stage-1 routing on Hilbert-ordered q, k of shape [B, H, N, d] (float32 values)."""
+    """Stage-1 routing on Hilbert-ordered q, k of shape [B, H, N, d] (float32 values).
+
+    Follows: xllm-io review, 三 Stage 1; alanhou.org explainer, "Key Concepts".
+    """
     B, H, N, d = qh.shape
     sizes = block_sizes(N, block)
     nb = sizes.size
@@ -269,7 +297,10 @@ def route(qh: np.ndarray, kh: np.ndarray, block: int, p: float, k_floor: int) ->
 
 
 def workloads(counts: np.ndarray):
-    """work_h = sum_i count'_{h,i} (exact); L_h = work_h / nb (float32 division)."""
+    """work_h = sum_i count'_{h,i} (exact); L_h = work_h / nb (float32 division).
+
+    Follows: xllm-io review, 核心公式 Eq. 1.
+    """
     nb = counts.shape[-1]
     work = counts.sum(axis=-1).astype(np.int64)
     L = (work.astype(np.float32) / np.float32(nb)).astype(np.float32)
@@ -288,12 +319,16 @@ def imbalance(loads: Sequence[float]) -> float:
 
 
 def slack_budget(counts: np.ndarray, beta: float) -> int:
-    """E = floor(beta * sum count'), in float64."""
+    """E = floor(beta * sum count'), in float64.
+
+    Follows: xllm-io review, 3.3 and the SASA steps of 五, read for one GPU.
+    """
     return int(math.floor(np.float64(beta) * np.float64(int(counts.sum()))))
 
 
 def slack_fill(counts: np.ndarray, beta: float) -> np.ndarray:
     """Heap loop: E times, raise the tile with the smallest (count, tile id) among tiles below nb.
+    Follows: xllm-io review, 3.3 and the SASA steps of 五, read for one GPU.
 
     counts: any shape whose last axis is the nb query blocks of a head; tile id
     is the flat row-major index. Returns the new counts (same shape). Each raise
@@ -316,7 +351,10 @@ def slack_fill(counts: np.ndarray, beta: float) -> np.ndarray:
 
 
 def slack_fill_level(counts: np.ndarray, beta: float) -> np.ndarray:
-    """Closed form of the heap loop: a water level lambda plus a remainder by tile id."""
+    """Closed form of the heap loop: a water level lambda plus a remainder by tile id.
+
+    Follows: xllm-io review, 3.3, read for one GPU.
+    """
     nb = counts.shape[-1]
     flat = counts.reshape(-1).astype(np.int64)
     E = slack_budget(counts, beta)
@@ -346,7 +384,10 @@ def slack_fill_level(counts: np.ndarray, beta: float) -> np.ndarray:
 
 
 def lpt_queue(counts: np.ndarray) -> np.ndarray:
-    """Tile ids (flat row-major) by retained count descending, ties by ascending tile id."""
+    """Tile ids (flat row-major) by retained count descending, ties by ascending tile id.
+
+    Follows: xllm-io review, 3.2 and the RLB steps of 五, read for one GPU.
+    """
     flat = counts.reshape(-1)
     ids = np.arange(flat.size)
     return np.lexsort((ids, -flat)).astype(np.int64)
@@ -354,6 +395,7 @@ def lpt_queue(counts: np.ndarray) -> np.ndarray:
 
 def list_schedule(costs: Sequence[float], order: Sequence[int], workers: int):
     """Greedy list scheduling: each next item goes to the earliest-free worker (ties: lowest id).
+    Follows: R. L. Graham, "Bounds on multiprocessing timing anomalies", 1969; review Eq. 2 for rho.
 
     Returns (per-worker loads, makespan).
     """
@@ -372,7 +414,10 @@ def list_schedule(costs: Sequence[float], order: Sequence[int], workers: int):
 
 
 def anchor_offset(stride: int, shift: int, step: int) -> int:
-    """Offset of the anchor blocks at diffusion step `step`: (step * shift) mod stride (0 without anchors)."""
+    """Offset of the anchor blocks at diffusion step `step`: (step * shift) mod stride (0 without anchors).
+
+    Follows: LVSA note: global anchors rotating across diffusion steps.
+    """
     return (step * shift) % stride if stride > 0 else 0
 
 
@@ -392,7 +437,10 @@ def window_anchor_list(nb: int, i: int, window: int, stride: int, shift: int, st
 
 
 def window_anchor_counts(nb: int, window: int, stride: int, shift: int, step: int) -> np.ndarray:
-    """Retained count of every query block (the same for every head)."""
+    """Retained count of every query block (the same for every head).
+
+    Follows: LVSA note.
+    """
     return np.array([window_anchor_list(nb, i, window, stride, shift, step).size for i in range(nb)],
                     dtype=np.int64)
 
@@ -459,7 +507,10 @@ def rlb_options(work: np.ndarray, owner: np.ndarray, R: int = RANKS):
 
 
 def rlb_space(work: np.ndarray, owner: np.ndarray, R: int = RANKS) -> int:
-    """Number of option combinations RLB enumerates (product of the senders' option counts)."""
+    """Number of option combinations RLB enumerates (product of the senders' option counts).
+
+    Follows: xllm-io review, Eq. 6 (the restricted migration space).
+    """
     n = 1
     for o in rlb_options(work, owner, R)[1]:
         n *= len(o)
@@ -517,6 +568,7 @@ def sasa_budgets(W: np.ndarray, n1: float = SASA_N1, n2: float = SASA_N2) -> np.
 
 def water_fill(flat: np.ndarray, nb: int, E: int) -> np.ndarray:
     """Raise the lightest of the given counts E times by one (ties: lowest position; full ones skipped).
+    Follows: xllm-io review, the SASA steps of 五 (augmentation inside a rank).
 
     Closed form of that loop: the highest level lambda whose need sum max(0,
     lambda - c) is at most E, then one more for the first E - need(lambda) counts
@@ -544,6 +596,7 @@ def water_fill(flat: np.ndarray, nb: int, E: int) -> np.ndarray:
 def rank_stage(counts: np.ndarray, R: int = RANKS, k1: float = RLB_K1, k2: float = RLB_K2,
                n1: float = SASA_N1, n2: float = SASA_N2, policy: Optional[str] = None) -> dict:
     """RLB then SASA over ranks, enabled by the piecewise policy on rho (or a forced policy:
+    Follows: xllm-io review, Eq. 2, 5-10, 3.2 and 3.3.
     'none', 'sasa', 'rlb+sasa', or 'rlb' for migration alone).
 
     counts: [B, H, nb] retained counts after Top-p and the floor. Returns the
@@ -586,6 +639,7 @@ def rank_stage(counts: np.ndarray, R: int = RANKS, k1: float = RLB_K1, k2: float
 def attention_tile(qh_bh: np.ndarray, kh_bh: np.ndarray, vh_bh: np.ndarray,
                    block: int, i: int, kv_blocks: Sequence[int]) -> np.ndarray:
     """Output rows of query block i over the tokens of the given key blocks (float64).
+    Follows: xllm-io review, 三 "Block-Sparse Attention Execution"; alanhou.org explainer, "Core Mechanism", layer 3.
 
     qh_bh, kh_bh, vh_bh: [N, d] one head's rows in Hilbert order.
     Returns [n_i, d].
@@ -606,6 +660,7 @@ def attention_tile(qh_bh: np.ndarray, kh_bh: np.ndarray, vh_bh: np.ndarray,
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, perm: np.ndarray, block: int,
               retained: Optional[callable] = None) -> np.ndarray:
     """Block-sparse attention in grid order: [B, N, H, d] in, float64 [B, N, H, d] out.
+    Follows: xllm-io review, 三 "Block-Sparse Attention Execution"; alanhou.org explainer, "Core Mechanism", layer 3.
 
     retained(b, h, i) gives the key-block ids of tile (b, h, i); None means every block.
     """
@@ -624,6 +679,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, perm: np.ndarray, blo
 
 def retained_flops(sizes: np.ndarray, d: int, tiles) -> float:
     """F_ret = sum over tiles and retained blocks of 4 * n_i * n_j * d (true token counts).
+    Follows: the attention work measure of the benchmark: 4 n_i n_j d per retained pair.
 
     tiles: iterable of (i, retained block ids) pairs.
     """
@@ -673,7 +729,10 @@ def e4m3_encode(x) -> np.ndarray:
 
 
 def e4m3_decode(code) -> np.ndarray:
-    """Values of E4M3 codes as float64 (NaN for 0x7f and 0xff)."""
+    """Values of E4M3 codes as float64 (NaN for 0x7f and 0xff).
+
+    Follows: OCP 8-bit floating point specification, E4M3.
+    """
     c = np.asarray(code, dtype=np.int64)
     ef = (c >> 3) & 15
     m = c & 7
@@ -685,6 +744,7 @@ def e4m3_decode(code) -> np.ndarray:
 
 def v_scale_exponent(amax) -> np.ndarray:
     """Smallest integer e with amax * 2^-e <= 448 (0 where amax is 0).
+    Follows: xllm-io review, "Block-Sparse Attention Execution" and 3.4 (V quantization); reading: power-of-two scales.
 
     With amax = f 2^E, f in [0.5, 1): amax 2^-e <= 0.875 * 2^9 holds for
     E - e <= 9 when f <= 0.875 and for E - e <= 8 otherwise.
@@ -697,6 +757,7 @@ def v_scale_exponent(amax) -> np.ndarray:
 
 def quantize_v(v: np.ndarray):
     """Per-channel E4M3 quantization of one head's values v [n, d].
+    Follows: xllm-io review, "Block-Sparse Attention Execution" and 3.4 (V quantization).
 
     Returns (codes uint8 [n, d], e int64 [d]): codes = E4M3(v * 2^-e) with e from
     the channel's largest magnitude. The scaling by 2^-e is exact, so the only
@@ -709,12 +770,16 @@ def quantize_v(v: np.ndarray):
 
 
 def dequantize_v(codes: np.ndarray, e: np.ndarray) -> np.ndarray:
-    """v~ = E4M3 value of the code times 2^e, exactly (float64)."""
+    """v~ = E4M3 value of the code times 2^e, exactly (float64).
+
+    Follows: xllm-io review, 3.4 (V quantization).
+    """
     return np.ldexp(e4m3_decode(codes), np.asarray(e, dtype=np.int64)[None, :])
 
 
 def quantized_v(v: np.ndarray) -> np.ndarray:
     """Grid-order [B, N, H, d] values replaced by their dequantized E4M3 values, each
+    Follows: xllm-io review, "Block-Sparse Attention Execution" and 3.4 (V quantization).
     (batch, head) with its own per-channel scales over all N tokens (float64)."""
     v = np.asarray(v)
     out = np.empty(v.shape, dtype=np.float64)
@@ -728,6 +793,7 @@ def quantized_v(v: np.ndarray) -> np.ndarray:
 def attention_tile_spread(qh_bh: np.ndarray, kh_bh: np.ndarray, vh_bh: np.ndarray,
                           block: int, i: int, kv_blocks: Sequence[int], small: float = 0.0):
     """Output rows of query block i as in attention_tile, with spreads of the values
+    Follows: xllm-io review, 三 "Block-Sparse Attention Execution" (the attention); the spreads bound weight rounding.
     around each output under the softmax weights w:
       A1[r, c] = sum_j w_rj |v_jc - O_rc|,
       A2[r, c] = sqrt(sum_j w_rj^2 (v_jc - O_rc)^2),
