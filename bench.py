@@ -77,6 +77,10 @@ def parse():
 
 def main():
     args = parse()
+    if args.values == "fp8" and args.schedule == "lpt":
+        print("bench.py: 8-bit values run on the group schedules (order, xcd, ranks), not on single tiles (lpt).",
+              file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the path would shard by head across GPUs).", file=sys.stderr)
