@@ -216,6 +216,10 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
     key[t] = (valid[t] && P[t] != 0.0) ? ordered_bits(s[t]) + 1u : 0u;
   }
 
+  // the Top-p threshold, when the count c came from it (then a count of exactly c
+  // has the same threshold: every key above it and the first ties at it)
+  uint32_t tau_p = 0;
+  bool tau_p_set = false;
   if (!reselect) {
     int c = nb;
     if (p < 1.0) {
@@ -252,14 +256,19 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
           ++m;
         }
         c = n_above + m;
+        tau_p = tau;
+        tau_p_set = true;
       }
     }
     want = max(c, min(k_floor, nb));
+    tau_p_set = tau_p_set && want == c;
   }
 
-  // Top-`want` blocks by (key desc, id asc): count search on the key.
-  uint32_t tau = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  // Top-`want` blocks by (key desc, id asc): count search on the key. When the
+  // floor did not raise the Top-p count, the search would end at the Top-p
+  // threshold (n_above < want <= n_above + n_at there), so it is skipped.
+  uint32_t tau = tau_p_set ? tau_p : 0u;
+  for (int bit = 31; bit >= 0 && !tau_p_set; --bit) {
     const uint32_t cand = tau | (1u << bit);
     int cnt = 0;
 #pragma unroll
