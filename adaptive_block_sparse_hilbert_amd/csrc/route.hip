@@ -141,6 +141,10 @@ __device__ __forceinline__ double wave_sum(double v) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
   return v;
 }
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
@@ -223,13 +227,29 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
   if (!reselect) {
     int c = nb;
     if (p < 1.0) {
+      // Each step compares the mass of {key >= cand} with p. A float32 sum of the
+      // float32-rounded probabilities (at most 32 terms per lane, then a 6-level
+      // tree across the wave) is within (1 + 31 + 6)·2^-24 < 3e-6 of the exact
+      // mass (which is at most 1), so outside 1e-5 of p it takes the same
+      // decision as the float64 sum; inside that band the float64 sum decides.
+      float P32[J];
+#pragma unroll
+      for (int t = 0; t < J; ++t) P32[t] = (float)P[t];
       uint32_t tau = 0;
       for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = tau | (1u << bit);
-        double f = 0.0;
+        float f32 = 0.f;
 #pragma unroll
-        for (int t = 0; t < J; ++t) f += (valid[t] && key[t] >= cand) ? P[t] : 0.0;
-        if (wave_sum(f) >= p) tau = cand;
+        for (int t = 0; t < J; ++t) f32 += (valid[t] && key[t] >= cand) ? P32[t] : 0.f;
+        const double m32 = (double)wave_sum_f32(f32);
+        bool take = m32 >= p;
+        if (fabs(m32 - p) <= 1e-5) {
+          double f = 0.0;
+#pragma unroll
+          for (int t = 0; t < J; ++t) f += (valid[t] && key[t] >= cand) ? P[t] : 0.0;
+          take = wave_sum(f) >= p;
+        }
+        if (take) tau = cand;
       }
       double above = 0.0, at = 0.0, f_tau = 0.0;
       int n_above = 0, n_at = 0;
