@@ -267,6 +267,48 @@ def test_route_deterministic():
             assert torch.equal(x, y)
 
 
+
+@pytest.mark.parametrize("delta", [1e-7, 2e-6])
+def test_route_threshold_next_to_p(delta):
+    """p set a hair below or above an exact prefix mass: the count is decided there.
+
+    Channel 0 alone is non-zero (q = 1, k of Hilbert block j = b_j / 2 with a
+    per-head order of the b_j), so every block mean and every score b_j / 16 is
+    exact in float32 and in float64 alike, and all tiles share one sorted mass
+    curve. With p = cdf_m -/+ delta the fewest blocks reaching p are m, resp. m + 1,
+    for every tile; delta sits inside the error of a float32 sum of the masses.
+    """
+    T, Y, X, block, H, d = 4, 8, 8, 16, 2, 64
+    N = T * Y * X
+    nb = N // block
+    perm, _ = O.hilbert_perm(T, Y, X)
+    ranks = np.stack([np.arange(nb), (np.arange(nb) * 7) % nb])      # head 1: another order
+    qh = np.zeros((1, H, N, d), np.float32)
+    kh = np.zeros((1, H, N, d), np.float32)
+    qh[..., 0] = 1.0
+    for h in range(H):
+        kh[0, h, :, 0] = np.repeat(ranks[h] / 2.0, block)
+    q = np.empty((1, N, H, d), np.float32)
+    k = np.empty((1, N, H, d), np.float32)
+    q[:, perm] = np.transpose(qh, (0, 2, 1, 3))
+    k[:, perm] = np.transpose(kh, (0, 2, 1, 3))
+    ctx = absh.create(T, Y, X, block)
+    qd = absh.permute(ctx, torch.from_numpy(q).to(DEV).bfloat16())
+    kd = absh.permute(ctx, torch.from_numpy(k).to(DEV).bfloat16())
+    cdf = O.route(qh, kh, block, 0.5, 1).cdf[0, 0, 0]
+    for m in (2, 5, 9, 14):
+        for p, want in ((cdf[m - 1] - delta, m), (cdf[m - 1] + delta, m + 1)):
+            R = O.route(qh, kh, block, float(p), 1)
+            assert (R.counts == want).all()
+            r = absh.route(ctx, qd, kd, float(p), 1, schedule="lpt")
+            torch.cuda.synchronize()
+            counts, kv, _ = check_lists_valid(r, nb)
+            assert (counts == want).all(), (m, p, np.unique(counts))
+            for h in range(H):
+                top = np.sort(R.order[0, h, 0, :want])
+                assert (kv[0, h, :, :want] == top).all()
+
+
 # ---------------------------------------------------------------- attention
 
 def attention_errors(c, r, tiles):
