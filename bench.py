@@ -25,9 +25,12 @@ Prints one JSON line. Inputs are synthetic (see workloads/), data = "synthetic".
 from __future__ import annotations
 
 import argparse
+import glob
 import json
 import os
+import re
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -39,6 +42,64 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 # half the attention's FLOPs on each: the time-weighted peak of bf16 Q K^T + fp8 P V
 PEAK_MIXED_TFLOPS = 1.0 / (0.5 / PEAK_BF16_TFLOPS + 0.5 / PEAK_FP8_TFLOPS)
 PEAK_HBM_GBS = 8000.0
+
+
+class ClockSampler(threading.Thread):
+    """Reads the current graphics-clock level from sysfs every `period` seconds until stopped.
+
+    pp_dpm_sclk lists the clock levels and marks the current one with '*'. Host-side
+    reads only: the GPU's work is untouched.
+    """
+
+    def __init__(self, path, period=0.02):
+        super().__init__(daemon=True)
+        self.path, self.period, self.samples = path, period, []
+        self.halt = threading.Event()
+
+    def run(self):
+        while not self.halt.wait(self.period):
+            try:
+                text = open(self.path).read()
+            except OSError:
+                return
+            for line in text.splitlines():
+                m = re.search(r"(\d+)\s*mhz\s*\*\s*$", line, re.IGNORECASE)
+                if m:
+                    self.samples.append(int(m.group(1)))
+
+    def report(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v)}
+
+
+def gpu_sysfs():
+    """(sclk file, power cap in W) of the first GPU card in sysfs; None where the host hides them."""
+    files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not files:
+        return None, None
+    cap = None
+    for f in sorted(glob.glob(os.path.join(os.path.dirname(files[0]), "hwmon", "hwmon*", "power1_cap"))):
+        try:
+            cap = int(open(f).read().strip()) / 1e6
+            break
+        except (OSError, ValueError):
+            pass
+    return files[0], cap
+
+
+def gpu_env(dev, clock, cap):
+    import torch
+
+    props = torch.cuda.get_device_properties(dev)
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        rocm = None
+    return {"device": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hip_runtime": torch.version.hip, "rocm": rocm,
+            "power_cap_w": cap, "sclk_during_timed_steps": clock}
 
 
 def parse():
@@ -164,12 +225,19 @@ def main():
     torch.cuda.synchronize()
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    sclk_file, power_cap = gpu_sysfs()
+    sampler = ClockSampler(sclk_file) if sclk_file else None
     torch.cuda.synchronize()
+    if sampler:
+        sampler.start()
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    if sampler:
+        sampler.halt.set()
+        sampler.join()
     ms_per_step = wall * 1e3 / args.steps
     stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events])) for i, s in enumerate(stages)}
     stage_min = {s: float(np.min([e[i].elapsed_time(e[i + 1]) for e in events])) for i, s in enumerate(stages)}
@@ -187,6 +255,11 @@ def main():
     qi = np.tile(sizes, B * H)
     f_ret = float(4.0 * d * np.sum(qi * kv_tokens))
     density = float(counts.mean() / ctx.nb)
+    L_h = routing.L.cpu().numpy().reshape(-1).astype(np.float64)
+    work = {"sum_counts": int(counts.astype(np.int64).sum()),
+            "L_h": {"min": round(float(L_h.min()), 3), "mean": round(float(L_h.mean()), 3),
+                    "max": round(float(L_h.max()), 3)},
+            "density_h": {"min": round(float(L_h.min()) / ctx.nb, 5), "max": round(float(L_h.max()) / ctx.nb, 5)}}
 
     value = f_ret / (ms_per_step * 1e-3) / 1e12
     attn_tflops = f_ret / (stage_ms["attn"] * 1e-3) / 1e12
@@ -254,6 +327,7 @@ def main():
         },
         "ranks": rank_report(routing, args) if args.schedule == "ranks" else None,
         "density": round(density, 5),
+        "work": work,
         "retained_tflop": round(f_ret / 1e12, 4),
         "dense_tflop": round(n_all / 1e12, 4),
         "stage_ms": {s: round(x, 4) for s, x in stage_ms.items()},
@@ -267,6 +341,7 @@ def main():
         round(dense_ms / (stage_ms["attn"] + stage_ms["route"]), 3),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "env": gpu_env(dev, sampler.report() if sampler else None, power_cap),
     }
     print(json.dumps(out))
 
