@@ -42,6 +42,7 @@
 // LDS layout: rows are stored unpadded (the direct loads write 1 KB runs) and the
 // sixteen-byte chunks of a row are XOR-swizzled by a function of the row, chosen
 // so that the sixteen rows one quarter-wave reads land on distinct banks.
+#include <atomic>
 #include <type_traits>
 
 #include "absh_internal.h"
@@ -466,12 +467,15 @@ template <int D, int BLK, int GROUPS>
 hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B, int H,
                   const AttnLists& L, bool dense, hipStream_t s) {
   using C = Cfg<D, BLK, GROUPS>;
-  static int per_cu = 0;  // resident workgroups per CU for this instantiation
+  // resident workgroups per CU for this instantiation (one gfx950 value; computed once,
+  // an atomic so that concurrent first calls from several threads are well defined)
+  static std::atomic<int> occupancy{0};
+  int per_cu = occupancy.load(std::memory_order_relaxed);
   if (per_cu == 0) {
-    hipError_t e =
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<D, BLK, GROUPS>, C::THREADS, 0);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<D, BLK, GROUPS>, C::THREADS, 0);
     if (e != hipSuccess) return e;
     if (per_cu < 1) per_cu = 1;
+    occupancy.store(per_cu, std::memory_order_relaxed);
   }
   const int members = dense ? C::MEMBERS : L.members;
   const int units = B * H * ((c->nb + members - 1) / members);

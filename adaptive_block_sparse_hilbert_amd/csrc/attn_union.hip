@@ -52,6 +52,7 @@
 // k and K of step k + 1, so a pair (k, k + 1) holds V^T of k, k + 1 and K of
 // k + 1, k + 2; at its barrier it issues V^T of k + 2, k + 3 and K of k + 3, k + 4
 // into the slots the previous pair released, to land before the next pair.
+#include <atomic>
 #include <type_traits>
 
 #include "absh_internal.h"
@@ -581,12 +582,15 @@ template <int D, int BLK, bool F8>
 hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void* vt, const float* vscale, void* oh,
                   int B, int H, const AttnLists& L, bool dense, hipStream_t s) {
   using C = UCfg<D, BLK, F8>;
-  static int per_cu = 0;
+  // resident workgroups per CU for this instantiation (one gfx950 value; computed once,
+  // an atomic so that concurrent first calls from several threads are well defined)
+  static std::atomic<int> occupancy{0};
+  int per_cu = occupancy.load(std::memory_order_relaxed);
   if (per_cu == 0) {
-    hipError_t e =
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, union_attn_kernel<D, BLK, F8>, C::THREADS, 0);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, union_attn_kernel<D, BLK, F8>, C::THREADS, 0);
     if (e != hipSuccess) return e;
     if (per_cu < 1) per_cu = 1;
+    occupancy.store(per_cu, std::memory_order_relaxed);
   }
   const int units = B * H * ((c->nb + C::MEMBERS - 1) / C::MEMBERS);
   const int grid = c->num_cus * per_cu;
