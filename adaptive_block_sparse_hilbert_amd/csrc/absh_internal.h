@@ -54,7 +54,9 @@ struct RouteBuffers {
   int32_t* queue;
   int32_t* target;      // [tiles] slack-fill target counts
   int64_t* slack_info;  // [4] lambda, remainder, E, total
-  int32_t* chunk_hist;  // [chunks][nb + 1]
+  int32_t* chunk_hist;  // [nb + 1][chunks] chunk histograms of counts, bin nb first (LPT queue)
+  int32_t* scan_sums;   // [queue_scan_tiles] totals of the queue scan's tiles
+  int32_t* slack_aux;   // [slack_aux_words] count histogram and per-chunk raised tiles (slack fill)
   int32_t* rank;        // [tiles]
   int32_t* sched;        // [10] queue segment bounds (one segment per XCD) and query blocks per unit
   uint32_t* unit_list;   // [units][nb] union lists of query-block groups
@@ -80,6 +82,8 @@ int unit_count(const absh_ctx* c, int BH, int members);
 hipError_t launch_groups(const absh_ctx* c, const RouteBuffers& rb, int BH, int members, hipStream_t s);
 hipError_t launch_segments(const absh_ctx* c, const RouteBuffers& rb, int BH, int schedule, hipStream_t s);
 int queue_chunks(int tiles);
+int queue_scan_tiles(int tiles, int nb);
+int slack_aux_words(int tiles);
 hipError_t launch_rank_stage(const absh_ctx* c, const RouteBuffers& rb, int BH, const RankOpts& o, hipStream_t s);
 hipError_t launch_rank_fill(const absh_ctx* c, const RouteBuffers& rb, hipStream_t s);
 hipError_t launch_rank_final(const RouteBuffers& rb, int BH, hipStream_t s);

@@ -65,7 +65,7 @@ absh_status check_shape(const absh_ctx* c, int B, int H, int d) {
 
 // Byte offsets of the route workspace regions.
 struct WsLayout {
-  size_t qbar, kbar, S, target, info, chunk_hist, rank, owner, budget, total;
+  size_t qbar, kbar, S, target, info, chunk_hist, scan_sums, slack_aux, rank, owner, budget, total;
 };
 
 WsLayout ws_layout(const absh_ctx* c, int B, int H, int d) {
@@ -78,6 +78,8 @@ WsLayout ws_layout(const absh_ctx* c, int B, int H, int d) {
   w.target = off; off = align_up(off + tiles * sizeof(int32_t));
   w.info = off; off = align_up(off + 4 * sizeof(int64_t));
   w.chunk_hist = off; off = align_up(off + (size_t)absh::queue_chunks((int)tiles) * (c->nb + 1) * sizeof(int32_t));
+  w.scan_sums = off; off = align_up(off + (size_t)absh::queue_scan_tiles((int)tiles, c->nb) * sizeof(int32_t));
+  w.slack_aux = off; off = align_up(off + (size_t)absh::slack_aux_words((int)tiles) * sizeof(int32_t));
   w.rank = off; off = align_up(off + tiles * sizeof(int32_t));
   w.owner = off; off = align_up(off + (size_t)B * H * sizeof(int32_t));
   w.budget = off; off = align_up(off + 8 * sizeof(int64_t));
@@ -329,6 +331,8 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
   rb.target = reinterpret_cast<int32_t*>(base + w.target);
   rb.slack_info = reinterpret_cast<int64_t*>(base + w.info);
   rb.chunk_hist = reinterpret_cast<int32_t*>(base + w.chunk_hist);
+  rb.scan_sums = reinterpret_cast<int32_t*>(base + w.scan_sums);
+  rb.slack_aux = reinterpret_cast<int32_t*>(base + w.slack_aux);
   rb.rank = reinterpret_cast<int32_t*>(base + w.rank);
   rb.sched = out->sched;
   rb.unit_list = out->unit_list;

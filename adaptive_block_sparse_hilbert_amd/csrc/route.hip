@@ -179,6 +179,9 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
 // tied blocks at tau (each of the same probability) as the running sum needs to
 // reach p. The floor then asks for count' = max(c, min(k, nb)) blocks, and the
 // retained set is the top count' blocks, found the same way by counting.
+// wanted counts up to this take the arg-max route
+constexpr int kArgmaxWant = 16;
+
 template <int J>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S, int nb, int tiles, double p,
                                                      int k_floor, int order_depth, int reselect,
@@ -207,17 +210,32 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
   smax = wave_max(smax);
   double P[J];
   uint32_t key[J];
-  double z = 0.0;
+  // A re-selection needs only the keys, and a block's key is 0 only where its
+  // probability underflows to 0. Within 700 of the row's max it cannot: exp then
+  // exceeds 9.8e-305 and the row sum is at most nb <= 2048, so the quotient is a
+  // normal double. The probabilities are computed only where some block lies further down.
+  bool far = false;
 #pragma unroll
-  for (int t = 0; t < J; ++t) {
-    P[t] = valid[t] ? exp((double)s[t] - (double)smax) : 0.0;
-    z += P[t];
-  }
-  z = wave_sum(z);
+  for (int t = 0; t < J; ++t) far = far || (valid[t] && (double)s[t] - (double)smax <= -700.0);
+  if (reselect && !__any(far)) {
 #pragma unroll
-  for (int t = 0; t < J; ++t) {
-    P[t] = P[t] / z;
-    key[t] = (valid[t] && P[t] != 0.0) ? ordered_bits(s[t]) + 1u : 0u;
+    for (int t = 0; t < J; ++t) {
+      P[t] = 0.0;
+      key[t] = valid[t] ? ordered_bits(s[t]) + 1u : 0u;
+    }
+  } else {
+    double z = 0.0;
+#pragma unroll
+    for (int t = 0; t < J; ++t) {
+      P[t] = valid[t] ? exp((double)s[t] - (double)smax) : 0.0;
+      z += P[t];
+    }
+    z = wave_sum(z);
+#pragma unroll
+    for (int t = 0; t < J; ++t) {
+      P[t] = P[t] / z;
+      key[t] = (valid[t] && P[t] != 0.0) ? ordered_bits(s[t]) + 1u : 0u;
+    }
   }
 
   // the Top-p threshold, when the count c came from it (then a count of exactly c
@@ -284,34 +302,58 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
     tau_p_set = tau_p_set && want == c;
   }
 
-  // Top-`want` blocks by (key desc, id asc): count search on the key. When the
-  // floor did not raise the Top-p count, the search would end at the Top-p
-  // threshold (n_above < want <= n_above + n_at there), so it is skipped.
-  uint32_t tau = tau_p_set ? tau_p : 0u;
-  for (int bit = 31; bit >= 0 && !tau_p_set; --bit) {
-    const uint32_t cand = tau | (1u << bit);
-    int cnt = 0;
+  // Top-`want` blocks by (key desc, id asc), as bit t of `takebits` for block
+  // lane + 64 t. A small `want` (the floor, a few slack blocks) takes the arg-max
+  // of (key, -id) want times. Otherwise a count search on the key finds the
+  // want-th key; when the floor did not raise the Top-p count the search would end
+  // at the Top-p threshold (n_above < want <= n_above + n_at there), so it is skipped.
+  uint32_t takebits = 0;
+  if (!tau_p_set && want <= kArgmaxWant) {
+    for (int r = 0; r < want; ++r) {
+      uint64_t best = 0;
 #pragma unroll
-    for (int t = 0; t < J; ++t) cnt += popc64(__ballot(valid[t] && key[t] >= cand));
-    if (cnt >= want) tau = cand;
+      for (int t = 0; t < J; ++t) {
+        const uint64_t cand = ((uint64_t)key[t] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * t));
+        best = (valid[t] && !((takebits >> t) & 1u) && cand > best) ? cand : best;
+      }
+      best = wave_max_u64(best);
+      const int j = (int)(0xFFFFFFFFu - (uint32_t)best);
+      if ((j & 63) == lane) takebits |= 1u << (j >> 6);
+    }
+  } else {
+    uint32_t tau = tau_p_set ? tau_p : 0u;
+    for (int bit = 31; bit >= 0 && !tau_p_set; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int t = 0; t < J; ++t) cnt += popc64(__ballot(valid[t] && key[t] >= cand));
+      if (cnt >= want) tau = cand;
+    }
+    int n_above = 0;
+#pragma unroll
+    for (int t = 0; t < J; ++t) n_above += popc64(__ballot(valid[t] && key[t] > tau));
+    const int ties_needed = want - n_above;
+    int ties_seen = 0;
+    const uint64_t below = lanes_below(lane);
+#pragma unroll
+    for (int t = 0; t < J; ++t) {
+      const bool gt = valid[t] && key[t] > tau;
+      const bool eq = valid[t] && key[t] == tau;
+      const uint64_t eq_mask = __ballot(eq);
+      if (gt || (eq && ties_seen + popc64(eq_mask & below) < ties_needed)) takebits |= 1u << t;
+      ties_seen += popc64(eq_mask);
+    }
   }
-  int n_above = 0;
-#pragma unroll
-  for (int t = 0; t < J; ++t) n_above += popc64(__ballot(valid[t] && key[t] > tau));
-  const int ties_needed = want - n_above;
+  // the list in ascending block id
   int32_t* out = kv_idx + (size_t)row * nb;
-  int written = 0, ties_seen = 0;
+  int written = 0;
   const uint64_t below = lanes_below(lane);
 #pragma unroll
   for (int t = 0; t < J; ++t) {
-    const bool gt = valid[t] && key[t] > tau;
-    const bool eq = valid[t] && key[t] == tau;
-    const uint64_t eq_mask = __ballot(eq);
-    const bool take = gt || (eq && ties_seen + popc64(eq_mask & below) < ties_needed);
+    const bool take = (takebits >> t) & 1u;
     const uint64_t take_mask = __ballot(take);
     if (take) out[written + popc64(take_mask & below)] = lane + 64 * t;
     written += popc64(take_mask);
-    ties_seen += popc64(eq_mask);
   }
   if (lane == 0) counts[row] = want;
 
@@ -374,32 +416,48 @@ __device__ T block_exclusive_scan(T v, T* buf, T& total) {
 
 // ------------------------------------------------------------------ slack fill plan
 
-// One workgroup. E = floor(beta * sum counts) extra blocks; the water level is
-// the largest lambda with need(lambda) = sum_t max(0, lambda - c_t) <= E (tiles
-// at nb never rise); every tile at or below lambda rises to lambda, and the first
+// E = floor(beta * sum counts) extra blocks; the water level is the largest
+// lambda with need(lambda) = sum_t max(0, lambda - c_t) <= E (tiles at nb never
+// rise); every tile at or below lambda rises to lambda, and the first
 // E - need(lambda) of them by tile id take one more. target[t] is the result.
+// Four passes: a histogram of the counts over chunks of kQChunk tiles, the plan
+// (lambda and the remainder) in one workgroup, the chunks' numbers of tiles at or
+// below lambda, and the targets with each tile's rank among those tiles.
 constexpr int kMaxBins = 2049;
+constexpr int kQChunk = 256;
 
-__global__ __launch_bounds__(1024) void slack_plan_kernel(const int32_t* __restrict__ counts, int tiles, int nb,
-                                                          double beta, int32_t* __restrict__ target,
-                                                          int64_t* __restrict__ info) {
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// One workgroup per chunk: an LDS histogram, then one global add per non-empty bin
+// (a chunk's tiles often share one count, e.g. the floor).
+__global__ __launch_bounds__(kQChunk) void slack_hist_kernel(const int32_t* __restrict__ counts, int tiles, int nb,
+                                                             int32_t* __restrict__ hist_g) {
   __shared__ int32_t hist[kMaxBins];
+  for (int b = threadIdx.x; b <= nb; b += kQChunk) hist[b] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kQChunk + threadIdx.x;
+  if (t < tiles) atomicAdd(&hist[counts[t]], 1);
+  __syncthreads();
+  for (int b = threadIdx.x; b <= nb; b += kQChunk)
+    if (hist[b]) atomicAdd(&hist_g[b], hist[b]);
+}
+
+__global__ __launch_bounds__(1024) void slack_plan_kernel(const int32_t* __restrict__ hist_g, int nb, double beta,
+                                                          int64_t* __restrict__ info) {
   __shared__ int64_t buf[1024];
   __shared__ int64_t cnt_lt_s[kMaxBins + 1];
   __shared__ int64_t sum_lt_s[kMaxBins + 1];
-  __shared__ int64_t lam_s, rest_s;
-  for (int b = threadIdx.x; b <= nb; b += 1024) hist[b] = 0;
-  __syncthreads();
-  for (int t = threadIdx.x; t < tiles; t += 1024) atomicAdd(&hist[counts[t]], 1);
-  __syncthreads();
   // exclusive prefix over bins of hist[c] and c*hist[c]: each thread owns a run of bins
   const int bins = nb + 1;
   const int per = (bins + 1023) / 1024;
   const int b0 = threadIdx.x * per;
   int64_t my_cnt = 0, my_sum = 0;
   for (int b = b0; b < min(bins, b0 + per); ++b) {
-    my_cnt += hist[b];
-    my_sum += (int64_t)b * hist[b];
+    my_cnt += hist_g[b];
+    my_sum += (int64_t)b * hist_g[b];
   }
   int64_t tot_cnt, tot_sum;
   int64_t run_cnt = block_exclusive_scan<int64_t>(my_cnt, buf, tot_cnt);
@@ -407,8 +465,8 @@ __global__ __launch_bounds__(1024) void slack_plan_kernel(const int32_t* __restr
   for (int b = b0; b < min(bins, b0 + per); ++b) {
     cnt_lt_s[b] = run_cnt;
     sum_lt_s[b] = run_sum;
-    run_cnt += hist[b];
-    run_sum += (int64_t)b * hist[b];
+    run_cnt += hist_g[b];
+    run_sum += (int64_t)b * hist_g[b];
   }
   __syncthreads();
   const int64_t E = (int64_t)floor(beta * (double)tot_sum);
@@ -419,34 +477,68 @@ __global__ __launch_bounds__(1024) void slack_plan_kernel(const int32_t* __restr
   block_exclusive_scan<int64_t>(ok, buf, n_ok);
   if (threadIdx.x == 0) {
     const int64_t lam = n_ok - 1;
-    lam_s = lam;
-    rest_s = E - (lam * cnt_lt_s[lam] - sum_lt_s[lam]);
     info[0] = lam;
-    info[1] = rest_s;
+    info[1] = E - (lam * cnt_lt_s[lam] - sum_lt_s[lam]);
     info[2] = E;
     info[3] = tot_sum;
   }
+}
+
+// Tiles of this workgroup's chunk that the water level raises (count <= lambda < nb).
+__device__ __forceinline__ bool slack_low(int t, int tiles, int nb, int64_t lam, const int32_t* counts) {
+  return t < tiles && lam < nb && counts[t] <= lam;
+}
+
+// Sum over the workgroup (kQChunk threads = 4 waves) through `red`.
+__device__ __forceinline__ int64_t chunk_sum(int64_t v, int64_t* red) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  const int lam = (int)lam_s;
-  const int64_t rest = rest_s;
-  int64_t seen = 0;
-  for (int base = 0; base < tiles; base += 1024) {
-    const int t = base + threadIdx.x;
-    const int c = t < tiles ? counts[t] : nb;
-    const int64_t low = (lam < nb && c <= lam) ? 1 : 0;
-    int64_t chunk_total;
-    const int64_t rank = seen + block_exclusive_scan<int64_t>(low, buf, chunk_total);
-    if (t < tiles) target[t] = lam >= nb ? nb : (low ? lam + (rank < rest ? 1 : 0) : c);
-    seen += chunk_total;
-  }
+  const int64_t all = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return all;
+}
+
+__global__ __launch_bounds__(kQChunk) void slack_low_kernel(const int32_t* __restrict__ counts, int tiles, int nb,
+                                                            const int64_t* __restrict__ info,
+                                                            int32_t* __restrict__ low_cnt) {
+  __shared__ int64_t red[4];
+  const int t = blockIdx.x * kQChunk + threadIdx.x;
+  const int64_t all = chunk_sum(slack_low(t, tiles, nb, info[0], counts) ? 1 : 0, red);
+  if (threadIdx.x == 0) low_cnt[blockIdx.x] = (int32_t)all;
+}
+
+__global__ __launch_bounds__(kQChunk) void slack_target_kernel(const int32_t* __restrict__ counts, int tiles,
+                                                               int nb, const int64_t* __restrict__ info,
+                                                               const int32_t* __restrict__ low_cnt,
+                                                               int32_t* __restrict__ target) {
+  __shared__ int64_t red[4];
+  __shared__ int32_t wave_low[4];
+  const int64_t lam = info[0], rest = info[1];
+  // raised tiles in the chunks before this one
+  int64_t before = 0;
+  for (int ch = threadIdx.x; ch < (int)blockIdx.x; ch += kQChunk) before += low_cnt[ch];
+  before = chunk_sum(before, red);
+  const int t = blockIdx.x * kQChunk + threadIdx.x;
+  const bool low = slack_low(t, tiles, nb, lam, counts);
+  // rank among the chunk's raised tiles: earlier waves, then earlier lanes of this wave
+  const uint64_t mask = __ballot(low);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) wave_low[wave] = __popcll(mask);
+  __syncthreads();
+  int64_t rank = before + __popcll(mask & ((1ull << lane) - 1ull));
+  for (int v = 0; v < wave; ++v) rank += wave_low[v];
+  if (t < tiles) target[t] = lam >= nb ? nb : (low ? (int32_t)lam + (rank < rest ? 1 : 0) : counts[t]);
 }
 
 // ------------------------------------------------------------------ tile queue
 
-constexpr int kQChunk = 256;
-
+// Longest first, ties by tile id: a counting sort over chunks of kQChunk tiles.
+// Each chunk's histogram of counts goes to hist[(nb - c) * chunks + chunk], so an
+// exclusive scan of the flat array gives, for each (count, chunk), the number of
+// tiles that precede that chunk's tiles of that count in the queue.
 __global__ __launch_bounds__(kQChunk) void queue_hist_kernel(const int32_t* __restrict__ counts, int tiles, int nb,
-                                                             int32_t* __restrict__ chunk_hist,
+                                                             int chunks, int32_t* __restrict__ hist_flat,
                                                              int32_t* __restrict__ rank) {
   __shared__ int32_t c[kQChunk];
   __shared__ int32_t hist[kMaxBins];
@@ -462,49 +554,67 @@ __global__ __launch_bounds__(kQChunk) void queue_hist_kernel(const int32_t* __re
     atomicAdd(&hist[mine], 1);
   }
   __syncthreads();
-  int32_t* row = chunk_hist + (size_t)blockIdx.x * (nb + 1);
-  for (int b = threadIdx.x; b <= nb; b += kQChunk) row[b] = hist[b];
+  for (int b = threadIdx.x; b <= nb; b += kQChunk) hist_flat[(size_t)(nb - b) * chunks + blockIdx.x] = hist[b];
 }
 
-// Turn per-chunk histograms into output offsets: bins in descending count,
-// chunks (tile-id order) in ascending order within a bin. Thread u owns the
-// bin positions q = nb - b in [u * per, (u + 1) * per).
-__global__ __launch_bounds__(1024) void queue_scan_kernel(int32_t* __restrict__ chunk_hist, int chunks, int nb) {
-  __shared__ int64_t buf[1024];
-  __shared__ int64_t bin_total[kMaxBins];
-  const int bins = nb + 1;
-  const int per = (bins + 1023) / 1024;
-  const int q0 = threadIdx.x * per, q1 = min(bins, q0 + per);
-  int64_t my_total = 0;
-  for (int q = q0; q < q1; ++q) {
-    const int b = nb - q;
-    int64_t off = 0;
-    for (int ch = 0; ch < chunks; ++ch) {
-      int32_t* cell = chunk_hist + (size_t)ch * bins + b;
-      const int32_t v = *cell;
-      *cell = (int32_t)off;
-      off += v;
-    }
-    bin_total[b] = off;
-    my_total += off;
+// Exclusive scan of n ints in tiles of kScanTile: each workgroup scans its tile in
+// place and writes the tile's total to sums[tile].
+constexpr int kScanPer = 8;
+constexpr int kScanTile = 256 * kScanPer;
+
+__global__ __launch_bounds__(256) void scan_tile_kernel(int32_t* __restrict__ a, size_t n,
+                                                        int32_t* __restrict__ sums) {
+  __shared__ int32_t wave_tot[4];
+  const size_t base = (size_t)blockIdx.x * kScanTile + (size_t)threadIdx.x * kScanPer;
+  int32_t v[kScanPer];
+  int32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    v[i] = base + i < n ? a[base + i] : 0;
+    mine += v[i];
   }
-  int64_t all;
-  int64_t base = block_exclusive_scan<int64_t>(my_total, buf, all);
-  for (int q = q0; q < q1; ++q) {
-    const int b = nb - q;
-    for (int ch = 0; ch < chunks; ++ch) chunk_hist[(size_t)ch * bins + b] += (int32_t)base;
-    base += bin_total[b];
+  // inclusive scan of the threads' totals within the wave, then across the 4 waves
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t incl = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t up = __shfl_up(incl, off);
+    if (lane >= off) incl += up;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int32_t run = incl - mine;
+  for (int w = 0; w < wave; ++w) run += wave_tot[w];
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    if (base + i < n) a[base + i] = run;
+    run += v[i];
+  }
+  if (threadIdx.x == 255) sums[blockIdx.x] = run;
+}
+
+// Exclusive scan of the m tile totals in place (one workgroup, batches of 1024).
+__global__ __launch_bounds__(1024) void scan_sums_kernel(int32_t* __restrict__ sums, int m) {
+  __shared__ int64_t buf[1024];
+  int64_t carry = 0;
+  for (int b = 0; b < m; b += 1024) {
+    const int i = b + threadIdx.x;
+    const int64_t v = i < m ? sums[i] : 0;
+    int64_t tot;
+    const int64_t ex = block_exclusive_scan<int64_t>(v, buf, tot);
+    if (i < m) sums[i] = (int32_t)(carry + ex);
+    carry += tot;
   }
 }
 
 __global__ __launch_bounds__(256) void queue_scatter_kernel(const int32_t* __restrict__ counts, int tiles, int nb,
-                                                            const int32_t* __restrict__ chunk_hist,
+                                                            int chunks, const int32_t* __restrict__ hist_flat,
+                                                            const int32_t* __restrict__ sums,
                                                             const int32_t* __restrict__ rank,
                                                             int32_t* __restrict__ queue) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= tiles) return;
-  const int ch = t / kQChunk;
-  queue[chunk_hist[(size_t)ch * (nb + 1) + counts[t]] + rank[t]] = t;
+  const size_t pos = (size_t)(nb - counts[t]) * chunks + t / kQChunk;
+  queue[hist_flat[pos] + sums[pos / kScanTile] + rank[t]] = t;
 }
 
 __global__ __launch_bounds__(256) void queue_identity_kernel(int tiles, int32_t* __restrict__ queue) {
@@ -948,7 +1058,14 @@ hipError_t launch_select(const absh_ctx* c, const RouteBuffers& rb, int tiles, d
 }
 
 hipError_t launch_slack_plan(const absh_ctx* c, const RouteBuffers& rb, int tiles, double beta, hipStream_t s) {
-  slack_plan_kernel<<<1, 1024, 0, s>>>(rb.counts, tiles, c->nb, beta, rb.target, rb.slack_info);
+  const int chunks = queue_chunks(tiles);
+  int32_t* hist_g = rb.slack_aux;            // [nb + 1]
+  int32_t* low_cnt = rb.slack_aux + kMaxBins;  // [chunks]
+  zero_i32_kernel<<<(c->nb + 1 + 255) / 256, 256, 0, s>>>(hist_g, c->nb + 1);
+  slack_hist_kernel<<<chunks, kQChunk, 0, s>>>(rb.counts, tiles, c->nb, hist_g);
+  slack_plan_kernel<<<1, 1024, 0, s>>>(hist_g, c->nb, beta, rb.slack_info);
+  slack_low_kernel<<<chunks, kQChunk, 0, s>>>(rb.counts, tiles, c->nb, rb.slack_info, low_cnt);
+  slack_target_kernel<<<chunks, kQChunk, 0, s>>>(rb.counts, tiles, c->nb, rb.slack_info, low_cnt, rb.target);
   return hipGetLastError();
 }
 
@@ -987,6 +1104,12 @@ hipError_t launch_window_anchor(const absh_ctx* c, const RouteBuffers& rb, int t
 
 int queue_chunks(int tiles) { return (tiles + kQChunk - 1) / kQChunk; }
 
+int queue_scan_tiles(int tiles, int nb) {
+  return (int)(((size_t)queue_chunks(tiles) * (nb + 1) + kScanTile - 1) / kScanTile);
+}
+
+int slack_aux_words(int tiles) { return kMaxBins + queue_chunks(tiles); }
+
 int unit_members(const absh_ctx* c, int schedule) {
   if (schedule == ABSH_SCHED_LPT) return 1;
   return c->block >= 128 ? 2 : 4;
@@ -1024,9 +1147,13 @@ hipError_t launch_queue(const absh_ctx* c, const RouteBuffers& rb, int tiles, in
     return hipGetLastError();
   }
   const int chunks = queue_chunks(tiles);
-  queue_hist_kernel<<<chunks, kQChunk, 0, s>>>(rb.counts, tiles, c->nb, rb.chunk_hist, rb.rank);
-  queue_scan_kernel<<<1, 1024, 0, s>>>(rb.chunk_hist, chunks, c->nb);
-  queue_scatter_kernel<<<grid, 256, 0, s>>>(rb.counts, tiles, c->nb, rb.chunk_hist, rb.rank, rb.queue);
+  const size_t n = (size_t)chunks * (c->nb + 1);
+  const int scan_tiles = queue_scan_tiles(tiles, c->nb);
+  queue_hist_kernel<<<chunks, kQChunk, 0, s>>>(rb.counts, tiles, c->nb, chunks, rb.chunk_hist, rb.rank);
+  scan_tile_kernel<<<scan_tiles, 256, 0, s>>>(rb.chunk_hist, n, rb.scan_sums);
+  scan_sums_kernel<<<1, 1024, 0, s>>>(rb.scan_sums, scan_tiles);
+  queue_scatter_kernel<<<grid, 256, 0, s>>>(rb.counts, tiles, c->nb, chunks, rb.chunk_hist, rb.scan_sums, rb.rank,
+                                            rb.queue);
   return hipGetLastError();
 }
 

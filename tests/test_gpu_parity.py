@@ -252,6 +252,29 @@ def test_slack_fill_matches_oracle():
     assert np.array_equal(work, c1.sum(-1))
 
 
+
+@pytest.mark.parametrize("index,p,beta", [(0, 0.9, 0.3), (0, 0.99, 0.99), (1, 0.9, 0.02), (1, 0.9, 0.5),
+                                          (1, 0.995, 0.99), (4, 0.8, 0.1)])
+def test_slack_fill_sweep(index, p, beta):
+    """Slack fill and longest-first queue over one chunk (32 tiles) and many (6,144 and
+    18,432 tiles, ragged last chunk), from a sliver of slack to a budget that fills
+    most tiles up to nb: counts equal the closed-form water level exactly, the queue
+    equals the stable longest-first order of the new counts."""
+    c = case(index)
+    w = c.w
+    base = absh.route(c.ctx, c.qh, c.kh, p, w.k_floor, slack_frac=0.0, schedule="lpt")
+    filled = absh.route(c.ctx, c.qh, c.kh, p, w.k_floor, slack_frac=beta, schedule="lpt")
+    torch.cuda.synchronize()
+    c0, _, _ = check_lists_valid(base, w.nb)
+    c1, _, q1 = check_lists_valid(filled, w.nb)
+    want = O.slack_fill_level(c0, beta)
+    print(f"[slack sweep] {w.name} p={p} beta={beta}: E {O.slack_budget(c0, beta)}, "
+          f"tiles at nb {(want == w.nb).mean():.3f}")
+    assert np.array_equal(c1, want)
+    assert np.array_equal(q1, O.lpt_queue(c1))
+    assert np.array_equal(filled.work.cpu().numpy(), c1.sum(-1))
+
+
 def test_route_deterministic():
     c = case(1)
     w = c.w
