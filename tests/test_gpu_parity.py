@@ -476,6 +476,53 @@ def test_schedules_bit_identical(index):
 
 # ---------------------------------------------------------------- edge shapes
 
+
+@pytest.mark.parametrize("grid,block,d,H,p,k", [
+    ((16, 128, 128), 128, 64, 1, 0.9, 4),   # nb = 2048, the router's maximum, all blocks full
+    ((16, 127, 127), 128, 128, 1, 0.8, 8),  # nb = 2017, ragged tail of 16 tokens
+    ((5, 20, 40), 16, 64, 2, 0.9, 2),       # nb = 250
+    ((9, 30, 41), 16, 128, 2, 0.95, 3),     # nb = 692, ragged tail of 14
+])
+@pytest.mark.parametrize("schedule", ["xcd", "lpt"])
+def test_block_counts_up_to_the_maximum(grid, block, d, H, p, k, schedule):
+    """Routing and attention at block counts that use every row width of the
+    selection (up to nb = 2048): lists against the oracle's (the routing rule's
+    excuses apply), sampled tiles against its attention."""
+    T, Y, X = grid
+    N = T * Y * X
+    print(f"[max-blocks] grid {grid} block {block} d {d} H {H} schedule {schedule}", flush=True)
+    rng = np.random.default_rng(11)
+    q32 = rng.standard_normal((1, N, H, d)).astype(np.float32) * 2
+    k32 = rng.standard_normal((1, N, H, d)).astype(np.float32) * 2
+    v32 = rng.standard_normal((1, N, H, d)).astype(np.float32)
+    bits = [W.bf16_bits(a) for a in (q32, k32, v32)]
+    ctx = absh.create(T, Y, X, block)
+    nb = ctx.nb
+    qd, kd, vd = (to_dev_bf16(b) for b in bits)
+    qh, kh = absh.permute(ctx, qd), absh.permute(ctx, kd)
+    vt = absh.permute(ctx, vd, layout=absh.ABSH_VT)
+    r = absh.route(ctx, qh, kh, p, k, schedule=schedule)
+    counts, kv, _ = check_lists_valid(r, nb)
+    perm, _ = O.hilbert_perm(T, Y, X)
+    hq, hk, hv = (O.to_hilbert(W.bf16_to_f32(b), perm) for b in bits)
+    R = O.route(hq, hk, block, p, k)
+    excused, failures = compare_routing(R, counts, kv, p)
+    assert not failures, failures[:5]
+    assert excused <= 0.01 * counts.size
+    oh = absh.sparse_attn(ctx, qh, kh, vt, r)
+    o = absh.unpermute(ctx, oh).float().cpu().numpy()
+    flat = counts.reshape(-1)
+    pick = sorted({0, nb - 1, int(np.argmax(flat)), int(np.argmin(flat)), flat.size - 1}
+                  | set(rng.choice(flat.size, size=4, replace=False).tolist()))
+    kvf = kv.reshape(flat.size, nb)
+    for t in pick:
+        h, i = divmod(t, nb)
+        ref = O.attention_tile(hq[0, h], hk[0, h], hv[0, h], block, i, kvf[t, : flat[t]])
+        rows = perm[i * block: min((i + 1) * block, N)]
+        e = np.abs(o[0, rows, h, :] - ref)
+        assert e.max() <= ATOL_MAX and e.mean() <= ATOL_MEAN, (t, e.max(), e.mean())
+
+
 @pytest.mark.parametrize("grid,block,d,H,B,p,k", [
     ((1, 1, 1), 16, 64, 1, 1, 0.9, 2),      # one token, one partial block
     ((2, 3, 5), 16, 64, 2, 2, 0.5, 0),      # N = 30 < 2 blocks, batch of 2
