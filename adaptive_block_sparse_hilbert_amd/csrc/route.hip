@@ -62,30 +62,39 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const bf16_t* __rest
 // ------------------------------------------------------------------ scores
 
 // S[bh, i, j] = float32( sum_c double(qbar[bh,i,c]) * double(kbar[bh,j,c]) / sqrt_d ).
-// 128 x 128 output tile per workgroup, 8 x 8 per thread (rows ty + 16 u, columns
-// tx + 16 v), channels staged in LDS sixteen at a time as float64. Each float32
-// product is exact in float64; only the order of the additions is the kernel's.
+// 128 x 128 output tile per workgroup; wave w takes the 64 x 64 quadrant (w / 2, w % 2)
+// as 4 x 4 tiles of the float64 MFMA D(16x16) += A(16x4) B(4x16), with A = block means
+// of q (rows i, channels) and B = block means of k (channels, columns j). Channels
+// are staged in LDS sixteen at a time as float64. Each float32 product is exact in
+// float64; only the order of the additions is the kernel's.
+// MFMA operand layout (lane l): A[l % 16][l / 16], B[l / 16][l % 16]; result element
+// v of lane l is D[4 v + l / 16][l % 16].
 constexpr int kTile = 128;
 constexpr int kDepth = 16;
+constexpr int kLdsRow = kTile + 4;  // doubles per staged channel (padding spreads the four lane groups)
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                      float* __restrict__ S, int nb, int d, double sqrt_d,
                                                      int tiles_per_side) {
-  __shared__ double qs[kDepth][kTile];
-  __shared__ double ks[kDepth][kTile];
+  __shared__ double qs[kDepth][kLdsRow];
+  __shared__ double ks[kDepth][kLdsRow];
   const int per_head = tiles_per_side * tiles_per_side;
   const uint64_t bh = blockIdx.x / per_head;
   const int tile = blockIdx.x % per_head;
   const int i0 = (tile / tiles_per_side) * kTile;
   const int j0 = (tile % tiles_per_side) * kTile;
-  const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
+  const int r16 = lane & 15, k4 = lane >> 4;
   const float* qb = qbar + bh * nb * (size_t)d;
   const float* kb = kbar + bh * nb * (size_t)d;
-  double acc[8][8];
+  f64x4 acc[4][4];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = 0.0;
+    for (int b = 0; b < 4; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
   // loader: thread -> (row lr, 8 channels at lc)
   const int lr = threadIdx.x / 2, lc = (threadIdx.x % 2) * 8;
   for (int c0 = 0; c0 < d; c0 += kDepth) {
@@ -108,31 +117,33 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
       ks[lc + e][lr] = kv[e];
     }
     __syncthreads();
-#pragma unroll 4
-    for (int c = 0; c < kDepth; ++c) {
-      double a[8], b[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        a[u] = qs[c][ty + 16 * u];
-        b[u] = ks[c][tx + 16 * u];
+    for (int c = 0; c < kDepth; c += 4) {
+      double a[4], b[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        a[t] = qs[c + k4][wr + 16 * t + r16];
+        b[t] = ks[c + k4][wc + 16 * t + r16];
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int v = 0; v < 8; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+        for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[u], b[v], acc[u][v], 0, 0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int i = i0 + ty + 16 * u;
-    if (i >= nb) continue;
+  for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int j = j0 + tx + 16 * v;
-      if (j < nb) S[(bh * nb + i) * (size_t)nb + j] = __double2float_rn(acc[u][v] / sqrt_d);
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + wr + 16 * u + 4 * e + k4;
+      if (i >= nb) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = j0 + wc + 16 * v + r16;
+        if (j < nb) S[(bh * nb + i) * (size_t)nb + j] = __double2float_rn(acc[u][v][e] / sqrt_d);
+      }
     }
-  }
 }
 
 // ------------------------------------------------------------------ Top-p select
