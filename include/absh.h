@@ -24,8 +24,10 @@
  *    rows N..n_pad-1 are zero. nb = ceil(N / block) blocks of `block` tokens;
  *    block j holds Hilbert positions [j*block, min((j+1)*block, N)).
  *  - A tile is one (batch b, head h, query block i); its id is (b*H + h)*nb + i.
- *  - Calls on one context must not overlap in time (the attention kernel's
- *    tile counters live in the context); use one context per stream.
+ *  - Attention calls (absh_sparse_attn, absh_sparse_attn_v8) on one context
+ *    must not overlap in time: the attention kernels' tile counters live in the
+ *    context. Every other call only reads the context and may run on another
+ *    stream concurrently with any call on the same context.
  *  - Arguments are validated on the host before any HIP call; a failure returns
  *    ABSH_EINVAL / ABSH_EUNSUPPORTED / ABSH_EWORKSPACE and launches nothing.
  *    HIP failures return ABSH_EHIP. absh_last_error() gives the detail of the
