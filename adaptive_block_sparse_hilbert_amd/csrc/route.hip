@@ -409,20 +409,31 @@ __global__ __launch_bounds__(256) void workload_kernel(const int32_t* __restrict
 
 // ------------------------------------------------------------------ block-wide scans (1024 threads)
 
+// Exclusive prefix sum over the 1024 threads of the workgroup (integer types, so
+// the result does not depend on the order of the additions) and the total: an
+// inclusive scan within each wave by shuffles, then the 16 wave totals through
+// buf[0..15]. Every thread of the workgroup must call it.
 template <typename T>
 __device__ T block_exclusive_scan(T v, T* buf, T& total) {
-  buf[threadIdx.x] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const T add = threadIdx.x >= (unsigned)off ? buf[threadIdx.x - off] : (T)0;
-    __syncthreads();
-    buf[threadIdx.x] += add;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  T incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T up = __shfl_up(incl, off);
+    if (lane >= off) incl += up;
   }
-  const T incl = buf[threadIdx.x];
-  total = buf[1023];
+  if (lane == 63) buf[wave] = incl;
   __syncthreads();
-  return incl - v;
+  T base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const T t = buf[w];
+    base += w < wave ? t : (T)0;
+    all += t;
+  }
+  total = all;
+  __syncthreads();  // buf is free again for the next call
+  return base + incl - v;
 }
 
 // ------------------------------------------------------------------ slack fill plan
