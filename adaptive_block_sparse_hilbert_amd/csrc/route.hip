@@ -219,22 +219,22 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
 #pragma unroll
   for (int t = 0; t < J; ++t) smax = fmaxf(smax, s[t]);
   smax = wave_max(smax);
+  // Probabilities. The float64 softmax is the definition; a float32 one (the
+  // exponent s - smax in float32, v_exp_f32, the row sum per lane then across the
+  // wave) carries a relative error below 2e-6 per block plus 1.8e-7 times
+  // |s - smax|, so any mass it sums is within 5.4e-6 of the exact one (the mean of
+  // |s - smax| under the softmax is at most ln nb < 7.7). Decisions further than
+  // kBand from p are therefore the float64 ones; closer ones, and ties at the
+  // threshold, take the float64 probabilities, computed for the row on first need.
+  // A block's key is 0 only where its float64 probability underflows to 0, which
+  // cannot happen within 700 of the row's max (exp > 9.8e-305, row sum <= 2048);
+  // rows with a block further down take the float64 path from the start.
+  constexpr double kBand = 2e-5;
   double P[J];
+  float P32[J];
   uint32_t key[J];
-  // A re-selection needs only the keys, and a block's key is 0 only where its
-  // probability underflows to 0. Within 700 of the row's max it cannot: exp then
-  // exceeds 9.8e-305 and the row sum is at most nb <= 2048, so the quotient is a
-  // normal double. The probabilities are computed only where some block lies further down.
-  bool far = false;
-#pragma unroll
-  for (int t = 0; t < J; ++t) far = far || (valid[t] && (double)s[t] - (double)smax <= -700.0);
-  if (reselect && !__any(far)) {
-#pragma unroll
-    for (int t = 0; t < J; ++t) {
-      P[t] = 0.0;
-      key[t] = valid[t] ? ordered_bits(s[t]) + 1u : 0u;
-    }
-  } else {
+  bool have64 = false;
+  auto exact = [&]() __attribute__((always_inline)) {
     double z = 0.0;
 #pragma unroll
     for (int t = 0; t < J; ++t) {
@@ -243,9 +243,32 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
     }
     z = wave_sum(z);
 #pragma unroll
+    for (int t = 0; t < J; ++t) P[t] = P[t] / z;
+    have64 = true;
+  };
+  bool far = false;
+#pragma unroll
+  for (int t = 0; t < J; ++t) far = far || (valid[t] && (double)s[t] - (double)smax <= -700.0);
+  if (__any(far)) {
+    exact();
+#pragma unroll
     for (int t = 0; t < J; ++t) {
-      P[t] = P[t] / z;
       key[t] = (valid[t] && P[t] != 0.0) ? ordered_bits(s[t]) + 1u : 0u;
+      P32[t] = (float)P[t];
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < J; ++t) key[t] = valid[t] ? ordered_bits(s[t]) + 1u : 0u;
+    if (!reselect) {  // a re-selection needs only the keys
+      float z32 = 0.f;
+#pragma unroll
+      for (int t = 0; t < J; ++t) {
+        P32[t] = valid[t] ? __builtin_amdgcn_exp2f((s[t] - smax) * 1.44269504f) : 0.f;
+        z32 += P32[t];
+      }
+      const float inv = 1.f / wave_sum_f32(z32);
+#pragma unroll
+      for (int t = 0; t < J; ++t) P32[t] *= inv;
     }
   }
 
@@ -256,57 +279,69 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
   if (!reselect) {
     int c = nb;
     if (p < 1.0) {
-      // Each step compares the mass of {key >= cand} with p. A float32 sum of the
-      // float32-rounded probabilities (at most 32 terms per lane, then a 6-level
-      // tree across the wave) is within (1 + 31 + 6)·2^-24 < 3e-6 of the exact
-      // mass (which is at most 1), so outside 1e-5 of p it takes the same
-      // decision as the float64 sum; inside that band the float64 sum decides.
-      float P32[J];
-#pragma unroll
-      for (int t = 0; t < J; ++t) P32[t] = (float)P[t];
+      // each step: is the mass of {key >= cand} at least p?
       uint32_t tau = 0;
       for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = tau | (1u << bit);
         float f32 = 0.f;
 #pragma unroll
-        for (int t = 0; t < J; ++t) f32 += (valid[t] && key[t] >= cand) ? P32[t] : 0.f;
+        for (int t = 0; t < J; ++t) f32 += key[t] >= cand ? P32[t] : 0.f;
         const double m32 = (double)wave_sum_f32(f32);
         bool take = m32 >= p;
-        if (fabs(m32 - p) <= 1e-5) {
+        if (fabs(m32 - p) <= kBand) {
+          if (!have64) exact();
           double f = 0.0;
 #pragma unroll
-          for (int t = 0; t < J; ++t) f += (valid[t] && key[t] >= cand) ? P[t] : 0.0;
+          for (int t = 0; t < J; ++t) f += key[t] >= cand ? P[t] : 0.0;
           take = wave_sum(f) >= p;
         }
         if (take) tau = cand;
       }
-      double above = 0.0, at = 0.0, f_tau = 0.0;
       int n_above = 0, n_at = 0;
+      float f32 = 0.f;
 #pragma unroll
       for (int t = 0; t < J; ++t) {
         const bool gt = valid[t] && key[t] > tau;
         const bool eq = valid[t] && key[t] == tau;
-        above += gt ? P[t] : 0.0;
-        at = eq ? P[t] : at;
-        f_tau += (gt || eq) ? P[t] : 0.0;
+        f32 += (gt || eq) ? P32[t] : 0.f;
         n_above += popc64(__ballot(gt));
         n_at += popc64(__ballot(eq));
       }
-      above = wave_sum(above);
-      f_tau = wave_sum(f_tau);
-      // every tied block has the same probability; take it from any lane holding one
-      const uint64_t holders = __ballot(at != 0.0);
-      const double tied = holders ? __shfl(at, __ffsll((long long)holders) - 1) : 0.0;
-      if (f_tau >= p) {
-        int m = 1;
-        double run = above + tied;
-        while (run < p && m < n_at) {
-          run += tied;
-          ++m;
+      const double f_tau32 = (double)wave_sum_f32(f32);
+      if (n_at == 1 && fabs(f_tau32 - p) > kBand) {
+        // one block at the threshold: the count is n_above + 1 when the mass reaches p
+        if (f_tau32 >= p) {
+          c = n_above + 1;
+          tau_p = tau;
+          tau_p_set = true;
         }
-        c = n_above + m;
-        tau_p = tau;
-        tau_p_set = true;
+      } else {
+        if (!have64) exact();
+        double above = 0.0, at = 0.0, f_tau = 0.0;
+#pragma unroll
+        for (int t = 0; t < J; ++t) {
+          const bool gt = valid[t] && key[t] > tau;
+          const bool eq = valid[t] && key[t] == tau;
+          above += gt ? P[t] : 0.0;
+          at = eq ? P[t] : at;
+          f_tau += (gt || eq) ? P[t] : 0.0;
+        }
+        above = wave_sum(above);
+        f_tau = wave_sum(f_tau);
+        // every tied block has the same probability; take it from any lane holding one
+        const uint64_t holders = __ballot(at != 0.0);
+        const double tied = holders ? __shfl(at, __ffsll((long long)holders) - 1) : 0.0;
+        if (f_tau >= p) {
+          int m = 1;
+          double run = above + tied;
+          while (run < p && m < n_at) {
+            run += tied;
+            ++m;
+          }
+          c = n_above + m;
+          tau_p = tau;
+          tau_p_set = true;
+        }
       }
     }
     want = max(c, min(k_floor, nb));
