@@ -684,13 +684,16 @@ __global__ __launch_bounds__(256) void queue_identity_kernel(int tiles, int32_t*
 // One wave per group unit u = (bh, q): the M neighbouring query blocks qM .. qM+M-1
 // of head bh (those past nb are absent). Writes the ascending union of their
 // retained lists, each entry j | (member m retains j) << (28 + m), and its length.
-// Lane l owns block ids 32l .. 32l + 31 as M bitmaps in LDS.
+// Lane l owns block ids 32l .. 32l + 31 as M bitmaps in LDS. The list is staged in
+// LDS and then written out by consecutive lanes (coalesced stores).
+constexpr int kMaxUnion = 2048;  // the router's largest nb
 template <int M>
 __global__ __launch_bounds__(256) void group_merge_kernel(const int32_t* __restrict__ counts,
                                                           const int32_t* __restrict__ kv_idx, int nb, int per_head,
                                                           int units, uint32_t* __restrict__ unit_list,
                                                           int32_t* __restrict__ unit_cnt) {
   __shared__ uint32_t bits[4][M][64];
+  __shared__ uint32_t stage[4][kMaxUnion];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int u = blockIdx.x * 4 + w;
@@ -728,15 +731,19 @@ __global__ __launch_bounds__(256) void group_merge_kernel(const int32_t* __restr
     if (lane >= off) incl += o;
   }
   int pos = incl - mine;
-  uint32_t* out = unit_list + (size_t)u * nb;
   for (int k = 0; k < 32; ++k) {
     if ((any >> k) & 1u) {
       uint32_t e = (uint32_t)(lane * 32 + k);
 #pragma unroll
       for (int m = 0; m < M; ++m) e |= ((word[m] >> k) & 1u) << (28 + m);
-      out[pos++] = e;
+      stage[w][pos++] = e;
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int total = __shfl(incl, 63);
+  uint32_t* out = unit_list + (size_t)u * nb;
+  for (int i = lane; i < total; i += 64) out[i] = stage[w][i];
   if (lane == 63) unit_cnt[u] = incl;
 }
 
