@@ -193,16 +193,17 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
 // wanted counts up to this take the arg-max route
 constexpr int kArgmaxWant = 16;
 
-template <int J>
+// RS: re-selection to the counts in `target` (keys only), as its own instance
+template <int J, bool RS>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S, int nb, int tiles, double p,
-                                                     int k_floor, int order_depth, int reselect,
+                                                     int k_floor, int order_depth,
                                                      const int32_t* __restrict__ target, int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ kv_idx, int32_t* __restrict__ order) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= tiles) return;
   int want = 0;
-  if (reselect) {
+  if (RS) {
     want = target[row];
     if (want <= counts[row]) return;
   }
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
   } else {
 #pragma unroll
     for (int t = 0; t < J; ++t) key[t] = valid[t] ? ordered_bits(s[t]) + 1u : 0u;
-    if (!reselect) {  // a re-selection needs only the keys
+    if (!RS) {  // a re-selection needs only the keys
       float z32 = 0.f;
 #pragma unroll
       for (int t = 0; t < J; ++t) {
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
   // has the same threshold: every key above it and the first ties at it)
   uint32_t tau_p = 0;
   bool tau_p_set = false;
-  if (!reselect) {
+  if (!RS) {
     int c = nb;
     if (p < 1.0) {
       // each step: is the mass of {key >= cand} at least p?
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
   if (lane == 0) counts[row] = want;
 
   // Importance-order prefix: repeated arg-max of (key, -id) over the blocks not yet taken.
-  if (!reselect && order_depth > 0) {
+  if (!RS && order_depth > 0) {
     uint32_t taken = 0;
     int32_t* ord = order + (size_t)row * order_depth;
     for (int r = 0; r < order_depth; ++r) {
@@ -1106,9 +1107,15 @@ hipError_t launch_select(const absh_ctx* c, const RouteBuffers& rb, int tiles, d
                          int order_depth, int reselect, hipStream_t s) {
   const unsigned grid = (unsigned)((tiles + 3) / 4);
   const int nb = c->nb;
-#define ABSH_SELECT(JJ)                                                                                  \
-  select_kernel<JJ><<<grid, 256, 0, s>>>(rb.S, nb, tiles, p, k_floor, order_depth, reselect, rb.target, \
-                                         rb.counts, rb.kv_idx, rb.order)
+#define ABSH_SELECT(JJ)                                                                             \
+  do {                                                                                              \
+    if (reselect)                                                                                   \
+      select_kernel<JJ, true><<<grid, 256, 0, s>>>(rb.S, nb, tiles, p, k_floor, order_depth, rb.target,  \
+                                                   rb.counts, rb.kv_idx, rb.order);                 \
+    else                                                                                            \
+      select_kernel<JJ, false><<<grid, 256, 0, s>>>(rb.S, nb, tiles, p, k_floor, order_depth, rb.target, \
+                                                    rb.counts, rb.kv_idx, rb.order);                \
+  } while (0)
   if (nb <= 64) ABSH_SELECT(1);
   else if (nb <= 256) ABSH_SELECT(4);
   else if (nb <= 512) ABSH_SELECT(8);
