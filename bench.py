@@ -42,6 +42,7 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 # half the attention's FLOPs on each: the time-weighted peak of bf16 Q K^T + fp8 P V
 PEAK_MIXED_TFLOPS = 1.0 / (0.5 / PEAK_BF16_TFLOPS + 0.5 / PEAK_FP8_TFLOPS)
 PEAK_HBM_GBS = 8000.0
+PEAK_CLOCK_MHZ = 2400.0      # MI355X peak engine clock, at which the MFMA peaks are quoted
 
 
 class ClockSampler(threading.Thread):
@@ -290,6 +291,10 @@ def main():
         w.name, args.schedule, args.values)
 
     peak = PEAK_MIXED_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    clock = sampler.report() if sampler else None
+    # the published peak assumes the 2.4 GHz peak engine clock; the same peak at the
+    # clock sampled over the timed steps, for reference
+    peak_clk = None if clock is None else peak * clock["median_mhz"] / PEAK_CLOCK_MHZ
     roof = {
         "bound": "mfma",
         "kernel": attention_kernel_name(d, w.block, 1 if args.schedule == "lpt" else (2 if w.block >= 128 else 4),
@@ -299,6 +304,8 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(attn_tflops / peak, 4),
         "traffic": traffic,
+        "peak_at_measured_clock": None if peak_clk is None else round(peak_clk, 1),
+        "frac_at_measured_clock": None if peak_clk is None else round(attn_tflops / peak_clk, 4),
     }
 
     cpu = None
@@ -341,7 +348,7 @@ def main():
         round(dense_ms / (stage_ms["attn"] + stage_ms["route"]), 3),
         "roofline": roof,
         "cpu_baseline": cpu,
-        "env": gpu_env(dev, sampler.report() if sampler else None, power_cap),
+        "env": gpu_env(dev, clock, power_cap),
     }
     print(json.dumps(out))
 
