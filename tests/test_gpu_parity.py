@@ -275,6 +275,44 @@ def test_slack_fill_sweep(index, p, beta):
     assert np.array_equal(filled.work.cpu().numpy(), c1.sum(-1))
 
 
+
+def test_route_underflowed_probabilities():
+    """Scores 128 apart (exact in float32 and float64): all but the top six blocks of
+    a row have probability 0 in float64, so they tie at 0 and follow by block id.
+    The floor (10) and a slack fill (to 15) reach into them, in both the Top-p pass
+    and the re-selection: counts, lists and the importance order equal the oracle's."""
+    T, Y, X, block, H, d = 4, 16, 16, 16, 2, 64
+    N = T * Y * X
+    nb = N // block
+    perm, _ = O.hilbert_perm(T, Y, X)
+    ranks = np.stack([np.arange(nb), (np.arange(nb) * 37) % nb])
+    qh = np.zeros((1, H, N, d), np.float32)
+    kh = np.zeros((1, H, N, d), np.float32)
+    qh[..., 0] = 1.0
+    for h in range(H):
+        kh[0, h, :, 0] = np.repeat(ranks[h] * 1024.0, block)
+    q = np.empty((1, N, H, d), np.float32)
+    k = np.empty((1, N, H, d), np.float32)
+    q[:, perm] = np.transpose(qh, (0, 2, 1, 3))
+    k[:, perm] = np.transpose(kh, (0, 2, 1, 3))
+    ctx = absh.create(T, Y, X, block)
+    qd = absh.permute(ctx, torch.from_numpy(q).to(DEV).bfloat16())
+    kd = absh.permute(ctx, torch.from_numpy(k).to(DEV).bfloat16())
+    R = O.route(qh, kh, block, 0.9, 10)
+    assert (R.P[..., :] == 0).sum(-1).min() == nb - 6
+    for beta in (0.0, 0.5):
+        want = O.slack_fill_level(R.counts, beta)
+        r = absh.route(ctx, qd, kd, 0.9, 10, slack_frac=beta, schedule="lpt", order_depth=12)
+        torch.cuda.synchronize()
+        counts, kv, _ = check_lists_valid(r, nb)
+        assert np.array_equal(counts, want), (beta, np.unique(counts))
+        for h in range(H):
+            for i in range(nb):
+                c = int(want[0, h, i])
+                assert np.array_equal(kv[0, h, i, :c], np.sort(R.order[0, h, i, :c])), (beta, h, i)
+        assert np.array_equal(r.order.cpu().numpy(), R.order[..., :12])
+
+
 def test_route_deterministic():
     c = case(1)
     w = c.w
