@@ -313,6 +313,28 @@ def test_route_underflowed_probabilities():
         assert np.array_equal(r.order.cpu().numpy(), R.order[..., :12])
 
 
+
+@pytest.mark.parametrize("p", [0.5, 0.9, 1 / 3, 0.25, 0.999])
+def test_route_uniform_scores(p):
+    """All block scores equal (q = k = 0): every block ties, P = 1/60, and the count
+    is where the float64 running sum of 1/60 first reaches p. Its rounding decides
+    (30 terms sum to just under 0.5, so p = 0.5 takes 31); counts and the lists
+    (the first c block ids) equal the oracle's."""
+    T, Y, X, block, H, d = 4, 15, 16, 16, 2, 64
+    N = T * Y * X
+    nb = N // block
+    zero = np.zeros((1, H, N, d), np.float32)
+    ctx = absh.create(T, Y, X, block)
+    zd = absh.permute(ctx, torch.zeros((1, N, H, d), dtype=torch.bfloat16, device=DEV))
+    R = O.route(zero, zero, block, p, 2)
+    r = absh.route(ctx, zd, zd, p, 2, schedule="lpt")
+    torch.cuda.synchronize()
+    counts, kv, _ = check_lists_valid(r, nb)
+    assert np.array_equal(counts, R.counts), (p, np.unique(counts), np.unique(R.counts))
+    c = int(R.counts.reshape(-1)[0])
+    assert (kv[..., :c] == np.arange(c)).all()
+
+
 def test_route_deterministic():
     c = case(1)
     w = c.w
