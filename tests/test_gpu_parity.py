@@ -453,6 +453,45 @@ def test_p_one_sparse_equals_dense(index):
     assert torch.equal(sparse.view(torch.int16), dense.view(torch.int16))
 
 
+
+@pytest.mark.parametrize("schedule", ["xcd", "lpt"])
+def test_attention_rising_logits(schedule):
+    """Logits that rise by about 2.5 per key block in the walk order, so a row's
+    maximum keeps overtaking the kernel's reference maximum and the lazy rescale
+    fires again and again (plus a ragged tail). Dense routing (p = 1); output
+    against the oracle's float64 attention with the attention bar."""
+    T, Y, X, block, H, d = 3, 17, 19, 64, 2, 128   # N = 969 tokens: 16 blocks, tail of 9
+    N = T * Y * X
+    rng = np.random.default_rng(5)
+    perm, _ = O.hilbert_perm(T, Y, X)
+    nb = -(-N // block)
+    # in Hilbert order: q = 1 on channel 0; k on channel 0 grows with the block index
+    qh = np.zeros((1, H, N, d), np.float32)
+    kh = (rng.standard_normal((1, H, N, d)) * 0.25).astype(np.float32)
+    qh[..., 0] = 1.0
+    blk = np.arange(N) // block
+    kh[..., 0] = (2.5 * np.sqrt(d) * blk)[None, None, :] + rng.standard_normal((1, H, N)).astype(np.float32)
+    vh = rng.standard_normal((1, H, N, d)).astype(np.float32)
+    grid = lambda a: np.ascontiguousarray(np.transpose(a, (0, 2, 1, 3)))  # [B, N(hilbert), H, d]
+    q = np.empty((1, N, H, d), np.float32)
+    k = np.empty_like(q)
+    v = np.empty_like(q)
+    q[:, perm], k[:, perm], v[:, perm] = grid(qh), grid(kh), grid(vh)
+    bits = [W.bf16_bits(a) for a in (q, k, v)]
+    ctx = absh.create(T, Y, X, block)
+    qd, kd, vd = (to_dev_bf16(b) for b in bits)
+    qhd, khd = absh.permute(ctx, qd), absh.permute(ctx, kd)
+    vt = absh.permute(ctx, vd, layout=absh.ABSH_VT)
+    r = absh.route(ctx, qhd, khd, 1.0, 0, schedule=schedule)
+    counts, _, _ = check_lists_valid(r, nb)
+    assert (counts == nb).all()
+    o = absh.unpermute(ctx, absh.sparse_attn(ctx, qhd, khd, vt, r)).float().cpu().numpy()
+    ref = O.attention(W.bf16_to_f32(bits[0]), W.bf16_to_f32(bits[1]), W.bf16_to_f32(bits[2]), perm, block)
+    e = np.abs(o - ref)
+    print(f"[rising] {schedule}: max {e.max():.3e} mean {e.mean():.3e}")
+    assert e.max() <= ATOL_MAX and e.mean() <= ATOL_MEAN
+
+
 def test_dense_matches_oracle_tiny():
     c = case(0)
     w = c.w
