@@ -248,6 +248,52 @@ def test_v8_edge_shapes(grid, block, d, H, B, schedule):
                 assert err.mean() <= ATOL_MEAN + (U * A2).mean()
 
 
+
+@pytest.mark.parametrize("schedule", ["xcd", "dense"])
+def test_v8_rising_logits(schedule):
+    """Logits rising by about 2.5 per key block along the walk: with the 8-bit
+    path's lazy threshold of 2^2 the reference maximum moves at almost every
+    block, and each move rescales O and re-bases the E4M3 probabilities. Every
+    tile meets the derived bound (ragged tail of 9 tokens)."""
+    T, Y, X, block, H, d = 3, 17, 19, 64, 2, 128   # N = 969: 16 blocks
+    N = T * Y * X
+    rng = np.random.default_rng(5)
+    perm, _ = O.hilbert_perm(T, Y, X)
+    qh = np.zeros((1, H, N, d), np.float32)
+    kh = (rng.standard_normal((1, H, N, d)) * 0.25).astype(np.float32)
+    qh[..., 0] = 1.0
+    blk = np.arange(N) // block
+    kh[..., 0] = (2.5 * np.sqrt(d) * blk)[None, None, :] + rng.standard_normal((1, H, N)).astype(np.float32)
+    vh = (rng.standard_normal((1, H, N, d)) * rng.uniform(0.1, 4.0, d)).astype(np.float32)
+    q = np.empty((1, N, H, d), np.float32)
+    k = np.empty_like(q)
+    v = np.empty_like(q)
+    for dst, src in ((q, qh), (k, kh), (v, vh)):
+        dst[:, perm] = np.transpose(src, (0, 2, 1, 3))
+    bits = [W.bf16_bits(a) for a in (q, k, v)]
+    ctx = absh.create(T, Y, X, block)
+    qd, kd, vd = (torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(DEV) for b in bits)
+    qhd, khd, vhd = absh.permute(ctx, qd), absh.permute(ctx, kd), absh.permute(ctx, vd)
+    vt8, vscale = absh.quantize_v(ctx, vhd)
+    r = None if schedule == "dense" else absh.route(ctx, qhd, khd, 1.0, 0, schedule=schedule)
+    o = absh.unpermute(ctx, absh.sparse_attn_v8(ctx, qhd, khd, vt8, vscale, r)).float().cpu().numpy()
+    hq, hk, hv = (O.to_hilbert(W.bf16_to_f32(b), perm) for b in bits)
+    nb = ctx.nb
+    worst = 0.0
+    for h in range(H):
+        codes, e = O.quantize_v(hv[0, h])
+        v8 = O.dequantize_v(codes, e)
+        for i in range(nb):
+            ref, A1, A2, As = O.attention_tile_spread(hq[0, h], hk[0, h], v8, block, i, range(nb), small=SMALL)
+            rows = perm[i * block: min((i + 1) * block, N)]
+            err = np.abs(o[0, rows, h, :] - ref)
+            bound = ATOL_MAX + U / (1 - U) * A1 + 2.0 ** -16 / (1 - U) * As
+            worst = max(worst, float((err / bound).max()))
+            assert (err <= bound).all(), (h, i, float((err - bound).max()))
+            assert err.mean() <= ATOL_MEAN + (U * A2).mean()
+    print(f"[v8 rising] {schedule}: worst error / bound {worst:.3f}", flush=True)
+
+
 def test_v8_rejects_unsupported_shapes():
     # block 16 has no 64-key steps; the longest-first schedule runs single tiles
     ctx16 = absh.create(2, 3, 5, 16)
