@@ -161,3 +161,31 @@ def test_bench_refuses_more_than_one_gpu():
                          text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_bench_clock_sampler_reads_the_current_level(tmp_path):
+    """The bench's clock sampler takes the level pp_dpm_sclk marks with '*', and reports
+    median / min / max over its samples; a missing file gives no report."""
+    import importlib.util
+    import time
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 2031Mhz *\n2: 2400Mhz\n")
+    s = bench.ClockSampler(str(f), period=0.005)
+    s.start()
+    time.sleep(0.05)
+    f.write_text("0: 500Mhz\n1: 1987Mhz *\n2: 2400Mhz\n")
+    time.sleep(0.05)
+    s.halt.set()
+    s.join()
+    rep = s.report()
+    assert rep["samples"] >= 2 and rep["min_mhz"] == 1987 and rep["max_mhz"] == 2031
+    assert rep["median_mhz"] in (1987, 2031)
+    gone = bench.ClockSampler(str(tmp_path / "absent"), period=0.005)
+    gone.start()
+    time.sleep(0.02)
+    gone.halt.set()
+    gone.join()
+    assert gone.report() is None
