@@ -34,8 +34,10 @@ each is named where it is used:
     the diffusion step.
   * Rank-level RLB and SASA (review Eq. 2, 5-10, 3.2, 3.3) with the eight XCDs
     of one GPU as the ranks: contiguous head placement, the piecewise policy on
-    rho, an exhaustive search of a restricted one-send-one-receive migration
-    space, and per-rank slack budgets spent by water-filling the rank's tiles.
+    rho, an exact search of the one-send-one-receive migration space over the
+    review's pair topologies (ranks matched in pairs; a pair moves one head
+    either way or swaps one head each), and per-rank slack budgets spent by
+    water-filling the rank's tiles.
   * Attention: exact softmax(Q K_R^T / sqrt(d)) V_R over the tokens of the
     retained key blocks R of each query block.
   * V quantization (review, "Block-Sparse Attention Execution" and 3.4): V is
@@ -454,7 +456,6 @@ def window_anchor_counts(nb: int, window: int, stride: int, shift: int, step: in
 RANKS = 8                     # XCDs of an MI355X, each with its own L2
 RLB_K1, RLB_K2 = 1.05, 1.10   # rho below k1: nothing; below k2: SASA only; else RLB, then SASA
 SASA_N1, SASA_N2 = 0.8, 0.07  # augmentation coefficient, trigger threshold
-MAX_PLANS = 1 << 26           # size limit of the enumerated migration space
 
 
 def rank_of_heads(BH: int, R: int = RANKS) -> np.ndarray:
@@ -485,69 +486,103 @@ def rank_policy(rho: float, k1: float = RLB_K1, k2: float = RLB_K2) -> str:
     return "sasa" if rho < k2 else "rlb+sasa"
 
 
-def rlb_options(work: np.ndarray, owner: np.ndarray, R: int = RANKS):
-    """The migration space searched by RLB, as options per sending rank.
+def pair_matchings(R: int = RANKS):
+    """The pair topologies of R ranks (R even): every perfect matching, in canonical order.
 
-    Reading of S_20% (Eq. 6; "each rank migrates at most one local head", 五):
-    every rank above the mean load may send one of its heads to a rank below the
-    mean load, and each such rank receives at most one head; a rank does not both
-    send and receive. Returns (senders, options), where options[i] lists the
-    choices of senders[i] in enumeration order: None, then (head, receiver) with
-    heads ascending and, per head, receivers ascending.
+    Follows: xllm-io review, 3.2 (pair topologies over which the candidate matchings of
+    S_20% are enumerated). Canonical order: the lowest unpaired rank is paired with each
+    higher unpaired rank in ascending order, recursively; a matching is a list of pairs
+    (a, b), a < b, by ascending a.
     """
-    W = rank_loads(work, owner, R)
-    total = int(W.sum())
-    senders = [r for r in range(R) if int(W[r]) * R > total]
-    receivers = [r for r in range(R) if int(W[r]) * R < total]
-    options = []
-    for r in senders:
-        heads = np.nonzero(owner == r)[0]
-        options.append([None] + [(int(h), int(l)) for h in heads for l in receivers])
-    return senders, options
+    if R % 2:
+        raise ValueError("pair topologies need an even number of ranks")
+
+    def rec(free):
+        if not free:
+            yield []
+            return
+        a = free[0]
+        for j in range(1, len(free)):
+            rest = free[1:j] + free[j + 1:]
+            for m in rec(rest):
+                yield [(a, free[j])] + m
+
+    return list(rec(list(range(R))))
+
+
+def pair_options(owner: np.ndarray, a: int, b: int):
+    """The moves pair (a, b) may make: one head each way at most (one send and one receive per rank).
+
+    Follows: xllm-io review, Eq. 5-6 and the RLB steps of 五 (rank r sends h_r to
+    sigma(r) and receives from sigma^-1(r), at most one local head per rank). Order:
+    no move; a sends one of its heads to b (heads ascending); b sends one to a; a and
+    b swap one head each (a's head varying slowest). A move is (head, from, to).
+    """
+    ha = [int(h) for h in np.nonzero(owner == a)[0]]
+    hb = [int(h) for h in np.nonzero(owner == b)[0]]
+    opts = [()]
+    opts += [((h, a, b),) for h in ha]
+    opts += [((h, b, a),) for h in hb]
+    opts += [((x, a, b), (y, b, a)) for x in ha for y in hb]
+    return opts
 
 
 def rlb_space(work: np.ndarray, owner: np.ndarray, R: int = RANKS) -> int:
-    """Number of option combinations RLB enumerates (product of the senders' option counts).
+    """Number of candidate plans: the sum over pair topologies of the product of their pairs' option counts.
 
-    Follows: xllm-io review, Eq. 6 (the restricted migration space).
+    Follows: xllm-io review, Eq. 6 (the space S_20% read as pair topologies).
     """
-    n = 1
-    for o in rlb_options(work, owner, R)[1]:
-        n *= len(o)
-    return n
+    total = 0
+    for m in pair_matchings(R):
+        n = 1
+        for a, b in m:
+            n *= len(pair_options(owner, a, b))
+        total += n
+    return total
 
 
 def rlb_plan(work: np.ndarray, owner: np.ndarray, R: int = RANKS):
     """Eq. 5-6: the plan of least (max_r W_r^new, Var_r W_r^new), ties to the first in enumeration order.
 
-    The candidate plans are the product of the senders' options (the first sender
-    varies slowest) with distinct receivers. Var is compared through sum W^2, which
-    orders plans the same way because migration keeps the total. A space of more
-    than MAX_PLANS combinations is not searched (no migration). Returns (new
-    owner array, list of moves (head, from, to)).
+    Follows: xllm-io review, Eq. 5-6, 3.2 and the RLB steps of 五. Plans are
+    enumerated pair topology by pair topology (canonical order), and within one the
+    pairs' options as a product with the first pair varying slowest. Var is compared
+    through sum W^2 (migration keeps the total). The pairs of a topology touch
+    disjoint ranks, so its best plan is found pair by pair: its least maximum M is the
+    largest over its pairs of the pair's least maximum, and each pair then takes,
+    among its options whose maximum is at most M, the first of least sum of squares.
+    Returns (new owner array, moves (head, from, to) by sending rank).
     """
     work = np.asarray(work, dtype=np.int64).reshape(-1)
     W = rank_loads(work, owner, R)
-    senders, options = rlb_options(work, owner, R)
-    if rlb_space(work, owner, R) > MAX_PLANS:  # too many to enumerate: no migration
-        return owner.copy(), []
-    best_key, best = None, ()
-    for choice in itertools.product(*options):
-        moves = [(s, c) for s, c in zip(senders, choice) if c is not None]
-        dsts = [c[1] for _, c in moves]
-        if len(set(dsts)) != len(dsts):
-            continue
-        Wn = W.copy()
-        for s, (h, l) in moves:  # Eq. 5: L_r - L_{h_r} + L_{h_{sigma^-1(r)}}
-            Wn[s] -= work[h]
-            Wn[l] += work[h]
-        key = (int(Wn.max()), int((Wn * Wn).sum()))
-        if best_key is None or key < best_key:
-            best_key, best = key, tuple(moves)
+    best = None
+    for m in pair_matchings(R):
+        pairs = []
+        for a, b in m:
+            opts = []
+            for moves in pair_options(owner, a, b):
+                wa, wb = int(W[a]), int(W[b])
+                for h, src, dst in moves:  # Eq. 5: L_r - L_{h_r} + L_{h_{sigma^-1(r)}}
+                    d = int(work[h])
+                    if src == a:
+                        wa, wb = wa - d, wb + d
+                    else:
+                        wa, wb = wa + d, wb - d
+                opts.append((max(wa, wb), wa * wa + wb * wb, moves))
+            pairs.append(opts)
+        M = max(min(o[0] for o in opts) for opts in pairs)
+        chosen, S = [], 0
+        for opts in pairs:
+            least = min(o[1] for o in opts if o[0] <= M)
+            S += least
+            chosen.append(next(o[2] for o in opts if o[0] <= M and o[1] == least))
+        if best is None or (M, S) < best[0]:
+            best = ((M, S), chosen)
+    moves = sorted((mv for ch in best[1] for mv in ch), key=lambda mv: mv[1])
     new_owner = owner.copy()
-    for s, (h, l) in best:
-        new_owner[h] = l
-    return new_owner, [(h, s, l) for s, (h, l) in best]
+    for h, _, dst in moves:
+        new_owner[h] = dst
+    return new_owner, moves
 
 
 def sasa_budgets(W: np.ndarray, n1: float = SASA_N1, n2: float = SASA_N2) -> np.ndarray:
