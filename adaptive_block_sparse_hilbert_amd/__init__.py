@@ -17,11 +17,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libabsh.so")
 
 ABSH_BF16, ABSH_F32 = 0, 1
-ABSH_ROWS, ABSH_VT, ABSH_VT8 = 0, 1, 2
+ABSH_ROWS, ABSH_VT, ABSH_VT8, ABSH_ROWS_F32 = 0, 1, 2, 3
 SCHED_ORDER, SCHED_LPT, SCHED_XCD, SCHED_RANKS = 0, 1, 2, 3
 SCHEDULES = {"order": SCHED_ORDER, "lpt": SCHED_LPT, "xcd": SCHED_XCD, "ranks": SCHED_RANKS}
 RANK_POLICIES = {"auto": -1, "none": 0, "sasa": 1, "rlb+sasa": 2, "rlb": 3}
 RANK_INFO = 64  # doubles in Routing.rank_info (layout in include/absh.h)
+PULL_WORDS = 16  # int32 work counters in Routing.pull
 ROUTERS = {"topp": 0, "window-anchor": 1}
 # the review's parameters of the rank-level stages (section 五)
 RLB_K1, RLB_K2, SASA_N1, SASA_N2 = 1.05, 1.10, 0.8, 0.07
@@ -30,7 +31,7 @@ EXPORTED = (
     "absh_version", "absh_status_string", "absh_last_error", "absh_create", "absh_destroy", "absh_dims",
     "absh_perm", "absh_perm_copy", "absh_permute", "absh_unpermute", "absh_pool", "absh_block_scores",
     "absh_route_workspace_bytes", "absh_route", "absh_sparse_attn", "absh_lists_units", "absh_quantize_v",
-    "absh_sparse_attn_v8",
+    "absh_sparse_attn_v8", "absh_lists_bytes", "absh_lists_carve", "absh_workspace_bytes", "absh_attn_workgroups",
 )
 
 
@@ -56,7 +57,8 @@ class Lists(ctypes.Structure):
                 ("work", ctypes.c_void_p), ("L", ctypes.c_void_p), ("queue", ctypes.c_void_p),
                 ("sched", ctypes.c_void_p), ("unit_list", ctypes.c_void_p), ("unit_cnt", ctypes.c_void_p),
                 ("schedule", ctypes.c_int32), ("head_order", ctypes.c_void_p), ("rank_info", ctypes.c_void_p),
-                ("strict_ranks", ctypes.c_int32)]
+                ("strict_ranks", ctypes.c_int32), ("unit_queue", ctypes.c_void_p), ("pull", ctypes.c_void_p),
+                ("wg_busy", ctypes.c_void_p)]
 
 
 _lib = None
@@ -85,8 +87,12 @@ def lib() -> ctypes.CDLL:
         "absh_pool": ([vp, vp, vp, i, i, i, vp], i),
         "absh_block_scores": ([vp, vp, vp, vp, i, i, i, vp], i),
         "absh_route_workspace_bytes": ([vp, i, i, i], sz),
+        "absh_workspace_bytes": ([vp, i, i, i], sz),
+        "absh_attn_workgroups": ([vp], i),
         "absh_lists_units": ([vp, i, i, i], i),
-        "absh_route": ([vp, vp, vp, i, i, i, ctypes.POINTER(RouteOpts), ctypes.POINTER(Lists), vp, sz, vp], i),
+        "absh_route": ([vp, vp, vp, i, i, i, i, ctypes.POINTER(RouteOpts), ctypes.POINTER(Lists), vp, sz, vp], i),
+        "absh_lists_bytes": ([vp, i, i, i], sz),
+        "absh_lists_carve": ([vp, i, i, i, vp, sz, ctypes.POINTER(Lists)], i),
         "absh_sparse_attn": ([vp, vp, vp, vp, i, i, i, ctypes.POINTER(Lists), vp, vp], i),
         "absh_quantize_v": ([vp, vp, i, i, i, vp, vp, vp], i),
         "absh_sparse_attn_v8": ([vp, vp, vp, vp, vp, i, i, i, ctypes.POINTER(Lists), vp, vp], i),
@@ -163,14 +169,18 @@ def perm_copy(ctx: Context, stream=None):
 
 
 def permute(ctx: Context, x, layout: int = ABSH_ROWS, out=None, stream=None):
-    """x [B, N, H, d] (bf16 or f32, grid order) -> bf16 Hilbert-order tensor in `layout`."""
+    """x [B, N, H, d] (bf16 or f32, grid order) -> Hilbert-order tensor in `layout` (bf16, or
+    float32 rows for ABSH_ROWS_F32)."""
     import torch
     B, N, H, d = x.shape
     assert N == ctx.N and x.is_contiguous() and x.dtype in (torch.bfloat16, torch.float32)
     xt = ABSH_F32 if x.dtype == torch.float32 else ABSH_BF16
+    rows = layout in (ABSH_ROWS, ABSH_ROWS_F32)
+    shape = (B, H, ctx.n_pad, d) if rows else (B, H, ctx.nb, d, vt_keys(ctx.block))
+    dtype = torch.float32 if layout == ABSH_ROWS_F32 else torch.bfloat16
     if out is None:
-        shape = (B, H, ctx.n_pad, d) if layout == ABSH_ROWS else (B, H, ctx.nb, d, vt_keys(ctx.block))
-        out = torch.empty(shape, dtype=torch.bfloat16, device=x.device)
+        out = torch.empty(shape, dtype=dtype, device=x.device)
+    assert tuple(out.shape) == shape and out.dtype == dtype and out.is_contiguous(), "out does not fit the layout"
     _check(lib().absh_permute(ctx.handle, _ptr(x), xt, _ptr(out), B, H, d, layout, _stream(stream)))
     return out
 
@@ -224,15 +234,45 @@ class Routing:
     unit_cnt: object   # int32 [units]
     head_order: object  # int32 [B*H] heads by rank (schedule "ranks")
     rank_info: object   # float64 [RANK_INFO] rank-stage report (schedule "ranks")
+    unit_queue: object = None  # int32 [units] units longest first within each run (schedule "lpt")
+    pull: object = None        # int32 [PULL_WORDS] the attention launches' work counters
+    wg_busy: object = None     # optional uint64 [attn_workgroups, 2]: per-workgroup start / end ticks
     schedule: int = -1  # the schedule absh_route made these lists for
     strict_ranks: int = 0
 
     def lists(self) -> Lists:
-        return Lists(self.counts.data_ptr(), self.kv_idx.data_ptr(),
-                     self.order.data_ptr() if self.order is not None else 0,
+        opt = lambda t: t.data_ptr() if t is not None else 0
+        return Lists(self.counts.data_ptr(), self.kv_idx.data_ptr(), opt(self.order),
                      self.work.data_ptr(), self.L.data_ptr(), self.queue.data_ptr(), self.sched.data_ptr(),
                      self.unit_list.data_ptr(), self.unit_cnt.data_ptr(), self.schedule,
-                     self.head_order.data_ptr(), self.rank_info.data_ptr(), self.strict_ranks)
+                     self.head_order.data_ptr(), self.rank_info.data_ptr(), self.strict_ranks,
+                     opt(self.unit_queue), opt(self.pull), opt(self.wg_busy))
+
+    def check(self, ctx: "Context", B: int, H: int, order_depth: int) -> None:
+        """Raise unless every buffer has the shape and dtype absh_route writes for (ctx, B, H,
+        order_depth): the library cannot see buffer sizes, so this is where a mismatch is caught."""
+        import torch
+        nb = ctx.nb
+        units = max_units(ctx, B, H)
+        want = {"counts": ((B, H, nb), torch.int32), "kv_idx": ((B, H, nb, nb), torch.int32),
+                "work": ((B, H), torch.int32), "L": ((B, H), torch.float32),
+                "queue": ((B * H * nb,), torch.int32), "sched": ((10,), torch.int32),
+                "unit_list": ((units, nb), torch.int32), "unit_cnt": ((units,), torch.int32),
+                "head_order": ((B * H,), torch.int32), "rank_info": ((RANK_INFO,), torch.float64),
+                "unit_queue": ((units,), torch.int32), "pull": ((PULL_WORDS,), torch.int32)}
+        if order_depth > 0:
+            want["order"] = ((B, H, nb, order_depth), torch.int32)
+        elif self.order is not None and self.order.dim() != 4:
+            raise ValueError("order must be [B, H, nb, depth]")
+        for name, (shape, dtype) in want.items():
+            t = getattr(self, name)
+            if t is None or tuple(t.shape) != shape or t.dtype != dtype or not t.is_contiguous():
+                got = None if t is None else (tuple(t.shape), t.dtype)
+                raise ValueError(f"Routing.{name} is {got}, expected {shape} {dtype}")
+        for name in want:
+            t = getattr(self, name)
+            if t.device != torch.device("cuda", ctx.device):
+                raise ValueError(f"Routing.{name} is on {t.device}, not cuda:{ctx.device}")
 
 
 def route_workspace_bytes(ctx: Context, B: int, H: int, d: int) -> int:
@@ -245,12 +285,41 @@ def lists_units(ctx: Context, B: int, H: int, schedule) -> int:
     return int(lib().absh_lists_units(ctx.handle, B, H, sched))
 
 
+def max_units(ctx: Context, B: int, H: int) -> int:
+    """The most work units any schedule makes for this shape (rows of the unit buffers)."""
+    return max(max(lists_units(ctx, B, H, s) for s in SCHEDULES), 1)
+
+
+def attn_workgroups(ctx: Context) -> int:
+    """Rows of a per-workgroup busy record (Routing.wg_busy) for attention on this context."""
+    return int(lib().absh_attn_workgroups(ctx.handle))
+
+
+def busy_record(ctx: Context, routing: Routing):
+    """Attach a zeroed per-workgroup busy record to `routing`; attention launches on it fill it."""
+    import torch
+    routing.wg_busy = torch.zeros((attn_workgroups(ctx), 2), dtype=torch.int64, device=_dev(ctx))
+    return routing.wg_busy
+
+
+def busy_ticks(wg_busy):
+    """Busy time of each workgroup that ran (end - start, in 100 MHz ticks) from a busy record."""
+    rec = wg_busy.cpu()
+    ran = rec[:, 1] > 0
+    return (rec[ran, 1] - rec[ran, 0]).numpy()
+
+
+def lists_bytes(ctx: Context, B: int, H: int, order_depth: int = 0) -> int:
+    """Device bytes of all routing buffers in one arena (absh_lists_bytes)."""
+    return int(lib().absh_lists_bytes(ctx.handle, B, H, order_depth))
+
+
 def alloc_routing(ctx: Context, B: int, H: int, order_depth: int = 0) -> Routing:
     """Routing buffers sized for every schedule."""
     import torch
     dev = _dev(ctx)
     nb = ctx.nb
-    units = max(lists_units(ctx, B, H, "order"), 1)
+    units = max_units(ctx, B, H)
     return Routing(
         counts=torch.empty((B, H, nb), dtype=torch.int32, device=dev),
         kv_idx=torch.empty((B, H, nb, nb), dtype=torch.int32, device=dev),
@@ -263,6 +332,8 @@ def alloc_routing(ctx: Context, B: int, H: int, order_depth: int = 0) -> Routing
         unit_cnt=torch.empty((units,), dtype=torch.int32, device=dev),
         head_order=torch.empty((B * H,), dtype=torch.int32, device=dev),
         rank_info=torch.zeros((RANK_INFO,), dtype=torch.float64, device=dev),
+        unit_queue=torch.empty((units,), dtype=torch.int32, device=dev),
+        pull=torch.zeros((PULL_WORDS,), dtype=torch.int32, device=dev),
     )
 
 
@@ -271,7 +342,8 @@ def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0,
           rank_policy="auto", strict_ranks: bool = False, k1: float = RLB_K1, k2: float = RLB_K2,
           n1: float = SASA_N1, n2: float = SASA_N2, router="topp", window: int = 0, anchor_stride: int = 0,
           anchor_shift: int = 0, step: int = 0) -> Routing:
-    """Stage-1 routing of Hilbert-order qh, kh [B, H, n_pad, d] bf16 -> Routing (device tensors).
+    """Stage-1 routing of Hilbert-order qh, kh [B, H, n_pad, d] (bf16 rows, or float32 rows from
+    permute(..., ABSH_ROWS_F32)) -> Routing (device tensors).
 
     schedule: "order", "lpt", "xcd" or "ranks" (or the SCHED_* integer). The
     rank_* and k/n arguments apply to "ranks" only: rank_policy "auto" (by rho),
@@ -282,8 +354,15 @@ def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0,
     """
     import torch
     B, H, n_pad, d = qh.shape
+    if qh.dtype != kh.dtype or qh.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("qh and kh must both be bf16 or both float32")
+    if tuple(kh.shape) != tuple(qh.shape) or n_pad != ctx.n_pad or not (qh.is_contiguous() and kh.is_contiguous()):
+        raise ValueError(f"qh, kh must be contiguous [B, H, {ctx.n_pad}, d] (got {tuple(qh.shape)}, {tuple(kh.shape)})")
+    qk_type = ABSH_F32 if qh.dtype == torch.float32 else ABSH_BF16
     if out is None:
         out = alloc_routing(ctx, B, H, order_depth)
+    else:
+        out.check(ctx, B, H, order_depth)
     need = route_workspace_bytes(ctx, B, H, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=qh.device)
@@ -294,7 +373,7 @@ def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0,
                      ROUTERS[router] if isinstance(router, str) else int(router), int(window), int(anchor_stride),
                      int(anchor_shift), int(step))
     lists = out.lists()
-    _check(lib().absh_route(ctx.handle, _ptr(qh), _ptr(kh), B, H, d, ctypes.byref(opts), ctypes.byref(lists),
+    _check(lib().absh_route(ctx.handle, _ptr(qh), _ptr(kh), qk_type, B, H, d, ctypes.byref(opts), ctypes.byref(lists),
                             _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream)))
     out.schedule = lists.schedule
     out.strict_ranks = lists.strict_ranks

@@ -37,10 +37,12 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(
 // Launchers (each returns hipGetLastError() of its launches).
 int hilbert_chunks(int m);
 hipError_t launch_hilbert_perm(const absh_ctx* c, int32_t* chunk_counts, int chunks, hipStream_t s);
+// layout: ABSH_ROWS (bf16 rows), ABSH_VT (bf16, block-transposed) or ABSH_ROWS_F32 (float rows)
 hipError_t launch_permute(const absh_ctx* c, const void* x, int x_is_f32, void* xh, int B, int H, int d,
-                          int layout_vt, hipStream_t s);
+                          int layout, hipStream_t s);
 hipError_t launch_unpermute(const absh_ctx* c, const void* oh, void* o, int B, int H, int d, hipStream_t s);
-hipError_t launch_pool(const absh_ctx* c, const void* xh, float* xbar, int B, int H, int d, hipStream_t s);
+hipError_t launch_pool(const absh_ctx* c, const void* xh, int xh_is_f32, float* xbar, int B, int H, int d,
+                       hipStream_t s);
 hipError_t launch_scores(const absh_ctx* c, const float* qbar, const float* kbar, float* S, int BH, int d,
                          hipStream_t s);
 
@@ -61,6 +63,7 @@ struct RouteBuffers {
   int32_t* sched;        // [10] queue segment bounds (one segment per XCD) and query blocks per unit
   uint32_t* unit_list;   // [units][nb] union lists of query-block groups
   int32_t* unit_cnt;     // [units]
+  int32_t* unit_queue;   // [units] group units longest first within each XCD run (ABSH_SCHED_LPT)
   int32_t* owner;        // [B*H] rank of each head after migration (ABSH_SCHED_RANKS)
   int32_t* head_order;   // [B*H] heads by rank, ascending within a rank (ABSH_SCHED_RANKS)
   int64_t* budget;       // [8] SASA budgets E_r in retained blocks (ABSH_SCHED_RANKS)
@@ -81,6 +84,9 @@ int unit_members(const absh_ctx* c, int schedule);  // query blocks per attentio
 int unit_count(const absh_ctx* c, int BH, int members);
 hipError_t launch_groups(const absh_ctx* c, const RouteBuffers& rb, int BH, int members, hipStream_t s);
 hipError_t launch_segments(const absh_ctx* c, const RouteBuffers& rb, int BH, int schedule, hipStream_t s);
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
+// unit_queue: the group units of each XCD run (sched bounds) by union length, descending, ties by unit
+hipError_t launch_unit_lpt(const absh_ctx* c, const RouteBuffers& rb, int BH, hipStream_t s);
 int queue_chunks(int tiles);
 int queue_scan_tiles(int tiles, int nb);
 int slack_aux_words(int tiles);
@@ -103,7 +109,12 @@ struct AttnLists {
   int members;                // host copy of sched[9]
   const int32_t* head_order;  // group units: segment position p / per_head -> head (NULL: identity)
   int strict;                 // 1: a workgroup takes units from its own XCD's segment only
+  const int32_t* unit_queue;  // group units: segment position -> unit (NULL: identity or head_order)
+  int32_t* counters;          // [16] pull counters (NULL: the context's)
+  uint64_t* wg_busy;          // [grid][2] start / end times per workgroup (NULL: none)
 };
+// Most resident workgroups per CU of any attention kernel (bounds wg_busy).
+constexpr int kMaxAttnWgPerCu = 8;
 hipError_t launch_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B,
                             int H, int d, const AttnLists* lists, hipStream_t s);
 // Group units of 64- and 128-row query blocks (four and two members) run on the

@@ -3,6 +3,7 @@
 // stream. See include/absh.h for the contract of every function.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -210,11 +211,11 @@ absh_status absh_permute(absh_ctx* c, const void* x, absh_dtype xt, void* xh, in
   if (absh_status st = check_shape(c, B, H, d)) return st;
   if (!x || !xh) return fail(ABSH_EINVAL, "x or xh is NULL");
   if (xt != ABSH_BF16 && xt != ABSH_F32) return fail(ABSH_EINVAL, "unknown dtype %d", (int)xt);
-  if (layout != ABSH_ROWS && layout != ABSH_VT) return fail(ABSH_EINVAL, "unknown layout %d", (int)layout);
+  if (layout != ABSH_ROWS && layout != ABSH_VT && layout != ABSH_ROWS_F32)
+    return fail(ABSH_EINVAL, "unknown layout %d", (int)layout);
   if (!aligned16(x) || !aligned16(xh)) return fail(ABSH_EINVAL, "x and xh must be 16-byte aligned");
   if (absh_status st = use_device(c)) return st;
-  ABSH_HIP(absh::launch_permute(c, x, xt == ABSH_F32, xh, B, H, d, layout == ABSH_VT,
-                                reinterpret_cast<hipStream_t>(stream)),
+  ABSH_HIP(absh::launch_permute(c, x, xt == ABSH_F32, xh, B, H, d, (int)layout, reinterpret_cast<hipStream_t>(stream)),
            "absh_permute");
   return ABSH_OK;
 }
@@ -236,7 +237,7 @@ absh_status absh_pool(absh_ctx* c, const void* xh, float* xbar, int B, int H, in
   if (absh_status st = check_shape(c, B, H, d)) return st;
   if (!xh || !xbar) return fail(ABSH_EINVAL, "xh or xbar is NULL");
   if (absh_status st = use_device(c)) return st;
-  ABSH_HIP(absh::launch_pool(c, xh, xbar, B, H, d, reinterpret_cast<hipStream_t>(stream)), "absh_pool");
+  ABSH_HIP(absh::launch_pool(c, xh, 0, xbar, B, H, d, reinterpret_cast<hipStream_t>(stream)), "absh_pool");
   return ABSH_OK;
 }
 
@@ -254,16 +255,100 @@ absh_status absh_block_scores(absh_ctx* c, const float* qbar, const float* kbar,
 }
 
 int absh_lists_units(const absh_ctx* c, int B, int H, int schedule) {
-  if (!c || B < 1 || H < 1 || schedule < ABSH_SCHED_ORDER || schedule > ABSH_SCHED_XCD) return 0;
+  if (!c || B < 1 || H < 1 || schedule < ABSH_SCHED_ORDER || schedule > ABSH_SCHED_RANKS) return 0;
+  if ((double)B * H * c->nb >= 2147483647.0) return 0;
   return absh::unit_count(c, B * H, absh::unit_members(c, schedule));
 }
+
+}  // extern "C"
+
+namespace {
+
+// The buffers of absh_lists in field order, each 256-byte aligned inside one
+// arena; units = the most any schedule makes. Offsets in bytes; -1 = absent.
+struct ListsLayout {
+  size_t counts, kv_idx, order, work, L, queue, sched, unit_list, unit_cnt, head_order, rank_info, unit_queue, pull,
+      total;
+};
+
+bool lists_layout(const absh_ctx* c, int B, int H, int order_depth, ListsLayout* l) {
+  if (!c || B < 1 || H < 1 || order_depth < 0 || order_depth > 64) return false;
+  if ((double)B * H * c->nb >= 2147483647.0) return false;
+  const size_t BH = (size_t)B * H, tiles = BH * c->nb, nb = (size_t)c->nb;
+  size_t units = 0;
+  for (int sch = ABSH_SCHED_ORDER; sch <= ABSH_SCHED_RANKS; ++sch)
+    units = std::max(units, (size_t)absh::unit_count(c, B * H, absh::unit_members(c, sch)));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  l->counts = take(tiles * 4);
+  l->kv_idx = take(tiles * nb * 4);
+  l->order = order_depth > 0 ? take(tiles * (size_t)order_depth * 4) : (size_t)-1;
+  l->work = take(BH * 4);
+  l->L = take(BH * 4);
+  l->queue = take(tiles * 4);
+  l->sched = take(10 * 4);
+  l->unit_list = take(units * nb * 4);
+  l->unit_cnt = take(units * 4);
+  l->head_order = take(BH * 4);
+  l->rank_info = take(ABSH_RANK_INFO * 8);
+  l->unit_queue = take(units * 4);
+  l->pull = take(ABSH_PULL_WORDS * 4);
+  l->total = off;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t absh_lists_bytes(const absh_ctx* c, int B, int H, int order_depth) {
+  ListsLayout l;
+  return lists_layout(c, B, H, order_depth, &l) ? l.total : 0;
+}
+
+absh_status absh_lists_carve(const absh_ctx* c, int B, int H, int order_depth, void* arena, size_t arena_bytes,
+                             absh_lists* out) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (!arena || !out) return fail(ABSH_EINVAL, "arena or out is NULL");
+  ListsLayout l;
+  if (!lists_layout(c, B, H, order_depth, &l)) return fail(ABSH_EINVAL, "bad shape or order_depth");
+  if (arena_bytes < l.total) return fail(ABSH_EWORKSPACE, "arena has %zu bytes, %zu needed", arena_bytes, l.total);
+  if ((reinterpret_cast<uintptr_t>(arena) & (kAlign - 1)) != 0)
+    return fail(ABSH_EINVAL, "arena must be %zu-byte aligned", kAlign);
+  char* base = reinterpret_cast<char*>(arena);
+  *out = absh_lists{};
+  out->counts = reinterpret_cast<int32_t*>(base + l.counts);
+  out->kv_idx = reinterpret_cast<int32_t*>(base + l.kv_idx);
+  out->order = l.order == (size_t)-1 ? nullptr : reinterpret_cast<int32_t*>(base + l.order);
+  out->work = reinterpret_cast<int32_t*>(base + l.work);
+  out->L = reinterpret_cast<float*>(base + l.L);
+  out->queue = reinterpret_cast<int32_t*>(base + l.queue);
+  out->sched = reinterpret_cast<int32_t*>(base + l.sched);
+  out->unit_list = reinterpret_cast<uint32_t*>(base + l.unit_list);
+  out->unit_cnt = reinterpret_cast<int32_t*>(base + l.unit_cnt);
+  out->head_order = reinterpret_cast<int32_t*>(base + l.head_order);
+  out->rank_info = reinterpret_cast<double*>(base + l.rank_info);
+  out->unit_queue = reinterpret_cast<int32_t*>(base + l.unit_queue);
+  out->pull = reinterpret_cast<int32_t*>(base + l.pull);
+  out->schedule = -1;
+  return ABSH_OK;
+}
+
+int absh_attn_workgroups(const absh_ctx* c) { return c ? c->num_cus * absh::kMaxAttnWgPerCu : 0; }
 
 size_t absh_route_workspace_bytes(const absh_ctx* c, int B, int H, int d) {
   if (!c || B < 1 || H < 1 || d < 1) return 0;
   return ws_layout(c, B, H, d).total;
 }
 
-absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H, int d,
+size_t absh_workspace_bytes(const absh_ctx* c, int B, int H, int d) { return absh_route_workspace_bytes(c, B, H, d); }
+
+absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, absh_dtype qk_type, int B, int H, int d,
                        const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
   if (absh_status st = check_ctx(c)) return st;
@@ -281,6 +366,8 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
       return fail(ABSH_EUNSUPPORTED, "the window/anchor router has no importance order for ABSH_SCHED_RANKS");
   } else {
     if (!qh || !kh) return fail(ABSH_EINVAL, "qh or kh is NULL");
+    if (qk_type != ABSH_BF16 && qk_type != ABSH_F32) return fail(ABSH_EINVAL, "unknown dtype %d", (int)qk_type);
+    if (!aligned16(qh) || !aligned16(kh)) return fail(ABSH_EINVAL, "qh and kh must be 16-byte aligned");
     if (!(opts->p > 0.0 && opts->p <= 1.0)) return fail(ABSH_EINVAL, "p must lie in (0, 1] (got %g)", opts->p);
     if (opts->k_floor < 0) return fail(ABSH_EINVAL, "k_floor must be >= 0 (got %d)", opts->k_floor);
   }
@@ -302,12 +389,19 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
       return fail(ABSH_EINVAL, "need 0 <= n1 < 1 and n2 >= 0 (got %g, %g)", opts->n1, opts->n2);
     if (!out->head_order || !out->rank_info)
       return fail(ABSH_EINVAL, "head_order and rank_info must be non-NULL for ABSH_SCHED_RANKS");
+    if ((int64_t)B * H > 1024)
+      return fail(ABSH_EUNSUPPORTED, "ABSH_SCHED_RANKS takes at most 1024 heads (B*H = %lld)", (long long)B * H);
+    if ((double)B * H * c->nb * c->nb >= 2147483648.0)
+      return fail(ABSH_EUNSUPPORTED, "ABSH_SCHED_RANKS needs B*H*nb*nb < 2^31 (rank loads squared in int64)");
   }
   if (!out->counts || !out->kv_idx || !out->work || !out->L || !out->queue || !out->sched)
     return fail(ABSH_EINVAL, "counts, kv_idx, work, L, queue and sched must be non-NULL");
   if (opts->order_depth > 0 && !out->order) return fail(ABSH_EINVAL, "order is NULL but order_depth > 0");
-  if (opts->schedule != ABSH_SCHED_LPT && (!out->unit_list || !out->unit_cnt))
+  const int members = absh::unit_members(c, opts->schedule);
+  if (members > 1 && (!out->unit_list || !out->unit_cnt))
     return fail(ABSH_EINVAL, "unit_list and unit_cnt must be non-NULL for this schedule");
+  if (opts->schedule == ABSH_SCHED_LPT && members > 1 && !out->unit_queue)
+    return fail(ABSH_EINVAL, "unit_queue must be non-NULL for ABSH_SCHED_LPT with blocks of 64 or 128");
   if (c->nb > kMaxNb) return fail(ABSH_EUNSUPPORTED, "nb = %d above the router's %d", c->nb, kMaxNb);
   const WsLayout w = ws_layout(c, B, H, d);
   if (!ws) return fail(ABSH_EWORKSPACE, "workspace is NULL (%zu bytes needed)", w.total);
@@ -337,6 +431,7 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
   rb.sched = out->sched;
   rb.unit_list = out->unit_list;
   rb.unit_cnt = out->unit_cnt;
+  rb.unit_queue = out->unit_queue;
   rb.owner = reinterpret_cast<int32_t*>(base + w.owner);
   rb.budget = reinterpret_cast<int64_t*>(base + w.budget);
   rb.head_order = ranks ? out->head_order : nullptr;
@@ -347,11 +442,13 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
     const int offset = opts->anchor_stride > 0
                            ? (int)(((int64_t)opts->step * opts->anchor_shift) % opts->anchor_stride)
                            : 0;
-    ABSH_HIP(absh::launch_window_anchor(c, rb, tiles, opts->window, opts->anchor_stride, offset, s),
+    // a window of nb - 1 already reaches every block: larger ones are the same pattern
+    const int window = std::min(opts->window, c->nb - 1);
+    ABSH_HIP(absh::launch_window_anchor(c, rb, tiles, window, opts->anchor_stride, offset, s),
              "absh_route: window/anchor lists");
   } else {
-    ABSH_HIP(absh::launch_pool(c, qh, qbar, B, H, d, s), "absh_route: pool q");
-    ABSH_HIP(absh::launch_pool(c, kh, kbar, B, H, d, s), "absh_route: pool k");
+    ABSH_HIP(absh::launch_pool(c, qh, qk_type == ABSH_F32, qbar, B, H, d, s), "absh_route: pool q");
+    ABSH_HIP(absh::launch_pool(c, kh, qk_type == ABSH_F32, kbar, B, H, d, s), "absh_route: pool k");
     ABSH_HIP(absh::launch_scores(c, qbar, kbar, const_cast<float*>(rb.S), B * H, d, s), "absh_route: scores");
     ABSH_HIP(absh::launch_select(c, rb, tiles, opts->p, opts->k_floor, opts->order_depth, 0, s),
              "absh_route: select");
@@ -372,9 +469,11 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, int B, int H
     ABSH_HIP(absh::launch_rank_final(rb, B * H, s), "absh_route: rank report");
   }
   ABSH_HIP(absh::launch_queue(c, rb, tiles, opts->schedule == ABSH_SCHED_LPT, s), "absh_route: queue");
-  if (opts->schedule != ABSH_SCHED_LPT)
-    ABSH_HIP(absh::launch_groups(c, rb, B * H, absh::unit_members(c, opts->schedule), s), "absh_route: groups");
+  if (members > 1) ABSH_HIP(absh::launch_groups(c, rb, B * H, members, s), "absh_route: groups");
   if (!ranks) ABSH_HIP(absh::launch_segments(c, rb, B * H, opts->schedule, s), "absh_route: segments");
+  if (opts->schedule == ABSH_SCHED_LPT && members > 1)
+    ABSH_HIP(absh::launch_unit_lpt(c, rb, B * H, s), "absh_route: unit queue");
+  if (out->pull) ABSH_HIP(absh::launch_zero_i32(out->pull, ABSH_PULL_WORDS, s), "absh_route: pull counters");
   out->schedule = opts->schedule;
   out->strict_ranks = ranks ? opts->strict_ranks : 0;
   return ABSH_OK;
@@ -394,15 +493,21 @@ absh_status attn_lists(const absh_ctx* c, const absh_lists* lists, absh::AttnLis
     return fail(ABSH_EINVAL, "lists->schedule %d is not a schedule (was absh_route run?)", lists->schedule);
   if (lists->schedule == ABSH_SCHED_RANKS && !lists->head_order)
     return fail(ABSH_EINVAL, "lists needs head_order for ABSH_SCHED_RANKS");
-  if (lists->schedule != ABSH_SCHED_LPT && (!lists->unit_list || !lists->unit_cnt))
+  const int members = absh::unit_members(c, lists->schedule);
+  if (members > 1 && (!lists->unit_list || !lists->unit_cnt))
     return fail(ABSH_EINVAL, "lists needs unit_list and unit_cnt for this schedule");
+  if (lists->schedule == ABSH_SCHED_LPT && members > 1 && !lists->unit_queue)
+    return fail(ABSH_EINVAL, "lists needs unit_queue for ABSH_SCHED_LPT");
   L->queue = lists->queue;
   L->counts = lists->counts;
   L->kv_idx = lists->kv_idx;
   L->unit_list = lists->unit_list;
   L->unit_cnt = lists->unit_cnt;
   L->sched = lists->sched;
-  L->members = absh::unit_members(c, lists->schedule);
+  L->members = members;
+  if (lists->schedule == ABSH_SCHED_LPT && members > 1) L->unit_queue = lists->unit_queue;
+  L->counters = lists->pull;
+  L->wg_busy = lists->wg_busy;
   if (lists->schedule == ABSH_SCHED_RANKS) {
     L->head_order = lists->head_order;
     L->strict = lists->strict_ranks ? 1 : 0;
@@ -460,7 +565,7 @@ absh_status absh_sparse_attn_v8(absh_ctx* c, const void* qh, const void* kh, con
   if (absh_status st = attn_lists(c, lists, &L)) return st;
   const int members = lists ? L.members : (c->block >= 128 ? 2 : 4);
   if (!absh::union_attention_supported(d, c->block, members))
-    return fail(ABSH_EUNSUPPORTED, "8-bit values need block 64 or 128 and a group schedule (not ABSH_SCHED_LPT)");
+    return fail(ABSH_EUNSUPPORTED, "8-bit values need block 64 or 128");
   if (absh_status st = use_device(c)) return st;
   ABSH_HIP(absh::launch_union_attention(c, qh, kh, vt8, vscale, oh, B, H, d, lists ? &L : nullptr,
                                         reinterpret_cast<hipStream_t>(stream)),

@@ -169,6 +169,7 @@ void attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, c
   __shared__ __attribute__((aligned(1024))) char ring[NS * C::STAGE];
   __shared__ int s_next[2];  // next unit, double-buffered: read one slot while the other is written
 
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();  // for the optional busy record
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -234,11 +235,18 @@ void attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, c
       cnt = as_const(L.counts)[tile];
       plain = as_const(L.kv_idx + (size_t)tile * nb);
     } else {
-      // segment position -> head (through head_order when the segments follow ranks) and unit
-      const int slot = pos / per_head;
-      bh = L.head_order ? __builtin_amdgcn_readfirstlane(as_const(L.head_order)[slot]) : slot;
-      const int unit = bh * per_head + (pos - slot * per_head);
-      qb0 = (pos - slot * per_head) * members;
+      // segment position -> unit: through unit_queue, or head_order (segments
+      // following ranks), or in order
+      int unit;
+      if (L.unit_queue) {
+        unit = __builtin_amdgcn_readfirstlane(as_const(L.unit_queue)[pos]);
+      } else {
+        const int slot = pos / per_head;
+        const int bh_ = L.head_order ? __builtin_amdgcn_readfirstlane(as_const(L.head_order)[slot]) : slot;
+        unit = bh_ * per_head + (pos - slot * per_head);
+      }
+      bh = unit / per_head;
+      qb0 = (unit - bh * per_head) * members;
       cnt = dense ? nb : as_const(L.unit_cnt)[unit];
       if (!dense) flagged = as_const(reinterpret_cast<const int32_t*>(L.unit_list) + (size_t)unit * nb);
     }
@@ -313,7 +321,7 @@ void attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, c
     // has padding keys; otherwise only the last block of a head can be short, and
     // lists are ascending, so only a unit's final entry can need the mask.
     const bool tail_partial =
-        ((entry(cnt - 1) & kBlockMask) == (uint32_t)(nb - 1)) && (N - (nb - 1) * BLK < C::KB);
+        cnt > 0 && ((entry(cnt - 1) & kBlockMask) == (uint32_t)(nb - 1)) && (N - (nb - 1) * BLK < C::KB);
 
     // One staged key block for this wave's members in MASK (bit 0: 2 grp, bit 1: 2 grp + 1).
     auto compute = [&](const char* cur, int j, auto members_c, auto masked_c) __attribute__((always_inline)) {
@@ -455,6 +463,10 @@ void attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, c
 
   // The last workgroup to finish resets the pull counters for the next launch.
   if (tid == 0) {
+    if (L.wg_busy) {
+      L.wg_busy[2 * blockIdx.x] = t_start;
+      L.wg_busy[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+    }
     __threadfence();
     if (atomicAdd(&counters[kSegments], 1) == (int)gridDim.x - 1) {
       for (int s = 0; s <= kSegments; ++s) atomicExch(&counters[s], 0);
@@ -483,9 +495,11 @@ hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void*
   const float scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
   AttnLists Lk = L;
   if (dense) Lk = AttnLists{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, C::MEMBERS};
+  if (grid > c->num_cus * kMaxAttnWgPerCu) return hipErrorInvalidConfiguration;  // wg_busy's bound
+  int32_t* counters = Lk.counters ? Lk.counters : c->counters;
   attn_kernel<D, BLK, GROUPS><<<grid, C::THREADS, 0, s>>>(
       reinterpret_cast<const bf16_t*>(qh), reinterpret_cast<const bf16_t*>(kh), reinterpret_cast<const bf16_t*>(vt),
-      reinterpret_cast<bf16_t*>(oh), Lk, c->counters, units, c->nb, c->n_pad, c->N, scale_log2);
+      reinterpret_cast<bf16_t*>(oh), Lk, counters, units, c->nb, c->n_pad, c->N, scale_log2);
   return hipGetLastError();
 }
 

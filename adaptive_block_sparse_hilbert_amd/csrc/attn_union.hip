@@ -164,6 +164,7 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
   };
   __shared__ int s_next[2];
 
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();  // for the optional busy record
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets per-wave branches be scalar
@@ -203,11 +204,18 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
     __syncthreads();  // s_next[parity] is published; every wave is done with the previous unit
     const int pos = __builtin_amdgcn_readfirstlane(s_next[parity]);
     if (pos < 0) break;
-    // segment position -> head (through head_order when the segments follow ranks) and unit
-    const int slot = pos / per_head;
-    const int bh = L.head_order ? __builtin_amdgcn_readfirstlane(as_const(L.head_order)[slot]) : slot;
-    const int unit = bh * per_head + (pos - slot * per_head);
-    const int qb0 = (pos - slot * per_head) * C::MEMBERS;
+    // segment position -> unit: through unit_queue (longest first within each run),
+    // or head_order (segments following ranks), or in order
+    int unit;
+    if (L.unit_queue) {
+      unit = __builtin_amdgcn_readfirstlane(as_const(L.unit_queue)[pos]);
+    } else {
+      const int slot = pos / per_head;
+      const int bh_ = L.head_order ? __builtin_amdgcn_readfirstlane(as_const(L.head_order)[slot]) : slot;
+      unit = bh_ * per_head + (pos - slot * per_head);
+    }
+    const int bh = unit / per_head;
+    const int qb0 = (unit - bh * per_head) * C::MEMBERS;
     const int cnt = dense ? nb : as_const(L.unit_cnt)[unit];
     const_i32 list = dense ? nullptr : as_const(reinterpret_cast<const int32_t*>(L.unit_list) + (size_t)unit * nb);
     uint32_t present = 0;
@@ -570,6 +578,10 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
 
   // The last workgroup to finish resets the pull counters for the next launch.
   if (tid == 0) {
+    if (L.wg_busy) {
+      L.wg_busy[2 * blockIdx.x] = t_start;
+      L.wg_busy[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+    }
     __threadfence();
     if (atomicAdd(&counters[kSegments], 1) == (int)gridDim.x - 1) {
       for (int s = 0; s <= kSegments; ++s) atomicExch(&counters[s], 0);
@@ -597,9 +609,11 @@ hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void*
   const float scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
   AttnLists Lk = L;
   if (dense) Lk = AttnLists{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, C::MEMBERS};
+  if (grid > c->num_cus * kMaxAttnWgPerCu) return hipErrorInvalidConfiguration;  // wg_busy's bound
+  int32_t* counters = Lk.counters ? Lk.counters : c->counters;
   union_attn_kernel<D, BLK, F8><<<grid, C::THREADS, 0, s>>>(
       reinterpret_cast<const bf16_t*>(qh), reinterpret_cast<const bf16_t*>(kh), reinterpret_cast<const char*>(vt),
-      vscale, reinterpret_cast<bf16_t*>(oh), Lk, c->counters, units, c->nb, c->n_pad, c->N, scale_log2);
+      vscale, reinterpret_cast<bf16_t*>(oh), Lk, counters, units, c->nb, c->n_pad, c->N, scale_log2);
   return hipGetLastError();
 }
 

@@ -49,6 +49,34 @@ __global__ __launch_bounds__(kThreads) void gather_rows(const void* __restrict__
   *reinterpret_cast<Pack8*>(xh + row * d + (size_t)e * 8) = v;
 }
 
+// The same gather with float rows out: bf16 inputs widen exactly, float inputs
+// are copied unchanged (routing from float queries and keys).
+__global__ __launch_bounds__(kThreads) void gather_rows_f32(const void* __restrict__ x, int is_f32,
+                                                            float* __restrict__ xh, const int32_t* __restrict__ perm,
+                                                            int N, int n_pad, int H, int d, uint64_t pieces) {
+  const uint64_t id = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (id >= pieces) return;
+  const int per_row = d >> 2;
+  const int e = (int)(id % per_row);
+  const uint64_t row = id / per_row;  // (b*H + h)*n_pad + r
+  const int r = (int)(row % n_pad);
+  const uint64_t bh = row / n_pad;
+  const int h = (int)(bh % H);
+  const uint64_t b = bh / H;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (r < N) {
+    const size_t elem = ((b * N + perm[r]) * H + h) * d + (size_t)e * 4;
+    if (is_f32) {
+      v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + elem);
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(x) + elem);
+      v = make_float4(bf16_to_f32((bf16_t)(w.x & 0xFFFFu)), bf16_to_f32((bf16_t)(w.x >> 16)),
+                      bf16_to_f32((bf16_t)(w.y & 0xFFFFu)), bf16_to_f32((bf16_t)(w.y >> 16)));
+    }
+  }
+  *reinterpret_cast<float4*>(xh + row * d + (size_t)e * 4) = v;
+}
+
 // vt[b, h, j, c, k] = x[b, perm[j*blk + k], h, c] for k < blk, with KB = vt_keys(blk)
 // keys per block (keys blk..KB-1 and pad tokens are zero): one workgroup per
 // (b, h, j) stages the block's rows in LDS and writes them back transposed.
@@ -116,9 +144,16 @@ void launch_vt(const void* x, int is_f32, bf16_t* vt, const int32_t* perm, int N
 }  // namespace
 
 hipError_t launch_permute(const absh_ctx* c, const void* x, int x_is_f32, void* xh, int B, int H, int d,
-                          int layout_vt, hipStream_t s) {
+                          int layout, hipStream_t s) {
   bf16_t* out = reinterpret_cast<bf16_t*>(xh);
-  if (!layout_vt) {
+  if (layout == ABSH_ROWS_F32) {
+    const uint64_t pieces = (uint64_t)B * H * c->n_pad * (d / 4);
+    const unsigned grid = (unsigned)((pieces + kThreads - 1) / kThreads);
+    gather_rows_f32<<<grid, kThreads, 0, s>>>(x, x_is_f32, reinterpret_cast<float*>(xh), c->perm, c->N, c->n_pad,
+                                              H, d, pieces);
+    return hipGetLastError();
+  }
+  if (layout == ABSH_ROWS) {
     const uint64_t pieces = (uint64_t)B * H * c->n_pad * (d / 8);
     const unsigned grid = (unsigned)((pieces + kThreads - 1) / kThreads);
     gather_rows<<<grid, kThreads, 0, s>>>(x, x_is_f32, out, c->perm, c->N, c->n_pad, H, d, pieces);

@@ -19,17 +19,18 @@ namespace {
 // ------------------------------------------------------------------ pooling
 
 // xbar[bh, j, c] = (sum over the block's true rows of xh[bh, r, c]) / n_j.
-// One workgroup per (bh, j). Each thread reads 16-byte pieces (8 channels) of
-// every ROWS-th row and keeps eight float64 partial sums; the partials of a
-// channel are then added in LDS. Sums of bf16 values in float64 are exact for
-// any operands whose exponents lie within 45 binades of each other, so the
-// order of the additions does not change the result.
+// One workgroup per (bh, j). Each thread reads 16-byte pieces (8 bf16 or 4 float
+// channels) of every ROWS-th row and keeps float64 partial sums; the partials of
+// a channel are then added in LDS. Sums of bf16 values in float64 are exact for
+// any operands whose exponents lie within 45 binades of each other, so the order
+// of the additions does not change the result (float values: within 29 binades).
 constexpr int kPoolThreads = 256;
 
-template <int D>
-__global__ __launch_bounds__(kPoolThreads) void pool_kernel(const bf16_t* __restrict__ xh, float* __restrict__ xbar,
+template <int D, typename T>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(const T* __restrict__ xh, float* __restrict__ xbar,
                                                             int N, int n_pad, int nb, int blk) {
-  constexpr int PIECES = D / 8;
+  constexpr int EPP = 16 / (int)sizeof(T);  // channels per 16-byte piece
+  constexpr int PIECES = D / EPP;
   constexpr int ROWS = kPoolThreads / PIECES;
   __shared__ double part[ROWS][D + 1];
   const int j = blockIdx.x % nb;
@@ -37,20 +38,27 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const bf16_t* __rest
   const int piece = threadIdx.x % PIECES;
   const int r0 = threadIdx.x / PIECES;
   const int n = min(blk, N - j * blk);
-  const bf16_t* src = xh + (bh * n_pad + (size_t)j * blk) * D + piece * 8;
-  double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  const T* src = xh + (bh * n_pad + (size_t)j * blk) * D + piece * EPP;
+  double acc[EPP];
+#pragma unroll
+  for (int e = 0; e < EPP; ++e) acc[e] = 0.0;
 #pragma unroll 4
   for (int r = r0; r < n; r += ROWS) {
     const uint4 w = *reinterpret_cast<const uint4*>(src + (size_t)r * D);
     const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += (double)bf16_to_f32((bf16_t)(u[e] & 0xFFFFu));
-      acc[2 * e + 1] += (double)bf16_to_f32((bf16_t)(u[e] >> 16));
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)bf16_to_f32((bf16_t)(u[e] & 0xFFFFu));
+        acc[2 * e + 1] += (double)bf16_to_f32((bf16_t)(u[e] >> 16));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(u[e]);
     }
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) part[r0][piece * 8 + e] = acc[e];
+  for (int e = 0; e < EPP; ++e) part[r0][piece * EPP + e] = acc[e];
   __syncthreads();
   for (int c = threadIdx.x; c < D; c += kPoolThreads) {
     double sum = 0.0;
@@ -797,6 +805,52 @@ __global__ __launch_bounds__(1024) void segments_kernel(const int32_t* __restric
   if (threadIdx.x <= kSegments) sched[threadIdx.x] = threadIdx.x == 0 ? 0 : bound[threadIdx.x];
 }
 
+// The longest-first order of the group units inside each XCD run (the one-GPU
+// reading of the review's RLB as a longest-processing-time-first queue, with the
+// XCDs' contiguous runs as in the "xcd" schedule): run x = blockIdx.x holds the
+// units sched[x] .. sched[x + 1] - 1, ordered by union length (cost) descending,
+// ties by unit index. A stable counting sort over the run in chunks of 1024: each
+// unit's place is the start of its cost's bin plus the units of equal cost before
+// it in its chunk.
+__global__ __launch_bounds__(1024) void unit_lpt_kernel(const int32_t* __restrict__ cost, int units, int nb,
+                                                        const int32_t* __restrict__ sched,
+                                                        int32_t* __restrict__ unit_queue) {
+  __shared__ int32_t start[kMaxBins];
+  __shared__ int32_t chunk_cost[1024];
+  __shared__ int64_t buf[1024];
+  const int lo = sched[blockIdx.x], hi = sched[blockIdx.x + 1];
+  for (int b = threadIdx.x; b <= nb; b += 1024) start[b] = 0;
+  __syncthreads();
+  for (int u = lo + (int)threadIdx.x; u < hi; u += 1024) atomicAdd(&start[cost[u]], 1);
+  __syncthreads();
+  // bins in descending cost: the exclusive scan of the counts from cost nb down
+  int64_t carry = 0;
+  for (int b0 = 0; b0 <= nb; b0 += 1024) {
+    const int b = nb - (b0 + (int)threadIdx.x);  // cost of this thread's bin
+    const int64_t v = b >= 0 ? start[b] : 0;
+    int64_t tot;
+    const int64_t ex = block_exclusive_scan<int64_t>(v, buf, tot);
+    __syncthreads();
+    if (b >= 0) start[b] = (int32_t)(carry + ex);
+    carry += tot;
+    __syncthreads();
+  }
+  for (int c0 = lo; c0 < hi; c0 += 1024) {
+    const int u = c0 + (int)threadIdx.x;
+    const int mine = u < hi ? cost[u] : -1;
+    chunk_cost[threadIdx.x] = mine;
+    __syncthreads();
+    if (u < hi) {
+      int r = 0;
+      for (int v = 0; v < (int)threadIdx.x; ++v) r += chunk_cost[v] == mine;
+      unit_queue[lo + start[mine] + r] = u;
+    }
+    __syncthreads();
+    if (u < hi) atomicAdd(&start[mine], 1);
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------ structured router
 
 // The LVSA note's block-sparse pattern (a structured local window plus global
@@ -833,23 +887,29 @@ __global__ __launch_bounds__(256) void window_anchor_kernel(int nb, int tiles, i
 // blocks, W_r = sum of work_h over the rank's heads; L_r of Eq. 1 is W_r / nb,
 // and every ratio below is the same in either unit.
 //
-// RLB searches, exhaustively, the plans in which every rank above the mean load
-// gives at most one of its heads to a distinct rank below the mean load (the
-// one-send-one-receive space with at most one head per rank); the plan of least
-// (max W^new, sum (W^new)^2) wins, ties to the first in enumeration order (the
-// first sender's option varies slowest; a sender's options are: none, then
-// (head, receiver) with heads ascending and receivers ascending per head). A
-// space above kMaxPlans combinations is not searched. SASA gives rank r the
-// budget E_r = floor(n1 dW_r) when dW_r = W_max - W_r exceeds n2 W_max (float64),
-// spent by water-filling the rank's tiles along their importance order.
+// RLB searches the one-send-one-receive plans over the review's pair topologies
+// (3.2): the eight ranks are matched in pairs (the 105 perfect matchings, in
+// canonical order: the lowest unpaired rank with each higher unpaired rank,
+// ascending, recursively), and a pair (a, b) either moves nothing, or a sends one
+// of its heads to b, or b one of its heads to a, or they swap one head each (in
+// that order; heads ascending, a's head varying slowest in a swap). The plan of
+// least (max W^new, sum (W^new)^2) wins, ties to the first in the order matching,
+// then the pairs' options with the first pair varying slowest. The pairs of a
+// matching touch disjoint ranks, so each matching's best plan is exact pair by
+// pair: its least maximum M is the largest over its pairs of the pair's least
+// maximum, and each pair takes, among its options of maximum at most M, the first
+// of least sum of squares. SASA gives rank r the budget E_r = floor(n1 dW_r) when
+// dW_r = W_max - W_r exceeds n2 W_max (float64), spent by water-filling the
+// rank's tiles along their importance order.
 //
 // info (float64, kRankInfo entries): [0] rho before, [1] after migration, [2]
 // after augmentation; [3] policy taken (0 none, 1 SASA, 2 RLB + SASA, 3 RLB); [4]
 // moves; [5..12] W before, [13..20] after migration, [21..28] after
-// augmentation; [29..36] E_r; [37..60] the moves as (head, from, to); [61]
-// combinations searched; [62] 1 if the space was too large to search.
+// augmentation; [29..36] E_r; [37..60] the moves as (head, from, to), by sending
+// rank; [61] candidate plans in the space (sum over matchings of the product of
+// the pairs' option counts); [62] 0.
 constexpr int kRanks = kSegments;
-constexpr int kMaxPlans = 1 << 26;
+constexpr int kMatchings = 105;  // perfect matchings of eight ranks
 
 __device__ double rank_rho(const int64_t* W) {
   int64_t mx = W[0], sum = 0;
@@ -860,89 +920,107 @@ __device__ double rank_rho(const int64_t* W) {
   return (double)mx / ((double)sum / kRanks);
 }
 
-__global__ __launch_bounds__(1024) void rank_plan_kernel(const int32_t* __restrict__ work, int BH, int per_head,
-                                                         int members, int policy, double k1, double k2, double n1,
-                                                         double n2, int32_t* __restrict__ owner,
-                                                         int32_t* __restrict__ head_order,
-                                                         int64_t* __restrict__ budget, int32_t* __restrict__ sched,
-                                                         double* __restrict__ info) {
+// matching t in canonical order: pairs (a[i], b[i]), i = 0..3, a ascending
+__device__ void rank_matching(int t, int* pa, int* pb) {
+  int free_[kRanks];
+  for (int r = 0; r < kRanks; ++r) free_[r] = r;
+  int n = kRanks;
+  const int pick[3] = {t / 15 + 1, (t / 3) % 5 + 1, t % 3 + 1};
+  for (int i = 0; i < 4; ++i) {
+    const int j = i < 3 ? pick[i] : 1;
+    pa[i] = free_[0];
+    pb[i] = free_[j];
+    for (int k = j; k + 1 < n; ++k) free_[k] = free_[k + 1];  // drop free_[j], then free_[0]
+    for (int k = 0; k + 1 < n - 1; ++k) free_[k] = free_[k + 1];
+    n -= 2;
+  }
+}
+
+// The options of pair (a, b) in order; fn(index, moved head of a or -1, of b or -1, wa, wb)
+// returns true to stop.
+template <typename Fn>
+__device__ void pair_options(const int32_t* work, const int* hlo, const int64_t* W, int a, int b, Fn fn) {
+  const int na = hlo[a + 1] - hlo[a], nb_ = hlo[b + 1] - hlo[b];
+  int idx = 0;
+  if (fn(idx++, -1, -1, W[a], W[b])) return;
+  for (int i = 0; i < na; ++i) {
+    const int64_t d = work[hlo[a] + i];
+    if (fn(idx++, hlo[a] + i, -1, W[a] - d, W[b] + d)) return;
+  }
+  for (int i = 0; i < nb_; ++i) {
+    const int64_t d = work[hlo[b] + i];
+    if (fn(idx++, -1, hlo[b] + i, W[a] + d, W[b] - d)) return;
+  }
+  for (int i = 0; i < na; ++i)
+    for (int j = 0; j < nb_; ++j) {
+      const int64_t x = work[hlo[a] + i], y = work[hlo[b] + j];
+      if (fn(idx++, hlo[a] + i, hlo[b] + j, W[a] - x + y, W[b] - y + x)) return;
+    }
+}
+
+__global__ __launch_bounds__(128) void rank_plan_kernel(const int32_t* __restrict__ work, int BH, int per_head,
+                                                        int members, int policy, double k1, double k2, double n1,
+                                                        double n2, int32_t* __restrict__ owner,
+                                                        int32_t* __restrict__ head_order,
+                                                        int64_t* __restrict__ budget, int32_t* __restrict__ sched,
+                                                        double* __restrict__ info) {
   __shared__ int64_t W0[kRanks];
   __shared__ int hlo[kRanks + 1];
-  __shared__ int snd[kRanks], rcv[kRanks], opt[kRanks];
-  __shared__ int n_snd, n_rcv, mode;
-  __shared__ int n_plans;
-  __shared__ int64_t red_max[1024], red_sq[1024];
-  __shared__ int red_idx[1024];
+  __shared__ int mode;
+  __shared__ int64_t red_max[128], red_sq[128];
+  __shared__ int red_idx[128];
   const int tid = threadIdx.x;
   if (tid == 0) {
-    int64_t total = 0;
     for (int r = 0; r <= kRanks; ++r) hlo[r] = (int)((int64_t)r * BH / kRanks);
     for (int r = 0; r < kRanks; ++r) {
       int64_t w = 0;
       for (int h = hlo[r]; h < hlo[r + 1]; ++h) w += work[h];
       W0[r] = w;
-      total += w;
     }
     const double rho = rank_rho(W0);
     mode = policy >= 0 ? policy : (rho < k1 ? 0 : rho < k2 ? 1 : 2);
-    n_snd = n_rcv = 0;
-    int64_t space = 1;
-    if (mode == 2 || mode == 3) {
-      for (int r = 0; r < kRanks; ++r) {
-        if (W0[r] * kRanks > total) snd[n_snd++] = r;
-        if (W0[r] * kRanks < total) rcv[n_rcv++] = r;
-      }
-      for (int i = 0; i < n_snd; ++i) {
-        opt[i] = 1 + (hlo[snd[i] + 1] - hlo[snd[i]]) * n_rcv;
-        space = space * opt[i] > (int64_t)kMaxPlans ? (int64_t)kMaxPlans + 1 : space * opt[i];
-      }
-    }
-    info[61] = (double)space;
-    info[62] = space > kMaxPlans ? 1.0 : 0.0;
-    if (space > kMaxPlans) n_snd = 0;  // not searched: no migration
-    int64_t np = 1;
-    for (int i = 0; i < n_snd; ++i) np *= opt[i];
-    n_plans = (int)np;
     info[0] = rho;
     info[3] = (double)mode;
   }
   __syncthreads();
-  // every plan p: decode the senders' choices, keep the least (max, sum of squares, p)
+  const bool rlb = mode == 2 || mode == 3;
+  // matching tid: its least maximum M and least sum of squares under M
   int64_t best_max = INT64_MAX, best_sq = INT64_MAX;
-  int best_p = INT32_MAX;
-  for (int p = tid; p < n_plans; p += 1024) {
-    int64_t w[kRanks];
-    for (int r = 0; r < kRanks; ++r) w[r] = W0[r];
-    unsigned used = 0;
-    bool ok = true;
-    int q = p;
-    for (int i = n_snd - 1; i >= 0; --i) {
-      const int c = q % opt[i];
-      q /= opt[i];
-      if (c == 0) continue;
-      const int h = hlo[snd[i]] + (c - 1) / n_rcv, dst = rcv[(c - 1) % n_rcv];
-      if (used & (1u << dst)) ok = false;
-      used |= 1u << dst;
-      w[snd[i]] -= work[h];
-      w[dst] += work[h];
+  int best_t = INT32_MAX;
+  if (rlb && tid < kMatchings) {
+    int pa[4], pb[4];
+    rank_matching(tid, pa, pb);
+    int64_t M = 0;
+    for (int i = 0; i < 4; ++i) {
+      int64_t bm = INT64_MAX;
+      pair_options(work, hlo, W0, pa[i], pb[i], [&](int, int, int, int64_t wa, int64_t wb) {
+        const int64_t m = wa > wb ? wa : wb;
+        bm = m < bm ? m : bm;
+        return false;
+      });
+      M = bm > M ? bm : M;
     }
-    if (!ok) continue;
-    int64_t mx = w[0], sq = 0;
-    for (int r = 0; r < kRanks; ++r) {
-      mx = w[r] > mx ? w[r] : mx;
-      sq += w[r] * w[r];
+    int64_t S = 0;
+    for (int i = 0; i < 4; ++i) {
+      int64_t least = INT64_MAX;
+      pair_options(work, hlo, W0, pa[i], pb[i], [&](int, int, int, int64_t wa, int64_t wb) {
+        if ((wa > wb ? wa : wb) <= M) {
+          const int64_t q = wa * wa + wb * wb;
+          least = q < least ? q : least;
+        }
+        return false;
+      });
+      S += least;
     }
-    if (mx < best_max || (mx == best_max && (sq < best_sq || (sq == best_sq && p < best_p)))) {
-      best_max = mx;
-      best_sq = sq;
-      best_p = p;
-    }
+    best_max = M;
+    best_sq = S;
+    best_t = tid;
   }
   red_max[tid] = best_max;
   red_sq[tid] = best_sq;
-  red_idx[tid] = best_p;
+  red_idx[tid] = best_t;
   __syncthreads();
-  for (int off = 512; off > 0; off >>= 1) {
+  for (int off = 64; off > 0; off >>= 1) {
     if (tid < off) {
       const int o = tid + off;
       if (red_max[o] < red_max[tid] ||
@@ -958,20 +1036,57 @@ __global__ __launch_bounds__(1024) void rank_plan_kernel(const int32_t* __restri
   if (tid != 0) return;
   for (int r = 0; r < kRanks; ++r)
     for (int h = hlo[r]; h < hlo[r + 1]; ++h) owner[h] = r;
-  int choice[kRanks];
-  int q = red_idx[0];
-  for (int i = n_snd - 1; i >= 0; --i) {
-    choice[i] = q % opt[i];
-    q /= opt[i];
+  // candidate plans in the space
+  double space = 0.0;
+  for (int t = 0; t < kMatchings; ++t) {
+    int pa[4], pb[4];
+    rank_matching(t, pa, pb);
+    double n = 1.0;
+    for (int i = 0; i < 4; ++i) {
+      const double na = hlo[pa[i] + 1] - hlo[pa[i]], nb_ = hlo[pb[i] + 1] - hlo[pb[i]];
+      n *= 1.0 + na + nb_ + na * nb_;
+    }
+    space += n;
   }
-  int n_moves = 0;  // the moves in sender order
-  for (int i = 0; i < n_snd; ++i) {
-    if (choice[i] == 0) continue;
-    const int h = hlo[snd[i]] + (choice[i] - 1) / n_rcv, dst = rcv[(choice[i] - 1) % n_rcv];
-    owner[h] = dst;
-    info[37 + 3 * n_moves] = h;
-    info[38 + 3 * n_moves] = snd[i];
-    info[39 + 3 * n_moves] = dst;
+  info[61] = rlb ? space : 0.0;
+  info[62] = 0.0;
+  int send_head[kRanks], send_to[kRanks];
+  for (int r = 0; r < kRanks; ++r) send_head[r] = -1;
+  if (rlb) {
+    int pa[4], pb[4];
+    rank_matching(red_idx[0], pa, pb);
+    const int64_t M = red_max[0];
+    for (int i = 0; i < 4; ++i) {
+      int64_t least = INT64_MAX;
+      pair_options(work, hlo, W0, pa[i], pb[i], [&](int, int, int, int64_t wa, int64_t wb) {
+        if ((wa > wb ? wa : wb) <= M) {
+          const int64_t q = wa * wa + wb * wb;
+          least = q < least ? q : least;
+        }
+        return false;
+      });
+      const int a = pa[i], b = pb[i];
+      pair_options(work, hlo, W0, a, b, [&](int, int ha, int hb, int64_t wa, int64_t wb) {
+        if ((wa > wb ? wa : wb) > M || wa * wa + wb * wb != least) return false;
+        if (ha >= 0) {
+          send_head[a] = ha;
+          send_to[a] = b;
+        }
+        if (hb >= 0) {
+          send_head[b] = hb;
+          send_to[b] = a;
+        }
+        return true;
+      });
+    }
+  }
+  int n_moves = 0;  // the moves by sending rank
+  for (int r = 0; r < kRanks; ++r) {
+    if (send_head[r] < 0) continue;
+    owner[send_head[r]] = send_to[r];
+    info[37 + 3 * n_moves] = send_head[r];
+    info[38 + 3 * n_moves] = r;
+    info[39 + 3 * n_moves] = send_to[r];
     ++n_moves;
   }
   int64_t W1[kRanks] = {};
@@ -1083,13 +1198,19 @@ __global__ void rank_final_kernel(const int32_t* __restrict__ work, const int32_
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_pool(const absh_ctx* c, const void* xh, float* xbar, int B, int H, int d, hipStream_t s) {
+hipError_t launch_pool(const absh_ctx* c, const void* xh, int xh_is_f32, float* xbar, int B, int H, int d,
+                       hipStream_t s) {
   const unsigned grid = (unsigned)((uint64_t)B * H * c->nb);
   const bf16_t* x = reinterpret_cast<const bf16_t*>(xh);
-  if (d == 64)
-    pool_kernel<64><<<grid, kPoolThreads, 0, s>>>(x, xbar, c->N, c->n_pad, c->nb, c->block);
+  const float* xf = reinterpret_cast<const float*>(xh);
+  if (d == 64 && !xh_is_f32)
+    pool_kernel<64, bf16_t><<<grid, kPoolThreads, 0, s>>>(x, xbar, c->N, c->n_pad, c->nb, c->block);
+  else if (d == 128 && !xh_is_f32)
+    pool_kernel<128, bf16_t><<<grid, kPoolThreads, 0, s>>>(x, xbar, c->N, c->n_pad, c->nb, c->block);
+  else if (d == 64)
+    pool_kernel<64, float><<<grid, kPoolThreads, 0, s>>>(xf, xbar, c->N, c->n_pad, c->nb, c->block);
   else if (d == 128)
-    pool_kernel<128><<<grid, kPoolThreads, 0, s>>>(x, xbar, c->N, c->n_pad, c->nb, c->block);
+    pool_kernel<128, float><<<grid, kPoolThreads, 0, s>>>(xf, xbar, c->N, c->n_pad, c->nb, c->block);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -1148,7 +1269,7 @@ hipError_t launch_workload(const absh_ctx* c, const RouteBuffers& rb, int BH, hi
 hipError_t launch_rank_stage(const absh_ctx* c, const RouteBuffers& rb, int BH, const RankOpts& o, hipStream_t s) {
   const int members = unit_members(c, ABSH_SCHED_RANKS);
   const int per_head = (c->nb + members - 1) / members;
-  rank_plan_kernel<<<1, 1024, 0, s>>>(rb.work, BH, per_head, members, o.policy, o.k1, o.k2, o.n1, o.n2, rb.owner,
+  rank_plan_kernel<<<1, 128, 0, s>>>(rb.work, BH, per_head, members, o.policy, o.k1, o.k2, o.n1, o.n2, rb.owner,
                                       rb.head_order, rb.budget, rb.sched, rb.rank_info);
   return hipGetLastError();
 }
@@ -1182,7 +1303,9 @@ int queue_scan_tiles(int tiles, int nb) {
 int slack_aux_words(int tiles) { return kMaxBins + queue_chunks(tiles); }
 
 int unit_members(const absh_ctx* c, int schedule) {
-  if (schedule == ABSH_SCHED_LPT) return 1;
+  // longest first: group units where the union kernel runs them (blocks of 64 and
+  // 128), single tiles in the tile queue's order otherwise
+  if (schedule == ABSH_SCHED_LPT && c->block < 64) return 1;
   return c->block >= 128 ? 2 : 4;
 }
 
@@ -1201,13 +1324,25 @@ hipError_t launch_groups(const absh_ctx* c, const RouteBuffers& rb, int BH, int 
   return hipGetLastError();
 }
 
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s) {
+  zero_i32_kernel<<<(n + 255) / 256, 256, 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_segments(const absh_ctx* c, const RouteBuffers& rb, int BH, int schedule, hipStream_t s) {
   const int members = unit_members(c, schedule);
   if (members == 1)
     segments_kernel<<<1, 1024, 0, s>>>(rb.counts, BH * c->nb, 0, 1, rb.sched);
   else
-    segments_kernel<<<1, 1024, 0, s>>>(rb.unit_cnt, unit_count(c, BH, members), schedule == ABSH_SCHED_XCD,
-                                       members, rb.sched);
+    segments_kernel<<<1, 1024, 0, s>>>(rb.unit_cnt, unit_count(c, BH, members),
+                                       schedule == ABSH_SCHED_XCD || schedule == ABSH_SCHED_LPT, members, rb.sched);
+  return hipGetLastError();
+}
+
+hipError_t launch_unit_lpt(const absh_ctx* c, const RouteBuffers& rb, int BH, hipStream_t s) {
+  const int members = unit_members(c, ABSH_SCHED_LPT);
+  unit_lpt_kernel<<<kSegments, 1024, 0, s>>>(rb.unit_cnt, unit_count(c, BH, members), c->nb, rb.sched,
+                                             rb.unit_queue);
   return hipGetLastError();
 }
 

@@ -7,7 +7,10 @@ already resident in HBM:
     -> block-sparse attention over the retained blocks
     -> unpermute the output back to grid order.
 The default workload is 720p video at 40 heads (grid 21 x 45 x 80 = 75,600 tokens,
-d = 128, block 64, p = 0.9, k = 4, longest-first queue).
+d = 128, block 64, p = 0.9, k = 4, the "xcd" schedule). --all-configs runs the
+five synthetic workloads one after another (the 6x horizon at p = 0.8, 0.9 and
+0.95), one JSON line each; the head-skew workload runs on the longest-first
+schedule its configuration names, the tiny one routes from float32 q and k.
 
 value = retained FLOPs / step time, where retained FLOPs = sum over tiles and
 retained blocks of 4 * n_i * n_j * d with true token counts. Each stage is timed
@@ -20,7 +23,16 @@ value product runs on fp8 MFMAs. Half the retained FLOPs (Q K^T) stay bf16 and
 half (P V) are fp8, so the roofline peak is then 1 / (0.5 / 2.5 + 0.5 / 5.0)
 PFLOP/s = 3.33 PFLOP/s.
 
-Prints one JSON line. Inputs are synthetic (see workloads/), data = "synthetic".
+Besides the throughput, each line reports the balance of the attention launch:
+rho_wg = max / mean busy time over its workgroups, from the per-workgroup busy
+record the attention kernel writes (Eq. 2 of the review read over workgroups),
+and rho_sim, the same ratio for a list schedule of the launch's work units over
+as many workers, each worker pulling from its XCD's run first as the kernel does,
+with unit cost = union length + 1. The cpu_baseline leg also checks head 0's
+lists (before slack fill) against the oracle's routing of that head and reports
+how many tiles differ and how many of those the routing tolerance excuses.
+
+Prints one JSON line per workload. Inputs are synthetic (see workloads/), data = "synthetic".
 """
 from __future__ import annotations
 
@@ -109,6 +121,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="720p-40h")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="run every synthetic workload (one JSON line each) instead of --workload")
+    ap.add_argument("--route-f32", action="store_true",
+                    help="route from float32 q and k rows (an extra float32 permute of q and k)")
     ap.add_argument("--p", type=float, default=None, help="override the workload's Top-p")
     ap.add_argument("--schedule", default="xcd", choices=("order", "lpt", "xcd", "ranks"),
                     help="tile schedule of the attention kernel")
@@ -137,29 +153,39 @@ def parse():
     return ap.parse_args()
 
 
+ALL_RUNS = ((0, None), (1, None), (2, None), (3, None), (4, 0.8), (4, 0.9), (4, 0.95))
+
+
 def main():
     args = parse()
-    if args.values == "fp8" and args.schedule == "lpt":
-        print("bench.py: 8-bit values run on the group schedules (order, xcd, ranks), not on single tiles (lpt).",
-              file=sys.stderr)
-        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the path would shard by head across GPUs).", file=sys.stderr)
         sys.exit(2)
+    import workloads as W
 
+    if not args.all_configs:
+        print(json.dumps(measure(args, W.workload(args.workload), args.p, args.schedule, args.route_f32)))
+        return
+    for index, p in ALL_RUNS:
+        w = W.workload(index)
+        schedule = "lpt" if w.lpt else args.schedule
+        print(json.dumps(measure(args, w, p, schedule, args.route_f32 or w.dtype == "fp32")), flush=True)
+
+
+def measure(args, w, p, schedule, route_f32):
+    """One workload: warm-up, timed steps, dense reference, balance, cpu baseline -> the JSON record."""
     import numpy as np
     import torch
 
     import adaptive_block_sparse_hilbert_amd as absh
     import workloads as W
 
-    w = W.workload(args.workload)
-    p = w.p if args.p is None else args.p
+    p = w.p if p is None else p
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     t0 = time.time()
-    data = W.generate(w)
+    data = W.generate(w, want_fp32=route_f32)
     to_dev = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
     q, k, v = to_dev(data["q16"]), to_dev(data["k16"]), to_dev(data["v16"])
     gen_s = time.time() - t0
@@ -181,7 +207,13 @@ def main():
     oh = torch.empty_like(qh)
     o = torch.empty_like(q)
     routing = absh.alloc_routing(ctx, B, H)
+    wg_busy = absh.busy_record(ctx, routing)
     ws = torch.empty(absh.route_workspace_bytes(ctx, B, H, d), dtype=torch.uint8, device=dev)
+    if route_f32:  # float32 rows of q and k for the router
+        q32 = torch.from_numpy(data["q32"]).to(dev)
+        k32 = torch.from_numpy(data["k32"]).to(dev)
+        qr = torch.empty((B, H, ctx.n_pad, d), dtype=torch.float32, device=dev)
+        kr = torch.empty_like(qr)
 
     stages = ("permute", "quantize", "route", "attn", "unpermute")
 
@@ -196,6 +228,9 @@ def main():
             ev[0].record(stream)
         absh.permute(ctx, q, out=qh)
         absh.permute(ctx, k, out=kh)
+        if route_f32:
+            absh.permute(ctx, q32, layout=absh.ABSH_ROWS_F32, out=qr)
+            absh.permute(ctx, k32, layout=absh.ABSH_ROWS_F32, out=kr)
         if fp8:
             absh.permute(ctx, v, out=vh)
         else:
@@ -206,8 +241,8 @@ def main():
             absh.quantize_v(ctx, vh, out=vt8, scale=vscale)
         if ev is not None:
             ev[2].record(stream)
-        absh.route(ctx, qh, kh, p, w.k_floor, slack_frac=w.slack_frac if args.router == "topp" else 0.0,
-                   schedule=args.schedule, out=routing,
+        absh.route(ctx, qr if route_f32 else qh, kr if route_f32 else kh, p, w.k_floor,
+                   slack_frac=w.slack_frac if args.router == "topp" else 0.0, schedule=schedule, out=routing,
                    rank_policy=args.rank_policy, strict_ranks=args.strict_ranks, router=args.router,
                    window=args.window, anchor_stride=args.anchor_stride, anchor_shift=args.anchor_shift,
                    step=args.step,
@@ -262,6 +297,8 @@ def main():
                     "max": round(float(L_h.max()), 3)},
             "density_h": {"min": round(float(L_h.min()) / ctx.nb, 5), "max": round(float(L_h.max()) / ctx.nb, 5)}}
 
+    balance = launch_balance(absh, routing, schedule, wg_busy, w.block)
+
     value = f_ret / (ms_per_step * 1e-3) / 1e12
     attn_tflops = f_ret / (stage_ms["attn"] * 1e-3) / 1e12
 
@@ -288,7 +325,7 @@ def main():
 
     traffic = measured_traffic(args.traffic_profile or os.path.join(
         ROOT, "profiles", "attn_" + w.name.replace("-", "") + ("_fp8" if fp8 else "") + "_hbm.md"),
-        w.name, args.schedule, args.values)
+        w.name, schedule, args.values)
 
     peak = PEAK_MIXED_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     clock = sampler.report() if sampler else None
@@ -297,8 +334,7 @@ def main():
     peak_clk = None if clock is None else peak * clock["median_mhz"] / PEAK_CLOCK_MHZ
     roof = {
         "bound": "mfma",
-        "kernel": attention_kernel_name(d, w.block, 1 if args.schedule == "lpt" else (2 if w.block >= 128 else 4),
-                                        fp8),
+        "kernel": attention_kernel_name(d, w.block, unit_members(w.block, schedule), fp8),
         "achieved": round(attn_tflops, 2),
         "peak": round(peak, 1),
         "unit": "TFLOP/s",
@@ -310,7 +346,12 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, p, data, args.cpu_seconds)
+        # head 0's lists before any slack fill, for the parity sample of the baseline leg
+        base = routing
+        if w.slack_frac > 0 and args.router == "topp":
+            base = absh.route(ctx, qr if route_f32 else qh, kr if route_f32 else kh, p, w.k_floor, schedule=schedule)
+        head0 = (base.counts[:, :1].cpu().numpy(), base.kv_idx[:, :1].cpu().numpy())
+        cpu = cpu_baseline(w, p, data, args.cpu_seconds, head0 if args.router == "topp" else None)
 
     out = {
         "metric": "effective bf16 TFLOP/s on retained blocks + speedup vs dense, 720p 40-head",
@@ -328,11 +369,13 @@ def main():
         "config": {
             "workload": w.name, "batch": B, "heads": H, "head_dim": d, "grid_t_y_x": [w.T, w.Y, w.X],
             "tokens": w.N, "block": w.block, "blocks": ctx.nb, "p": p, "k_floor": w.k_floor,
-            "slack_frac": w.slack_frac, "schedule": args.schedule, "router": args.router, "values": args.values,
+            "slack_frac": w.slack_frac, "schedule": schedule, "router": args.router, "values": args.values,
+            "route_inputs": "f32" if route_f32 else "bf16",
             **({"window": args.window, "anchor_stride": args.anchor_stride, "anchor_shift": args.anchor_shift,
                 "step": args.step} if args.router == "window-anchor" else {}),
         },
-        "ranks": rank_report(routing, args) if args.schedule == "ranks" else None,
+        "ranks": rank_report(routing, args) if schedule == "ranks" else None,
+        "balance": balance,
         "density": round(density, 5),
         "work": work,
         "retained_tflop": round(f_ret / 1e12, 4),
@@ -350,7 +393,7 @@ def main():
         "cpu_baseline": cpu,
         "env": gpu_env(dev, clock, power_cap),
     }
-    print(json.dumps(out))
+    return out
 
 
 def rank_report(routing, args):
@@ -365,6 +408,14 @@ def rank_report(routing, args):
         "rank_blocks_before": [int(x) for x in info[5:13]], "rank_blocks_after": [int(x) for x in info[21:29]],
         "sasa_budgets": [int(x) for x in info[29:37]],
     }
+
+
+def unit_members(block, schedule):
+    """Query blocks per attention work unit: four 64-row or two 128-row blocks on every
+    schedule, single tiles for blocks of 16 under the longest-first schedule."""
+    if schedule == "lpt" and block < 64:
+        return 1
+    return 2 if block >= 128 else 4
 
 
 def attention_kernel_name(d, block, members, fp8=False):
@@ -408,7 +459,53 @@ def measured_traffic(path, workload, schedule, values="bf16"):
     return int(fields["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(w, p, data, budget_s):
+def launch_balance(absh, routing, schedule, wg_busy, block):
+    """rho over the workgroups of the last attention launch (from its busy record), and
+    rho_sim of a list schedule of the same work units over as many workers."""
+    import heapq
+
+    import numpy as np
+
+    busy = absh.busy_ticks(wg_busy).astype(np.float64)
+    if busy.size == 0:
+        return None
+    bounds = routing.sched.cpu().numpy().tolist()
+    members = bounds[9]
+    if members == 1:  # single tiles in queue order
+        cost = routing.counts.cpu().numpy().reshape(-1)[routing.queue.cpu().numpy()]
+    else:
+        ucnt = routing.unit_cnt.cpu().numpy()
+        n = bounds[8]
+        if schedule == "lpt":
+            units = routing.unit_queue.cpu().numpy()[:n]
+        elif schedule == "ranks":
+            per_head = -(-routing.counts.shape[2] // members)
+            pos = np.arange(n)
+            units = routing.head_order.cpu().numpy()[pos // per_head] * per_head + pos % per_head
+        else:
+            units = np.arange(n)
+        cost = ucnt[units]
+    cost = cost.astype(np.float64) + 1.0
+    workers = busy.size
+    nxt, hi = list(bounds[:8]), bounds[1:9]
+    load = np.zeros(workers)
+    heap = [(0.0, x) for x in range(workers)]
+    while heap:
+        t, x = heapq.heappop(heap)
+        for k in range(8):
+            seg = (x + k) & 7
+            if nxt[seg] < hi[seg]:
+                c = cost[nxt[seg]]
+                nxt[seg] += 1
+                load[x] += c
+                heapq.heappush(heap, (t + c, x))
+                break
+    return {"workgroups": int(workers), "rho_wg": round(float(busy.max() / busy.mean()), 4),
+            "min_over_mean_wg": round(float(busy.min() / busy.mean()), 4),
+            "rho_sim": round(float(load.max() / load.mean()), 4), "block": block}
+
+
+def cpu_baseline(w, p, data, budget_s, head0=None):
     """The oracle on a bounded sample of the same workload, timed on the host cores.
 
     Sample: head 0 of the workload. The oracle computes the Hilbert order, gathers
@@ -430,8 +527,22 @@ def cpu_baseline(w, p, data, budget_s):
     perm, _ = O.hilbert_perm(w.T, w.Y, w.X)
     head = lambda name: W.bf16_to_f32(data[name + "16"][:, :, :1, :])
     qh, kh, vh = (O.to_hilbert(head(n), perm) for n in ("q", "k", "v"))
-    R = O.route(qh, kh, w.block, p, w.k_floor)
+    if "q32" in data:  # routing from the float32 rows
+        qr, kr = (O.to_hilbert(np.ascontiguousarray(data[n][:, :, :1, :]), perm) for n in ("q32", "k32"))
+    else:
+        qr, kr = qh, kh
+    R = O.route(qr, kr, w.block, p, w.k_floor)
     t_route = time.perf_counter() - t0
+    parity = None
+    if head0 is not None:  # head 0's GPU lists against the oracle's, under the routing tolerance
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from routing_compare import compare_routing
+
+        counts_g, kv_g = head0
+        same = sum(int(np.array_equal(kv_g[0, 0, i, : counts_g[0, 0, i]], R.retained(0, 0, i)))
+                   for i in range(R.nb))
+        excused, failures = compare_routing(R, counts_g, kv_g, p)
+        parity = {"tiles": int(R.nb), "identical": same, "excused": int(excused), "failures": len(failures)}
     nb = R.nb
     order = np.argsort((np.arange(nb) * 0.6180339887) % 1.0, kind="stable")  # spread over the head
     t1 = time.perf_counter()
@@ -453,6 +564,7 @@ def cpu_baseline(w, p, data, budget_s):
         "sample": (f"head 0 of {w.name}: Hilbert order + full routing of its {nb} query blocks "
                    f"({t_route:.2f} s, prorated to the sample), attention for {done} query blocks "
                    f"spread over the head ({t_attn:.2f} s); float64 NumPy"),
+        "route_parity_head0": parity,
     }
 
 

@@ -24,10 +24,12 @@
  *    rows N..n_pad-1 are zero. nb = ceil(N / block) blocks of `block` tokens;
  *    block j holds Hilbert positions [j*block, min((j+1)*block, N)).
  *  - A tile is one (batch b, head h, query block i); its id is (b*H + h)*nb + i.
- *  - Attention calls (absh_sparse_attn, absh_sparse_attn_v8) on one context
- *    must not overlap in time: the attention kernels' tile counters live in the
- *    context. Every other call only reads the context and may run on another
- *    stream concurrently with any call on the same context.
+ *  - Attention calls (absh_sparse_attn, absh_sparse_attn_v8) take their work
+ *    counters from lists->pull, so calls with different lists may overlap in
+ *    time; calls that share one set of counters (the same lists, or dense mode
+ *    and lists without pull, which use the context's own) must not. Every other
+ *    call only reads the context and may run on another stream concurrently with
+ *    any call on the same context.
  *  - Arguments are validated on the host before any HIP call; a failure returns
  *    ABSH_EINVAL / ABSH_EUNSUPPORTED / ABSH_EWORKSPACE and launches nothing.
  *    HIP failures return ABSH_EHIP. absh_last_error() gives the detail of the
@@ -64,7 +66,9 @@ typedef enum {
                     8-bit floating point): per 64-key step an image of 64*d bytes in which
                     byte e*32*d + 32*c + 16*(g ^ ((c >> 3) & 1)) + 8*a + i holds channel c
                     of key 32*e + 16*a + 8*g + i of the step (e, a, g in {0, 1}, i < 8),
-                    as an OCP FP8 E4M3 code of the value divided by the channel's scale */
+                    as an OCP FP8 E4M3 code of the value divided by the channel's scale */,
+  ABSH_ROWS_F32 = 3 /* [B, H, n_pad, d] float32 rows (bf16 inputs widened exactly, float32
+                    inputs copied): queries and keys for routing from float32 (absh_route) */
 } absh_layout;
 
 typedef struct absh_ctx absh_ctx;
@@ -73,7 +77,12 @@ typedef struct absh_ctx absh_ctx;
  * review's runtime load balancing, section 三 Stage 2 and section 3.2). */
 typedef enum {
   ABSH_SCHED_ORDER = 0, /* queue = tile ids in order, pulled by whichever CU is free          */
-  ABSH_SCHED_LPT = 1,   /* queue = tiles by retained count, longest first (ties: lower id)    */
+  ABSH_SCHED_LPT = 1,   /* queue = tiles by retained count, longest first (ties: lower id). With
+                           blocks of 64 or 128 the attention work units are query-block groups
+                           as for ABSH_SCHED_XCD, cut into the same eight runs, and each run
+                           is taken longest first: unit_queue orders its units by union length,
+                           descending, ties by unit index. With blocks of 16 the work units are
+                           single tiles taken in queue order                                     */
   ABSH_SCHED_XCD = 2,   /* queue = tile ids in order, cut into eight runs of equal retained
                            cost, one per XCD (L2 cache); an XCD whose run is done takes tiles
                            from the next runs                                                  */
@@ -81,13 +90,15 @@ typedef enum {
                            (核心公式 Eq. 2, 5-10; 3.2 RLB; 3.3 SASA and its piecewise policy):
                            XCD r runs the heads of rank r, which first holds the contiguous
                            heads floor(r*B*H/8) .. floor((r+1)*B*H/8)-1; by the policy on
-                           rho = max/mean of the rank loads, RLB moves at most one head from
-                           each rank above the mean load to a distinct rank below it (the
-                           plan of least (max, variance) of the new loads, searched
-                           exhaustively), then SASA gives rank r E_r = floor(n1 * dW_r)
-                           extra blocks when dW_r = W_max - W_r > n2 * W_max, filling the
-                           rank's lightest tiles along their importance order. Work units are
-                           query-block groups as for ABSH_SCHED_XCD.                          */
+                           rho = max/mean of the rank loads, RLB moves heads within the
+                           review's pair topologies (3.2): the ranks are matched in pairs and
+                           a pair moves at most one head each way (one send and one receive
+                           per rank; a swap moves one each), the plan of least (max,
+                           variance) of the new loads over all 105 matchings (exact search);
+                           then SASA gives rank r E_r = floor(n1 * dW_r) extra blocks when
+                           dW_r = W_max - W_r > n2 * W_max, filling the rank's lightest tiles
+                           along their importance order. Work units are query-block groups as
+                           for ABSH_SCHED_XCD. Needs B*H <= 1024 and B*H*nb*nb < 2^31.        */
 } absh_schedule;
 
 /* Routing options (xllm-io review of FVAttn, section 五 "关键超参数": Top-p
@@ -134,10 +145,12 @@ typedef struct {
   int32_t* queue;  /* [tiles] tiles by retained count (ABSH_SCHED_LPT) or in order (others)       */
   int32_t* sched;  /* [10] bounds of the eight runs of the attention work queue, one per XCD,
                       then the query blocks per work unit (see absh_sparse_attn)                 */
-  uint32_t* unit_list; /* [units][nb] for ABSH_SCHED_ORDER / ABSH_SCHED_XCD (else unused, may be
-                      NULL; units = absh_lists_units()): the ascending union of the retained
-                      lists of the M neighbouring query blocks qM .. qM+M-1 of a head, entry =
-                      block id | (member m retains it) << (28 + m); M = 4 (block <= 64) or 2  */
+  uint32_t* unit_list; /* [units][nb] for every schedule whose work units are query-block groups
+                      (ABSH_SCHED_ORDER, _XCD, _RANKS, and _LPT with blocks of 64 or 128; else
+                      unused, may be NULL; units = absh_lists_units()): the ascending union of
+                      the retained lists of the M neighbouring query blocks qM .. qM+M-1 of a
+                      head, entry = block id | (member m retains it) << (28 + m); M = 4
+                      (block <= 64) or 2                                                        */
   int32_t* unit_cnt; /* [units] length of each union list (same condition as unit_list)         */
   int32_t schedule;  /* HOST field, written by absh_route: the absh_schedule the lists were made
                         for; absh_sparse_attn reads it                                           */
@@ -148,12 +161,25 @@ typedef struct {
                         [2] after augmentation; [3] policy taken (0 none, 1 SASA, 2 RLB + SASA, 3 RLB);
                         [4] number of moves; [5..12] rank loads W_r in retained blocks before,
                         [13..20] after migration, [21..28] after augmentation; [29..36] E_r;
-                        [37..60] the moves as (head, from, to), in sender order; [61] plans
-                        searched; [62] 1 if the search space was too large (no migration)
+                        [37..60] the moves as (head, from, to), by sending rank; [61] candidate
+                        plans in the migration space (0 without RLB); [62] 0
                         (else unused, may be NULL)                                               */
   int32_t strict_ranks; /* HOST field, written by absh_route (opts->strict_ranks); absh_sparse_attn
                         reads it                                                                 */
+  int32_t* unit_queue; /* [units] ABSH_SCHED_LPT with blocks of 64 or 128: the group units of each
+                        of the eight runs (sched), by union length descending, ties by unit
+                        index (else unused, may be NULL)                                         */
+  int32_t* pull;       /* [ABSH_PULL_WORDS] work counters of the attention launches on these lists:
+                        absh_route zeroes them and every attention launch leaves them zero. NULL:
+                        attention uses the context's counters                                     */
+  uint64_t* wg_busy;   /* optional [absh_attn_workgroups()][2], set by the caller (NULL: none): each
+                        attention workgroup writes its start time and the time its last pull found
+                        no work, in ticks of the 100 MHz constant clock (s_memrealtime), at index
+                        2 * workgroup; entries of workgroups a launch does not have keep their
+                        values. For the balance over workers (Eq. 2 over workgroups)            */
 } absh_lists;
+
+#define ABSH_PULL_WORDS 16
 
 #define ABSH_RANK_INFO 64
 
@@ -195,8 +221,9 @@ absh_status absh_perm_copy(const absh_ctx* ctx, int32_t* perm_dst, int32_t* inv_
 /* Gather a grid-order tensor x [B, N, H, d] (bf16, or f32 rounded to bf16 to
  * nearest-even) into Hilbert order, in the given layout, zero-filling pad rows.
  * ABSH_ROWS: xh holds B*H*n_pad*d bf16. ABSH_VT: xh holds B*H*nb*d*KB bf16 with
- * KB = max(block, 32) keys per block (keys past `block` are zero). d must be 64
- * or 128. */
+ * KB = max(block, 32) keys per block (keys past `block` are zero).
+ * ABSH_ROWS_F32: xh holds B*H*n_pad*d float32, x unrounded (bf16 widened
+ * exactly). d must be 64 or 128. */
 absh_status absh_permute(absh_ctx* ctx, const void* x, absh_dtype xt, void* xh, int B, int H, int d,
                          absh_layout layout, void* stream);
 
@@ -216,16 +243,41 @@ absh_status absh_block_scores(absh_ctx* ctx, const float* qbar, const float* kba
                               int d, void* stream);
 
 /* Number of attention work units absh_route makes for this shape and schedule
- * (the row count of absh_lists.unit_list): B*H*ceil(nb/M) with M query blocks per
- * unit, M = 1 for ABSH_SCHED_LPT, else 4 (block <= 64) or 2 (block 128). 0 on a
- * bad argument. */
+ * (the row count of absh_lists.unit_list and unit_queue): B*H*ceil(nb/M) with M
+ * query blocks per unit, M = 1 for ABSH_SCHED_LPT with blocks of 16, else 4
+ * (block <= 64) or 2 (block 128). Every schedule, ABSH_SCHED_RANKS included. 0
+ * on a bad argument. */
 int absh_lists_units(const absh_ctx* ctx, int B, int H, int schedule);
+
+/* Device bytes of every buffer of absh_lists for this shape, sized for any
+ * schedule (units = the largest absh_lists_units()), each buffer 256-byte
+ * aligned, in field order: what one arena for absh_lists_carve must hold. 0 on a
+ * bad argument (order_depth outside 0..64). */
+size_t absh_lists_bytes(const absh_ctx* ctx, int B, int H, int order_depth);
+
+/* Point every device buffer of *out into `arena` (a caller-owned device
+ * allocation of at least absh_lists_bytes(), 256-byte aligned): counts, kv_idx,
+ * order (NULL when order_depth == 0), work, L, queue, sched, unit_list,
+ * unit_cnt, head_order, rank_info, unit_queue. The host fields are reset (schedule
+ * -1, strict_ranks 0). Touches no device memory. */
+absh_status absh_lists_carve(const absh_ctx* ctx, int B, int H, int order_depth, void* arena, size_t arena_bytes,
+                             absh_lists* out);
+
+/* An upper bound on the workgroups of one attention launch on this context (its
+ * compute units times the most resident workgroups per compute unit of any
+ * attention kernel): the rows of absh_lists.wg_busy. 0 for a NULL context. */
+int absh_attn_workgroups(const absh_ctx* ctx);
 
 /* Device workspace needed by absh_route for this shape, in bytes. */
 size_t absh_route_workspace_bytes(const absh_ctx* ctx, int B, int H, int d);
 
+/* Device workspace the library's calls need for this shape, in bytes: absh_route's
+ * (the attention calls need none). The same value as absh_route_workspace_bytes. */
+size_t absh_workspace_bytes(const absh_ctx* ctx, int B, int H, int d);
+
 /* Stage-1 routing (xllm-io review of FVAttn, Stage 1; explainer, "Key Concepts"):
- * from Hilbert-order qh, kh ([B, H, n_pad, d] bf16, ABSH_ROWS):
+ * from Hilbert-order qh, kh ([B, H, n_pad, d]; qk_type ABSH_BF16: bf16 rows,
+ * ABSH_ROWS; ABSH_F32: float32 rows, ABSH_ROWS_F32; 16-byte aligned):
  *   block means -> float32 block scores -> softmax over key blocks (float64) ->
  *   Top-p: the fewest blocks, by probability descending (ties: smaller id),
  *   whose cumulative probability reaches p -> floor count' = max(c, min(k, nb))
@@ -235,7 +287,7 @@ size_t absh_route_workspace_bytes(const absh_ctx* ctx, int B, int H, int d);
  * nb must be <= 2048. Writes every field of *out (order only if
  * opts->order_depth > 0). ws must hold absh_route_workspace_bytes(); its
  * contents are scratch. No host synchronisation. */
-absh_status absh_route(absh_ctx* ctx, const void* qh, const void* kh, int B, int H, int d,
+absh_status absh_route(absh_ctx* ctx, const void* qh, const void* kh, absh_dtype qk_type, int B, int H, int d,
                        const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Block-sparse attention (xllm-io review of FVAttn, "Block-Sparse Attention
@@ -247,10 +299,11 @@ absh_status absh_route(absh_ctx* ctx, const void* qh, const void* kh, int B, int
  * bf16 (ABSH_ROWS); vt: ABSH_VT layout; oh: [B, H, n_pad, d] bf16 out (pad rows
  * hold unspecified values). Scores and softmax in float32, probabilities rounded
  * to bf16 for the value product, float32 accumulation. Work is pulled by a
- * persistent grid (one workgroup per CU slot) following lists->sched. Under
- * ABSH_SCHED_LPT a work unit is one tile, in lists->queue order; otherwise it is a
- * group of neighbouring query blocks walking the union of their lists
- * (lists->unit_list), so each staged K/V block serves all of them. Dense mode
+ * persistent grid (one workgroup per CU slot) following lists->sched. A work
+ * unit is a group of neighbouring query blocks walking the union of their lists
+ * (lists->unit_list), so each staged K/V block serves all of them, taken in unit
+ * order (ABSH_SCHED_LPT: lists->unit_queue order within each run); under
+ * ABSH_SCHED_LPT with blocks of 16 it is one tile, in lists->queue order. Dense mode
  * uses groups split evenly over the XCDs. Every query row is computed the same way whatever
  * the schedule (same blocks, same ascending order), so outputs do not depend on
  * it. */
@@ -276,8 +329,8 @@ absh_status absh_quantize_v(absh_ctx* ctx, const void* vh, int B, int H, int d, 
  * reference maximum maps to at least 2^6 and none exceeds 2^8, is rounded to
  * E4M3, and the row sum adds the same rounded values; the output is multiplied
  * by the channel scales before its bf16 rounding. Scores and softmax as in
- * absh_sparse_attn. Group schedules only (ABSH_SCHED_ORDER, _XCD, _RANKS, or
- * lists == NULL for dense); block 64 or 128. ABSH_EUNSUPPORTED otherwise. */
+ * absh_sparse_attn. Block 64 or 128 (every schedule, or lists == NULL for
+ * dense). ABSH_EUNSUPPORTED otherwise. */
 absh_status absh_sparse_attn_v8(absh_ctx* ctx, const void* qh, const void* kh, const void* vt8,
                                 const float* vscale, int B, int H, int d, const absh_lists* lists, void* oh,
                                 void* stream);

@@ -36,6 +36,49 @@ def test_every_declared_function_is_exported(L):
     assert set(names) == set(absh.EXPORTED)
 
 
+# The calls of the boundary as the hot-path scope lays it out (context, sizes,
+# permute, route, sparse attention, errors); the library may export more.
+BOUNDARY = ("absh_create", "absh_destroy", "absh_dims", "absh_perm", "absh_lists_bytes", "absh_workspace_bytes",
+            "absh_permute", "absh_unpermute", "absh_route", "absh_sparse_attn", "absh_status_string",
+            "absh_last_error")
+
+
+def test_boundary_calls_are_declared_and_exported(L):
+    names = set(declared_functions())
+    for name in BOUNDARY:
+        assert name in names and hasattr(L, name), name
+
+
+def test_routing_buffers_are_checked_before_the_call():
+    """The binding rejects a caller-supplied Routing whose buffers do not fit the shape:
+    the library cannot see buffer sizes, so an undersized buffer would be written past its end."""
+    import types
+    import torch
+    if not os.path.exists(absh.LIB_PATH):
+        pytest.skip("libabsh.so not built")
+    ctx = types.SimpleNamespace(nb=4, n_pad=64, device=0, handle=ctypes.c_void_p())
+    good = dict(counts=((1, 2, 4), torch.int32), kv_idx=((1, 2, 4, 4), torch.int32), work=((1, 2), torch.int32),
+                L=((1, 2), torch.float32), queue=((8,), torch.int32), sched=((10,), torch.int32),
+                unit_list=((1, 4), torch.int32), unit_cnt=((1,), torch.int32), head_order=((2,), torch.int32),
+                rank_info=((absh.RANK_INFO,), torch.float64), unit_queue=((1,), torch.int32),
+                pull=((absh.PULL_WORDS,), torch.int32))
+    for bad, shape in (("kv_idx", (1, 2, 4, 3)), ("counts", (1, 2, 3)), ("unit_list", (0, 4)),
+                       ("unit_queue", (0,)), ("rank_info", (8,)), ("pull", (8,))):
+        fields = {k: torch.empty(sh, dtype=dt) for k, (sh, dt) in good.items()}
+        fields[bad] = torch.empty(shape, dtype=good[bad][1])
+        r = absh.Routing(order=None, **fields)
+        with pytest.raises(ValueError, match=bad):
+            r.check(ctx, 1, 2, 0)
+    fields = {k: torch.empty(sh, dtype=dt) for k, (sh, dt) in good.items()}
+    with pytest.raises(ValueError, match="order"):  # order_depth 2 needs an order buffer
+        absh.Routing(order=None, **fields).check(ctx, 1, 2, 2)
+    with pytest.raises(ValueError, match="cuda:0"):  # right shapes, host memory
+        absh.Routing(order=None, **fields).check(ctx, 1, 2, 0)
+    with pytest.raises(ValueError, match="counts"):  # wrong dtype
+        fields["counts"] = torch.empty((1, 2, 4), dtype=torch.int64)
+        absh.Routing(order=None, **fields).check(ctx, 1, 2, 0)
+
+
 def test_version_and_status_strings(L):
     assert L.absh_version() >= 100
     for code, name in [(OK, b"ABSH_OK"), (EINVAL, b"ABSH_EINVAL"), (EUNSUPPORTED, b"ABSH_EUNSUPPORTED"),
@@ -92,7 +135,7 @@ def test_null_context_everywhere(L):
     assert L.absh_block_scores(None, vp(16), vp(16), vp(16), 1, 1, 64, None) == EINVAL
     opts = absh.RouteOpts(0.9, 4, 0.0, 1, 0)
     lists = absh.Lists()
-    assert L.absh_route(None, vp(16), vp(16), 1, 1, 64, ctypes.byref(opts), ctypes.byref(lists), vp(256),
+    assert L.absh_route(None, vp(16), vp(16), 0, 1, 1, 64, ctypes.byref(opts), ctypes.byref(lists), vp(256),
                         ctypes.c_size_t(1 << 20), None) == EINVAL
     assert L.absh_sparse_attn(None, vp(16), vp(16), vp(16), 1, 1, 64, None, vp(16), None) == EINVAL
     assert b"ctx is NULL" in L.absh_last_error()
@@ -101,6 +144,10 @@ def test_null_context_everywhere(L):
     assert b"ctx is NULL" in L.absh_last_error()
     assert L.absh_route_workspace_bytes(None, 1, 1, 64) == 0
     assert L.absh_lists_units(None, 1, 1, 0) == 0
+    assert L.absh_lists_bytes(None, 1, 1, 0) == 0
+    assert L.absh_workspace_bytes(None, 1, 1, 64) == 0
+    assert L.absh_attn_workgroups(None) == 0
+    assert L.absh_lists_carve(None, 1, 1, 0, vp(256), ctypes.c_size_t(1 << 20), ctypes.byref(lists)) == EINVAL
     assert L.absh_destroy(None) == OK
 
 
@@ -189,3 +236,25 @@ def test_bench_clock_sampler_reads_the_current_level(tmp_path):
     gone.halt.set()
     gone.join()
     assert gone.report() is None
+
+
+def test_bench_balance_from_busy_record():
+    """The bench's rho over workgroups comes from the busy record (end - start of the
+    workgroups that ran) and rho_sim from a list schedule that pulls the XCD's own run
+    first: four units of union length 3, 1, 1, 1 (cost + 1) on two workers give loads
+    6 and 4, so rho_sim = 1.2."""
+    import importlib.util
+    import types
+    import torch
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    routing = types.SimpleNamespace(
+        sched=torch.tensor([0, 1, 2, 3, 4, 4, 4, 4, 4, 4], dtype=torch.int32),
+        unit_cnt=torch.tensor([3, 1, 1, 1], dtype=torch.int32),
+        counts=torch.ones((1, 1, 16), dtype=torch.int32))
+    busy = torch.tensor([[100, 700], [100, 500], [0, 0]], dtype=torch.int64)  # the third never ran
+    rep = bench.launch_balance(absh, routing, "xcd", busy, 64)
+    assert rep["workgroups"] == 2
+    assert rep["rho_wg"] == round(600 / 500, 4) and rep["min_over_mean_wg"] == round(400 / 500, 4)
+    assert rep["rho_sim"] == 1.2

@@ -24,13 +24,13 @@ def env():
 
 
 def call_route(ctx, qh, r, ws, p=0.9, k=2, slack=0.0, sched=1, depth=0, nbytes=None, ws_ptr=None, d=64,
-               lists=None):
+               lists=None, qk_type=0):
     opts = absh.RouteOpts(p, k, slack, sched, depth)
     lists = r.lists() if lists is None else lists
     ptr = ws.data_ptr() if ws_ptr is None else ws_ptr
     n = ws.numel() if nbytes is None else nbytes
     return absh.lib().absh_route(ctx.handle, ctypes.c_void_p(qh.data_ptr()), ctypes.c_void_p(qh.data_ptr()),
-                                 1, 2, d, ctypes.byref(opts), ctypes.byref(lists), ctypes.c_void_p(ptr),
+                                 qk_type, 1, 2, d, ctypes.byref(opts), ctypes.byref(lists), ctypes.c_void_p(ptr),
                                  ctypes.c_size_t(n), None)
 
 
@@ -39,6 +39,7 @@ def call_route(ctx, qh, r, ws, p=0.9, k=2, slack=0.0, sched=1, depth=0, nbytes=N
     (dict(k=-1), EINVAL), (dict(slack=1.0), EINVAL), (dict(slack=-0.1), EINVAL),
     (dict(depth=65), EINVAL), (dict(depth=-1), EINVAL), (dict(sched=3), EINVAL), (dict(sched=-1), EINVAL),
     (dict(d=96), EUNSUPPORTED), (dict(nbytes=1024), EWORKSPACE), (dict(ws_ptr=0), EWORKSPACE),
+    (dict(qk_type=2), EINVAL), (dict(qk_type=-1), EINVAL),
 ])
 def test_route_rejects(env, kw, status):
     ctx, qh, r, ws = env
@@ -76,7 +77,7 @@ def test_router_block_count_limit():
     qh = torch.zeros((1, 1, ctx.n_pad, 64), dtype=torch.bfloat16, device=DEV)
     opts = absh.RouteOpts(0.9, 2, 0.0, 1, 0)
     lists = absh.Lists(*([ctypes.c_void_p(qh.data_ptr()).value] * 9 + [1]))
-    st = absh.lib().absh_route(ctx.handle, ctypes.c_void_p(qh.data_ptr()), ctypes.c_void_p(qh.data_ptr()), 1, 1,
+    st = absh.lib().absh_route(ctx.handle, ctypes.c_void_p(qh.data_ptr()), ctypes.c_void_p(qh.data_ptr()), 0, 1, 1,
                                64, ctypes.byref(opts), ctypes.byref(lists), ctypes.c_void_p(qh.data_ptr()),
                                ctypes.c_size_t(1 << 40), None)
     assert st == EUNSUPPORTED and b"nb" in absh.lib().absh_last_error()
@@ -119,3 +120,41 @@ def test_dims_and_units(env):
     assert (ctx.N, ctx.nb, ctx.n_pad) == (192, 12, 192)
     assert absh.lists_units(ctx, 1, 2, "lpt") == 24
     assert absh.lists_units(ctx, 1, 2, "xcd") == 2 * 3      # groups of 4 query blocks
+
+
+def test_lpt_group_units_need_the_unit_queue():
+    """Blocks of 64: the longest-first schedule runs group units, so it needs unit lists
+    and the unit queue; a carved arena supplies every buffer."""
+    ctx = absh.create(2, 8, 16, 64)           # N = 256, nb = 4
+    B, H, d = 1, 3, 64
+    qh = torch.zeros((B, H, ctx.n_pad, d), dtype=torch.bfloat16, device=DEV)
+    r = absh.alloc_routing(ctx, B, H)
+    ws = torch.empty(absh.route_workspace_bytes(ctx, B, H, d), dtype=torch.uint8, device=DEV)
+    assert absh.lists_units(ctx, B, H, "lpt") == H * 1
+    opts = absh.RouteOpts(0.9, 2, 0.0, absh.SCHEDULES["lpt"], 0)
+    L = absh.lib()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def call(lists):
+        return L.absh_route(ctx.handle, p(qh), p(qh), 0, B, H, d, ctypes.byref(opts), ctypes.byref(lists), p(ws),
+                            ctypes.c_size_t(ws.numel()), None)
+    lists = r.lists()
+    lists.unit_queue = None
+    assert call(lists) == EINVAL and b"unit_queue" in L.absh_last_error()
+    lists = r.lists()
+    lists.unit_list = None
+    assert call(lists) == EINVAL
+    assert call(r.lists()) == 0
+    nbytes = absh.lists_bytes(ctx, B, H)
+    arena = torch.empty(nbytes + 256, dtype=torch.uint8, device=DEV)
+    carved = absh.Lists()
+    assert L.absh_lists_carve(ctx.handle, B, H, 0, ctypes.c_void_p(arena.data_ptr() + 1), ctypes.c_size_t(nbytes),
+                              ctypes.byref(carved)) == EINVAL
+    assert L.absh_lists_carve(ctx.handle, B, H, 0, p(arena), ctypes.c_size_t(nbytes - 1),
+                              ctypes.byref(carved)) == EWORKSPACE
+    assert L.absh_lists_carve(ctx.handle, B, H, 0, p(arena), ctypes.c_size_t(nbytes), ctypes.byref(carved)) == 0
+    assert carved.order is None and carved.unit_queue is not None
+    assert call(carved) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(arena[carved.counts - arena.data_ptr():][: B * H * ctx.nb * 4].view(torch.int32),
+                       r.counts.view(-1))

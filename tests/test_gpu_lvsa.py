@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("index,window,stride,shift,step,schedule", [
-    (4, 24, 32, 5, 3, "xcd"), (4, 6, 0, 0, 0, "order"), (1, 3, 7, 2, 11, "lpt"), (0, 1, 3, 1, 1, "xcd")])
+    (4, 24, 32, 5, 3, "xcd"), (4, 6, 0, 0, 0, "order"), (1, 3, 7, 2, 11, "lpt"), (0, 1, 3, 1, 1, "xcd"),
+    (0, 2 ** 31 - 1, 0, 0, 0, "xcd")])  # a window past int range: every block, no overflow
 def test_window_anchor_lists(index, window, stride, shift, step, schedule):
     c = case(index)
     w = c.w

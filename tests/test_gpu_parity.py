@@ -9,11 +9,10 @@ Bars (written here, per step):
     work and L then follow exactly from the counts;
   * attention on the GPU's own mask: max-abs <= 2e-2 and mean-abs <= 2e-3 against
     the float64 oracle (bf16 inputs, bf16 probabilities in the value product);
-  * same-kernel invariants: p = 1 sparse == dense, the group schedules (order,
-    xcd) against each other, and two runs, all bit-identical. Longest-first
-    single tiles run on the tile kernel and group units of 64- and 128-row
-    blocks on the union kernel; the two sum in different orders, so across them
-    the attention bar above applies.
+  * same-kernel invariants: p = 1 sparse == dense, the three schedules (order,
+    xcd, longest-first) against each other, and two runs, all bit-identical:
+    with blocks of 64 and 128 every schedule runs the same group units on the
+    union kernel, with blocks of 16 the same single tiles on the tile kernel.
 """
 import functools
 
@@ -178,7 +177,7 @@ def test_scores_within_one_ulp(index):
 
 # ---------------------------------------------------------------- routing
 
-@pytest.mark.parametrize("index,p", [(0, None), (1, None), (2, None), (4, 0.8), (4, 0.9), (4, 0.95)])
+@pytest.mark.parametrize("index,p", [(0, None), (1, None), (2, None), (3, None), (4, 0.8), (4, 0.9), (4, 0.95)])
 def test_route_matches_oracle(index, p):
     c = case(index)
     w = c.w
@@ -196,12 +195,43 @@ def test_route_matches_oracle(index, p):
     assert np.array_equal(work, counts.sum(-1))
     assert np.array_equal(L, (work.astype(np.float32) / np.float32(w.nb)).astype(np.float32))
     assert (counts >= min(w.k_floor, w.nb)).all()
-    # LPT queue: exactly the oracle's order for these counts; one run holds it all
+    # LPT tile queue: exactly the oracle's order for these counts
     assert np.array_equal(queue, O.lpt_queue(counts))
-    assert r.sched.cpu().numpy().tolist() == [0] + [w.tiles] * 8 + [1]
+    if w.block < 64:  # single tiles: one run holds the whole queue
+        assert r.sched.cpu().numpy().tolist() == [0] + [w.tiles] * 8 + [1]
     if excused == 0:
         wo, Lo = O.workloads(R.counts)
         assert np.array_equal(work, wo) and np.array_equal(L, Lo)
+
+
+@pytest.mark.parametrize("schedule", ["xcd", "lpt"])
+def test_route_fp32_inputs(schedule):
+    """The tiny fp32 workload routed from float32 rows (ABSH_ROWS_F32), against the
+    oracle on the same float32 values; then attention on the bf16 rounding of those
+    rows under the GPU's lists, against the oracle's."""
+    w = W.workload(0)
+    d = W.generate(w, want_fp32=True)
+    ctx = absh.create(w.T, w.Y, w.X, w.block)
+    q, k = (torch.from_numpy(d[n]).to(DEV) for n in ("q32", "k32"))
+    qh, kh = (absh.permute(ctx, x, layout=absh.ABSH_ROWS_F32) for x in (q, k))
+    perm, _ = O.hilbert_perm(w.T, w.Y, w.X)
+    hq, hk = (O.to_hilbert(d[n], perm) for n in ("q32", "k32"))
+    got_qh = qh.cpu().numpy()
+    assert np.array_equal(got_qh[:, :, : w.N], hq) and (got_qh[:, :, w.N:] == 0).all()
+    r = absh.route(ctx, qh, kh, w.p, w.k_floor, schedule=schedule)
+    counts, kv, _ = check_lists_valid(r, ctx.nb)
+    R = O.route(hq, hk, w.block, w.p, w.k_floor)
+    excused, failures = compare_routing(R, counts, kv, w.p)
+    print(f"[route f32] {w.name} {schedule}: excused tiles {excused}")
+    assert not failures, failures[:5]
+    assert excused <= 0.01 * counts.size
+    qb, kb = absh.permute(ctx, q), absh.permute(ctx, k)
+    vt = absh.permute(ctx, torch.from_numpy(d["v32"]).to(DEV), layout=absh.ABSH_VT)
+    o = absh.unpermute(ctx, absh.sparse_attn(ctx, qb, kb, vt, r)).float().cpu().numpy()
+    bf = [W.bf16_to_f32(W.bf16_bits(d[n])) for n in ("q32", "k32", "v32")]
+    ref = O.attention(*bf, perm, w.block, lambda b, h, i: kv[b, h, i, : counts[b, h, i]])
+    e = np.abs(o - ref)
+    assert e.max() <= ATOL_MAX and e.mean() <= ATOL_MEAN
 
 
 def test_importance_order_prefix():
@@ -238,6 +268,9 @@ def test_slack_fill_matches_oracle():
     c1, kv1, q1 = check_lists_valid(filled, w.nb)
     want = O.slack_fill(c0, w.slack_frac)
     assert np.array_equal(c1, want)
+    R0 = c.oracle_route()
+    if np.array_equal(c0, R0.counts):  # no excused tile: the fill of the oracle's own counts
+        assert np.array_equal(c1, O.slack_fill(R0.counts, w.slack_frac))
     added = int((c1 - c0).sum())
     E = O.slack_budget(c0, w.slack_frac)
     print(f"[slack] {w.name}: sum before {int(c0.sum())}, E {E}, added {added}")
@@ -423,17 +456,29 @@ def test_attention_tiny_all_tiles():
     assert mx <= ATOL_MAX and mean <= ATOL_MEAN
 
 
-@pytest.mark.parametrize("index,schedule", [(1, "xcd"), (2, "xcd"), (3, "xcd"), (4, "xcd"), (2, "lpt")])
+def stratified_tiles(counts, rng):
+    """Tiles to check: per head one random tile and its last (partial) query block; over
+    all tiles the lightest, the heaviest and one random tile per count quintile."""
+    B, H, nb = counts.shape
+    flat = counts.reshape(-1)
+    pick = {int(np.argmax(flat)), int(np.argmin(flat))}
+    for bh in range(B * H):
+        pick |= {bh * nb + int(rng.integers(nb)), bh * nb + nb - 1}
+    order = np.argsort(flat, kind="stable")
+    for part in np.array_split(order, 5):
+        pick.add(int(rng.choice(part)))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("index,schedule", [(1, "xcd"), (2, "xcd"), (3, "xcd"), (4, "xcd"), (2, "lpt"),
+                                            (3, "lpt")])
 def test_attention_sampled_tiles(index, schedule):
     c = case(index)
     w = c.w
     r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, schedule=schedule)
     counts, _, _ = check_lists_valid(r, w.nb)
     rng = np.random.default_rng(100 + index)
-    flat = counts.reshape(-1)
-    # the heaviest tile, the last (partial) query block of a few heads, and random tiles
-    pick = {int(np.argmax(flat)), w.nb - 1, w.tiles - 1}
-    pick |= set(rng.choice(w.tiles, size=10, replace=False).tolist())
+    pick = stratified_tiles(counts, rng)
     mx, mean = attention_errors(c, r, sorted(pick))
     print(f"[attn] {w.name}: max {mx:.3e} mean {mean:.3e} over {len(pick)} tiles")
     assert mx <= ATOL_MAX and mean <= ATOL_MEAN
@@ -530,23 +575,41 @@ def expected_xcd_bounds(cost, overhead=1, segments=8):
     return bounds + [cost.size]
 
 
+def expected_unit_queue(cost, bounds):
+    """Inside each XCD run, the units by union length descending, ties by unit index."""
+    cost = np.asarray(cost)
+    out = []
+    for x in range(8):
+        run = np.arange(bounds[x], bounds[x + 1])
+        out.extend(run[np.lexsort((run, -cost[run]))].tolist())
+    return np.array(out, dtype=np.int64)
+
+
 @pytest.mark.parametrize("index", [0, 1, 3, 4])
 def test_schedules_bit_identical(index):
+    """Every schedule runs the same units with the same kernel, so the outputs agree bit for bit;
+    the schedules differ only in the units' order (and the longest-first queue in its grouping,
+    single tiles below blocks of 64)."""
     c = case(index)
     w = c.w
     M = 2 if w.block >= 128 else 4
+    union = w.block in (64, 128)  # group units on the union kernel, single tiles on the tile kernel
     units = w.B * w.H * (-(-w.nb // M))
     assert absh.lists_units(c.ctx, w.B, w.H, "xcd") == units
-    assert absh.lists_units(c.ctx, w.B, w.H, "lpt") == w.tiles
+    assert absh.lists_units(c.ctx, w.B, w.H, "ranks") == units
+    assert absh.lists_units(c.ctx, w.B, w.H, "lpt") == (units if union else w.tiles)
     outs = {}
     for sched in ("order", "lpt", "xcd"):
         r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, slack_frac=w.slack_frac, schedule=sched)
         counts, kv, queue = check_lists_valid(r, w.nb)
         bounds = r.sched.cpu().numpy().tolist()
         if sched == "lpt":
-            assert np.array_equal(queue, O.lpt_queue(counts)) and bounds == [0] + [w.tiles] * 8 + [1]
+            assert np.array_equal(queue, O.lpt_queue(counts))
         else:
             assert np.array_equal(queue, np.arange(w.tiles))
+        if sched == "lpt" and not union:
+            assert bounds == [0] + [w.tiles] * 8 + [1]
+        else:
             want_lists, want_len = expected_groups(counts, kv, w.nb, M)
             got_len = r.unit_cnt.cpu().numpy()[:units]
             got = r.unit_list.cpu().numpy().view(np.uint32)
@@ -557,20 +620,16 @@ def test_schedules_bit_identical(index):
                 assert bounds == [0] + [units] * 8 + [M]
             else:
                 assert bounds == expected_xcd_bounds(got_len) + [M], (bounds, expected_xcd_bounds(got_len))
+            if sched == "lpt":
+                uq = r.unit_queue.cpu().numpy()[:units]
+                assert np.array_equal(uq, expected_unit_queue(got_len, bounds))
         outs[sched] = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r)
         outs[sched + "2"] = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r)
     torch.cuda.synchronize()
     rows = torch.arange(w.N, device=DEV)
     ref = outs["order"][:, :, rows].view(torch.int16)
-    union = w.block in (64, 128)  # group units on the union kernel, single tiles on the tile kernel
     for k, v in outs.items():
-        if union and k.startswith("lpt"):
-            continue
         assert torch.equal(v[:, :, rows].view(torch.int16), ref), k
-    assert torch.equal(outs["lpt"].view(torch.int16), outs["lpt2"].view(torch.int16))
-    if union:
-        e = (outs["lpt"][:, :, rows].float() - outs["order"][:, :, rows].float()).abs()
-        assert e.max().item() <= ATOL_MAX and e.mean().item() <= ATOL_MEAN
 
 
 # ---------------------------------------------------------------- edge shapes

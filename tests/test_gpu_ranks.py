@@ -30,7 +30,7 @@ def gpu_rank_report(r):
     moves = [tuple(int(x) for x in info[37 + 3 * i: 40 + 3 * i]) for i in range(int(info[4]))]
     return dict(rho0=info[0], rho_rlb=info[1], rho_final=info[2], policy=["none", "sasa", "rlb+sasa", "rlb"][int(info[3])],
                 moves=moves, W0=info[5:13].astype(np.int64), W1=info[13:21].astype(np.int64),
-                W2=info[21:29].astype(np.int64), E=info[29:37].astype(np.int64), too_large=info[62])
+                W2=info[21:29].astype(np.int64), E=info[29:37].astype(np.int64), space=info[61], reserved=info[62])
 
 
 @pytest.mark.parametrize("index,policy", [(1, "auto"), (2, "auto"), (3, "auto"), (2, "rlb+sasa"), (3, "sasa"),
@@ -48,8 +48,11 @@ def test_rank_stage_matches_oracle(index, policy):
     got = gpu_rank_report(ranked)
     print(f"[ranks] {w.name} {policy}: rho {got['rho0']:.4f} -> {got['rho_rlb']:.4f} -> {got['rho_final']:.4f}, "
           f"policy {got['policy']}, moves {got['moves']}, E {list(got['E'])}")
-    assert got["too_large"] == 0
+    assert got["reserved"] == 0
     assert got["policy"] == want["policy"]
+    if want["policy"] in ("rlb+sasa", "rlb"):
+        owner0 = O.rank_of_heads(w.B * w.H)
+        assert got["space"] == O.rlb_space(c0.reshape(w.B * w.H, -1).sum(-1), owner0)
     assert got["rho0"] == want["rho0"] and got["rho_rlb"] == want["rho_rlb"] and got["rho_final"] == want["rho_final"]
     assert got["moves"] == [(h, s, d) for h, s, d in want["moves"]]
     for k in ("W0", "W1", "W2", "E"):

@@ -36,6 +36,7 @@ def test_special_cases():
     for i in range(nb):
         assert list(O.window_anchor_list(nb, i, 2, 0, 0, 0)) == [j for j in range(nb) if abs(i - j) <= 2]
         assert list(O.window_anchor_list(nb, i, nb, 5, 1, 3)) == list(range(nb))
+        assert list(O.window_anchor_list(nb, i, 2 ** 31 - 1, 0, 0, 0)) == list(range(nb))
         assert list(O.window_anchor_list(nb, i, 0, 1, 0, 0)) == list(range(nb))
     assert list(O.window_anchor_list(10, 0, 0, 4, 1, 1)) == [0, 1, 5, 9]   # window {0}, anchors 1, 5, 9
 
