@@ -23,6 +23,7 @@ SCHEDULES = {"order": SCHED_ORDER, "lpt": SCHED_LPT, "xcd": SCHED_XCD, "ranks": 
 RANK_POLICIES = {"auto": -1, "none": 0, "sasa": 1, "rlb+sasa": 2, "rlb": 3}
 RANK_INFO = 64  # doubles in Routing.rank_info (layout in include/absh.h)
 PULL_WORDS = 16  # int32 work counters in Routing.pull
+STATIC_SCRATCH_BYTES = 64 << 20  # route workspace limit of absh_route_static
 ROUTERS = {"topp": 0, "window-anchor": 1}
 # the review's parameters of the rank-level stages (section 五)
 RLB_K1, RLB_K2, SASA_N1, SASA_N2 = 1.05, 1.10, 0.8, 0.07
@@ -32,6 +33,7 @@ EXPORTED = (
     "absh_perm", "absh_perm_copy", "absh_permute", "absh_unpermute", "absh_pool", "absh_block_scores",
     "absh_route_workspace_bytes", "absh_route", "absh_sparse_attn", "absh_lists_units", "absh_quantize_v",
     "absh_sparse_attn_v8", "absh_lists_bytes", "absh_lists_carve", "absh_workspace_bytes", "absh_attn_workgroups",
+    "absh_route_static",
 )
 
 
@@ -91,6 +93,7 @@ def lib() -> ctypes.CDLL:
         "absh_attn_workgroups": ([vp], i),
         "absh_lists_units": ([vp, i, i, i], i),
         "absh_route": ([vp, vp, vp, i, i, i, i, ctypes.POINTER(RouteOpts), ctypes.POINTER(Lists), vp, sz, vp], i),
+        "absh_route_static": ([vp, vp, vp, i, i, i, i, ctypes.POINTER(RouteOpts), ctypes.POINTER(Lists), vp], i),
         "absh_lists_bytes": ([vp, i, i, i], sz),
         "absh_lists_carve": ([vp, i, i, i, vp, sz, ctypes.POINTER(Lists)], i),
         "absh_sparse_attn": ([vp, vp, vp, vp, i, i, i, ctypes.POINTER(Lists), vp, vp], i),

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -42,6 +43,34 @@ constexpr int kMaxNb = 2048;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Route workspace of absh_route_static: one file-scope device array, of which each
+// GPU the library runs on holds its own copy until the process ends. In host code
+// `scratch` names a host-side stand-in, so its device address on each GPU is looked
+// up once (scratch_setup, with that GPU current) and only that address is used.
+constexpr size_t kStaticScratchBytes = (size_t)ABSH_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on `device`, which must be current.
+hipError_t scratch_setup(int device) {
+  if (device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch_ptr[device] = ptr;
+  return hipSuccess;
+}
+
+void* scratch_ptr(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
 
 absh_status use_device(const absh_ctx* c) {
   int cur = -1;
@@ -127,7 +156,9 @@ absh_status absh_create(absh_ctx** out, int T, int Y, int X, int block, int devi
     return fail(ABSH_ENODEV, "no HIP device available");
   }
   if (device >= ndev) return fail(ABSH_ENODEV, "device %d does not exist (%d present)", device, ndev);
+  if (device >= kMaxDevices) return fail(ABSH_EUNSUPPORTED, "device index %d above %d", device, kMaxDevices - 1);
   ABSH_HIP(hipSetDevice(device), "hipSetDevice");
+  ABSH_HIP(scratch_setup(device), "absh_create: static scratch address");
 
   absh_ctx* c = new (std::nothrow) absh_ctx();
   if (!c) return fail(ABSH_EINVAL, "out of host memory");
@@ -477,6 +508,20 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
   out->schedule = opts->schedule;
   out->strict_ranks = ranks ? opts->strict_ranks : 0;
   return ABSH_OK;
+}
+
+absh_status absh_route_static(absh_ctx* c, const void* qh, const void* kh, absh_dtype qk_type, int B, int H, int d,
+                              const absh_route_opts* opts, absh_lists* out, void* stream) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (absh_status st = check_shape(c, B, H, d)) return st;
+  const size_t need = ws_layout(c, B, H, d).total;
+  if (need > kStaticScratchBytes)
+    return fail(ABSH_EWORKSPACE, "absh_route_static: this shape needs %zu bytes of scratch, above its %zu-byte maximum",
+                need, kStaticScratchBytes);
+  void* ptr = scratch_ptr(c->device);
+  if (!ptr) return fail(ABSH_EINVAL, "absh_route_static: no static scratch on device %d", c->device);
+  return absh_route(c, qh, kh, qk_type, B, H, d, opts, out, ptr, kStaticScratchBytes, stream);
 }
 
 }  // extern "C"

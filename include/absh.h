@@ -290,6 +290,22 @@ size_t absh_workspace_bytes(const absh_ctx* ctx, int B, int H, int d);
 absh_status absh_route(absh_ctx* ctx, const void* qh, const void* kh, absh_dtype qk_type, int B, int H, int d,
                        const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream);
 
+/* absh_route for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same routing,
+ * same arguments and outputs, with the workspace taken from a static device array
+ * of ABSH_STATIC_SCRATCH_BYTES that the library holds on each GPU until the process
+ * ends (its address is looked up by absh_create). The call allocates nothing. A
+ * shape whose absh_route_workspace_bytes() exceeds the maximum returns
+ * ABSH_EWORKSPACE and launches nothing (e.g. 480p at 12 heads, about 19 MB, fits;
+ * 720p at 40 heads, about 272 MB, does not). All calls on one GPU share the array:
+ * calls that overlap in time on one GPU (other streams, other threads, other
+ * contexts on the same device) race and must be serialised by the caller. The
+ * kernels write every scratch word they read within the call, so nothing carries
+ * over from the previous call. */
+#define ABSH_STATIC_SCRATCH_BYTES (64u << 20)
+absh_status absh_route_static(absh_ctx* ctx, const void* qh, const void* kh, absh_dtype qk_type, int B, int H,
+                              int d, const absh_route_opts* opts, absh_lists* out, void* stream);
+
 /* Block-sparse attention (xllm-io review of FVAttn, "Block-Sparse Attention
  * Execution"): for every tile (b, h, i) in lists->queue order,
  *   O_i = softmax(Q_i K_R^T / sqrt(d)) V_R

@@ -1,0 +1,88 @@
+"""absh_route_static (routing with the library's static device scratch, no allocation)
+against absh_route with a caller workspace, on the same inputs, bit for bit: two calls
+in a row, the second with a smaller input (fewer heads, then a smaller grid), and the
+rejection of a shape whose workspace exceeds the static maximum."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import adaptive_block_sparse_hilbert_amd as absh
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+EWORKSPACE = -3
+
+
+def inputs(index, heads=None, seed=None):
+    w = W.workload(index)
+    d = W.generate(w, seed=seed)
+    H = w.H if heads is None else heads
+    to_dev = lambda b: torch.from_numpy(np.ascontiguousarray(b[:, :, :H]).view(np.int16)).view(torch.bfloat16).to(DEV)
+    ctx = absh.create(w.T, w.Y, w.X, w.block)
+    qh, kh = absh.permute(ctx, to_dev(d["q16"])), absh.permute(ctx, to_dev(d["k16"]))
+    return w, ctx, qh, kh, H
+
+
+def route_static(ctx, qh, kh, opts, out):
+    B, H, _, d = qh.shape
+    lists = out.lists()
+    st = absh.lib().absh_route_static(ctx.handle, ctypes.c_void_p(qh.data_ptr()), ctypes.c_void_p(kh.data_ptr()),
+                                      absh.ABSH_BF16, B, H, d, ctypes.byref(opts), ctypes.byref(lists),
+                                      ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    out.schedule = lists.schedule
+    return st
+
+
+def same(a, b, units, schedule):
+    """Every field the call defines: counts, work, L, the queue and run bounds whole, each list
+    up to its count (entries past it are unspecified), the unit queue for the longest-first
+    schedule."""
+    for f in ("counts", "work", "L", "queue", "sched"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+    nb = a.kv_idx.shape[-1]
+    keep = torch.arange(nb, device=DEV) < a.counts.unsqueeze(-1)
+    assert torch.equal(torch.where(keep, a.kv_idx, -1), torch.where(keep, b.kv_idx, -1)), "kv_idx"
+    if int(a.sched[9]) == 1:  # single tiles: no unit lists
+        return
+    assert torch.equal(a.unit_cnt[:units], b.unit_cnt[:units]), "unit_cnt"
+    if schedule == "lpt":
+        assert torch.equal(a.unit_queue[:units], b.unit_queue[:units])
+    ucnt = a.unit_cnt[:units]
+    keep = torch.arange(nb, device=DEV) < ucnt.unsqueeze(-1)
+    assert torch.equal(torch.where(keep, a.unit_list[:units], -1), torch.where(keep, b.unit_list[:units], -1)), "unit_list"
+
+
+@pytest.mark.parametrize("schedule", ["xcd", "lpt"])
+def test_static_route_equals_workspace_route(schedule):
+    print(f"[no-alloc] schedule {schedule}", flush=True)
+    cases = [(1, None, 0.9, 0.05), (1, 5, 0.8, 0.0), (0, None, 0.9, 0.3)]  # 480p 12 heads, 5 heads, tiny
+    for index, heads, p, beta in cases:
+        w, ctx, qh, kh, H = inputs(index, heads)
+        print(f"[no-alloc] {w.name} heads {H} p {p} slack {beta}", flush=True)
+        assert absh.route_workspace_bytes(ctx, w.B, H, w.d) <= absh.STATIC_SCRATCH_BYTES
+        ref = absh.route(ctx, qh, kh, p, w.k_floor, slack_frac=beta, schedule=schedule)
+        out = absh.alloc_routing(ctx, w.B, H)
+        opts = absh.RouteOpts(p, w.k_floor, beta, absh.SCHEDULES[schedule], 0)
+        assert route_static(ctx, qh, kh, opts, out) == 0, absh.lib().absh_last_error()
+        torch.cuda.synchronize()
+        same(ref, out, absh.lists_units(ctx, w.B, H, schedule), schedule)
+
+
+def test_static_route_rejects_large_shapes():
+    w = W.workload(2)  # 720p at 40 heads: about 272 MB of workspace
+    H = w.H
+    ctx = absh.create(w.T, w.Y, w.X, w.block)
+    qh = kh = torch.zeros((w.B, H, ctx.n_pad, w.d), dtype=torch.bfloat16, device=DEV)
+    need = absh.route_workspace_bytes(ctx, w.B, H, w.d)
+    assert need > absh.STATIC_SCRATCH_BYTES
+    out = absh.alloc_routing(ctx, w.B, H)
+    out.counts.fill_(-7)
+    opts = absh.RouteOpts(0.9, 4, 0.0, absh.SCHEDULES["xcd"], 0)
+    assert route_static(ctx, qh, kh, opts, out) == EWORKSPACE
+    assert b"maximum" in absh.lib().absh_last_error()
+    torch.cuda.synchronize()
+    assert (out.counts == -7).all()
