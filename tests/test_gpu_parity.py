@@ -714,3 +714,54 @@ def test_edge_shapes(grid, block, d, H, B, p, k, schedule):
                       lambda b, h, i: kv[b, h, i, : counts[b, h, i]])
     e = np.abs(o - ref)
     assert e.max() <= ATOL_MAX and e.mean() <= ATOL_MEAN
+
+
+# ---------------------------------------------------------------- launch state
+
+def test_attention_on_two_streams_with_own_counters():
+    """Each set of lists carries its own work counters, so attention on two sets can run
+    concurrently on two streams; every output equals the same call run alone, and the
+    counters are zero again afterwards."""
+    c = case(1)
+    w = c.w
+    r1 = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, schedule="xcd")
+    r2 = absh.route(c.ctx, c.qh, c.kh, 0.8, w.k_floor, schedule="lpt")
+    ref1 = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r1)
+    ref2 = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r2)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        o1, o2 = torch.empty_like(ref1), torch.empty_like(ref2)
+        absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r1, out=o1, stream=s1)
+        absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r2, out=o2, stream=s2)
+        outs.append((o1, o2))
+    torch.cuda.synchronize()
+    rows = torch.arange(w.N, device=DEV)
+    for o1, o2 in outs:
+        assert torch.equal(o1[:, :, rows].view(torch.int16), ref1[:, :, rows].view(torch.int16))
+        assert torch.equal(o2[:, :, rows].view(torch.int16), ref2[:, :, rows].view(torch.int16))
+    assert (r1.pull == 0).all() and (r2.pull == 0).all()
+
+
+@pytest.mark.parametrize("index,schedule", [(1, "xcd"), (0, "lpt")])
+def test_busy_record(index, schedule):
+    """The busy record holds one (start, end) pair per workgroup of the launch, end after
+    start, and leaves the rows past the grid untouched."""
+    c = case(index)
+    w = c.w
+    r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, schedule=schedule)
+    rec = absh.busy_record(c.ctx, r)
+    rec.fill_(0)
+    absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r)
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    host = rec.cpu().numpy()
+    ran = host[:, 1] > 0
+    n = int(ran.sum())
+    assert n >= cus and n % cus == 0 and ran[:n].all() and not ran[n:].any()
+    assert (host[:n, 1] > host[:n, 0]).all()
+    ticks = absh.busy_ticks(rec)
+    print(f"[busy] {w.name} {schedule}: {n} workgroups, rho {ticks.max() / ticks.mean():.3f}")
+    if w.tiles > 64 * n:  # enough work for every workgroup: the pulls keep them within 2x of the mean
+        assert ticks.max() / ticks.mean() < 2.0

@@ -54,7 +54,7 @@ class Workload:
     p: float
     k_floor: int
     slack_frac: float = 0.0
-    lpt: bool = True
+    lpt: bool = False             # the configuration names the longest-first queue
     dtype: str = "bf16"          # "fp32" for the tiny case, else "bf16"
     s_mode: str = "loguniform"   # how the per-head signal scale s_h is drawn
     p_sweep: Sequence[float] = ()
