@@ -50,8 +50,11 @@
 //
 // Steps go in pairs with one workgroup barrier per pair. Step k reads V^T of step
 // k and K of step k + 1, so a pair (k, k + 1) holds V^T of k, k + 1 and K of
-// k + 1, k + 2; at its barrier it issues V^T of k + 2, k + 3 and K of k + 3, k + 4
-// into the slots the previous pair released, to land before the next pair.
+// k + 1, k + 2. Its barrier releases the slots of the previous pair, and the pair
+// fills them for the next one at four points spread over its two steps (V^T of
+// k + 2 at the barrier, K of k + 3 inside step k, V^T of k + 3 after it, K of
+// k + 4 inside step k + 1): spread out, the direct loads disturb the compute less
+// than in one burst at the barrier.
 #include <atomic>
 #include <type_traits>
 
@@ -468,15 +471,20 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
     }
     // Pair start (k even): everything issued at the previous pair has landed, all
     // waves are done with steps k - 2 and k - 1, and their slots take V^T of
-    // k + 2, k + 3 and K of k + 3, k + 4.
+    // k + 2, k + 3 and K of k + 3, k + 4: the first here, the others at
+    // load_k3 / load_v3 / load_k4 further into the pair.
     auto pair_start = [&](int k) __attribute__((always_inline)) {
       wait_vm<0>();
       __syncthreads();
       if (k + 2 < nsteps) issue_v(k + 2, k + 2, e2);
-      if (k + 3 < nsteps) {
-        issue_v(k + 3, k + 3, e3);
-        issue_k(k + 3, k + 3, e3);
-      }
+    };
+    auto load_k3 = [&](int k) __attribute__((always_inline)) {
+      if (k + 3 < nsteps) issue_k(k + 3, k + 3, e3);
+    };
+    auto load_v3 = [&](int k) __attribute__((always_inline)) {
+      if (k + 3 < nsteps) issue_v(k + 3, k + 3, e3);
+    };
+    auto load_k4 = [&](int k) __attribute__((always_inline)) {
       if (k + 4 < nsteps) issue_k(k + 4, k + 4, e4);
     };
     auto pair_end = [&](int k) __attribute__((always_inline)) {
@@ -491,9 +499,10 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
     // with S^T of step k + 1 unmasked. The step is two straight-line parts that a
     // wave skips when its query block does not retain the block: softmax + value
     // product of step k, then S^T of step k + 1.
-    auto step_fast = [&](int k, auto slot_c, uint32_t ek, uint32_t ek1) __attribute__((always_inline)) {
+    auto step_fast = [&](int k, auto slot_c, uint32_t ek, uint32_t ek1, auto mid) __attribute__((always_inline)) {
       constexpr int SL = decltype(slot_c)::value;
       if (mine(k, ek)) solo_pv(vslot(SL) + v_rd);
+      mid();
       if (mine(k + 1, ek1)) {
         const float m = body(F_(), T_(), F_(), kslot(SL + 1) + k_rd, nullptr, kStepKeys);
         if (__any(m > m_run + C::LAZY)) rescale_to(m);
@@ -533,20 +542,25 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
     int k = 0;
     while (k + 2 < first_masked) {
       pair_start(k);
-      step_fast(k, I0(), e0, e1);
-      step_fast(k + 1, I1(), e1, e2);
+      step_fast(k, I0(), e0, e1, [&]() { load_k3(k); });
+      load_v3(k);
+      step_fast(k + 1, I1(), e1, e2, [&]() { load_k4(k); });
       pair_end(k);
       k += 2;
       if (k + 2 >= first_masked) break;
       pair_start(k);
-      step_fast(k, I2(), e0, e1);
-      step_fast(k + 1, I3(), e1, e2);
+      step_fast(k, I2(), e0, e1, [&]() { load_k3(k); });
+      load_v3(k);
+      step_fast(k + 1, I3(), e1, e2, [&]() { load_k4(k); });
       pair_end(k);
       k += 2;
     }
     for (; k < nsteps; k += 2) {
       pair_start(k);
+      load_k3(k);
       step_tail(k, e0, e1);
+      load_v3(k);
+      load_k4(k);
       if (k + 1 < nsteps) step_tail(k + 1, e1, e2);
       pair_end(k);
     }
