@@ -47,7 +47,10 @@ hipError_t launch_scores(const absh_ctx* c, const float* qbar, const float* kbar
                          hipStream_t s);
 
 struct RouteBuffers {
-  const float* S;     // [tiles][nb] block scores
+  const float* S;     // [tiles][nb] block scores, or NULL: computed on chip where needed
+  const float* qbar;  // [tiles][d] block means of q (float32)
+  const float* kbar;  // [tiles][d] block means of k
+  int d;              // head dimension
   int32_t* counts;
   int32_t* kv_idx;
   int32_t* order;

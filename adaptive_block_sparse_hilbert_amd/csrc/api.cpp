@@ -98,13 +98,19 @@ struct WsLayout {
   size_t qbar, kbar, S, target, info, chunk_hist, scan_sums, slack_aux, rank, owner, budget, total;
 };
 
-WsLayout ws_layout(const absh_ctx* c, int B, int H, int d) {
+// scores: room for the score matrix (absh_route); without it the selection computes
+// the scores on chip (absh_route_static)
+WsLayout ws_layout(const absh_ctx* c, int B, int H, int d, bool scores = true) {
   const size_t tiles = (size_t)B * H * c->nb;
   WsLayout w;
   size_t off = 0;
   w.qbar = off; off = align_up(off + tiles * d * sizeof(float));
   w.kbar = off; off = align_up(off + tiles * d * sizeof(float));
-  w.S = off; off = align_up(off + tiles * c->nb * sizeof(float));
+  w.S = (size_t)-1;
+  if (scores) {
+    w.S = off;
+    off = align_up(off + tiles * c->nb * sizeof(float));
+  }
   w.target = off; off = align_up(off + tiles * sizeof(int32_t));
   w.info = off; off = align_up(off + 4 * sizeof(int64_t));
   w.chunk_hist = off; off = align_up(off + (size_t)absh::queue_chunks((int)tiles) * (c->nb + 1) * sizeof(int32_t));
@@ -379,8 +385,15 @@ size_t absh_route_workspace_bytes(const absh_ctx* c, int B, int H, int d) {
 
 size_t absh_workspace_bytes(const absh_ctx* c, int B, int H, int d) { return absh_route_workspace_bytes(c, B, H, d); }
 
-absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, absh_dtype qk_type, int B, int H, int d,
-                       const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The routing of absh_route; `scores`: the score matrix goes through the workspace
+// (score and select kernels), else the selection computes the scores on chip.
+absh_status route_impl(absh_ctx* c, const void* qh, const void* kh, absh_dtype qk_type, int B, int H, int d,
+                       const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream,
+                       bool scores) {
   g_last_error.clear();
   if (absh_status st = check_ctx(c)) return st;
   if (absh_status st = check_shape(c, B, H, d)) return st;
@@ -434,7 +447,7 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
   if (opts->schedule == ABSH_SCHED_LPT && members > 1 && !out->unit_queue)
     return fail(ABSH_EINVAL, "unit_queue must be non-NULL for ABSH_SCHED_LPT with blocks of 64 or 128");
   if (c->nb > kMaxNb) return fail(ABSH_EUNSUPPORTED, "nb = %d above the router's %d", c->nb, kMaxNb);
-  const WsLayout w = ws_layout(c, B, H, d);
+  const WsLayout w = ws_layout(c, B, H, d, scores);
   if (!ws) return fail(ABSH_EWORKSPACE, "workspace is NULL (%zu bytes needed)", w.total);
   if (ws_bytes < w.total) return fail(ABSH_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, w.total);
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
@@ -446,7 +459,10 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
   float* qbar = reinterpret_cast<float*>(base + w.qbar);
   float* kbar = reinterpret_cast<float*>(base + w.kbar);
   absh::RouteBuffers rb;
-  rb.S = reinterpret_cast<float*>(base + w.S);
+  rb.S = scores ? reinterpret_cast<float*>(base + w.S) : nullptr;
+  rb.qbar = qbar;
+  rb.kbar = kbar;
+  rb.d = d;
   rb.counts = out->counts;
   rb.kv_idx = out->kv_idx;
   rb.order = out->order;
@@ -480,7 +496,7 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
   } else {
     ABSH_HIP(absh::launch_pool(c, qh, qk_type == ABSH_F32, qbar, B, H, d, s), "absh_route: pool q");
     ABSH_HIP(absh::launch_pool(c, kh, qk_type == ABSH_F32, kbar, B, H, d, s), "absh_route: pool k");
-    ABSH_HIP(absh::launch_scores(c, qbar, kbar, const_cast<float*>(rb.S), B * H, d, s), "absh_route: scores");
+    if (rb.S) ABSH_HIP(absh::launch_scores(c, qbar, kbar, const_cast<float*>(rb.S), B * H, d, s), "absh_route: scores");
     ABSH_HIP(absh::launch_select(c, rb, tiles, opts->p, opts->k_floor, opts->order_depth, 0, s),
              "absh_route: select");
   }
@@ -510,18 +526,27 @@ absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
   return ABSH_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, absh_dtype qk_type, int B, int H, int d,
+                       const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream) {
+  return route_impl(c, qh, kh, qk_type, B, H, d, opts, out, ws, ws_bytes, stream, true);
+}
+
 absh_status absh_route_static(absh_ctx* c, const void* qh, const void* kh, absh_dtype qk_type, int B, int H, int d,
                               const absh_route_opts* opts, absh_lists* out, void* stream) {
   g_last_error.clear();
   if (absh_status st = check_ctx(c)) return st;
   if (absh_status st = check_shape(c, B, H, d)) return st;
-  const size_t need = ws_layout(c, B, H, d).total;
+  const size_t need = ws_layout(c, B, H, d, false).total;
   if (need > kStaticScratchBytes)
     return fail(ABSH_EWORKSPACE, "absh_route_static: this shape needs %zu bytes of scratch, above its %zu-byte maximum",
                 need, kStaticScratchBytes);
   void* ptr = scratch_ptr(c->device);
   if (!ptr) return fail(ABSH_EINVAL, "absh_route_static: no static scratch on device %d", c->device);
-  return absh_route(c, qh, kh, qk_type, B, H, d, opts, out, ptr, kStaticScratchBytes, stream);
+  return route_impl(c, qh, kh, qk_type, B, H, d, opts, out, ptr, kStaticScratchBytes, stream, false);
 }
 
 }  // extern "C"

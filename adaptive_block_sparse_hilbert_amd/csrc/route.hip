@@ -201,21 +201,19 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
 // wanted counts up to this take the arg-max route
 constexpr int kArgmaxWant = 16;
 
-// RS: re-selection to the counts in `target` (keys only), as its own instance
+// RS: re-selection to the counts in `target` (keys only), as its own instance.
+// One wave, the scores of tile `row` at srow[0 .. nb - 1] (in LDS).
 template <int J, bool RS>
-__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S, int nb, int tiles, double p,
-                                                     int k_floor, int order_depth,
-                                                     const int32_t* __restrict__ target, int32_t* __restrict__ counts,
-                                                     int32_t* __restrict__ kv_idx, int32_t* __restrict__ order) {
+__device__ __forceinline__ void select_row(const float* srow, int row, int nb, double p, int k_floor,
+                                           int order_depth, const int32_t* __restrict__ target,
+                                           int32_t* __restrict__ counts, int32_t* __restrict__ kv_idx,
+                                           int32_t* __restrict__ order) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= tiles) return;
   int want = 0;
   if (RS) {
     want = target[row];
     if (want <= counts[row]) return;
   }
-  const float* srow = S + (size_t)row * nb;
   float s[J];
   bool valid[J];
 #pragma unroll
@@ -239,21 +237,21 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
   // cannot happen within 700 of the row's max (exp > 9.8e-305, row sum <= 2048);
   // rows with a block further down take the float64 path from the start.
   constexpr double kBand = 2e-5;
-  double P[J];
+  // the float64 probabilities are recomputed where used (the same value each time),
+  // not kept, to save registers: they are needed only close to p and for far rows
+  double z64 = 0.0;
   float P32[J];
   uint32_t key[J];
   bool have64 = false;
   auto exact = [&]() __attribute__((always_inline)) {
     double z = 0.0;
 #pragma unroll
-    for (int t = 0; t < J; ++t) {
-      P[t] = valid[t] ? exp((double)s[t] - (double)smax) : 0.0;
-      z += P[t];
-    }
-    z = wave_sum(z);
-#pragma unroll
-    for (int t = 0; t < J; ++t) P[t] = P[t] / z;
+    for (int t = 0; t < J; ++t) z += valid[t] ? exp((double)s[t] - (double)smax) : 0.0;
+    z64 = wave_sum(z);
     have64 = true;
+  };
+  auto P = [&](int t) __attribute__((always_inline)) -> double {
+    return valid[t] ? exp((double)s[t] - (double)smax) / z64 : 0.0;
   };
   bool far = false;
 #pragma unroll
@@ -262,8 +260,9 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
     exact();
 #pragma unroll
     for (int t = 0; t < J; ++t) {
-      key[t] = (valid[t] && P[t] != 0.0) ? ordered_bits(s[t]) + 1u : 0u;
-      P32[t] = (float)P[t];
+      const double pt = P(t);
+      key[t] = (valid[t] && pt != 0.0) ? ordered_bits(s[t]) + 1u : 0u;
+      P32[t] = (float)pt;
     }
   } else {
 #pragma unroll
@@ -301,7 +300,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
           if (!have64) exact();
           double f = 0.0;
 #pragma unroll
-          for (int t = 0; t < J; ++t) f += key[t] >= cand ? P[t] : 0.0;
+          for (int t = 0; t < J; ++t) f += key[t] >= cand ? P(t) : 0.0;
           take = wave_sum(f) >= p;
         }
         if (take) tau = cand;
@@ -331,9 +330,10 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
         for (int t = 0; t < J; ++t) {
           const bool gt = valid[t] && key[t] > tau;
           const bool eq = valid[t] && key[t] == tau;
-          above += gt ? P[t] : 0.0;
-          at = eq ? P[t] : at;
-          f_tau += (gt || eq) ? P[t] : 0.0;
+          const double pt = (gt || eq) ? P(t) : 0.0;
+          above += gt ? pt : 0.0;
+          at = eq ? pt : at;
+          f_tau += pt;
         }
         above = wave_sum(above);
         f_tau = wave_sum(f_tau);
@@ -431,6 +431,83 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
       if (lane == 0) ord[r] = j;
     }
   }
+}
+
+// Selection from scores in memory: one wave per tile row.
+template <int J, bool RS>
+__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S, int nb, int tiles, double p,
+                                                     int k_floor, int order_depth,
+                                                     const int32_t* __restrict__ target, int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ kv_idx, int32_t* __restrict__ order) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= tiles) return;
+  select_row<J, RS>(S + (size_t)row * nb, row, nb, p, k_floor, order_depth, target, counts, kv_idx, order);
+}
+
+// Block scores and selection in one kernel, for routing without a score matrix in
+// memory. A workgroup takes kSelRows consecutive query blocks i0 .. of one head. Its
+// four waves first compute their scores against every key block on the float64 MFMA
+// D(16x16) += A(16x4) B(4x16) (A: the rows' block means of q, B: block means of k),
+// divide by sqrt(d), round to float32 and keep them in LDS (ld floats per row, nb
+// rounded up to 16); then each wave runs the selection on rows w, w + 4, ... The k
+// index of lane group g = l / 16 at k-step t is channel 4 t + g and the steps go in
+// order, as in scores_kernel, so the scores are the same float32 values bit for bit.
+// Re-selection (RS) rows that need no new block skip the work, and a workgroup whose
+// rows all do skips the scores too.
+constexpr int kSelRows = 16;
+
+template <int J, bool RS, int D>
+__global__ __launch_bounds__(256) void score_select_kernel(const float* __restrict__ qbar,
+                                                           const float* __restrict__ kbar, int nb, int groups,
+                                                           double sqrt_d, double p, int k_floor, int order_depth,
+                                                           const int32_t* __restrict__ target,
+                                                           int32_t* __restrict__ counts, int32_t* __restrict__ kv_idx,
+                                                           int32_t* __restrict__ order) {
+  constexpr int KS = D / 4;  // k-steps of the float64 MFMA
+  extern __shared__ float srows[];  // [kSelRows][ld]
+  const int ld = (nb + 15) & ~15;
+  const int bh = blockIdx.x / groups;
+  const int i0 = (blockIdx.x - bh * groups) * kSelRows;
+  const int nrows = min(kSelRows, nb - i0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tile0 = bh * nb + i0;
+  if (RS) {
+    int need = 0;
+    for (int r = 0; r < nrows; ++r) need |= target[tile0 + r] > counts[tile0 + r];
+    if (!need) return;  // uniform over the workgroup
+  }
+  const int r16 = lane & 15, g = lane >> 4;
+  // lane group g's element of the four channels 4 t .. 4 t + 3
+  auto pick = [&](const float4& v) __attribute__((always_inline)) -> double {
+    return (double)(g == 0 ? v.x : g == 1 ? v.y : g == 2 ? v.z : v.w);
+  };
+  // A operand: row i0 + r16, channel 4 t + g at k-step t (zero past the head's last block)
+  double a[KS];
+  {
+    const float4* q4 = reinterpret_cast<const float4*>(qbar + ((size_t)tile0 + r16) * D);
+    const bool in = r16 < nrows;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) a[t] = in ? pick(q4[t]) : 0.0;
+  }
+  const float* kb = kbar + (size_t)bh * nb * D;
+  const int col_tiles = (nb + 15) / 16;
+  for (int ct = wave; ct < col_tiles; ct += 4) {
+    const int j = ct * 16 + r16;
+    const float4* k4 = reinterpret_cast<const float4*>(kb + (size_t)j * D);
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[t], j < nb ? pick(k4[t]) : 0.0, acc, 0, 0, 0);
+    // element e of lane l is row 4 e + l / 16, column l % 16 of the tile
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * e + g;
+      if (r < nrows && j < nb) srows[r * ld + j] = __double2float_rn(acc[e] / sqrt_d);
+    }
+  }
+  __syncthreads();
+  for (int r = wave; r < nrows; r += 4)
+    select_row<J, RS>(srows + r * ld, tile0 + r, nb, p, k_floor, order_depth, target, counts, kv_idx, order);
 }
 
 // ------------------------------------------------------------------ workloads (Eq. 1)
@@ -1226,17 +1303,52 @@ hipError_t launch_scores(const absh_ctx* c, const float* qbar, const float* kbar
 
 hipError_t launch_select(const absh_ctx* c, const RouteBuffers& rb, int tiles, double p, int k_floor,
                          int order_depth, int reselect, hipStream_t s) {
-  const unsigned grid = (unsigned)((tiles + 3) / 4);
   const int nb = c->nb;
-#define ABSH_SELECT(JJ)                                                                             \
-  do {                                                                                              \
-    if (reselect)                                                                                   \
-      select_kernel<JJ, true><<<grid, 256, 0, s>>>(rb.S, nb, tiles, p, k_floor, order_depth, rb.target,  \
-                                                   rb.counts, rb.kv_idx, rb.order);                 \
-    else                                                                                            \
-      select_kernel<JJ, false><<<grid, 256, 0, s>>>(rb.S, nb, tiles, p, k_floor, order_depth, rb.target, \
-                                                    rb.counts, rb.kv_idx, rb.order);                \
+  const int groups = (nb + kSelRows - 1) / kSelRows;
+  const unsigned grid = (unsigned)((uint64_t)(tiles / nb) * groups);
+  const double sqrt_d = sqrt((double)rb.d);
+  const size_t lds = (size_t)kSelRows * ((nb + 15) & ~15) * sizeof(float);
+#define ABSH_SELECT_D(JJ, DD)                                                                          \
+  do {                                                                                                 \
+    if (reselect)                                                                                      \
+      score_select_kernel<JJ, true, DD><<<grid, 256, lds, s>>>(rb.qbar, rb.kbar, nb, groups, sqrt_d, p, k_floor, \
+                                                             order_depth, rb.target, rb.counts, rb.kv_idx,  \
+                                                             rb.order);                                \
+    else                                                                                               \
+      score_select_kernel<JJ, false, DD><<<grid, 256, lds, s>>>(rb.qbar, rb.kbar, nb, groups, sqrt_d, p, k_floor, \
+                                                              order_depth, rb.target, rb.counts, rb.kv_idx, \
+                                                              rb.order);                               \
   } while (0)
+#define ABSH_SELECT(JJ)                          \
+  do {                                           \
+    if (rb.d == 64)                              \
+      ABSH_SELECT_D(JJ, 64);                     \
+    else                                         \
+      ABSH_SELECT_D(JJ, 128);                    \
+  } while (0)
+  if (rb.d != 64 && rb.d != 128) return hipErrorInvalidValue;
+  const unsigned row_grid = (unsigned)((tiles + 3) / 4);
+  if (rb.S) {  // scores in memory
+#define ABSH_SELECT_S(JJ)                                                                                  \
+  do {                                                                                                     \
+    if (reselect)                                                                                          \
+      select_kernel<JJ, true><<<row_grid, 256, 0, s>>>(rb.S, nb, tiles, p, k_floor, order_depth, rb.target,  \
+                                                       rb.counts, rb.kv_idx, rb.order);                   \
+    else                                                                                                   \
+      select_kernel<JJ, false><<<row_grid, 256, 0, s>>>(rb.S, nb, tiles, p, k_floor, order_depth, rb.target, \
+                                                        rb.counts, rb.kv_idx, rb.order);                  \
+  } while (0)
+    if (nb <= 64) ABSH_SELECT_S(1);
+    else if (nb <= 256) ABSH_SELECT_S(4);
+    else if (nb <= 512) ABSH_SELECT_S(8);
+    else if (nb <= 1024) ABSH_SELECT_S(16);
+    else if (nb <= 1280) ABSH_SELECT_S(20);
+    else if (nb <= 1536) ABSH_SELECT_S(24);
+    else if (nb <= 2048) ABSH_SELECT_S(32);
+    else return hipErrorInvalidValue;
+#undef ABSH_SELECT_S
+    return hipGetLastError();
+  }
   if (nb <= 64) ABSH_SELECT(1);
   else if (nb <= 256) ABSH_SELECT(4);
   else if (nb <= 512) ABSH_SELECT(8);
@@ -1246,6 +1358,7 @@ hipError_t launch_select(const absh_ctx* c, const RouteBuffers& rb, int tiles, d
   else if (nb <= 2048) ABSH_SELECT(32);
   else return hipErrorInvalidValue;
 #undef ABSH_SELECT
+#undef ABSH_SELECT_D
   return hipGetLastError();
 }
 

@@ -565,6 +565,9 @@ def cpu_baseline(w, p, data, budget_s, head0=None):
                    f"({t_route:.2f} s, prorated to the sample), attention for {done} query blocks "
                    f"spread over the head ({t_attn:.2f} s); float64 NumPy"),
         "route_parity_head0": parity,
+        "oracle_route_s_head0": round(t_route, 3),
+        "oracle_attn_s": round(t_attn, 3),
+        "oracle_attn_tiles": done,
     }
 
 

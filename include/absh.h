@@ -278,12 +278,14 @@ size_t absh_workspace_bytes(const absh_ctx* ctx, int B, int H, int d);
 /* Stage-1 routing (xllm-io review of FVAttn, Stage 1; explainer, "Key Concepts"):
  * from Hilbert-order qh, kh ([B, H, n_pad, d]; qk_type ABSH_BF16: bf16 rows,
  * ABSH_ROWS; ABSH_F32: float32 rows, ABSH_ROWS_F32; 16-byte aligned):
- *   block means -> float32 block scores -> softmax over key blocks (float64) ->
+ *   block means -> float32 block scores (through the workspace) -> softmax over
+ *   key blocks (float64) ->
  *   Top-p: the fewest blocks, by probability descending (ties: smaller id),
  *   whose cumulative probability reaches p -> floor count' = max(c, min(k, nb))
  *   -> optional slack fill of E = floor(beta * sum count') blocks raising the
  *   lightest tiles along their own importance order -> Eq. 1 workloads
- *   work_h and L_h -> the tile queue (longest first when opts->lpt).
+ *   work_h and L_h -> the tile queue (longest first for ABSH_SCHED_LPT), the
+ *   work units, and the pull counters (out->pull, if set) zeroed.
  * nb must be <= 2048. Writes every field of *out (order only if
  * opts->order_depth > 0). ws must hold absh_route_workspace_bytes(); its
  * contents are scratch. No host synchronisation. */
@@ -292,12 +294,14 @@ absh_status absh_route(absh_ctx* ctx, const void* qh, const void* kh, absh_dtype
 
 /* absh_route for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same routing,
- * same arguments and outputs, with the workspace taken from a static device array
+ * same arguments and bit-identical outputs, with the block scores computed on chip
+ * inside the selection (no score matrix) and the rest of the workspace (block means,
+ * slack and queue scratch) taken from a static device array
  * of ABSH_STATIC_SCRATCH_BYTES that the library holds on each GPU until the process
  * ends (its address is looked up by absh_create). The call allocates nothing. A
  * shape whose absh_route_workspace_bytes() exceeds the maximum returns
- * ABSH_EWORKSPACE and launches nothing (e.g. 480p at 12 heads, about 19 MB, fits;
- * 720p at 40 heads, about 272 MB, does not). All calls on one GPU share the array:
+ * ABSH_EWORKSPACE and launches nothing (720p at 40 heads, about 50 MB, fits; 720p
+ * at 64 heads, about 78 MB, does not). All calls on one GPU share the array:
  * calls that overlap in time on one GPU (other streams, other threads, other
  * contexts on the same device) race and must be serialised by the caller. The
  * kernels write every scratch word they read within the call, so nothing carries
