@@ -227,8 +227,8 @@ def block_scores(ctx: Context, qbar, kbar, out=None, stream=None):
 @dataclass
 class Routing:
     counts: object   # int32 [B, H, nb]
-    kv_idx: object   # int32 [B, H, nb, nb]
-    order: Optional[object]  # int32 [B, H, nb, depth] or None
+    kv_idx: object   # int16 [B, H, nb, nb]
+    order: Optional[object]  # int16 [B, H, nb, depth] or None
     work: object     # int32 [B, H]
     L: object        # float32 [B, H]
     queue: object    # int32 [B*H*nb]
@@ -257,14 +257,14 @@ class Routing:
         import torch
         nb = ctx.nb
         units = max_units(ctx, B, H)
-        want = {"counts": ((B, H, nb), torch.int32), "kv_idx": ((B, H, nb, nb), torch.int32),
+        want = {"counts": ((B, H, nb), torch.int32), "kv_idx": ((B, H, nb, nb), torch.int16),
                 "work": ((B, H), torch.int32), "L": ((B, H), torch.float32),
                 "queue": ((B * H * nb,), torch.int32), "sched": ((10,), torch.int32),
                 "unit_list": ((units, nb), torch.int32), "unit_cnt": ((units,), torch.int32),
                 "head_order": ((B * H,), torch.int32), "rank_info": ((RANK_INFO,), torch.float64),
                 "unit_queue": ((units,), torch.int32), "pull": ((PULL_WORDS,), torch.int32)}
         if order_depth > 0:
-            want["order"] = ((B, H, nb, order_depth), torch.int32)
+            want["order"] = ((B, H, nb, order_depth), torch.int16)
         elif self.order is not None and self.order.dim() != 4:
             raise ValueError("order must be [B, H, nb, depth]")
         for name, (shape, dtype) in want.items():
@@ -325,8 +325,8 @@ def alloc_routing(ctx: Context, B: int, H: int, order_depth: int = 0) -> Routing
     units = max_units(ctx, B, H)
     return Routing(
         counts=torch.empty((B, H, nb), dtype=torch.int32, device=dev),
-        kv_idx=torch.empty((B, H, nb, nb), dtype=torch.int32, device=dev),
-        order=torch.empty((B, H, nb, order_depth), dtype=torch.int32, device=dev) if order_depth else None,
+        kv_idx=torch.empty((B, H, nb, nb), dtype=torch.int16, device=dev),
+        order=torch.empty((B, H, nb, order_depth), dtype=torch.int16, device=dev) if order_depth else None,
         work=torch.empty((B, H), dtype=torch.int32, device=dev),
         L=torch.empty((B, H), dtype=torch.float32, device=dev),
         queue=torch.empty((B * H * nb,), dtype=torch.int32, device=dev),

@@ -52,8 +52,8 @@ struct RouteBuffers {
   const float* kbar;  // [tiles][d] block means of k
   int d;              // head dimension
   int32_t* counts;
-  int32_t* kv_idx;
-  int32_t* order;
+  int16_t* kv_idx;    // [tiles][nb] ascending block ids, row-padded
+  int16_t* order;     // [tiles][order_depth] importance-order prefix
   int32_t* work;
   float* L;
   int32_t* queue;
@@ -105,7 +105,7 @@ hipError_t launch_window_anchor(const absh_ctx* c, const RouteBuffers& rb, int t
 struct AttnLists {
   const int32_t* queue;       // single units: queue position -> tile
   const int32_t* counts;      // [tiles]
-  const int32_t* kv_idx;      // [tiles][nb]
+  const int16_t* kv_idx;      // [tiles][nb]
   const uint32_t* unit_list;  // group units: [units][nb] flagged union entries
   const int32_t* unit_cnt;    // [units]
   const int32_t* sched;       // [10] segment bounds + members (read by the kernel)

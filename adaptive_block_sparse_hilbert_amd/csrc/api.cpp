@@ -322,8 +322,8 @@ bool lists_layout(const absh_ctx* c, int B, int H, int order_depth, ListsLayout*
     return at;
   };
   l->counts = take(tiles * 4);
-  l->kv_idx = take(tiles * nb * 4);
-  l->order = order_depth > 0 ? take(tiles * (size_t)order_depth * 4) : (size_t)-1;
+  l->kv_idx = take(tiles * nb * 2);
+  l->order = order_depth > 0 ? take(tiles * (size_t)order_depth * 2) : (size_t)-1;
   l->work = take(BH * 4);
   l->L = take(BH * 4);
   l->queue = take(tiles * 4);
@@ -360,8 +360,8 @@ absh_status absh_lists_carve(const absh_ctx* c, int B, int H, int order_depth, v
   char* base = reinterpret_cast<char*>(arena);
   *out = absh_lists{};
   out->counts = reinterpret_cast<int32_t*>(base + l.counts);
-  out->kv_idx = reinterpret_cast<int32_t*>(base + l.kv_idx);
-  out->order = l.order == (size_t)-1 ? nullptr : reinterpret_cast<int32_t*>(base + l.order);
+  out->kv_idx = reinterpret_cast<int16_t*>(base + l.kv_idx);
+  out->order = l.order == (size_t)-1 ? nullptr : reinterpret_cast<int16_t*>(base + l.order);
   out->work = reinterpret_cast<int32_t*>(base + l.work);
   out->L = reinterpret_cast<float*>(base + l.L);
   out->queue = reinterpret_cast<int32_t*>(base + l.queue);

@@ -226,14 +226,14 @@ void attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, c
     const int pos = __builtin_amdgcn_readfirstlane(s_next[parity]);
     if (pos < 0) break;
     int bh, qb0, cnt;
-    const_i32 plain = nullptr;    // single unit: plain ascending block ids
+    const int16_t* plain = nullptr;  // single unit: plain ascending block ids
     const_i32 flagged = nullptr;  // group unit: flagged union entries
     if (members == 1) {
       const int tile = __builtin_amdgcn_readfirstlane(as_const(L.queue)[pos]);
       bh = tile / nb;
       qb0 = tile - bh * nb;
       cnt = as_const(L.counts)[tile];
-      plain = as_const(L.kv_idx + (size_t)tile * nb);
+      plain = L.kv_idx + (size_t)tile * nb;
     } else {
       // segment position -> unit: through unit_queue, or head_order (segments
       // following ranks), or in order

@@ -206,8 +206,8 @@ constexpr int kArgmaxWant = 16;
 template <int J, bool RS>
 __device__ __forceinline__ void select_row(const float* srow, int row, int nb, double p, int k_floor,
                                            int order_depth, const int32_t* __restrict__ target,
-                                           int32_t* __restrict__ counts, int32_t* __restrict__ kv_idx,
-                                           int32_t* __restrict__ order) {
+                                           int32_t* __restrict__ counts, int16_t* __restrict__ kv_idx,
+                                           int16_t* __restrict__ order) {
   const int lane = threadIdx.x & 63;
   int want = 0;
   if (RS) {
@@ -237,21 +237,21 @@ __device__ __forceinline__ void select_row(const float* srow, int row, int nb, d
   // cannot happen within 700 of the row's max (exp > 9.8e-305, row sum <= 2048);
   // rows with a block further down take the float64 path from the start.
   constexpr double kBand = 2e-5;
-  // the float64 probabilities are recomputed where used (the same value each time),
-  // not kept, to save registers: they are needed only close to p and for far rows
-  double z64 = 0.0;
+  double P[J];
   float P32[J];
   uint32_t key[J];
   bool have64 = false;
   auto exact = [&]() __attribute__((always_inline)) {
     double z = 0.0;
 #pragma unroll
-    for (int t = 0; t < J; ++t) z += valid[t] ? exp((double)s[t] - (double)smax) : 0.0;
-    z64 = wave_sum(z);
+    for (int t = 0; t < J; ++t) {
+      P[t] = valid[t] ? exp((double)s[t] - (double)smax) : 0.0;
+      z += P[t];
+    }
+    z = wave_sum(z);
+#pragma unroll
+    for (int t = 0; t < J; ++t) P[t] = P[t] / z;
     have64 = true;
-  };
-  auto P = [&](int t) __attribute__((always_inline)) -> double {
-    return valid[t] ? exp((double)s[t] - (double)smax) / z64 : 0.0;
   };
   bool far = false;
 #pragma unroll
@@ -260,9 +260,8 @@ __device__ __forceinline__ void select_row(const float* srow, int row, int nb, d
     exact();
 #pragma unroll
     for (int t = 0; t < J; ++t) {
-      const double pt = P(t);
-      key[t] = (valid[t] && pt != 0.0) ? ordered_bits(s[t]) + 1u : 0u;
-      P32[t] = (float)pt;
+      key[t] = (valid[t] && P[t] != 0.0) ? ordered_bits(s[t]) + 1u : 0u;
+      P32[t] = (float)P[t];
     }
   } else {
 #pragma unroll
@@ -300,7 +299,7 @@ __device__ __forceinline__ void select_row(const float* srow, int row, int nb, d
           if (!have64) exact();
           double f = 0.0;
 #pragma unroll
-          for (int t = 0; t < J; ++t) f += key[t] >= cand ? P(t) : 0.0;
+          for (int t = 0; t < J; ++t) f += key[t] >= cand ? P[t] : 0.0;
           take = wave_sum(f) >= p;
         }
         if (take) tau = cand;
@@ -330,10 +329,9 @@ __device__ __forceinline__ void select_row(const float* srow, int row, int nb, d
         for (int t = 0; t < J; ++t) {
           const bool gt = valid[t] && key[t] > tau;
           const bool eq = valid[t] && key[t] == tau;
-          const double pt = (gt || eq) ? P(t) : 0.0;
-          above += gt ? pt : 0.0;
-          at = eq ? pt : at;
-          f_tau += pt;
+          above += gt ? P[t] : 0.0;
+          at = eq ? P[t] : at;
+          f_tau += (gt || eq) ? P[t] : 0.0;
         }
         above = wave_sum(above);
         f_tau = wave_sum(f_tau);
@@ -400,14 +398,14 @@ __device__ __forceinline__ void select_row(const float* srow, int row, int nb, d
     }
   }
   // the list in ascending block id
-  int32_t* out = kv_idx + (size_t)row * nb;
+  int16_t* out = kv_idx + (size_t)row * nb;
   int written = 0;
   const uint64_t below = lanes_below(lane);
 #pragma unroll
   for (int t = 0; t < J; ++t) {
     const bool take = (takebits >> t) & 1u;
     const uint64_t take_mask = __ballot(take);
-    if (take) out[written + popc64(take_mask & below)] = lane + 64 * t;
+    if (take) out[written + popc64(take_mask & below)] = (int16_t)(lane + 64 * t);
     written += popc64(take_mask);
   }
   if (lane == 0) counts[row] = want;
@@ -415,7 +413,7 @@ __device__ __forceinline__ void select_row(const float* srow, int row, int nb, d
   // Importance-order prefix: repeated arg-max of (key, -id) over the blocks not yet taken.
   if (!RS && order_depth > 0) {
     uint32_t taken = 0;
-    int32_t* ord = order + (size_t)row * order_depth;
+    int16_t* ord = order + (size_t)row * order_depth;
     for (int r = 0; r < order_depth; ++r) {
       uint64_t best = 0;
 #pragma unroll
@@ -428,17 +426,19 @@ __device__ __forceinline__ void select_row(const float* srow, int row, int nb, d
       best = wave_max_u64(best);
       const int j = best ? (int)(0xFFFFFFFFu - (uint32_t)best) : -1;
       if (j >= 0 && (j & 63) == lane) taken |= 1u << (j >> 6);
-      if (lane == 0) ord[r] = j;
+      if (lane == 0) ord[r] = (int16_t)j;
     }
   }
 }
 
-// Selection from scores in memory: one wave per tile row.
+// Selection from scores in memory: one wave per tile row. The searches are
+// latency-bound, so rows of up to 1,280 blocks are held to three waves per SIMD's
+// worth of registers (wider rows would spill).
 template <int J, bool RS>
-__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S, int nb, int tiles, double p,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(J <= 20 ? 3 : 1))) void select_kernel(const float* __restrict__ S, int nb, int tiles, double p,
                                                      int k_floor, int order_depth,
                                                      const int32_t* __restrict__ target, int32_t* __restrict__ counts,
-                                                     int32_t* __restrict__ kv_idx, int32_t* __restrict__ order) {
+                                                     int16_t* __restrict__ kv_idx, int16_t* __restrict__ order) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= tiles) return;
   select_row<J, RS>(S + (size_t)row * nb, row, nb, p, k_floor, order_depth, target, counts, kv_idx, order);
@@ -461,8 +461,8 @@ __global__ __launch_bounds__(256) void score_select_kernel(const float* __restri
                                                            const float* __restrict__ kbar, int nb, int groups,
                                                            double sqrt_d, double p, int k_floor, int order_depth,
                                                            const int32_t* __restrict__ target,
-                                                           int32_t* __restrict__ counts, int32_t* __restrict__ kv_idx,
-                                                           int32_t* __restrict__ order) {
+                                                           int32_t* __restrict__ counts, int16_t* __restrict__ kv_idx,
+                                                           int16_t* __restrict__ order) {
   constexpr int KS = D / 4;  // k-steps of the float64 MFMA
   extern __shared__ float srows[];  // [kSelRows][ld]
   const int ld = (nb + 15) & ~15;
@@ -775,7 +775,7 @@ __global__ __launch_bounds__(256) void queue_identity_kernel(int tiles, int32_t*
 constexpr int kMaxUnion = 2048;  // the router's largest nb
 template <int M>
 __global__ __launch_bounds__(256) void group_merge_kernel(const int32_t* __restrict__ counts,
-                                                          const int32_t* __restrict__ kv_idx, int nb, int per_head,
+                                                          const int16_t* __restrict__ kv_idx, int nb, int per_head,
                                                           int units, uint32_t* __restrict__ unit_list,
                                                           int32_t* __restrict__ unit_cnt) {
   __shared__ uint32_t bits[4][M][64];
@@ -937,19 +937,19 @@ __global__ __launch_bounds__(1024) void unit_lpt_kernel(const int32_t* __restric
 // per tile row writes the ascending list by ballot and prefix count.
 __global__ __launch_bounds__(256) void window_anchor_kernel(int nb, int tiles, int window, int stride, int offset,
                                                             int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ kv_idx) {
+                                                            int16_t* __restrict__ kv_idx) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= tiles) return;
   const int i = row % nb;
   const int lo = max(0, i - window), hi = min(nb - 1, i + window);
-  int32_t* out = kv_idx + (size_t)row * nb;
+  int16_t* out = kv_idx + (size_t)row * nb;
   int n = 0;
   for (int j0 = 0; j0 < nb; j0 += 64) {
     const int j = j0 + lane;
     const bool in = j < nb && ((j >= lo && j <= hi) || (stride > 0 && j % stride == offset));
     const uint64_t mask = __ballot(in);
-    if (in) out[n + __popcll(mask & ((1ull << lane) - 1))] = j;
+    if (in) out[n + __popcll(mask & ((1ull << lane) - 1))] = (int16_t)j;
     n += __popcll(mask);
   }
   if (lane == 0) counts[row] = n;

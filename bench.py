@@ -282,7 +282,7 @@ def measure(args, w, p, schedule, route_f32):
 
     # retained work of this routing (identical every step: the path is deterministic)
     counts = routing.counts.cpu().numpy().reshape(-1)
-    kv = routing.kv_idx.cpu().numpy().reshape(counts.size, ctx.nb)
+    kv = routing.kv_idx.cpu().numpy().astype(np.int64).reshape(counts.size, ctx.nb)
     sizes = np.minimum(w.block, w.N - np.arange(ctx.nb) * w.block).astype(np.int64)
     # sum of n_j over each retained list: only the last block can be partial, and an
     # ascending list holds it in its last slot
@@ -350,7 +350,7 @@ def measure(args, w, p, schedule, route_f32):
         base = routing
         if w.slack_frac > 0 and args.router == "topp":
             base = absh.route(ctx, qr if route_f32 else qh, kr if route_f32 else kh, p, w.k_floor, schedule=schedule)
-        head0 = (base.counts[:, :1].cpu().numpy(), base.kv_idx[:, :1].cpu().numpy())
+        head0 = (base.counts[:, :1].cpu().numpy(), base.kv_idx[:, :1].cpu().numpy().astype(np.int64))
         cpu = cpu_baseline(w, p, data, args.cpu_seconds, head0 if args.router == "topp" else None)
 
     out = {

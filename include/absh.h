@@ -137,8 +137,9 @@ typedef struct {
  * nb, tiles = B*H*nb. */
 typedef struct {
   int32_t* counts; /* [tiles] retained key blocks per tile (after floor and slack fill)        */
-  int32_t* kv_idx; /* [tiles][nb] row-padded; the first counts[t] entries, ascending block id  */
-  int32_t* order;  /* [tiles][order_depth] block ids, probability descending, ties by smaller
+  int16_t* kv_idx; /* [tiles][nb] row-padded; the first counts[t] entries, ascending block id
+                      (block ids < nb <= 2048 fit in int16)                                     */
+  int16_t* order;  /* [tiles][order_depth] block ids, probability descending, ties by smaller
                       id; -1 past nb. May be NULL when order_depth == 0                         */
   int32_t* work;   /* [B*H] sum_i counts (the numerator of Eq. 1, exact)                        */
   float* L;        /* [B*H] L_h = work / nb, float32 division (Eq. 1)                           */

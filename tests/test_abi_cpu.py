@@ -57,7 +57,7 @@ def test_routing_buffers_are_checked_before_the_call():
     if not os.path.exists(absh.LIB_PATH):
         pytest.skip("libabsh.so not built")
     ctx = types.SimpleNamespace(nb=4, n_pad=64, device=0, handle=ctypes.c_void_p())
-    good = dict(counts=((1, 2, 4), torch.int32), kv_idx=((1, 2, 4, 4), torch.int32), work=((1, 2), torch.int32),
+    good = dict(counts=((1, 2, 4), torch.int32), kv_idx=((1, 2, 4, 4), torch.int16), work=((1, 2), torch.int32),
                 L=((1, 2), torch.float32), queue=((8,), torch.int32), sched=((10,), torch.int32),
                 unit_list=((1, 4), torch.int32), unit_cnt=((1,), torch.int32), head_order=((2,), torch.int32),
                 rank_info=((absh.RANK_INFO,), torch.float64), unit_queue=((1,), torch.int32),

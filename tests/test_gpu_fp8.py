@@ -122,7 +122,7 @@ def fp8_attention_check(c, r, tiles, label):
     o = absh.unpermute(c.ctx, oh).float().cpu().numpy()
     if r is not None:
         counts = r.counts.cpu().numpy().reshape(-1)
-        kv = r.kv_idx.cpu().numpy().reshape(counts.size, -1)
+        kv = r.kv_idx.cpu().numpy().astype(np.int64).reshape(counts.size, -1)
     errs, slack, a2 = [], [], []
     for t in tiles:
         bh, i = divmod(int(t), w.nb)

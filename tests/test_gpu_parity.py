@@ -89,7 +89,7 @@ def case(index):
 def check_lists_valid(r, nb):
     """Host-side validity of lists and queue before any kernel consumes them."""
     counts = r.counts.cpu().numpy()
-    kv = r.kv_idx.cpu().numpy()
+    kv = r.kv_idx.cpu().numpy().astype(np.int64)
     queue = r.queue.cpu().numpy()
     assert counts.min() >= 1 and counts.max() <= nb
     assert np.array_equal(np.sort(queue), np.arange(queue.size))
@@ -238,7 +238,7 @@ def test_importance_order_prefix():
     c = case(1)
     w = c.w
     r = absh.route(c.ctx, c.qh, c.kh, w.p, w.k_floor, order_depth=16)
-    got = r.order.cpu().numpy()
+    got = r.order.cpu().numpy().astype(np.int64)
     R = c.oracle_route()
     want = R.order[..., :16]
     mism = np.argwhere((got != want).any(-1))
@@ -253,7 +253,7 @@ def test_importance_order_prefix():
 def test_order_prefix_past_nb_is_minus_one():
     c = case(0)
     r = absh.route(c.ctx, c.qh, c.kh, 0.9, 2, order_depth=20)
-    got = r.order.cpu().numpy()
+    got = r.order.cpu().numpy().astype(np.int64)
     assert (got[..., 16:] == -1).all()
     assert all(sorted(row[:16].tolist()) == list(range(16)) for row in got.reshape(-1, 20))
 
@@ -343,7 +343,7 @@ def test_route_underflowed_probabilities():
             for i in range(nb):
                 c = int(want[0, h, i])
                 assert np.array_equal(kv[0, h, i, :c], np.sort(R.order[0, h, i, :c])), (beta, h, i)
-        assert np.array_equal(r.order.cpu().numpy(), R.order[..., :12])
+        assert np.array_equal(r.order.cpu().numpy().astype(np.int64), R.order[..., :12])
 
 
 
@@ -433,7 +433,7 @@ def attention_errors(c, r, tiles):
     oh = absh.sparse_attn(c.ctx, c.qh, c.kh, c.vt, r)
     o = absh.unpermute(c.ctx, oh).float().cpu().numpy()
     counts = r.counts.cpu().numpy().reshape(-1)
-    kv = r.kv_idx.cpu().numpy().reshape(counts.size, -1)
+    kv = r.kv_idx.cpu().numpy().astype(np.int64).reshape(counts.size, -1)
     errs = []
     for t in tiles:
         bh, i = divmod(int(t), w.nb)

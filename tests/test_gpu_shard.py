@@ -38,8 +38,8 @@ def test_one_rank_share_equals_full_run(schedule):
 
     assert torch.equal(part.counts, full.counts[:, h0:h1])
     n = full.counts[:, h0:h1].cpu().numpy()
-    kv_f = full.kv_idx[:, h0:h1].cpu().numpy()
-    kv_p = part.kv_idx.cpu().numpy()
+    kv_f = full.kv_idx[:, h0:h1].cpu().numpy().astype(np.int64)
+    kv_p = part.kv_idx.cpu().numpy().astype(np.int64)
     for i in range(w.nb):
         for hh in range(h1 - h0):
             assert np.array_equal(kv_p[0, hh, i, : n[0, hh, i]], kv_f[0, hh, i, : n[0, hh, i]])

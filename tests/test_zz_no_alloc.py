@@ -86,3 +86,27 @@ def test_static_route_rejects_large_shapes():
     assert b"maximum" in absh.lib().absh_last_error()
     torch.cuda.synchronize()
     assert (out.counts == -7).all()
+
+
+@pytest.mark.parametrize("grid,block,d,H,p,k,beta", [
+    ((16, 128, 128), 128, 64, 1, 0.9, 4, 0.1),    # nb = 2048, the router's maximum
+    ((5, 20, 40), 16, 128, 2, 0.8, 2, 0.0),       # nb = 250, blocks of 16
+    ((3, 9, 10), 128, 128, 2, 0.99, 1, 0.2),      # ragged tail of 14 tokens
+])
+def test_static_route_at_other_block_counts(grid, block, d, H, p, k, beta):
+    """The on-chip score path at every staged row width (up to nb = 2048, 128 KB of LDS per
+    workgroup), with and without slack fill, against absh_route bit for bit."""
+    T, Y, X = grid
+    N = T * Y * X
+    print(f"[no-alloc] grid {grid} block {block} d {d} H {H}", flush=True)
+    rng = np.random.default_rng(17)
+    ctx = absh.create(T, Y, X, block)
+    x = [torch.from_numpy((rng.standard_normal((1, N, H, d)) * 2).astype(np.float32)).to(DEV) for _ in range(2)]
+    qh, kh = (absh.permute(ctx, t) for t in x)
+    for schedule in ("xcd", "lpt"):
+        ref = absh.route(ctx, qh, kh, p, k, slack_frac=beta, schedule=schedule)
+        out = absh.alloc_routing(ctx, 1, H)
+        opts = absh.RouteOpts(p, k, beta, absh.SCHEDULES[schedule], 0)
+        assert route_static(ctx, qh, kh, opts, out) == 0, absh.lib().absh_last_error()
+        torch.cuda.synchronize()
+        same(ref, out, absh.lists_units(ctx, 1, H, schedule), schedule)
