@@ -33,7 +33,7 @@ EXPORTED = (
     "absh_perm", "absh_perm_copy", "absh_permute", "absh_unpermute", "absh_pool", "absh_block_scores",
     "absh_route_workspace_bytes", "absh_route", "absh_sparse_attn", "absh_lists_units", "absh_quantize_v",
     "absh_sparse_attn_v8", "absh_lists_bytes", "absh_lists_carve", "absh_workspace_bytes", "absh_attn_workgroups",
-    "absh_route_static",
+    "absh_route_static", "absh_permute_pool", "absh_route_means",
 )
 
 
@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
         "absh_sparse_attn": ([vp, vp, vp, vp, i, i, i, ctypes.POINTER(Lists), vp, vp], i),
         "absh_quantize_v": ([vp, vp, i, i, i, vp, vp, vp], i),
         "absh_sparse_attn_v8": ([vp, vp, vp, vp, vp, i, i, i, ctypes.POINTER(Lists), vp, vp], i),
+        "absh_permute_pool": ([vp, vp, i, vp, vp, i, i, i, i, vp], i),
+        "absh_route_means": ([vp, vp, vp, i, i, i, ctypes.POINTER(RouteOpts), ctypes.POINTER(Lists), vp, sz, vp], i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -186,6 +188,28 @@ def permute(ctx: Context, x, layout: int = ABSH_ROWS, out=None, stream=None):
     assert tuple(out.shape) == shape and out.dtype == dtype and out.is_contiguous(), "out does not fit the layout"
     _check(lib().absh_permute(ctx.handle, _ptr(x), xt, _ptr(out), B, H, d, layout, _stream(stream)))
     return out
+
+
+def permute_pool(ctx: Context, x, layout: int = ABSH_ROWS, out=None, means=None, stream=None):
+    """permute() in a rows layout and the block means of the rows it writes, in one pass
+    over x -> (xh, xbar float32 [B, H, nb, d])."""
+    import torch
+    B, N, H, d = x.shape
+    assert N == ctx.N and x.is_contiguous() and x.dtype in (torch.bfloat16, torch.float32)
+    if layout not in (ABSH_ROWS, ABSH_ROWS_F32):
+        raise ValueError("permute_pool writes rows: layout ABSH_ROWS or ABSH_ROWS_F32")
+    xt = ABSH_F32 if x.dtype == torch.float32 else ABSH_BF16
+    shape = (B, H, ctx.n_pad, d)
+    dtype = torch.float32 if layout == ABSH_ROWS_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty(shape, dtype=dtype, device=x.device)
+    if means is None:
+        means = torch.empty((B, H, ctx.nb, d), dtype=torch.float32, device=x.device)
+    assert tuple(out.shape) == shape and out.dtype == dtype and out.is_contiguous(), "out does not fit the layout"
+    assert tuple(means.shape) == (B, H, ctx.nb, d) and means.dtype == torch.float32 and means.is_contiguous()
+    _check(lib().absh_permute_pool(ctx.handle, _ptr(x), xt, _ptr(out), _ptr(means), B, H, d, layout,
+                                   _stream(stream)))
+    return out, means
 
 
 def vt_keys(block: int) -> int:
@@ -344,7 +368,7 @@ def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0,
           order_depth: int = 0, out: Optional[Routing] = None, workspace=None, stream=None,
           rank_policy="auto", strict_ranks: bool = False, k1: float = RLB_K1, k2: float = RLB_K2,
           n1: float = SASA_N1, n2: float = SASA_N2, router="topp", window: int = 0, anchor_stride: int = 0,
-          anchor_shift: int = 0, step: int = 0) -> Routing:
+          anchor_shift: int = 0, step: int = 0, qbar=None, kbar=None) -> Routing:
     """Stage-1 routing of Hilbert-order qh, kh [B, H, n_pad, d] (bf16 rows, or float32 rows from
     permute(..., ABSH_ROWS_F32)) -> Routing (device tensors).
 
@@ -353,22 +377,32 @@ def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0,
     "none", "sasa", "rlb+sasa" or "rlb"; strict_ranks keeps each XCD on its own rank.
     router "window-anchor" builds the structured lists (window, anchor_stride,
     anchor_shift, step; see include/absh.h) instead of Top-p; qh and kh then only
-    give the shape.
+    give the shape. qbar, kbar: block means already computed (permute_pool); then
+    qh and kh are not used (pass None) and the routing starts at the scores.
     """
     import torch
-    B, H, n_pad, d = qh.shape
-    if qh.dtype != kh.dtype or qh.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("qh and kh must both be bf16 or both float32")
-    if tuple(kh.shape) != tuple(qh.shape) or n_pad != ctx.n_pad or not (qh.is_contiguous() and kh.is_contiguous()):
-        raise ValueError(f"qh, kh must be contiguous [B, H, {ctx.n_pad}, d] (got {tuple(qh.shape)}, {tuple(kh.shape)})")
-    qk_type = ABSH_F32 if qh.dtype == torch.float32 else ABSH_BF16
+    if qbar is not None:
+        B, H, nb, d = qbar.shape
+        if kbar is None or tuple(kbar.shape) != tuple(qbar.shape) or nb != ctx.nb:
+            raise ValueError(f"qbar, kbar must be float32 [B, H, {ctx.nb}, d]")
+        if qbar.dtype != torch.float32 or kbar.dtype != torch.float32 or not (qbar.is_contiguous() and kbar.is_contiguous()):
+            raise ValueError("qbar and kbar must be contiguous float32")
+        device = qbar.device
+    else:
+        B, H, n_pad, d = qh.shape
+        if qh.dtype != kh.dtype or qh.dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("qh and kh must both be bf16 or both float32")
+        if tuple(kh.shape) != tuple(qh.shape) or n_pad != ctx.n_pad or not (qh.is_contiguous() and kh.is_contiguous()):
+            raise ValueError(f"qh, kh must be contiguous [B, H, {ctx.n_pad}, d] (got {tuple(qh.shape)}, {tuple(kh.shape)})")
+        qk_type = ABSH_F32 if qh.dtype == torch.float32 else ABSH_BF16
+        device = qh.device
     if out is None:
         out = alloc_routing(ctx, B, H, order_depth)
     else:
         out.check(ctx, B, H, order_depth)
     need = route_workspace_bytes(ctx, B, H, d)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=qh.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
     sched = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
     policy = RANK_POLICIES[rank_policy] if isinstance(rank_policy, str) else int(rank_policy)
     opts = RouteOpts(float(p), int(k_floor), float(slack_frac), sched, int(order_depth), policy,
@@ -376,8 +410,14 @@ def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0,
                      ROUTERS[router] if isinstance(router, str) else int(router), int(window), int(anchor_stride),
                      int(anchor_shift), int(step))
     lists = out.lists()
-    _check(lib().absh_route(ctx.handle, _ptr(qh), _ptr(kh), qk_type, B, H, d, ctypes.byref(opts), ctypes.byref(lists),
-                            _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    if qbar is not None:
+        _check(lib().absh_route_means(ctx.handle, _ptr(qbar), _ptr(kbar), B, H, d, ctypes.byref(opts),
+                                      ctypes.byref(lists), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                      _stream(stream)))
+    else:
+        _check(lib().absh_route(ctx.handle, _ptr(qh), _ptr(kh), qk_type, B, H, d, ctypes.byref(opts),
+                                ctypes.byref(lists), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                _stream(stream)))
     out.schedule = lists.schedule
     out.strict_ranks = lists.strict_ranks
     return out

@@ -40,6 +40,8 @@ hipError_t launch_hilbert_perm(const absh_ctx* c, int32_t* chunk_counts, int chu
 // layout: ABSH_ROWS (bf16 rows), ABSH_VT (bf16, block-transposed) or ABSH_ROWS_F32 (float rows)
 hipError_t launch_permute(const absh_ctx* c, const void* x, int x_is_f32, void* xh, int B, int H, int d,
                           int layout, hipStream_t s);
+hipError_t launch_permute_pool(const absh_ctx* c, const void* x, int x_is_f32, void* xh, float* xbar, int B, int H,
+                               int d, int layout, hipStream_t s);
 hipError_t launch_unpermute(const absh_ctx* c, const void* oh, void* o, int B, int H, int d, hipStream_t s);
 hipError_t launch_pool(const absh_ctx* c, const void* xh, int xh_is_f32, float* xbar, int B, int H, int d,
                        hipStream_t s);

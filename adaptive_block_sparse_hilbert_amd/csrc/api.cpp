@@ -257,6 +257,24 @@ absh_status absh_permute(absh_ctx* c, const void* x, absh_dtype xt, void* xh, in
   return ABSH_OK;
 }
 
+absh_status absh_permute_pool(absh_ctx* c, const void* x, absh_dtype xt, void* xh, float* xbar, int B, int H, int d,
+                              absh_layout layout, void* stream) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (absh_status st = check_shape(c, B, H, d)) return st;
+  if (!x || !xh || !xbar) return fail(ABSH_EINVAL, "x, xh or xbar is NULL");
+  if (xt != ABSH_BF16 && xt != ABSH_F32) return fail(ABSH_EINVAL, "unknown dtype %d", (int)xt);
+  if (layout != ABSH_ROWS && layout != ABSH_ROWS_F32)
+    return fail(ABSH_EINVAL, "absh_permute_pool writes rows: layout ABSH_ROWS or ABSH_ROWS_F32 (got %d)", (int)layout);
+  if (!aligned16(x) || !aligned16(xh) || !aligned16(xbar))
+    return fail(ABSH_EINVAL, "x, xh and xbar must be 16-byte aligned");
+  if (absh_status st = use_device(c)) return st;
+  ABSH_HIP(absh::launch_permute_pool(c, x, xt == ABSH_F32, xh, xbar, B, H, d, (int)layout,
+                                     reinterpret_cast<hipStream_t>(stream)),
+           "absh_permute_pool");
+  return ABSH_OK;
+}
+
 absh_status absh_unpermute(absh_ctx* c, const void* oh, void* o, int B, int H, int d, void* stream) {
   g_last_error.clear();
   if (absh_status st = check_ctx(c)) return st;
@@ -391,9 +409,11 @@ namespace {
 
 // The routing of absh_route; `scores`: the score matrix goes through the workspace
 // (score and select kernels), else the selection computes the scores on chip.
+// means_q / means_k: block means the caller already has (absh_route_means); then
+// qh and kh are not read and the pooling is skipped.
 absh_status route_impl(absh_ctx* c, const void* qh, const void* kh, absh_dtype qk_type, int B, int H, int d,
                        const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream,
-                       bool scores) {
+                       bool scores, const float* means_q = nullptr, const float* means_k = nullptr) {
   g_last_error.clear();
   if (absh_status st = check_ctx(c)) return st;
   if (absh_status st = check_shape(c, B, H, d)) return st;
@@ -401,6 +421,8 @@ absh_status route_impl(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
   if (opts->router != ABSH_ROUTER_TOPP && opts->router != ABSH_ROUTER_WINDOW_ANCHOR)
     return fail(ABSH_EINVAL, "unknown router %d", opts->router);
   const bool structured = opts->router == ABSH_ROUTER_WINDOW_ANCHOR;
+  const bool given = means_q != nullptr;
+  if (given && structured) return fail(ABSH_EINVAL, "routing from block means takes the Top-p router");
   if (structured) {
     if (opts->window < 0 || opts->anchor_stride < 0 || opts->anchor_shift < 0 || opts->step < 0)
       return fail(ABSH_EINVAL, "window, anchor_stride, anchor_shift and step must be >= 0");
@@ -409,9 +431,14 @@ absh_status route_impl(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
     if (opts->schedule == ABSH_SCHED_RANKS)
       return fail(ABSH_EUNSUPPORTED, "the window/anchor router has no importance order for ABSH_SCHED_RANKS");
   } else {
-    if (!qh || !kh) return fail(ABSH_EINVAL, "qh or kh is NULL");
-    if (qk_type != ABSH_BF16 && qk_type != ABSH_F32) return fail(ABSH_EINVAL, "unknown dtype %d", (int)qk_type);
-    if (!aligned16(qh) || !aligned16(kh)) return fail(ABSH_EINVAL, "qh and kh must be 16-byte aligned");
+    if (given) {
+      if (!means_k) return fail(ABSH_EINVAL, "kbar is NULL");
+      if (!aligned16(means_q) || !aligned16(means_k)) return fail(ABSH_EINVAL, "qbar and kbar must be 16-byte aligned");
+    } else {
+      if (!qh || !kh) return fail(ABSH_EINVAL, "qh or kh is NULL");
+      if (qk_type != ABSH_BF16 && qk_type != ABSH_F32) return fail(ABSH_EINVAL, "unknown dtype %d", (int)qk_type);
+      if (!aligned16(qh) || !aligned16(kh)) return fail(ABSH_EINVAL, "qh and kh must be 16-byte aligned");
+    }
     if (!(opts->p > 0.0 && opts->p <= 1.0)) return fail(ABSH_EINVAL, "p must lie in (0, 1] (got %g)", opts->p);
     if (opts->k_floor < 0) return fail(ABSH_EINVAL, "k_floor must be >= 0 (got %d)", opts->k_floor);
   }
@@ -456,8 +483,8 @@ absh_status route_impl(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = reinterpret_cast<char*>(ws);
-  float* qbar = reinterpret_cast<float*>(base + w.qbar);
-  float* kbar = reinterpret_cast<float*>(base + w.kbar);
+  float* qbar = given ? const_cast<float*>(means_q) : reinterpret_cast<float*>(base + w.qbar);
+  float* kbar = given ? const_cast<float*>(means_k) : reinterpret_cast<float*>(base + w.kbar);
   absh::RouteBuffers rb;
   rb.S = scores ? reinterpret_cast<float*>(base + w.S) : nullptr;
   rb.qbar = qbar;
@@ -494,8 +521,10 @@ absh_status route_impl(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
     ABSH_HIP(absh::launch_window_anchor(c, rb, tiles, window, opts->anchor_stride, offset, s),
              "absh_route: window/anchor lists");
   } else {
-    ABSH_HIP(absh::launch_pool(c, qh, qk_type == ABSH_F32, qbar, B, H, d, s), "absh_route: pool q");
-    ABSH_HIP(absh::launch_pool(c, kh, qk_type == ABSH_F32, kbar, B, H, d, s), "absh_route: pool k");
+    if (!given) {
+      ABSH_HIP(absh::launch_pool(c, qh, qk_type == ABSH_F32, qbar, B, H, d, s), "absh_route: pool q");
+      ABSH_HIP(absh::launch_pool(c, kh, qk_type == ABSH_F32, kbar, B, H, d, s), "absh_route: pool k");
+    }
     if (rb.S) ABSH_HIP(absh::launch_scores(c, qbar, kbar, const_cast<float*>(rb.S), B * H, d, s), "absh_route: scores");
     ABSH_HIP(absh::launch_select(c, rb, tiles, opts->p, opts->k_floor, opts->order_depth, 0, s),
              "absh_route: select");
@@ -533,6 +562,15 @@ extern "C" {
 absh_status absh_route(absh_ctx* c, const void* qh, const void* kh, absh_dtype qk_type, int B, int H, int d,
                        const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream) {
   return route_impl(c, qh, kh, qk_type, B, H, d, opts, out, ws, ws_bytes, stream, true);
+}
+
+absh_status absh_route_means(absh_ctx* c, const float* qbar, const float* kbar, int B, int H, int d,
+                             const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!qbar) {
+    g_last_error.clear();
+    return fail(ABSH_EINVAL, "qbar is NULL");
+  }
+  return route_impl(c, nullptr, nullptr, ABSH_F32, B, H, d, opts, out, ws, ws_bytes, stream, true, qbar, kbar);
 }
 
 absh_status absh_route_static(absh_ctx* c, const void* qh, const void* kh, absh_dtype qk_type, int B, int H, int d,

@@ -118,6 +118,75 @@ __global__ __launch_bounds__(kThreads) void gather_vt(const void* __restrict__ x
   }
 }
 
+// The rows gather fused with the block means of the rows it writes (the pooling
+// of the xllm-io review's Stage 1, done in the same pass over x): one workgroup
+// per (b, h, block j). Thread t moves the 16-byte output piece t % PIECES of rows
+// t / PIECES, + ROWS, ... of the block and sums those of its rows that hold tokens
+// in float64; the row groups' partial sums are then added in order and divided by
+// the block's token count in float64, rounded once to float32. That is the
+// order of the pooling kernel over the same rows, so the means are bit-identical
+// to pooling xh afterwards. TO: bf16_t (bf16 rows) or float (float32 rows).
+template <int D, typename TO>
+__global__ __launch_bounds__(kThreads) void gather_pool(const void* __restrict__ x, int is_f32, TO* __restrict__ xh,
+                                                        float* __restrict__ xbar, const int32_t* __restrict__ perm,
+                                                        int N, int n_pad, int nb, int blk, int H) {
+  constexpr int EPP = 16 / (int)sizeof(TO);  // channels per 16-byte output piece
+  constexpr int PIECES = D / EPP;
+  constexpr int ROWS = kThreads / PIECES;
+  __shared__ double part[ROWS][D + 1];
+  const int j = blockIdx.x % nb;
+  const uint64_t bh = blockIdx.x / nb;
+  const int h = (int)(bh % H);
+  const uint64_t b = bh / H;
+  const int piece = threadIdx.x % PIECES;
+  const int r0 = threadIdx.x / PIECES;
+  const int n = min(blk, N - j * blk);  // rows of the block that hold tokens
+  double acc[EPP];
+#pragma unroll
+  for (int e = 0; e < EPP; ++e) acc[e] = 0.0;
+  for (int r = r0; r < blk; r += ROWS) {
+    const int row = j * blk + r;  // Hilbert position
+    const size_t src = ((b * N + (r < n ? perm[row] : 0)) * H + h) * D + (size_t)piece * EPP;
+    TO* dst = xh + (bh * n_pad + row) * D + (size_t)piece * EPP;
+    if constexpr (sizeof(TO) == 2) {
+      Pack8 v = {{0u, 0u, 0u, 0u}};
+      if (r < n) {
+        v = load8(x, src, is_f32);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += (double)bf16_to_f32((bf16_t)(v.w[e] & 0xFFFFu));
+          acc[2 * e + 1] += (double)bf16_to_f32((bf16_t)(v.w[e] >> 16));
+        }
+      }
+      *reinterpret_cast<Pack8*>(dst) = v;
+    } else {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r < n) {
+        if (is_f32) {
+          v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + src);
+        } else {
+          const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(x) + src);
+          v = make_float4(bf16_to_f32((bf16_t)(w.x & 0xFFFFu)), bf16_to_f32((bf16_t)(w.x >> 16)),
+                          bf16_to_f32((bf16_t)(w.y & 0xFFFFu)), bf16_to_f32((bf16_t)(w.y >> 16)));
+        }
+        acc[0] += (double)v.x;
+        acc[1] += (double)v.y;
+        acc[2] += (double)v.z;
+        acc[3] += (double)v.w;
+      }
+      *reinterpret_cast<float4*>(dst) = v;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPP; ++e) part[r0][piece * EPP + e] = acc[e];
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += kThreads) {
+    double sum = 0.0;
+    for (int r = 0; r < ROWS; ++r) sum += part[r][c];
+    xbar[(bh * nb + j) * D + c] = __double2float_rn(sum / (double)n);
+  }
+}
+
 // o[b, n, h, :] = oh[b, h, inv[n], :]: one thread per 8 output elements.
 __global__ __launch_bounds__(kThreads) void scatter_rows(const bf16_t* __restrict__ oh, bf16_t* __restrict__ o,
                                                          const int32_t* __restrict__ inv, int N, int n_pad, int H,
@@ -172,6 +241,28 @@ hipError_t launch_permute(const absh_ctx* c, const void* x, int x_is_f32, void* 
   ABSH_VT_CASE(128, 128)
 #undef ABSH_VT_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_permute_pool(const absh_ctx* c, const void* x, int x_is_f32, void* xh, float* xbar, int B, int H,
+                               int d, int layout, hipStream_t s) {
+  const unsigned grid = (unsigned)((uint64_t)B * H * c->nb);
+  const bool f32 = layout == ABSH_ROWS_F32;
+  if (layout != ABSH_ROWS && !f32) return hipErrorInvalidValue;
+#define ABSH_GP(DD, TT)                                                                                       \
+  gather_pool<DD, TT><<<grid, kThreads, 0, s>>>(x, x_is_f32, reinterpret_cast<TT*>(xh), xbar, c->perm, c->N, \
+                                                c->n_pad, c->nb, c->block, H)
+  if (d == 64 && !f32)
+    ABSH_GP(64, bf16_t);
+  else if (d == 128 && !f32)
+    ABSH_GP(128, bf16_t);
+  else if (d == 64)
+    ABSH_GP(64, float);
+  else if (d == 128)
+    ABSH_GP(128, float);
+  else
+    return hipErrorInvalidValue;
+#undef ABSH_GP
+  return hipGetLastError();
 }
 
 hipError_t launch_unpermute(const absh_ctx* c, const void* oh, void* o, int B, int H, int d, hipStream_t s) {

@@ -138,6 +138,9 @@ def parse():
     ap.add_argument("--anchor-stride", type=int, default=32, help="window-anchor router: anchor spacing")
     ap.add_argument("--anchor-shift", type=int, default=5, help="window-anchor router: offset advance per step")
     ap.add_argument("--step", type=int, default=0, help="window-anchor router: diffusion step")
+    ap.add_argument("--pool", default="fused", choices=("fused", "separate"),
+                    help="block means of q and k: in the permute's pass (absh_permute_pool, then "
+                         "absh_route_means), or pooled inside absh_route")
     ap.add_argument("--values", default="bf16", choices=("bf16", "fp8"),
                     help="fp8: quantize V to E4M3 and run the value product on fp8 MFMAs")
     ap.add_argument("--dense-reps", type=int, default=3)
@@ -214,6 +217,10 @@ def measure(args, w, p, schedule, route_f32):
         k32 = torch.from_numpy(data["k32"]).to(dev)
         qr = torch.empty((B, H, ctx.n_pad, d), dtype=torch.float32, device=dev)
         kr = torch.empty_like(qr)
+    # block means of q and k from the permute's own pass (Top-p router), else pooled by the router
+    fused_pool = args.pool == "fused" and args.router == "topp"
+    qbar = torch.empty((B, H, ctx.nb, d), dtype=torch.float32, device=dev)
+    kbar = torch.empty_like(qbar)
 
     stages = ("permute", "quantize", "route", "attn", "unpermute")
 
@@ -226,9 +233,16 @@ def measure(args, w, p, schedule, route_f32):
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        absh.permute(ctx, q, out=qh)
-        absh.permute(ctx, k, out=kh)
-        if route_f32:
+        if fused_pool and not route_f32:
+            absh.permute_pool(ctx, q, out=qh, means=qbar)
+            absh.permute_pool(ctx, k, out=kh, means=kbar)
+        else:
+            absh.permute(ctx, q, out=qh)
+            absh.permute(ctx, k, out=kh)
+        if route_f32 and fused_pool:
+            absh.permute_pool(ctx, q32, layout=absh.ABSH_ROWS_F32, out=qr, means=qbar)
+            absh.permute_pool(ctx, k32, layout=absh.ABSH_ROWS_F32, out=kr, means=kbar)
+        elif route_f32:
             absh.permute(ctx, q32, layout=absh.ABSH_ROWS_F32, out=qr)
             absh.permute(ctx, k32, layout=absh.ABSH_ROWS_F32, out=kr)
         if fp8:
@@ -246,7 +260,7 @@ def measure(args, w, p, schedule, route_f32):
                    rank_policy=args.rank_policy, strict_ranks=args.strict_ranks, router=args.router,
                    window=args.window, anchor_stride=args.anchor_stride, anchor_shift=args.anchor_shift,
                    step=args.step,
-                   workspace=ws)
+                   workspace=ws, qbar=qbar if fused_pool else None, kbar=kbar if fused_pool else None)
         if ev is not None:
             ev[3].record(stream)
         attention(routing)
@@ -371,6 +385,7 @@ def measure(args, w, p, schedule, route_f32):
             "tokens": w.N, "block": w.block, "blocks": ctx.nb, "p": p, "k_floor": w.k_floor,
             "slack_frac": w.slack_frac, "schedule": schedule, "router": args.router, "values": args.values,
             "route_inputs": "f32" if route_f32 else "bf16",
+            "pooling": "in the permute pass" if fused_pool else "in the router",
             **({"window": args.window, "anchor_stride": args.anchor_stride, "anchor_shift": args.anchor_shift,
                 "step": args.step} if args.router == "window-anchor" else {}),
         },

@@ -237,6 +237,17 @@ absh_status absh_unpermute(absh_ctx* ctx, const void* oh, void* o, int B, int H,
  * count in float64, rounded once to float32. xbar: float32 [B, H, nb, d]. */
 absh_status absh_pool(absh_ctx* ctx, const void* xh, float* xbar, int B, int H, int d, void* stream);
 
+/* absh_permute and absh_pool in one pass over x (the Hilbert reordering and the
+ * block pooling of the xllm-io review's Stage 1): xh exactly as absh_permute
+ * writes it in a rows layout (ABSH_ROWS: bf16 rows; ABSH_ROWS_F32: float32 rows),
+ * and xbar[b, h, j, :] = the block means of the rows written to xh, bit-identical
+ * to absh_pool over them (float64 sums in the same order, one float64 division by
+ * the block's token count, rounded once to float32). Routing from these means
+ * (absh_route_means) then reads no row a second time. xbar: float32 [B, H, nb, d];
+ * x, xh and xbar 16-byte aligned. ABSH_VT is refused with ABSH_EINVAL. */
+absh_status absh_permute_pool(absh_ctx* ctx, const void* x, absh_dtype xt, void* xh, float* xbar, int B, int H,
+                              int d, absh_layout layout, void* stream);
+
 /* Block scores s[b, h, i, j] = qbar_i . kbar_j / sqrt(d), products and sums in
  * float64, rounded once to float32 (the routing-stage similarity of the xllm-io
  * review's Stage 1). qbar, kbar: float32 [B, H, nb, d]; s: float32 [B, H, nb, nb]. */
@@ -292,6 +303,15 @@ size_t absh_workspace_bytes(const absh_ctx* ctx, int B, int H, int d);
  * contents are scratch. No host synchronisation. */
 absh_status absh_route(absh_ctx* ctx, const void* qh, const void* kh, absh_dtype qk_type, int B, int H, int d,
                        const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream);
+
+/* absh_route from block means the caller already holds (absh_permute_pool, or
+ * absh_pool of qh and kh; xllm-io review of FVAttn, Stage 1): qbar, kbar float32
+ * [B, H, nb, d], 16-byte aligned. Everything after the pooling is absh_route's,
+ * with the same options, workspace size and outputs, so the lists are
+ * bit-identical to absh_route's on the rows the means were taken from. Top-p
+ * router only (the window/anchor router reads no means: ABSH_EINVAL). */
+absh_status absh_route_means(absh_ctx* ctx, const float* qbar, const float* kbar, int B, int H, int d,
+                             const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream);
 
 /* absh_route for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same routing,
