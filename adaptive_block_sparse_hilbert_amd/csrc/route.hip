@@ -283,16 +283,41 @@ __device__ __forceinline__ void select_row(const float* srow, int row, int nb, d
   // has the same threshold: every key above it and the first ties at it)
   uint32_t tau_p = 0;
   bool tau_p_set = false;
+  // Both threshold searches below fix the bits of the answer from the top. After
+  // a bit is fixed the answer lies in [tau, tau + 2^bit); the searches count the
+  // keys at or above each candidate on the way, so they know how many keys that
+  // interval holds, and when it holds one, that key is the answer (the property
+  // holds at tau, hence at the one key above it in the interval, and fails at the
+  // interval's end): the remaining steps would only spell it out bit by bit.
+  int n_keys = 0;  // keys >= 1 (every key of a block with a non-zero probability)
+#pragma unroll
+  for (int t = 0; t < J; ++t) n_keys += popc64(__ballot(key[t] != 0u));
+  // smallest key >= lo over the wave
+  auto min_key_from = [&](uint32_t lo) __attribute__((always_inline)) -> uint32_t {
+    uint64_t best = 0;
+#pragma unroll
+    for (int t = 0; t < J; ++t) {
+      const uint64_t inv = (uint64_t)(~key[t]);
+      best = key[t] >= lo && inv > best ? inv : best;
+    }
+    return ~(uint32_t)wave_max_u64(best);
+  };
   if (!RS) {
     int c = nb;
     if (p < 1.0) {
       // each step: is the mass of {key >= cand} at least p?
       uint32_t tau = 0;
+      int n_lo = n_keys, n_hi = 0;  // keys >= tau (tau >= 1 once set), keys >= the interval's end
       for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = tau | (1u << bit);
         float f32 = 0.f;
+        int n_c = 0;
 #pragma unroll
-        for (int t = 0; t < J; ++t) f32 += key[t] >= cand ? P32[t] : 0.f;
+        for (int t = 0; t < J; ++t) {
+          const bool ge = key[t] >= cand;
+          f32 += ge ? P32[t] : 0.f;
+          n_c += popc64(__ballot(ge));
+        }
         const double m32 = (double)wave_sum_f32(f32);
         bool take = m32 >= p;
         if (fabs(m32 - p) <= kBand) {
@@ -302,7 +327,16 @@ __device__ __forceinline__ void select_row(const float* srow, int row, int nb, d
           for (int t = 0; t < J; ++t) f += key[t] >= cand ? P[t] : 0.0;
           take = wave_sum(f) >= p;
         }
-        if (take) tau = cand;
+        if (take) {
+          tau = cand;
+          n_lo = n_c;
+        } else {
+          n_hi = n_c;
+        }
+        if (n_lo - n_hi == 1 && tau != 0u) {
+          tau = min_key_from(tau);
+          break;
+        }
       }
       int n_above = 0, n_at = 0;
       float f32 = 0.f;
@@ -375,12 +409,22 @@ __device__ __forceinline__ void select_row(const float* srow, int row, int nb, d
     }
   } else {
     uint32_t tau = tau_p_set ? tau_p : 0u;
+    int n_lo = n_keys, n_hi = 0;
     for (int bit = 31; bit >= 0 && !tau_p_set; --bit) {
       const uint32_t cand = tau | (1u << bit);
       int cnt = 0;
 #pragma unroll
       for (int t = 0; t < J; ++t) cnt += popc64(__ballot(valid[t] && key[t] >= cand));
-      if (cnt >= want) tau = cand;
+      if (cnt >= want) {
+        tau = cand;
+        n_lo = cnt;
+      } else {
+        n_hi = cnt;
+      }
+      if (n_lo - n_hi == 1 && tau != 0u) {
+        tau = min_key_from(tau);
+        break;
+      }
     }
     int n_above = 0;
 #pragma unroll
