@@ -834,15 +834,22 @@ __global__ __launch_bounds__(256) void group_merge_kernel(const int32_t* __restr
   for (int m = 0; m < M; ++m) bits[w][m][lane] = 0u;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  // eight list entries per lane in flight at a time (the loads do not wait on each other)
+  constexpr int kInFlight = 8;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const int qb = q * M + m;
     if (qb >= nb) continue;
     const int64_t t = (int64_t)bh * nb + qb;
     const int c = counts[t];
-    for (int i = lane; i < c; i += 64) {
-      const int j = kv_idx[t * nb + i];
-      atomicOr(&bits[w][m][j >> 5], 1u << (j & 31));
+    const int16_t* row = kv_idx + t * nb;
+    for (int i0 = lane; i0 < c; i0 += 64 * kInFlight) {
+      int j[kInFlight];
+#pragma unroll
+      for (int a = 0; a < kInFlight; ++a) j[a] = i0 + 64 * a < c ? row[i0 + 64 * a] : -1;
+#pragma unroll
+      for (int a = 0; a < kInFlight; ++a)
+        if (j[a] >= 0) atomicOr(&bits[w][m][j[a] >> 5], 1u << (j[a] & 31));
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -901,6 +908,7 @@ __global__ __launch_bounds__(1024) void segments_kernel(const int32_t* __restric
     return;
   }
   int64_t mine = 0;
+#pragma unroll 8
   for (int u = threadIdx.x; u < units; u += 1024) mine += (int64_t)cost[u] + kUnitOverhead;
   int64_t total;
   block_exclusive_scan<int64_t>(mine, buf, total);
@@ -912,9 +920,12 @@ __global__ __launch_bounds__(1024) void segments_kernel(const int32_t* __restric
   // bound x = the smallest u whose preceding cost reaches target x: the unit v
   // with before(v) < target <= before(v) + cost(v) ends just before it
   int64_t seen = 0;
+  // each chunk's costs are loaded while the previous chunk is scanned
+  int64_t c_next = (int)threadIdx.x < units ? (int64_t)cost[threadIdx.x] + kUnitOverhead : 0;
   for (int u0 = 0; u0 < units; u0 += 1024) {
     const int u = u0 + threadIdx.x;
-    const int64_t c = u < units ? (int64_t)cost[u] + kUnitOverhead : 0;
+    const int64_t c = c_next;
+    c_next = u + 1024 < units ? (int64_t)cost[u + 1024] + kUnitOverhead : 0;
     int64_t chunk;
     const int64_t before = seen + block_exclusive_scan<int64_t>(c, buf, chunk);
     if (u < units)
@@ -930,15 +941,19 @@ __global__ __launch_bounds__(1024) void segments_kernel(const int32_t* __restric
 // reading of the review's RLB as a longest-processing-time-first queue, with the
 // XCDs' contiguous runs as in the "xcd" schedule): run x = blockIdx.x holds the
 // units sched[x] .. sched[x + 1] - 1, ordered by union length (cost) descending,
-// ties by unit index. A stable counting sort over the run in chunks of 1024: each
-// unit's place is the start of its cost's bin plus the units of equal cost before
-// it in its chunk.
+// ties by unit index. A stable counting sort over the run: the bins' starts from a
+// histogram and its scan, then one wave walks the run 64 units at a time; a unit's
+// place is its bin's running start plus the units of equal cost before it among
+// the 64 (lanes of equal cost found by comparing the costs bit by bit across the
+// wave), and the lowest lane of each such group advances the bin's start.
+constexpr int kLptChunk = 4096;
+
 __global__ __launch_bounds__(1024) void unit_lpt_kernel(const int32_t* __restrict__ cost, int units, int nb,
                                                         const int32_t* __restrict__ sched,
                                                         int32_t* __restrict__ unit_queue) {
   __shared__ int32_t start[kMaxBins];
-  __shared__ int32_t chunk_cost[1024];
   __shared__ int64_t buf[1024];
+  __shared__ int32_t chunk[kLptChunk];
   const int lo = sched[blockIdx.x], hi = sched[blockIdx.x + 1];
   for (int b = threadIdx.x; b <= nb; b += 1024) start[b] = 0;
   __syncthreads();
@@ -956,18 +971,33 @@ __global__ __launch_bounds__(1024) void unit_lpt_kernel(const int32_t* __restric
     carry += tot;
     __syncthreads();
   }
-  for (int c0 = lo; c0 < hi; c0 += 1024) {
-    const int u = c0 + (int)threadIdx.x;
-    const int mine = u < hi ? cost[u] : -1;
-    chunk_cost[threadIdx.x] = mine;
+  // the run's costs are staged in LDS a chunk at a time, so the walk issues no loads
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int bits = 32 - __clz(nb);  // costs lie in 0 .. nb
+  for (int k0 = lo; k0 < hi; k0 += kLptChunk) {
+    const int k1 = min(hi, k0 + kLptChunk);
+    for (int u = k0 + (int)threadIdx.x; u < k1; u += 1024) chunk[u - k0] = cost[u];
     __syncthreads();
-    if (u < hi) {
-      int r = 0;
-      for (int v = 0; v < (int)threadIdx.x; ++v) r += chunk_cost[v] == mine;
-      unit_queue[lo + start[mine] + r] = u;
+    if (threadIdx.x < 64) {
+      for (int c0 = k0; c0 < k1; c0 += 64) {
+        const int u = c0 + lane;
+        const bool in = u < k1;
+        const int mine = in ? chunk[u - k0] : 0;
+        uint64_t eq = __ballot(in);
+        for (int b = 0; b < bits; ++b) {
+          const bool one = (mine >> b) & 1;
+          const uint64_t m = __ballot(in && one);
+          eq &= one ? m : ~m;
+        }
+        int pos = 0;
+        if (in) pos = start[mine] + __popcll(eq & below);
+        if (in) unit_queue[lo + pos] = u;
+        __builtin_amdgcn_wave_barrier();
+        if (in && (eq & below) == 0) start[mine] += __popcll(eq);
+        __builtin_amdgcn_wave_barrier();
+      }
     }
-    __syncthreads();
-    if (u < hi) atomicAdd(&start[mine], 1);
     __syncthreads();
   }
 }
