@@ -33,7 +33,7 @@ EXPORTED = (
     "absh_perm", "absh_perm_copy", "absh_permute", "absh_unpermute", "absh_pool", "absh_block_scores",
     "absh_route_workspace_bytes", "absh_route", "absh_sparse_attn", "absh_lists_units", "absh_quantize_v",
     "absh_sparse_attn_v8", "absh_lists_bytes", "absh_lists_carve", "absh_workspace_bytes", "absh_attn_workgroups",
-    "absh_route_static", "absh_permute_pool", "absh_route_means",
+    "absh_route_static", "absh_permute_pool", "absh_route_means", "absh_forward", "absh_forward_workspace_bytes",
 )
 
 
@@ -101,6 +101,9 @@ def lib() -> ctypes.CDLL:
         "absh_sparse_attn_v8": ([vp, vp, vp, vp, vp, i, i, i, ctypes.POINTER(Lists), vp, vp], i),
         "absh_permute_pool": ([vp, vp, i, vp, vp, i, i, i, i, vp], i),
         "absh_route_means": ([vp, vp, vp, i, i, i, ctypes.POINTER(RouteOpts), ctypes.POINTER(Lists), vp, sz, vp], i),
+        "absh_forward": ([vp, vp, vp, vp, i, vp, i, i, i, ctypes.POINTER(RouteOpts), ctypes.POINTER(Lists), vp, sz,
+                          vp], i),
+        "absh_forward_workspace_bytes": ([vp, i, i, i], sz),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -421,6 +424,45 @@ def route(ctx: Context, qh, kh, p: float, k_floor: int, slack_frac: float = 0.0,
     out.schedule = lists.schedule
     out.strict_ranks = lists.strict_ranks
     return out
+
+
+def forward_workspace_bytes(ctx: Context, B: int, H: int, d: int) -> int:
+    return int(lib().absh_forward_workspace_bytes(ctx.handle, B, H, d))
+
+
+def forward(ctx: Context, q, k, v, p: float, k_floor: int, slack_frac: float = 0.0, schedule="xcd",
+            order_depth: int = 0, routing: Optional[Routing] = None, out=None, workspace=None, stream=None):
+    """The whole path in one library call: grid-order q, k, v [B, N, H, d] (bf16 or float32)
+    -> (o [B, N, H, d] bf16, Routing)."""
+    import torch
+    B, N, H, d = q.shape
+    if N != ctx.N or tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape):
+        raise ValueError(f"q, k, v must be [B, {ctx.N}, H, d] of one shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must all be bf16 or all float32")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    xt = ABSH_F32 if q.dtype == torch.float32 else ABSH_BF16
+    if routing is None:
+        routing = alloc_routing(ctx, B, H, order_depth)
+    else:
+        routing.check(ctx, B, H, order_depth)
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=q.device)
+    assert tuple(out.shape) == (B, N, H, d) and out.dtype == torch.bfloat16 and out.is_contiguous()
+    need = forward_workspace_bytes(ctx, B, H, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    sched = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
+    opts = RouteOpts(float(p), int(k_floor), float(slack_frac), sched, int(order_depth), RANK_POLICIES["auto"], 0,
+                     RLB_K1, RLB_K2, SASA_N1, SASA_N2, ROUTERS["topp"], 0, 0, 0, 0)
+    lists = routing.lists()
+    _check(lib().absh_forward(ctx.handle, _ptr(q), _ptr(k), _ptr(v), xt, _ptr(out), B, H, d, ctypes.byref(opts),
+                              ctypes.byref(lists), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                              _stream(stream)))
+    routing.schedule = lists.schedule
+    routing.strict_ranks = lists.strict_ranks
+    return out, routing
 
 
 def sparse_attn(ctx: Context, qh, kh, vt, routing: Optional[Routing] = None, out=None, stream=None):

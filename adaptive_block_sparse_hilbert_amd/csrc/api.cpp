@@ -682,3 +682,69 @@ absh_status absh_sparse_attn_v8(absh_ctx* c, const void* qh, const void* kh, con
 }
 
 }  // extern "C"
+
+namespace {
+
+// absh_forward's workspace: the Hilbert-order rows of q, k and o, V^T, then
+// absh_route's workspace (whose block-mean slots take the means of q and k).
+struct FwdLayout {
+  size_t qh, kh, vt, oh, route, total;
+};
+
+FwdLayout fwd_layout(const absh_ctx* c, int B, int H, int d) {
+  FwdLayout f{};
+  const size_t rows = (size_t)B * H * c->n_pad * d * 2;
+  const size_t vt = (size_t)B * H * c->nb * d * absh::vt_keys(c->block) * 2;
+  size_t off = 0;
+  f.qh = off; off = align_up(off + rows);
+  f.kh = off; off = align_up(off + rows);
+  f.vt = off; off = align_up(off + vt);
+  f.oh = off; off = align_up(off + rows);
+  f.route = off; off = align_up(off + ws_layout(c, B, H, d).total);
+  f.total = off;
+  return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t absh_forward_workspace_bytes(const absh_ctx* c, int B, int H, int d) {
+  if (!c || B < 1 || H < 1 || d < 1) return 0;
+  return fwd_layout(c, B, H, d).total;
+}
+
+absh_status absh_forward(absh_ctx* c, const void* q, const void* k, const void* v, absh_dtype xt, void* o, int B,
+                         int H, int d, const absh_route_opts* opts, absh_lists* lists, void* ws, size_t ws_bytes,
+                         void* stream) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (absh_status st = check_shape(c, B, H, d)) return st;
+  if (!q || !k || !v || !o) return fail(ABSH_EINVAL, "q, k, v or o is NULL");
+  if (!opts || !lists) return fail(ABSH_EINVAL, "opts or lists is NULL");
+  if (opts->router != ABSH_ROUTER_TOPP) return fail(ABSH_EINVAL, "absh_forward takes the Top-p router");
+  const FwdLayout f = fwd_layout(c, B, H, d);
+  if (!ws) return fail(ABSH_EWORKSPACE, "workspace is NULL (%zu bytes needed)", f.total);
+  if (ws_bytes < f.total) return fail(ABSH_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, f.total);
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+    return fail(ABSH_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+  char* base = reinterpret_cast<char*>(ws);
+  void* qh = base + f.qh;
+  void* kh = base + f.kh;
+  void* vt = base + f.vt;
+  void* oh = base + f.oh;
+  char* rws = base + f.route;
+  const WsLayout w = ws_layout(c, B, H, d);
+  float* qbar = reinterpret_cast<float*>(rws + w.qbar);
+  float* kbar = reinterpret_cast<float*>(rws + w.kbar);
+  if (absh_status st = absh_permute_pool(c, q, xt, qh, qbar, B, H, d, ABSH_ROWS, stream)) return st;
+  if (absh_status st = absh_permute_pool(c, k, xt, kh, kbar, B, H, d, ABSH_ROWS, stream)) return st;
+  if (absh_status st = absh_permute(c, v, xt, vt, B, H, d, ABSH_VT, stream)) return st;
+  if (absh_status st = route_impl(c, nullptr, nullptr, ABSH_BF16, B, H, d, opts, lists, rws, ws_bytes - f.route,
+                                  stream, true, qbar, kbar))
+    return st;
+  if (absh_status st = absh_sparse_attn(c, qh, kh, vt, B, H, d, lists, oh, stream)) return st;
+  return absh_unpermute(c, oh, o, B, H, d, stream);
+}
+
+}  // extern "C"

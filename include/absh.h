@@ -313,6 +313,23 @@ absh_status absh_route(absh_ctx* ctx, const void* qh, const void* kh, absh_dtype
 absh_status absh_route_means(absh_ctx* ctx, const float* qbar, const float* kbar, int B, int H, int d,
                              const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream);
 
+/* The whole path in one call (the pages' drop-in use of the method: grid-order
+ * q, k, v in, grid-order attention output out): absh_permute_pool of q and k,
+ * absh_permute of v into ABSH_VT, absh_route_means (Top-p router, opts as for
+ * absh_route, lists written as absh_route writes them), absh_sparse_attn over
+ * those lists, absh_unpermute into o. q, k, v: [B, N, H, d] bf16 or float32 (xt;
+ * float32 is rounded to bf16, and routing uses the means of the rounded rows);
+ * o: [B, N, H, d] bf16. The Hilbert-order tensors and the routing scratch live in
+ * ws (absh_forward_workspace_bytes(), 256-byte aligned, contents scratch). The
+ * same kernels in the same order as the separate calls, so o is bit-identical to
+ * theirs. */
+absh_status absh_forward(absh_ctx* ctx, const void* q, const void* k, const void* v, absh_dtype xt, void* o, int B,
+                         int H, int d, const absh_route_opts* opts, absh_lists* lists, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Device workspace absh_forward needs for this shape, in bytes (0 on a bad argument). */
+size_t absh_forward_workspace_bytes(const absh_ctx* ctx, int B, int H, int d);
+
 /* absh_route for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same routing,
  * same arguments and bit-identical outputs, with the block scores computed on chip

@@ -146,6 +146,9 @@ def test_null_context_everywhere(L):
                               ctypes.c_size_t(1 << 20), None) == EINVAL
     assert b"qbar is NULL" in L.absh_last_error()
     assert L.absh_permute_pool(None, vp(16), 0, vp(16), vp(16), 1, 1, 64, 0, None) == EINVAL
+    assert L.absh_forward(None, vp(16), vp(16), vp(16), 0, vp(16), 1, 1, 64, ctypes.byref(opts), ctypes.byref(lists),
+                          vp(256), ctypes.c_size_t(1 << 20), None) == EINVAL
+    assert L.absh_forward_workspace_bytes(None, 1, 1, 64) == 0
     assert L.absh_sparse_attn(None, vp(16), vp(16), vp(16), 1, 1, 64, None, vp(16), None) == EINVAL
     assert b"ctx is NULL" in L.absh_last_error()
     assert L.absh_quantize_v(None, vp(16), 1, 1, 64, vp(16), vp(16), None) == EINVAL

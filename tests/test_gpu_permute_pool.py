@@ -118,3 +118,28 @@ def test_route_means_rejects_the_structured_router():
     bar = torch.zeros((w.B, w.H, ctx.nb, w.d), dtype=torch.float32, device=DEV)
     with pytest.raises(absh.AbshError, match="Top-p router"):
         absh.route(ctx, None, None, 0.9, 1, schedule="xcd", router="window-anchor", window=2, qbar=bar, kbar=bar)
+
+
+@pytest.mark.parametrize("index,schedule", [(1, "xcd"), (3, "lpt"), (0, "xcd")])
+def test_forward_equals_the_separate_calls(index, schedule):
+    """absh_forward (permute with pooling, route from the means, sparse attention,
+    unpermute in one call) against the same calls made one by one: lists and output
+    bit for bit."""
+    w = W.workload(index)
+    print(f"[forward] {w.name} {schedule}", flush=True)
+    d = W.generate(w, want_fp32=index == 0)
+    ctx = absh.create(w.T, w.Y, w.X, w.block)
+    if index == 0:  # float32 inputs, rounded to bf16 by the permutes
+        q, k, v = (torch.from_numpy(d[n]).to(DEV) for n in ("q32", "k32", "v32"))
+    else:
+        q, k, v = (bf16_dev(d[n]) for n in ("q16", "k16", "v16"))
+    o, got = absh.forward(ctx, q, k, v, w.p, w.k_floor, slack_frac=w.slack_frac, schedule=schedule)
+    qh, qbar = absh.permute_pool(ctx, q)
+    kh, kbar = absh.permute_pool(ctx, k)
+    vt = absh.permute(ctx, v, layout=absh.ABSH_VT)
+    ref = absh.route(ctx, None, None, w.p, w.k_floor, slack_frac=w.slack_frac, schedule=schedule,
+                     qbar=qbar, kbar=kbar)
+    o_ref = absh.unpermute(ctx, absh.sparse_attn(ctx, qh, kh, vt, ref))
+    torch.cuda.synchronize()
+    same_routing(ref, got, ctx, w.B, w.H, schedule)
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
