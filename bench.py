@@ -354,6 +354,10 @@ def measure(args, w, p, schedule, route_f32):
         "unit": "TFLOP/s",
         "frac": round(attn_tflops / peak, 4),
         "traffic": traffic,
+        # HBM bytes the launch must move at least: q, k, v read once (v in 8 bits with --values fp8), o written once
+        "traffic_minimum": float(B * H * w.N * d * (2 + 2 + (1 if fp8 else 2) + 2)),
+        "traffic_over_minimum": None if traffic is None else round(
+            traffic / float(B * H * w.N * d * (2 + 2 + (1 if fp8 else 2) + 2)), 2),
         "peak_at_measured_clock": None if peak_clk is None else round(peak_clk, 1),
         "frac_at_measured_clock": None if peak_clk is None else round(attn_tflops / peak_clk, 4),
     }
