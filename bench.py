@@ -291,8 +291,9 @@ def measure(args, w, p, schedule, route_f32):
     ms_per_step = wall * 1e3 / args.steps
     stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events])) for i, s in enumerate(stages)}
     stage_min = {s: float(np.min([e[i].elapsed_time(e[i + 1]) for e in events])) for i, s in enumerate(stages)}
+    stage_med = {s: float(np.median([e[i].elapsed_time(e[i + 1]) for e in events])) for i, s in enumerate(stages)}
     if not fp8:  # no quantization stage with bf16 values
-        del stage_ms["quantize"], stage_min["quantize"]
+        del stage_ms["quantize"], stage_min["quantize"], stage_med["quantize"]
 
     # retained work of this routing (identical every step: the path is deterministic)
     counts = routing.counts.cpu().numpy().reshape(-1)
@@ -401,6 +402,7 @@ def measure(args, w, p, schedule, route_f32):
         "dense_tflop": round(n_all / 1e12, 4),
         "stage_ms": {s: round(x, 4) for s, x in stage_ms.items()},
         "stage_ms_min": {s: round(x, 4) for s, x in stage_min.items()},
+        "stage_ms_median": {s: round(x, 4) for s, x in stage_med.items()},
         "attn_effective_tflops": round(attn_tflops, 2),
         "route_share_of_attn": round(stage_ms["route"] / stage_ms["attn"], 4),
         "dense_attn_ms": None if dense_ms is None else round(dense_ms, 3),
