@@ -143,3 +143,19 @@ def test_forward_equals_the_separate_calls(index, schedule):
     torch.cuda.synchronize()
     same_routing(ref, got, ctx, w.B, w.H, schedule)
     assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("schedule", ["xcd", "lpt"])
+def test_route_from_float_means_equals_float_route(schedule):
+    """Routing from float32 rows: the means absh_permute_pool writes with the float32 rows
+    route exactly as absh_route does from those rows."""
+    w = W.workload(0)
+    d = W.generate(w, want_fp32=True)
+    ctx = absh.create(w.T, w.Y, w.X, w.block)
+    q, k = (torch.from_numpy(d[n]).to(DEV) for n in ("q32", "k32"))
+    qr, qbar = absh.permute_pool(ctx, q, layout=absh.ABSH_ROWS_F32)
+    kr, kbar = absh.permute_pool(ctx, k, layout=absh.ABSH_ROWS_F32)
+    ref = absh.route(ctx, qr, kr, w.p, w.k_floor, schedule=schedule)
+    got = absh.route(ctx, None, None, w.p, w.k_floor, schedule=schedule, qbar=qbar, kbar=kbar)
+    torch.cuda.synchronize()
+    same_routing(ref, got, ctx, w.B, w.H, schedule)
