@@ -86,6 +86,9 @@ def same_routing(a, b, ctx, B, H, schedule):
     keep = torch.arange(nb, device=DEV) < a.counts.unsqueeze(-1)
     assert torch.equal(torch.where(keep, a.kv_idx, -1), torch.where(keep, b.kv_idx, -1)), "kv_idx"
     units = absh.lists_units(ctx, B, H, schedule)
+    if schedule == "ranks":
+        assert torch.equal(a.head_order, b.head_order), "head order"
+        assert torch.equal(a.rank_info.view(torch.int64), b.rank_info.view(torch.int64)), "rank report"
     if int(a.sched[9]) == 1:  # single tiles: no unit lists
         return
     assert torch.equal(a.unit_cnt[:units], b.unit_cnt[:units]), "unit_cnt"
@@ -96,7 +99,7 @@ def same_routing(a, b, ctx, B, H, schedule):
     assert torch.equal(torch.where(keep, a.unit_list[:units], -1), torch.where(keep, b.unit_list[:units], -1))
 
 
-@pytest.mark.parametrize("index,schedule", [(2, "xcd"), (3, "lpt"), (1, "lpt"), (4, "xcd")])
+@pytest.mark.parametrize("index,schedule", [(2, "xcd"), (3, "lpt"), (1, "lpt"), (4, "xcd"), (3, "ranks")])
 def test_route_from_means_equals_route(index, schedule):
     w = W.workload(index)
     print(f"[route-means] {w.name} {schedule}", flush=True)
