@@ -410,10 +410,12 @@ namespace {
 // The routing of absh_route; `scores`: the score matrix goes through the workspace
 // (score and select kernels), else the selection computes the scores on chip.
 // means_q / means_k: block means the caller already has (absh_route_means); then
-// qh and kh are not read and the pooling is skipped.
+// qh and kh are not read and the pooling is skipped. check_only: validate the
+// arguments and return before any HIP call.
 absh_status route_impl(absh_ctx* c, const void* qh, const void* kh, absh_dtype qk_type, int B, int H, int d,
                        const absh_route_opts* opts, absh_lists* out, void* ws, size_t ws_bytes, void* stream,
-                       bool scores, const float* means_q = nullptr, const float* means_k = nullptr) {
+                       bool scores, const float* means_q = nullptr, const float* means_k = nullptr,
+                       bool check_only = false) {
   g_last_error.clear();
   if (absh_status st = check_ctx(c)) return st;
   if (absh_status st = check_shape(c, B, H, d)) return st;
@@ -479,6 +481,7 @@ absh_status route_impl(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
   if (ws_bytes < w.total) return fail(ABSH_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, w.total);
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
     return fail(ABSH_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+  if (check_only) return ABSH_OK;
   if (absh_status st = use_device(c)) return st;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -737,6 +740,13 @@ absh_status absh_forward(absh_ctx* c, const void* q, const void* k, const void* 
   const WsLayout w = ws_layout(c, B, H, d);
   float* qbar = reinterpret_cast<float*>(rws + w.qbar);
   float* kbar = reinterpret_cast<float*>(rws + w.kbar);
+  // every argument is checked before the first launch
+  if (xt != ABSH_BF16 && xt != ABSH_F32) return fail(ABSH_EINVAL, "unknown dtype %d", (int)xt);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ABSH_EINVAL, "q, k, v and o must be 16-byte aligned");
+  if (absh_status st = route_impl(c, nullptr, nullptr, ABSH_BF16, B, H, d, opts, lists, rws, ws_bytes - f.route,
+                                  stream, true, qbar, kbar, true))
+    return st;  // (the lists' buffers the attention reads are the ones the routing checks)
   if (absh_status st = absh_permute_pool(c, q, xt, qh, qbar, B, H, d, ABSH_ROWS, stream)) return st;
   if (absh_status st = absh_permute_pool(c, k, xt, kh, kbar, B, H, d, ABSH_ROWS, stream)) return st;
   if (absh_status st = absh_permute(c, v, xt, vt, B, H, d, ABSH_VT, stream)) return st;

@@ -270,3 +270,4 @@ def test_bench_balance_from_busy_record():
     assert rep["workgroups"] == 2
     assert rep["rho_wg"] == round(600 / 500, 4) and rep["min_over_mean_wg"] == round(400 / 500, 4)
     assert rep["rho_sim"] == 1.2
+

@@ -162,3 +162,23 @@ def test_route_from_float_means_equals_float_route(schedule):
     got = absh.route(ctx, None, None, w.p, w.k_floor, schedule=schedule, qbar=qbar, kbar=kbar)
     torch.cuda.synchronize()
     same_routing(ref, got, ctx, w.B, w.H, schedule)
+
+
+def test_forward_rejects_bad_options_before_launching():
+    """A bad routing option makes absh_forward return ABSH_EINVAL before its first launch:
+    the output and the workspace keep their contents."""
+    import ctypes
+    w = W.workload(0)
+    d = W.generate(w)
+    ctx = absh.create(w.T, w.Y, w.X, w.block)
+    q, k, v = (bf16_dev(d[n]) for n in ("q16", "k16", "v16"))
+    o = torch.full((w.B, w.N, w.H, w.d), 7.0, dtype=torch.bfloat16, device=DEV)
+    ws = torch.full((absh.forward_workspace_bytes(ctx, w.B, w.H, w.d),), 0x5A, dtype=torch.uint8, device=DEV)
+    out = absh.alloc_routing(ctx, w.B, w.H)
+    out.counts.fill_(-3)
+    for p, k_floor, slack in ((1.5, 4, 0.0), (0.9, -1, 0.0), (0.9, 4, 1.0)):
+        with pytest.raises(absh.AbshError) as e:
+            absh.forward(ctx, q, k, v, p, k_floor, slack_frac=slack, schedule="xcd", routing=out, out=o, workspace=ws)
+        assert e.value.status == -1
+    torch.cuda.synchronize()
+    assert (o == 7.0).all() and (ws == 0x5A).all() and (out.counts == -3).all()
