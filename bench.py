@@ -141,6 +141,8 @@ def parse():
     ap.add_argument("--pool", default="fused", choices=("fused", "separate"),
                     help="block means of q and k: in the permute's pass (absh_permute_pool, then "
                          "absh_route_means), or pooled inside absh_route")
+    ap.add_argument("--overlap-v", action="store_true",
+                    help="permute (and quantize) v on a second stream while the router runs")
     ap.add_argument("--values", default="bf16", choices=("bf16", "fp8"),
                     help="fp8: quantize V to E4M3 and run the value product on fp8 MFMAs")
     ap.add_argument("--dense-reps", type=int, default=3)
@@ -223,6 +225,8 @@ def measure(args, w, p, schedule, route_f32):
     kbar = torch.empty_like(qbar)
 
     stages = ("permute", "quantize", "route", "attn", "unpermute")
+    overlap_v = args.overlap_v
+    side = torch.cuda.Stream(device=dev) if overlap_v else None  # default priority
 
     def attention(lists):
         if fp8:
@@ -245,13 +249,24 @@ def measure(args, w, p, schedule, route_f32):
         elif route_f32:
             absh.permute(ctx, q32, layout=absh.ABSH_ROWS_F32, out=qr)
             absh.permute(ctx, k32, layout=absh.ABSH_ROWS_F32, out=kr)
-        if fp8:
+        def v_work(st):
+            if fp8:
+                absh.permute(ctx, v, out=vh, stream=st)
+                absh.quantize_v(ctx, vh, out=vt8, scale=vscale, stream=st)
+            else:
+                absh.permute(ctx, v, layout=absh.ABSH_VT, out=vt, stream=st)
+        if overlap_v:
+            # v's permute (and quantization) on a second stream, beside the routing,
+            # which reads no rows; the attention waits for both
+            side.wait_stream(stream)
+            v_work(side)
+        elif fp8:
             absh.permute(ctx, v, out=vh)
         else:
             absh.permute(ctx, v, layout=absh.ABSH_VT, out=vt)
         if ev is not None:
             ev[1].record(stream)
-        if fp8:
+        if fp8 and not overlap_v:
             absh.quantize_v(ctx, vh, out=vt8, scale=vscale)
         if ev is not None:
             ev[2].record(stream)
@@ -263,6 +278,8 @@ def measure(args, w, p, schedule, route_f32):
                    workspace=ws, qbar=qbar if fused_pool else None, kbar=kbar if fused_pool else None)
         if ev is not None:
             ev[3].record(stream)
+        if overlap_v:
+            stream.wait_stream(side)
         attention(routing)
         if ev is not None:
             ev[4].record(stream)
@@ -391,6 +408,7 @@ def measure(args, w, p, schedule, route_f32):
             "slack_frac": w.slack_frac, "schedule": schedule, "router": args.router, "values": args.values,
             "route_inputs": "f32" if route_f32 else "bf16",
             "pooling": "in the permute pass" if fused_pool else "in the router",
+            "v_permute": "beside the routing, second stream" if overlap_v else "in order",
             **({"window": args.window, "anchor_stride": args.anchor_stride, "anchor_shift": args.anchor_shift,
                 "step": args.step} if args.router == "window-anchor" else {}),
         },
