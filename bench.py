@@ -174,6 +174,10 @@ def main():
         return
     for index, p in ALL_RUNS:
         w = W.workload(index)
+        if args.values == "fp8" and w.block not in (64, 128):
+            print(f"[bench] {w.name}: 8-bit values need blocks of 64 or 128 (block {w.block}); skipped",
+                  file=sys.stderr, flush=True)
+            continue
         schedule = "lpt" if w.lpt else args.schedule
         print(json.dumps(measure(args, w, p, schedule, args.route_f32 or w.dtype == "fp32")), flush=True)
 
