@@ -18,7 +18,8 @@ Fixed independently of the oracle's code by:
     the fill no rank exceeds the post-migration maximum (A = 0 in Eq. 10); counts
     never drop, never pass nb, and policy 'none' changes nothing.
 The pages' reported imbalance (1.34 to 1.08 on Wan2.2 with 8 GPUs) needs their
-model and data: parity unpinned for those figures.
+model and data, so it is not reproduced here; the rank stage is pinned by the
+properties above.
 """
 import heapq
 import itertools
