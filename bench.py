@@ -148,6 +148,8 @@ def parse():
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity-all", action="store_true",
+                    help="in the cpu_baseline leg, route and compare head 0 only (not every head)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="host time budget of the oracle's attention sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -391,7 +393,10 @@ def measure(args, w, p, schedule, route_f32):
         if w.slack_frac > 0 and args.router == "topp":
             base = absh.route(ctx, qr if route_f32 else qh, kr if route_f32 else kh, p, w.k_floor, schedule=schedule)
         head0 = (base.counts[:, :1].cpu().numpy(), base.kv_idx[:, :1].cpu().numpy().astype(np.int64))
-        cpu = cpu_baseline(w, p, data, args.cpu_seconds, head0 if args.router == "topp" else None)
+        lists_all = None
+        if args.router == "topp" and not args.no_parity_all:
+            lists_all = (base.counts.cpu().numpy(), base.kv_idx.cpu().numpy().astype(np.int64))
+        cpu = cpu_baseline(w, p, data, args.cpu_seconds, head0 if args.router == "topp" else None, lists_all)
 
     out = {
         "metric": "effective bf16 TFLOP/s on retained blocks + speedup vs dense, 720p 40-head",
@@ -548,7 +553,7 @@ def launch_balance(absh, routing, schedule, wg_busy, block):
             "rho_sim": round(float(load.max() / load.mean()), 4), "block": block}
 
 
-def cpu_baseline(w, p, data, budget_s, head0=None):
+def cpu_baseline(w, p, data, budget_s, head0=None, lists_all=None):
     """The oracle on a bounded sample of the same workload, timed on the host cores.
 
     Sample: head 0 of the workload. The oracle computes the Hilbert order, gathers
@@ -557,6 +562,8 @@ def cpu_baseline(w, p, data, budget_s, head0=None):
     in a fixed spread-out order until budget_s seconds of attention have run.
     Routing time is prorated to the tiles done (n / nb of it), so the figure is the
     retained FLOPs of the sample tiles divided by their share of the oracle's time.
+    With lists_all (the GPU's counts and lists of every head, before any slack fill)
+    the oracle also routes every head, timed, and every tile is compared.
     """
     import numpy as np
     import threadpoolctl
@@ -586,6 +593,24 @@ def cpu_baseline(w, p, data, budget_s, head0=None):
                    for i in range(R.nb))
         excused, failures = compare_routing(R, counts_g, kv_g, p)
         parity = {"tiles": int(R.nb), "identical": same, "excused": int(excused), "failures": len(failures)}
+    all_heads = None
+    if lists_all is not None:  # every head: the oracle's routing time and the GPU's lists against it
+        full = lambda name: O.to_hilbert(np.ascontiguousarray(
+            data[name + "32"] if name + "32" in data else W.bf16_to_f32(data[name + "16"])), perm)
+        qa, ka = full("q"), full("k")
+        t2 = time.perf_counter()
+        RA = O.route(qa, ka, w.block, p, w.k_floor)
+        t_all = time.perf_counter() - t2
+        del qa, ka
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from routing_compare import compare_routing
+
+        counts_a, kv_a = lists_all
+        excused, failures = compare_routing(RA, counts_a, kv_a, p)
+        all_heads = {"heads": int(counts_a.shape[0] * counts_a.shape[1]), "tiles": int(counts_a.size),
+                     "identical": int(counts_a.size) - int(excused) - len(failures), "excused": int(excused),
+                     "failures": len(failures), "oracle_route_s": round(t_all, 3)}
+        del RA
     nb = R.nb
     order = np.argsort((np.arange(nb) * 0.6180339887) % 1.0, kind="stable")  # spread over the head
     t1 = time.perf_counter()
@@ -608,6 +633,7 @@ def cpu_baseline(w, p, data, budget_s, head0=None):
                    f"({t_route:.2f} s, prorated to the sample), attention for {done} query blocks "
                    f"spread over the head ({t_attn:.2f} s); float64 NumPy"),
         "route_parity_head0": parity,
+        "route_parity_all_heads": all_heads,
         "oracle_route_s_head0": round(t_route, 3),
         "oracle_attn_s": round(t_attn, 3),
         "oracle_attn_tiles": done,

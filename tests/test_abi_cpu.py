@@ -271,3 +271,34 @@ def test_bench_balance_from_busy_record():
     assert rep["rho_wg"] == round(600 / 500, 4) and rep["min_over_mean_wg"] == round(400 / 500, 4)
     assert rep["rho_sim"] == 1.2
 
+
+
+def test_cpu_baseline_compares_every_head():
+    """The bench's CPU leg with every head's lists: lists equal to the oracle's own come
+    out identical on every tile, and one changed list is reported as a failure."""
+    import importlib.util
+    import numpy as np
+    import workloads as W
+    from oracle import absh_oracle as O
+    spec = importlib.util.spec_from_file_location("bench_under_test_cpu", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    w = W.workload(0)
+    data = W.generate(w, want_fp32=True)
+    perm, _ = O.hilbert_perm(w.T, w.Y, w.X)
+    R = O.route(O.to_hilbert(data["q32"], perm), O.to_hilbert(data["k32"], perm), w.block, w.p, w.k_floor)
+    counts = R.counts.astype(np.int32)
+    kv = np.full(counts.shape + (R.nb,), -1, dtype=np.int64)
+    for b in range(counts.shape[0]):
+        for h in range(counts.shape[1]):
+            for i in range(R.nb):
+                kv[b, h, i, : counts[b, h, i]] = R.retained(b, h, i)
+    out = bench.cpu_baseline(w, w.p, data, 0.05, (counts[:, :1], kv[:, :1]), (counts, kv))
+    a = out["route_parity_all_heads"]
+    assert a["tiles"] == counts.size and a["identical"] == counts.size and a["failures"] == 0
+    # a list that drops its last block is not excusable
+    t = np.unravel_index(int(np.argmax(counts)), counts.shape)
+    counts2 = counts.copy()
+    counts2[t] -= 1
+    out = bench.cpu_baseline(w, w.p, data, 0.05, None, (counts2, kv))
+    assert out["route_parity_all_heads"]["failures"] + out["route_parity_all_heads"]["excused"] == 1
