@@ -368,6 +368,47 @@ def test_route_uniform_scores(p):
     assert (kv[..., :c] == np.arange(c)).all()
 
 
+@pytest.mark.parametrize("p,k,beta", [(0.9, 4, 0.0), (0.5, 1, 0.0), (0.8, 2, 0.1), (0.3, 8, 0.05)])
+def test_route_block_patterns_with_many_ties(p, k, beta):
+    """Every token of a Hilbert block carries one of five row patterns (entries in
+    -1 .. 1 by halves), so the block means are the patterns themselves and the block
+    scores (dot products over d = 64, divided by 8) are exact in float32 and float64
+    and take at most 25 values per head: rows are made of large groups of exact ties,
+    at the threshold and elsewhere. The threshold searches (which stop once one key
+    is left in the interval) must reproduce the oracle's counts and lists exactly,
+    ties going to the smaller block id, with and without a slack fill."""
+    T, Y, X, block, H, d = 5, 20, 40, 16, 4, 64
+    N = T * Y * X
+    rng = np.random.default_rng(23)
+    ctx = absh.create(T, Y, X, block)
+    nb = ctx.nb
+    perm, _ = O.hilbert_perm(T, Y, X)
+    x = []
+    for _ in range(2):
+        pat = (rng.integers(-2, 3, size=(H, 5, d)) * 0.5).astype(np.float32)
+        which = rng.integers(0, 5, size=(H, nb))
+        hx = np.zeros((1, H, N, d), np.float32)
+        for h in range(H):
+            hx[0, h] = pat[h, which[h, np.arange(N) // block]]
+        g = np.zeros((1, N, H, d), np.float32)
+        g[0, perm] = hx[0].transpose(1, 0, 2)
+        x.append(g)
+    qh, kh = (absh.permute(ctx, torch.from_numpy(a).to(DEV), layout=absh.ABSH_ROWS_F32) for a in x)
+    hq, hk = (O.to_hilbert(a, perm) for a in x)
+    R = O.route(hq, hk, block, p, k)
+    assert max(len(np.unique(R.scores[0, h])) for h in range(H)) <= 25
+    want = R.counts.copy() if beta == 0 else O.slack_fill(R.counts, beta)
+    for schedule in ("xcd", "lpt"):
+        r = absh.route(ctx, qh, kh, p, k, slack_frac=beta, schedule=schedule)
+        torch.cuda.synchronize()
+        counts, kv, _ = check_lists_valid(r, nb)
+        assert np.array_equal(counts, want), (schedule, int((counts != want).sum()))
+        for h in range(H):
+            for i in range(nb):
+                expect = np.sort(R.order[0, h, i, : want[0, h, i]])
+                assert np.array_equal(kv[0, h, i, : counts[0, h, i]], expect), (schedule, h, i)
+
+
 def test_route_deterministic():
     c = case(1)
     w = c.w
