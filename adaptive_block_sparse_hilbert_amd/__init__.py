@@ -34,6 +34,7 @@ EXPORTED = (
     "absh_route_workspace_bytes", "absh_route", "absh_sparse_attn", "absh_lists_units", "absh_quantize_v",
     "absh_sparse_attn_v8", "absh_lists_bytes", "absh_lists_carve", "absh_workspace_bytes", "absh_attn_workgroups",
     "absh_route_static", "absh_permute_pool", "absh_route_means", "absh_forward", "absh_forward_workspace_bytes",
+    "absh_sparse_attn_grid",
 )
 
 
@@ -104,6 +105,7 @@ def lib() -> ctypes.CDLL:
         "absh_forward": ([vp, vp, vp, vp, i, vp, i, i, i, ctypes.POINTER(RouteOpts), ctypes.POINTER(Lists), vp, sz,
                           vp], i),
         "absh_forward_workspace_bytes": ([vp, i, i, i], sz),
+        "absh_sparse_attn_grid": ([vp, vp, vp, vp, vp, i, i, i, ctypes.POINTER(Lists), vp, vp], i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -474,6 +476,25 @@ def sparse_attn(ctx: Context, qh, kh, vt, routing: Optional[Routing] = None, out
     lists = routing.lists() if routing is not None else None
     _check(lib().absh_sparse_attn(ctx.handle, _ptr(qh), _ptr(kh), _ptr(vt), B, H, d,
                                   ctypes.byref(lists) if lists is not None else None, _ptr(out), _stream(stream)))
+    return out
+
+
+def sparse_attn_grid(ctx: Context, qh, kh, vt, routing: Optional[Routing] = None, vscale=None, out=None,
+                     stream=None):
+    """sparse_attn (vscale=None; vt from permute ABSH_VT) or sparse_attn_v8 (vt8 and vscale
+    from quantize_v) writing o [B, N, H, d] bf16 in grid order directly, as unpermute of
+    their Hilbert-order output would (routing=None: dense)."""
+    import torch
+    B, H, n_pad, d = qh.shape
+    assert n_pad == ctx.n_pad and qh.dtype == torch.bfloat16
+    if out is None:
+        out = torch.empty((B, ctx.N, H, d), dtype=torch.bfloat16, device=qh.device)
+    assert tuple(out.shape) == (B, ctx.N, H, d) and out.dtype == torch.bfloat16 and out.is_contiguous()
+    lists = routing.lists() if routing is not None else None
+    _check(lib().absh_sparse_attn_grid(ctx.handle, _ptr(qh), _ptr(kh), _ptr(vt),
+                                       _ptr(vscale) if vscale is not None else None, B, H, d,
+                                       ctypes.byref(lists) if lists is not None else None, _ptr(out),
+                                       _stream(stream)))
     return out
 
 

@@ -120,8 +120,11 @@ struct AttnLists {
 };
 // Most resident workgroups per CU of any attention kernel (bounds wg_busy).
 constexpr int kMaxAttnWgPerCu = 8;
+// grid_out: oh is the caller's [B, N, H, d] output in grid order; output row r
+// of head (b, h) goes to token perm[r] of batch b, and pad rows (r >= N) are not
+// written. Else oh is [B, H, n_pad, d] in Hilbert order.
 hipError_t launch_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B,
-                            int H, int d, const AttnLists* lists, hipStream_t s);
+                            int H, int d, const AttnLists* lists, hipStream_t s, bool grid_out = false);
 // Group units of 64- and 128-row query blocks (four and two members) run on the
 // union kernel; single tiles and other block sizes on the tile kernel.
 bool union_attention_supported(int d, int block, int members);
@@ -129,7 +132,7 @@ bool union_attention_supported(int d, int block, int members);
 // layout with per-channel scales vscale [B*H][d].
 hipError_t launch_union_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt,
                                   const float* vscale, void* oh, int B, int H, int d, const AttnLists* lists,
-                                  hipStream_t s);
+                                  hipStream_t s, bool grid_out = false);
 // V quantization: vh [B*H][n_pad][d] bf16 -> vt8 (ABSH_VT8) and vscale [B*H][d].
 hipError_t launch_quantize_v(const absh_ctx* c, const void* vh, void* vt8, float* vscale, int BH, int d,
                              hipStream_t s);

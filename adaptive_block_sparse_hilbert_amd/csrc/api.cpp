@@ -684,14 +684,39 @@ absh_status absh_sparse_attn_v8(absh_ctx* c, const void* qh, const void* kh, con
   return ABSH_OK;
 }
 
+absh_status absh_sparse_attn_grid(absh_ctx* c, const void* qh, const void* kh, const void* vt, const float* vscale,
+                                  int B, int H, int d, const absh_lists* lists, void* o, void* stream) {
+  g_last_error.clear();
+  if (absh_status st = check_ctx(c)) return st;
+  if (absh_status st = check_shape(c, B, H, d)) return st;
+  if (!qh || !kh || !vt || !o) return fail(ABSH_EINVAL, "qh, kh, vt or o is NULL");
+  if (!aligned16(qh) || !aligned16(kh) || !aligned16(vt) || !aligned16(o) || (vscale && !aligned16(vscale)))
+    return fail(ABSH_EINVAL, "qh, kh, vt, vscale and o must be 16-byte aligned");
+  absh::AttnLists L;
+  if (absh_status st = attn_lists(c, lists, &L)) return st;
+  const int members = lists ? L.members : (c->block >= 128 ? 2 : 4);
+  if (vscale && !absh::union_attention_supported(d, c->block, members))
+    return fail(ABSH_EUNSUPPORTED, "8-bit values need block 64 or 128");
+  if (absh_status st = use_device(c)) return st;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (vscale)
+    ABSH_HIP(absh::launch_union_attention(c, qh, kh, vt, vscale, o, B, H, d, lists ? &L : nullptr, s, true),
+             "absh_sparse_attn_grid");
+  else
+    ABSH_HIP(absh::launch_attention(c, qh, kh, vt, o, B, H, d, lists ? &L : nullptr, s, true),
+             "absh_sparse_attn_grid");
+  return ABSH_OK;
+}
+
 }  // extern "C"
 
 namespace {
 
-// absh_forward's workspace: the Hilbert-order rows of q, k and o, V^T, then
-// absh_route's workspace (whose block-mean slots take the means of q and k).
+// absh_forward's workspace: the Hilbert-order rows of q and k, V^T, then
+// absh_route's workspace (whose block-mean slots take the means of q and k). The
+// attention writes o in grid order itself, so no Hilbert-order output is kept.
 struct FwdLayout {
-  size_t qh, kh, vt, oh, route, total;
+  size_t qh, kh, vt, route, total;
 };
 
 FwdLayout fwd_layout(const absh_ctx* c, int B, int H, int d) {
@@ -702,7 +727,6 @@ FwdLayout fwd_layout(const absh_ctx* c, int B, int H, int d) {
   f.qh = off; off = align_up(off + rows);
   f.kh = off; off = align_up(off + rows);
   f.vt = off; off = align_up(off + vt);
-  f.oh = off; off = align_up(off + rows);
   f.route = off; off = align_up(off + ws_layout(c, B, H, d).total);
   f.total = off;
   return f;
@@ -735,7 +759,6 @@ absh_status absh_forward(absh_ctx* c, const void* q, const void* k, const void* 
   void* qh = base + f.qh;
   void* kh = base + f.kh;
   void* vt = base + f.vt;
-  void* oh = base + f.oh;
   char* rws = base + f.route;
   const WsLayout w = ws_layout(c, B, H, d);
   float* qbar = reinterpret_cast<float*>(rws + w.qbar);
@@ -753,8 +776,7 @@ absh_status absh_forward(absh_ctx* c, const void* q, const void* k, const void* 
   if (absh_status st = route_impl(c, nullptr, nullptr, ABSH_BF16, B, H, d, opts, lists, rws, ws_bytes - f.route,
                                   stream, true, qbar, kbar))
     return st;
-  if (absh_status st = absh_sparse_attn(c, qh, kh, vt, B, H, d, lists, oh, stream)) return st;
-  return absh_unpermute(c, oh, o, B, H, d, stream);
+  return absh_sparse_attn_grid(c, qh, kh, vt, nullptr, B, H, d, lists, o, stream);
 }
 
 }  // extern "C"

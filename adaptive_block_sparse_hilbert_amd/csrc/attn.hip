@@ -163,16 +163,24 @@ template <int D, int BLK, int GROUPS>
 __global__ __launch_bounds__((Cfg<D, BLK, GROUPS>::THREADS)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, const bf16_t* __restrict__ vt,
                  bf16_t* __restrict__ oh, AttnLists L, int32_t* __restrict__ counters, int units, int nb,
-                 int n_pad, int N, float scale_log2) {
+                 int n_pad, int N, float scale_log2, const int32_t* __restrict__ operm, int H) {
   using C = Cfg<D, BLK, GROUPS>;
   constexpr int NS = C::NS;
   __shared__ __attribute__((aligned(1024))) char ring[NS * C::STAGE];
   __shared__ int s_next[2];  // next unit, double-buffered: read one slot while the other is written
+  // The output map is needed only after each unit's last step: parked in LDS, it
+  // is not held in scalar registers across the step loop.
+  __shared__ const int32_t* s_operm;
+  __shared__ int s_heads;
 
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();  // for the optional busy record
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  if (tid == 0) {
+    s_operm = operm;
+    s_heads = H;
+  }
   const int grp = wave / C::WAVES;  // this wave's member pair: 2 grp, 2 grp + 1
   const int rw = wave % C::WAVES;   // this wave's 16-row slice of each member
   const int n = lane & 15;
@@ -450,13 +458,20 @@ void attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, c
       l += __shfl_xor(l, 32);
       const float inv = l > 0.f ? 1.f / l : 0.f;
       const int qrow = (qb0 + m0 + mm) * BLK + rw * 16 + n;
-      bf16_t* orow = oh + ((size_t)bh * n_pad + qrow) * D;
+      // Hilbert order (every padded row), or the caller's grid order: row r of
+      // head (b, h) is token perm[r] of batch b, and pad rows are not written
+      const int32_t* om = s_operm;
+      const int nh = s_heads;
+      const bool keep = om == nullptr || qrow < N;
+      const size_t out_row = om == nullptr ? (size_t)bh * n_pad + qrow
+                                           : ((size_t)(bh / nh) * N + (keep ? om[qrow] : 0)) * nh + bh % nh;
+      bf16_t* orow = oh + out_row * D;
 #pragma unroll
       for (int t = 0; t < C::DT; ++t) {
         uint2 w;
         w.x = (uint32_t)f32_to_bf16(o[mm][t][0] * inv) | ((uint32_t)f32_to_bf16(o[mm][t][1] * inv) << 16);
         w.y = (uint32_t)f32_to_bf16(o[mm][t][2] * inv) | ((uint32_t)f32_to_bf16(o[mm][t][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + 16 * t + 4 * g) = w;
+        if (keep) *reinterpret_cast<uint2*>(orow + 16 * t + 4 * g) = w;
       }
     }
   }
@@ -477,7 +492,7 @@ void attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, c
 
 template <int D, int BLK, int GROUPS>
 hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B, int H,
-                  const AttnLists& L, bool dense, hipStream_t s) {
+                  const AttnLists& L, bool dense, hipStream_t s, bool grid_out) {
   using C = Cfg<D, BLK, GROUPS>;
   // resident workgroups per CU for this instantiation (one gfx950 value; computed once,
   // an atomic so that concurrent first calls from several threads are well defined)
@@ -499,7 +514,8 @@ hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void*
   int32_t* counters = Lk.counters ? Lk.counters : c->counters;
   attn_kernel<D, BLK, GROUPS><<<grid, C::THREADS, 0, s>>>(
       reinterpret_cast<const bf16_t*>(qh), reinterpret_cast<const bf16_t*>(kh), reinterpret_cast<const bf16_t*>(vt),
-      reinterpret_cast<bf16_t*>(oh), Lk, counters, units, c->nb, c->n_pad, c->N, scale_log2);
+      reinterpret_cast<bf16_t*>(oh), Lk, counters, units, c->nb, c->n_pad, c->N, scale_log2,
+      grid_out ? c->perm : nullptr, H);
   return hipGetLastError();
 }
 
@@ -507,11 +523,11 @@ hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void*
 // and pairs use one group, quads two.
 template <int D, int BLK>
 hipError_t dispatch(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B, int H,
-                    const AttnLists* lists, hipStream_t s) {
+                    const AttnLists* lists, hipStream_t s, bool grid_out) {
   const int members = lists ? lists->members : (BLK >= 128 ? 2 : 4);
   AttnLists L = lists ? *lists : AttnLists{};
-  if (members == 4) return launch<D, BLK, (BLK >= 128 ? 1 : 2)>(c, qh, kh, vt, oh, B, H, L, !lists, s);
-  return launch<D, BLK, 1>(c, qh, kh, vt, oh, B, H, L, !lists, s);
+  if (members == 4) return launch<D, BLK, (BLK >= 128 ? 1 : 2)>(c, qh, kh, vt, oh, B, H, L, !lists, s, grid_out);
+  return launch<D, BLK, 1>(c, qh, kh, vt, oh, B, H, L, !lists, s, grid_out);
 }
 
 }  // namespace
@@ -521,12 +537,12 @@ int attention_members(const absh_ctx* c, const AttnLists* lists) {
 }
 
 hipError_t launch_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt, void* oh, int B,
-                            int H, int d, const AttnLists* lists, hipStream_t s) {
+                            int H, int d, const AttnLists* lists, hipStream_t s, bool grid_out) {
   const int members = lists ? lists->members : (c->block >= 128 ? 2 : 4);
   if (union_attention_supported(d, c->block, members))
-    return launch_union_attention(c, qh, kh, vt, nullptr, oh, B, H, d, lists, s);
+    return launch_union_attention(c, qh, kh, vt, nullptr, oh, B, H, d, lists, s, grid_out);
 #define ABSH_ATTN(DD, BB) \
-  if (d == DD && c->block == BB) return dispatch<DD, BB>(c, qh, kh, vt, oh, B, H, lists, s);
+  if (d == DD && c->block == BB) return dispatch<DD, BB>(c, qh, kh, vt, oh, B, H, lists, s, grid_out);
   ABSH_ATTN(64, 16)
   ABSH_ATTN(64, 64)
   ABSH_ATTN(64, 128)

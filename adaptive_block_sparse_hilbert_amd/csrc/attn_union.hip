@@ -143,7 +143,8 @@ template <int D, int BLK, bool F8>
 __global__ __launch_bounds__((UCfg<D, BLK, F8>::THREADS)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__ kh, const char* __restrict__ vt,
                        const float* __restrict__ vscale, bf16_t* __restrict__ oh, AttnLists L,
-                       int32_t* __restrict__ counters, int units, int nb, int n_pad, int N, float scale_log2) {
+                       int32_t* __restrict__ counters, int units, int nb, int n_pad, int N, float scale_log2,
+                       const int32_t* __restrict__ operm, int H) {
   using C = UCfg<D, BLK, F8>;
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -166,11 +167,19 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
     return i == 0 ? vs0 : i == 1 ? vs1 : i == 2 ? vs2 : vs3;
   };
   __shared__ int s_next[2];
+  // The output map is needed only after each unit's last step: parked in LDS, it
+  // is not held in scalar registers across the step loop.
+  __shared__ const int32_t* s_operm;
+  __shared__ int s_heads;
 
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();  // for the optional busy record
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets per-wave branches be scalar
+  if (tid == 0) {
+    s_operm = operm;
+    s_heads = H;
+  }
   const int col = lane & 31;
   const int g = lane >> 5;
   const int member = wave / C::WPM;
@@ -568,7 +577,14 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
     if (have) {
       const float l = sum_across_halves(l_run);
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      bf16_t* orow = oh + ((size_t)bh * n_pad + qrow) * D;
+      // Hilbert order (every padded row), or the caller's grid order: row r of
+      // head (b, h) is token perm[r] of batch b, and pad rows are not written
+      const int32_t* om = s_operm;
+      const int nh = s_heads;
+      const bool keep = om == nullptr || qrow < N;
+      const size_t out_row = om == nullptr ? (size_t)bh * n_pad + qrow
+                                           : ((size_t)(bh / nh) * N + (keep ? om[qrow] : 0)) * nh + bh % nh;
+      bf16_t* orow = oh + out_row * D;
 #pragma unroll
       for (int t = 0; t < C::DT; ++t)
 #pragma unroll
@@ -585,7 +601,7 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
           uint2 w;
           w.x = (uint32_t)f32_to_bf16(o[t][4 * q] * sc[0]) | ((uint32_t)f32_to_bf16(o[t][4 * q + 1] * sc[1]) << 16);
           w.y = (uint32_t)f32_to_bf16(o[t][4 * q + 2] * sc[2]) | ((uint32_t)f32_to_bf16(o[t][4 * q + 3] * sc[3]) << 16);
-          *reinterpret_cast<uint2*>(orow + 32 * t + 8 * q + 4 * g) = w;
+          if (keep) *reinterpret_cast<uint2*>(orow + 32 * t + 8 * q + 4 * g) = w;
         }
     }
   }
@@ -606,7 +622,7 @@ void union_attn_kernel(const bf16_t* __restrict__ qh, const bf16_t* __restrict__
 
 template <int D, int BLK, bool F8>
 hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void* vt, const float* vscale, void* oh,
-                  int B, int H, const AttnLists& L, bool dense, hipStream_t s) {
+                  int B, int H, const AttnLists& L, bool dense, hipStream_t s, bool grid_out) {
   using C = UCfg<D, BLK, F8>;
   // resident workgroups per CU for this instantiation (one gfx950 value; computed once,
   // an atomic so that concurrent first calls from several threads are well defined)
@@ -627,7 +643,8 @@ hipError_t launch(const absh_ctx* c, const void* qh, const void* kh, const void*
   int32_t* counters = Lk.counters ? Lk.counters : c->counters;
   union_attn_kernel<D, BLK, F8><<<grid, C::THREADS, 0, s>>>(
       reinterpret_cast<const bf16_t*>(qh), reinterpret_cast<const bf16_t*>(kh), reinterpret_cast<const char*>(vt),
-      vscale, reinterpret_cast<bf16_t*>(oh), Lk, counters, units, c->nb, c->n_pad, c->N, scale_log2);
+      vscale, reinterpret_cast<bf16_t*>(oh), Lk, counters, units, c->nb, c->n_pad, c->N, scale_log2,
+      grid_out ? c->perm : nullptr, H);
   return hipGetLastError();
 }
 
@@ -639,13 +656,13 @@ bool union_attention_supported(int d, int block, int members) {
 
 hipError_t launch_union_attention(const absh_ctx* c, const void* qh, const void* kh, const void* vt,
                                   const float* vscale, void* oh, int B, int H, int d, const AttnLists* lists,
-                                  hipStream_t s) {
+                                  hipStream_t s, bool grid_out) {
   AttnLists L = lists ? *lists : AttnLists{};
   const bool dense = lists == nullptr;
 #define ABSH_UNION(DD, BB)                                                                              \
   if (d == DD && c->block == BB)                                                                        \
-    return vscale ? launch<DD, BB, true>(c, qh, kh, vt, vscale, oh, B, H, L, dense, s)                  \
-                  : launch<DD, BB, false>(c, qh, kh, vt, nullptr, oh, B, H, L, dense, s);
+    return vscale ? launch<DD, BB, true>(c, qh, kh, vt, vscale, oh, B, H, L, dense, s, grid_out)        \
+                  : launch<DD, BB, false>(c, qh, kh, vt, nullptr, oh, B, H, L, dense, s, grid_out);
   ABSH_UNION(64, 64)
   ABSH_UNION(64, 128)
   ABSH_UNION(128, 64)

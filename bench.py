@@ -147,6 +147,9 @@ def parse():
                     help="fp8: quantize V to E4M3 and run the value product on fp8 MFMAs")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--out-order", choices=("grid", "hilbert"), default="grid",
+                    help="grid: the attention writes o in grid order itself (absh_sparse_attn_grid); "
+                         "hilbert: Hilbert-order output, then absh_unpermute as a stage of its own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity-all", action="store_true",
                     help="in the cpu_baseline leg, route and compare head 0 only (not every head)")
@@ -215,7 +218,8 @@ def measure(args, w, p, schedule, route_f32):
         vscale = torch.empty((B, H, d), dtype=torch.float32, device=dev)
     else:
         vt = torch.empty((B, H, ctx.nb, d, absh.vt_keys(w.block)), dtype=torch.bfloat16, device=dev)
-    oh = torch.empty_like(qh)
+    grid_out = args.out_order == "grid"
+    oh = None if grid_out else torch.empty_like(qh)
     o = torch.empty_like(q)
     routing = absh.alloc_routing(ctx, B, H)
     wg_busy = absh.busy_record(ctx, routing)
@@ -235,7 +239,9 @@ def measure(args, w, p, schedule, route_f32):
     side = torch.cuda.Stream(device=dev) if overlap_v else None  # default priority
 
     def attention(lists):
-        if fp8:
+        if grid_out:
+            absh.sparse_attn_grid(ctx, qh, kh, vt8 if fp8 else vt, lists, vscale=vscale if fp8 else None, out=o)
+        elif fp8:
             absh.sparse_attn_v8(ctx, qh, kh, vt8, vscale, lists, out=oh)
         else:
             absh.sparse_attn(ctx, qh, kh, vt, lists, out=oh)
@@ -289,7 +295,8 @@ def measure(args, w, p, schedule, route_f32):
         attention(routing)
         if ev is not None:
             ev[4].record(stream)
-        absh.unpermute(ctx, oh, out=o)
+        if not grid_out:
+            absh.unpermute(ctx, oh, out=o)
         if ev is not None:
             ev[5].record(stream)
 
@@ -317,6 +324,8 @@ def measure(args, w, p, schedule, route_f32):
     stage_med = {s: float(np.median([e[i].elapsed_time(e[i + 1]) for e in events])) for i, s in enumerate(stages)}
     if not fp8:  # no quantization stage with bf16 values
         del stage_ms["quantize"], stage_min["quantize"], stage_med["quantize"]
+    if grid_out:  # the attention writes o itself
+        del stage_ms["unpermute"], stage_min["unpermute"], stage_med["unpermute"]
 
     # retained work of this routing (identical every step: the path is deterministic)
     counts = routing.counts.cpu().numpy().reshape(-1)
@@ -418,6 +427,7 @@ def measure(args, w, p, schedule, route_f32):
             "route_inputs": "f32" if route_f32 else "bf16",
             "pooling": "in the permute pass" if fused_pool else "in the router",
             "v_permute": "beside the routing, second stream" if overlap_v else "in order",
+            "output": "grid order, written by the attention" if grid_out else "Hilbert order, then unpermute",
             **({"window": args.window, "anchor_stride": args.anchor_stride, "anchor_shift": args.anchor_shift,
                 "step": args.step} if args.router == "window-anchor" else {}),
         },

@@ -316,13 +316,14 @@ absh_status absh_route_means(absh_ctx* ctx, const float* qbar, const float* kbar
 /* The whole path in one call (the pages' drop-in use of the method: grid-order
  * q, k, v in, grid-order attention output out): absh_permute_pool of q and k,
  * absh_permute of v into ABSH_VT, absh_route_means (Top-p router, opts as for
- * absh_route, lists written as absh_route writes them), absh_sparse_attn over
- * those lists, absh_unpermute into o. q, k, v: [B, N, H, d] bf16 or float32 (xt;
- * float32 is rounded to bf16, and routing uses the means of the rounded rows);
- * o: [B, N, H, d] bf16. The Hilbert-order tensors and the routing scratch live in
- * ws (absh_forward_workspace_bytes(), 256-byte aligned, contents scratch). The
- * same kernels in the same order as the separate calls, so o is bit-identical to
- * theirs. */
+ * absh_route, lists written as absh_route writes them), then
+ * absh_sparse_attn_grid over those lists, which writes o in grid order. q, k, v:
+ * [B, N, H, d] bf16 or float32 (xt; float32 is rounded to bf16, and routing uses
+ * the means of the rounded rows); o: [B, N, H, d] bf16. The Hilbert-order q, k,
+ * V^T and the routing scratch live in ws (absh_forward_workspace_bytes(), 256-byte
+ * aligned, contents scratch). The same arithmetic in the same order as the
+ * separate calls (absh_sparse_attn then absh_unpermute), so o is bit-identical
+ * to theirs. */
 absh_status absh_forward(absh_ctx* ctx, const void* q, const void* k, const void* v, absh_dtype xt, void* o, int B,
                          int H, int d, const absh_route_opts* opts, absh_lists* lists, void* ws, size_t ws_bytes,
                          void* stream);
@@ -392,6 +393,19 @@ absh_status absh_quantize_v(absh_ctx* ctx, const void* vh, int B, int H, int d, 
 absh_status absh_sparse_attn_v8(absh_ctx* ctx, const void* qh, const void* kh, const void* vt8,
                                 const float* vscale, int B, int H, int d, const absh_lists* lists, void* oh,
                                 void* stream);
+
+/* The attention with the inverse of the Hilbert reordering (xllm-io review of
+ * FVAttn, 3.1) folded into its output write: absh_sparse_attn
+ * (vscale == NULL; vt in ABSH_VT) or absh_sparse_attn_v8 (vscale and vt8 from
+ * absh_quantize_v; block 64 or 128, else ABSH_EUNSUPPORTED), same lists, same
+ * arithmetic, but output row r of head (b, h) is stored at o[b, perm[r], h, :]
+ * of the caller's grid-order o ([B, N, H, d] bf16, 16-byte aligned), where
+ * perm[r] is the grid index of the r-th token in Hilbert order. Pad rows are not
+ * written. o is therefore bit-identical to absh_unpermute of the Hilbert-order
+ * output, without the Hilbert-order buffer or the extra pass over it. */
+absh_status absh_sparse_attn_grid(absh_ctx* ctx, const void* qh, const void* kh, const void* vt,
+                                  const float* vscale, int B, int H, int d, const absh_lists* lists, void* o,
+                                  void* stream);
 
 #ifdef __cplusplus
 }

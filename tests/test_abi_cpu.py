@@ -154,6 +154,9 @@ def test_null_context_everywhere(L):
     assert L.absh_quantize_v(None, vp(16), 1, 1, 64, vp(16), vp(16), None) == EINVAL
     assert L.absh_sparse_attn_v8(None, vp(16), vp(16), vp(16), vp(16), 1, 1, 64, None, vp(16), None) == EINVAL
     assert b"ctx is NULL" in L.absh_last_error()
+    assert L.absh_sparse_attn_grid(None, vp(16), vp(16), vp(16), None, 1, 1, 64, None, vp(16), None) == EINVAL
+    assert L.absh_sparse_attn_grid(None, vp(16), vp(16), vp(16), vp(16), 1, 1, 64, None, vp(16), None) == EINVAL
+    assert b"ctx is NULL" in L.absh_last_error()
     assert L.absh_route_workspace_bytes(None, 1, 1, 64) == 0
     assert L.absh_lists_units(None, 1, 1, 0) == 0
     assert L.absh_lists_bytes(None, 1, 1, 0) == 0
