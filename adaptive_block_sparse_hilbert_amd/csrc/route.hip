@@ -156,24 +156,96 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
 
 // ------------------------------------------------------------------ Top-p select
 
+// Reductions over the wave as a butterfly on the DPP and lane-swap paths, with no
+// LDS round trip: partners 1 and 2 apart within each quad, then the mirrors of 8
+// and 16 lanes (each half meets the other half's equal partial), then rows 16 and
+// half-waves 32 apart by the gfx950 lane swaps. At every step the two partners
+// combine the same two values in the same order, so every lane ends with the same
+// bits. The wave must be fully active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kQuadXor1 = 0xB1;    // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;    // quad_perm [2, 3, 0, 1]
+constexpr int kHalfMirror = 0x141;  // lane i of each 8 <- lane 7 - i
+constexpr int kMirror = 0x140;      // lane i of each 16 <- lane 15 - i
+
+template <typename T>
+struct LaneBits;
+template <>
+struct LaneBits<float> {
+  static constexpr int W = 1;
+  __device__ static void split(float v, uint32_t* u) { u[0] = __float_as_uint(v); }
+  __device__ static float join(const uint32_t* u) { return __uint_as_float(u[0]); }
+};
+template <>
+struct LaneBits<double> {
+  static constexpr int W = 2;
+  __device__ static void split(double v, uint32_t* u) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    u[0] = (uint32_t)b;
+    u[1] = (uint32_t)(b >> 32);
+  }
+  __device__ static double join(const uint32_t* u) {
+    return __longlong_as_double((long long)(((uint64_t)u[1] << 32) | u[0]));
+  }
+};
+template <>
+struct LaneBits<uint64_t> {
+  static constexpr int W = 2;
+  __device__ static void split(uint64_t v, uint32_t* u) {
+    u[0] = (uint32_t)v;
+    u[1] = (uint32_t)(v >> 32);
+  }
+  __device__ static uint64_t join(const uint32_t* u) { return ((uint64_t)u[1] << 32) | u[0]; }
+};
+
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_partner(T v) {
+  using LB = LaneBits<T>;
+  uint32_t u[LB::W];
+  LB::split(v, u);
+#pragma unroll
+  for (int w = 0; w < LB::W; ++w) u[w] = dpp_move<CTRL>(u[w]);
+  return LB::join(u);
+}
+// Combine with the lane 16 (R16) or 32 apart: the swap hands each lane its own
+// value and its partner's, ordered by lane group, so both partners see (a, b).
+template <bool R16, typename T, typename Op>
+__device__ __forceinline__ T swap_combine(T v, Op op) {
+  using LB = LaneBits<T>;
+  uint32_t u[LB::W], a[LB::W], b[LB::W];
+  LB::split(v, u);
+#pragma unroll
+  for (int w = 0; w < LB::W; ++w) {
+    const auto sw = R16 ? __builtin_amdgcn_permlane16_swap(u[w], u[w], false, false)
+                        : __builtin_amdgcn_permlane32_swap(u[w], u[w], false, false);
+    a[w] = sw[0];
+    b[w] = sw[1];
+  }
+  return op(LB::join(a), LB::join(b));
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = op(v, dpp_partner<kQuadXor1>(v));
+  v = op(v, dpp_partner<kQuadXor2>(v));
+  v = op(v, dpp_partner<kHalfMirror>(v));
+  v = op(v, dpp_partner<kMirror>(v));
+  v = swap_combine<true>(v, op);
+  return swap_combine<false>(v, op);
+}
 __device__ __forceinline__ double wave_sum(double v) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  return wave_reduce(v, [](double a, double b) { return a + b; });
 }
 __device__ __forceinline__ float wave_sum_f32(float v) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 __device__ __forceinline__ float wave_max(float v) {
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
-  return v;
+  return wave_reduce(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
 }
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return lane == 0 ? 0ull : (~0ull >> (64 - lane)); }
