@@ -2,10 +2,11 @@
 
 One step is one pass of the whole path over one batch of synthetic input that is
 already resident in HBM:
-    permute q, k (rows) and v (block-transposed) into Hilbert order
-    -> route (block means, block scores, Top-p + floor [+ slack fill], Eq. 1, tile queue)
-    -> block-sparse attention over the retained blocks
-    -> unpermute the output back to grid order.
+    permute q, k (rows, with their block means) and v (block-transposed) into
+    Hilbert order
+    -> route (block scores, Top-p + floor [+ slack fill], Eq. 1, tile queue)
+    -> block-sparse attention over the retained blocks, whose output stores put
+       each row back at its grid position (no separate unpermute).
 The default workload is 720p video at 40 heads (grid 21 x 45 x 80 = 75,600 tokens,
 d = 128, block 64, p = 0.9, k = 4, the "xcd" schedule). --all-configs runs the
 five synthetic workloads one after another (the 6x horizon at p = 0.8, 0.9 and
@@ -141,8 +142,10 @@ def parse():
     ap.add_argument("--pool", default="fused", choices=("fused", "separate"),
                     help="block means of q and k: in the permute's pass (absh_permute_pool, then "
                          "absh_route_means), or pooled inside absh_route")
-    ap.add_argument("--overlap-v", action="store_true",
-                    help="permute (and quantize) v on a second stream while the router runs")
+    ap.add_argument("--overlap-v", action=argparse.BooleanOptionalAction, default=False,
+                    help="permute (and quantize) v on a second stream (default priority) while the "
+                         "router runs, which reads no rows (off by default: the attention after it then "
+                         "runs at a lower clock, and the step takes longer)")
     ap.add_argument("--values", default="bf16", choices=("bf16", "fp8"),
                     help="fp8: quantize V to E4M3 and run the value product on fp8 MFMAs")
     ap.add_argument("--dense-reps", type=int, default=3)
