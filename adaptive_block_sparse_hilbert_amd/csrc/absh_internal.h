@@ -80,8 +80,11 @@ struct RankOpts {
   int policy;
   double k1, k2, n1, n2;
 };
+// unit_members > 1 (first selection from scores in memory only): the same pass also
+// writes the union lists of the work units of that many query blocks (rb.unit_list,
+// rb.unit_cnt), as launch_groups would from the written lists.
 hipError_t launch_select(const absh_ctx* c, const RouteBuffers& rb, int tiles, double p, int k_floor,
-                         int order_depth, int reselect, hipStream_t s);
+                         int order_depth, int reselect, hipStream_t s, int unit_members = 0);
 hipError_t launch_slack_plan(const absh_ctx* c, const RouteBuffers& rb, int tiles, double beta, hipStream_t s);
 hipError_t launch_workload(const absh_ctx* c, const RouteBuffers& rb, int BH, hipStream_t s);
 hipError_t launch_queue(const absh_ctx* c, const RouteBuffers& rb, int tiles, int lpt, hipStream_t s);

@@ -514,6 +514,7 @@ absh_status route_impl(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
   rb.head_order = ranks ? out->head_order : nullptr;
   rb.rank_info = ranks ? out->rank_info : nullptr;
   const int tiles = B * H * c->nb;
+  bool units_in_select = false;
 
   if (structured) {
     const int offset = opts->anchor_stride > 0
@@ -529,7 +530,10 @@ absh_status route_impl(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
       ABSH_HIP(absh::launch_pool(c, kh, qk_type == ABSH_F32, kbar, B, H, d, s), "absh_route: pool k");
     }
     if (rb.S) ABSH_HIP(absh::launch_scores(c, qbar, kbar, const_cast<float*>(rb.S), B * H, d, s), "absh_route: scores");
-    ABSH_HIP(absh::launch_select(c, rb, tiles, opts->p, opts->k_floor, opts->order_depth, 0, s),
+    // when no later stage changes the counts, the selection also writes the units' union lists
+    units_in_select = rb.S && members > 1 && opts->slack_frac <= 0.0 && !ranks;
+    ABSH_HIP(absh::launch_select(c, rb, tiles, opts->p, opts->k_floor, opts->order_depth, 0, s,
+                                 units_in_select ? members : 0),
              "absh_route: select");
   }
   if (opts->slack_frac > 0.0) {
@@ -548,7 +552,7 @@ absh_status route_impl(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
     ABSH_HIP(absh::launch_rank_final(rb, B * H, s), "absh_route: rank report");
   }
   ABSH_HIP(absh::launch_queue(c, rb, tiles, opts->schedule == ABSH_SCHED_LPT, s), "absh_route: queue");
-  if (members > 1) ABSH_HIP(absh::launch_groups(c, rb, B * H, members, s), "absh_route: groups");
+  if (members > 1 && !units_in_select) ABSH_HIP(absh::launch_groups(c, rb, B * H, members, s), "absh_route: groups");
   if (!ranks) ABSH_HIP(absh::launch_segments(c, rb, B * H, opts->schedule, s), "absh_route: segments");
   if (opts->schedule == ABSH_SCHED_LPT && members > 1)
     ABSH_HIP(absh::launch_unit_lpt(c, rb, B * H, s), "absh_route: unit queue");

@@ -275,8 +275,10 @@ constexpr int kArgmaxWant = 16;
 
 // RS: re-selection to the counts in `target` (keys only), as its own instance.
 // One wave, the scores of tile `row` at srow[0 .. nb - 1] (in LDS).
+// Returns the retained blocks as bit t for block lane + 64 t (0 for a re-selection
+// row that needs no new block).
 template <int J, bool RS>
-__device__ __forceinline__ void select_row(const float* srow, int row, int nb, double p, int k_floor,
+__device__ __forceinline__ uint32_t select_row(const float* srow, int row, int nb, double p, int k_floor,
                                            int order_depth, const int32_t* __restrict__ target,
                                            int32_t* __restrict__ counts, int16_t* __restrict__ kv_idx,
                                            int16_t* __restrict__ order) {
@@ -284,7 +286,7 @@ __device__ __forceinline__ void select_row(const float* srow, int row, int nb, d
   int want = 0;
   if (RS) {
     want = target[row];
-    if (want <= counts[row]) return;
+    if (want <= counts[row]) return 0u;
   }
   float s[J];
   bool valid[J];
@@ -545,6 +547,7 @@ __device__ __forceinline__ void select_row(const float* srow, int row, int nb, d
       if (lane == 0) ord[r] = (int16_t)j;
     }
   }
+  return takebits;
 }
 
 // Selection from scores in memory: one wave per tile row. The searches are
@@ -558,6 +561,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(J <= 20 ? 3
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= tiles) return;
   select_row<J, RS>(S + (size_t)row * nb, row, nb, p, k_floor, order_depth, target, counts, kv_idx, order);
+}
+
+// The first selection with the work units' union lists built in the same pass, for
+// routing whose counts do not change afterwards (no slack fill, no rank stage). A
+// workgroup takes 4 / M units of M neighbouring query blocks of one head (M = 4 or
+// 2), one wave per member row. Each wave selects its row as select_kernel does and
+// keeps the bit mask of its retained blocks; a unit's union is the OR of its
+// members' masks, so its entries (block id | member m's flag << (28 + m)) come out
+// in ascending block id: the list group_merge_kernel builds from the written lists.
+// The member rows' searches take different numbers of steps, so the unit's last
+// wave to finish builds the union (counted in LDS) and the others leave at once,
+// freeing their registers, instead of waiting at a barrier.
+template <int J>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(J <= 20 ? 3 : 1))) void select_units_kernel(
+    const float* __restrict__ S, int nb, int members, int per_head, int units, double p, int k_floor,
+    int order_depth, int32_t* __restrict__ counts, int16_t* __restrict__ kv_idx, int16_t* __restrict__ order,
+    uint32_t* __restrict__ unit_list, int32_t* __restrict__ unit_cnt) {
+  __shared__ uint32_t taken[4][64];
+  __shared__ int finished[4];  // member waves done, per unit of the workgroup
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int slot = w / members;
+  const int u = blockIdx.x * (4 / members) + slot;
+  const int m = w % members;
+  const int bh = u / per_head;
+  const int qb = (u - bh * per_head) * members + m;
+  if (threadIdx.x < 4) finished[threadIdx.x] = 0;
+  __syncthreads();
+  if (u >= units) return;  // every wave of this unit slot leaves here
+  uint32_t bits = 0u;
+  if (qb < nb) {
+    const int row = bh * nb + qb;
+    bits = select_row<J, false>(S + (size_t)row * nb, row, nb, p, k_floor, order_depth, nullptr, counts, kv_idx,
+                                order);
+  }
+  taken[w][lane] = bits;
+  __threadfence_block();  // this wave's mask is in LDS before it counts itself done
+  int before = 0;
+  if (lane == 0) before = atomicAdd(&finished[slot], 1);
+  before = __builtin_amdgcn_readfirstlane(before);
+  if (before != members - 1) return;
+  __threadfence_block();  // the other members' masks, written before their counts
+  const int w0 = slot * members;
+  uint32_t mine[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) mine[k] = k < members ? taken[w0 + k][lane] : 0u;
+  uint32_t* out = unit_list + (size_t)u * nb;
+  const uint64_t below = lanes_below(lane);
+  int n = 0;
+#pragma unroll
+  for (int t = 0; t < J; ++t) {
+    uint32_t flags = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) flags |= ((mine[k] >> t) & 1u) << k;
+    const uint64_t in = __ballot(flags != 0u);
+    if (flags) out[n + popc64(in & below)] = (uint32_t)(lane + 64 * t) | (flags << 28);
+    n += popc64(in);
+  }
+  if (lane == 0) unit_cnt[u] = n;
 }
 
 // Block scores and selection in one kernel, for routing without a score matrix in
@@ -1448,7 +1510,7 @@ hipError_t launch_scores(const absh_ctx* c, const float* qbar, const float* kbar
 }
 
 hipError_t launch_select(const absh_ctx* c, const RouteBuffers& rb, int tiles, double p, int k_floor,
-                         int order_depth, int reselect, hipStream_t s) {
+                         int order_depth, int reselect, hipStream_t s, int unit_members) {
   const int nb = c->nb;
   const int groups = (nb + kSelRows - 1) / kSelRows;
   const unsigned grid = (unsigned)((uint64_t)(tiles / nb) * groups);
@@ -1475,9 +1537,17 @@ hipError_t launch_select(const absh_ctx* c, const RouteBuffers& rb, int tiles, d
   if (rb.d != 64 && rb.d != 128) return hipErrorInvalidValue;
   const unsigned row_grid = (unsigned)((tiles + 3) / 4);
   if (rb.S) {  // scores in memory
+    const bool units_too = !reselect && (unit_members == 2 || unit_members == 4);
+    const int per_head = (nb + unit_members - 1) / (unit_members > 0 ? unit_members : 1);
+    const int units = units_too ? (tiles / nb) * per_head : 0;
+    const unsigned unit_grid = units_too ? (unsigned)((units + 4 / unit_members - 1) / (4 / unit_members)) : 0u;
 #define ABSH_SELECT_S(JJ)                                                                                  \
   do {                                                                                                     \
-    if (reselect)                                                                                          \
+    if (units_too)                                                                                         \
+      select_units_kernel<JJ><<<unit_grid, 256, 0, s>>>(rb.S, nb, unit_members, per_head, units, p, k_floor,  \
+                                                        order_depth, rb.counts, rb.kv_idx, rb.order,      \
+                                                        rb.unit_list, rb.unit_cnt);                       \
+    else if (reselect)                                                                                     \
       select_kernel<JJ, true><<<row_grid, 256, 0, s>>>(rb.S, nb, tiles, p, k_floor, order_depth, rb.target,  \
                                                        rb.counts, rb.kv_idx, rb.order);                   \
     else                                                                                                   \

@@ -708,6 +708,15 @@ def test_block_counts_up_to_the_maximum(grid, block, d, H, p, k, schedule):
     excused, failures = compare_routing(R, counts, kv, p)
     assert not failures, failures[:5]
     assert excused <= 0.01 * counts.size
+    if block >= 64 or schedule != "lpt":  # group units: their union lists, built inside the selection
+        M = 2 if block >= 128 else 4
+        units = absh.lists_units(ctx, 1, H, schedule)
+        want_lists, want_len = expected_groups(counts, kv, nb, M)
+        got_len = r.unit_cnt.cpu().numpy()[:units]
+        got = r.unit_list.cpu().numpy().view(np.uint32)
+        assert np.array_equal(got_len, want_len)
+        for u in range(units):
+            assert np.array_equal(got[u, : got_len[u]], want_lists[u]), u
     oh = absh.sparse_attn(ctx, qh, kh, vt, r)
     o = absh.unpermute(ctx, oh).float().cpu().numpy()
     flat = counts.reshape(-1)
