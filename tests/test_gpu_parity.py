@@ -499,7 +499,9 @@ def test_attention_tiny_all_tiles():
 
 def stratified_tiles(counts, rng):
     """Tiles to check: per head one random tile and its last (partial) query block; over
-    all tiles the lightest, the heaviest and one random tile per count quintile."""
+    all tiles the lightest, the heaviest and one random tile per count quintile; and one
+    random tile per position within a work unit (query block i mod 4: which member of
+    its unit, and so which waves and which half of a split unit, computed it)."""
     B, H, nb = counts.shape
     flat = counts.reshape(-1)
     pick = {int(np.argmax(flat)), int(np.argmin(flat))}
@@ -508,6 +510,9 @@ def stratified_tiles(counts, rng):
     order = np.argsort(flat, kind="stable")
     for part in np.array_split(order, 5):
         pick.add(int(rng.choice(part)))
+    for m in range(4):
+        i = int(rng.choice(np.arange(m, nb, 4)))
+        pick.add(int(rng.integers(B * H)) * nb + i)
     return sorted(pick)
 
 
