@@ -72,12 +72,30 @@ void* scratch_ptr(int device) {
   return g_scratch_ptr[device];
 }
 
-absh_status use_device(const absh_ctx* c) {
-  int cur = -1;
-  ABSH_HIP(hipGetDevice(&cur), "hipGetDevice");
-  if (cur != c->device) ABSH_HIP(hipSetDevice(c->device), "hipSetDevice");
-  return ABSH_OK;
-}
+// Makes a GPU current for the rest of an entry point and gives the caller's
+// current device back when the entry point returns (launches already queued on
+// a stream are not affected by the switch back).
+class DeviceScope {
+ public:
+  DeviceScope() = default;
+  DeviceScope(const DeviceScope&) = delete;
+  DeviceScope& operator=(const DeviceScope&) = delete;
+  ~DeviceScope() {
+    if (switched_) (void)hipSetDevice(prev_);
+  }
+  absh_status enter(int device) {
+    ABSH_HIP(hipGetDevice(&prev_), "hipGetDevice");
+    if (prev_ != device) {
+      ABSH_HIP(hipSetDevice(device), "hipSetDevice");
+      switched_ = true;
+    }
+    return ABSH_OK;
+  }
+
+ private:
+  int prev_ = -1;
+  bool switched_ = false;
+};
 
 absh_status check_ctx(const absh_ctx* c) {
   if (!c) return fail(ABSH_EINVAL, "ctx is NULL");
@@ -163,7 +181,8 @@ absh_status absh_create(absh_ctx** out, int T, int Y, int X, int block, int devi
   }
   if (device >= ndev) return fail(ABSH_ENODEV, "device %d does not exist (%d present)", device, ndev);
   if (device >= kMaxDevices) return fail(ABSH_EUNSUPPORTED, "device index %d above %d", device, kMaxDevices - 1);
-  ABSH_HIP(hipSetDevice(device), "hipSetDevice");
+  DeviceScope dev;
+  if (absh_status st = dev.enter(device)) return st;
   ABSH_HIP(scratch_setup(device), "absh_create: static scratch address");
 
   absh_ctx* c = new (std::nothrow) absh_ctx();
@@ -201,7 +220,8 @@ absh_status absh_create(absh_ctx** out, int T, int Y, int X, int block, int devi
 absh_status absh_destroy(absh_ctx* c) {
   g_last_error.clear();
   if (!c) return ABSH_OK;
-  absh_status st = use_device(c);
+  DeviceScope dev;
+  absh_status st = dev.enter(c->device);
   if (st == ABSH_OK) {
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) st = hip_fail(e, "absh_destroy");
@@ -233,7 +253,8 @@ absh_status absh_perm(const absh_ctx* c, const int32_t** perm, const int32_t** i
 absh_status absh_perm_copy(const absh_ctx* c, int32_t* perm_dst, int32_t* inv_dst, void* stream) {
   g_last_error.clear();
   if (absh_status st = check_ctx(c)) return st;
-  if (absh_status st = use_device(c)) return st;
+  DeviceScope dev;
+  if (absh_status st = dev.enter(c->device)) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const size_t bytes = sizeof(int32_t) * c->N;
   if (perm_dst) ABSH_HIP(hipMemcpyAsync(perm_dst, c->perm, bytes, hipMemcpyDeviceToDevice, s), "absh_perm_copy");
@@ -251,7 +272,8 @@ absh_status absh_permute(absh_ctx* c, const void* x, absh_dtype xt, void* xh, in
   if (layout != ABSH_ROWS && layout != ABSH_VT && layout != ABSH_ROWS_F32)
     return fail(ABSH_EINVAL, "unknown layout %d", (int)layout);
   if (!aligned16(x) || !aligned16(xh)) return fail(ABSH_EINVAL, "x and xh must be 16-byte aligned");
-  if (absh_status st = use_device(c)) return st;
+  DeviceScope dev;
+  if (absh_status st = dev.enter(c->device)) return st;
   ABSH_HIP(absh::launch_permute(c, x, xt == ABSH_F32, xh, B, H, d, (int)layout, reinterpret_cast<hipStream_t>(stream)),
            "absh_permute");
   return ABSH_OK;
@@ -268,7 +290,8 @@ absh_status absh_permute_pool(absh_ctx* c, const void* x, absh_dtype xt, void* x
     return fail(ABSH_EINVAL, "absh_permute_pool writes rows: layout ABSH_ROWS or ABSH_ROWS_F32 (got %d)", (int)layout);
   if (!aligned16(x) || !aligned16(xh) || !aligned16(xbar))
     return fail(ABSH_EINVAL, "x, xh and xbar must be 16-byte aligned");
-  if (absh_status st = use_device(c)) return st;
+  DeviceScope dev;
+  if (absh_status st = dev.enter(c->device)) return st;
   ABSH_HIP(absh::launch_permute_pool(c, x, xt == ABSH_F32, xh, xbar, B, H, d, (int)layout,
                                      reinterpret_cast<hipStream_t>(stream)),
            "absh_permute_pool");
@@ -281,7 +304,8 @@ absh_status absh_unpermute(absh_ctx* c, const void* oh, void* o, int B, int H, i
   if (absh_status st = check_shape(c, B, H, d)) return st;
   if (!oh || !o) return fail(ABSH_EINVAL, "oh or o is NULL");
   if (!aligned16(oh) || !aligned16(o)) return fail(ABSH_EINVAL, "oh and o must be 16-byte aligned");
-  if (absh_status st = use_device(c)) return st;
+  DeviceScope dev;
+  if (absh_status st = dev.enter(c->device)) return st;
   ABSH_HIP(absh::launch_unpermute(c, oh, o, B, H, d, reinterpret_cast<hipStream_t>(stream)), "absh_unpermute");
   return ABSH_OK;
 }
@@ -291,7 +315,8 @@ absh_status absh_pool(absh_ctx* c, const void* xh, float* xbar, int B, int H, in
   if (absh_status st = check_ctx(c)) return st;
   if (absh_status st = check_shape(c, B, H, d)) return st;
   if (!xh || !xbar) return fail(ABSH_EINVAL, "xh or xbar is NULL");
-  if (absh_status st = use_device(c)) return st;
+  DeviceScope dev;
+  if (absh_status st = dev.enter(c->device)) return st;
   ABSH_HIP(absh::launch_pool(c, xh, 0, xbar, B, H, d, reinterpret_cast<hipStream_t>(stream)), "absh_pool");
   return ABSH_OK;
 }
@@ -303,7 +328,8 @@ absh_status absh_block_scores(absh_ctx* c, const float* qbar, const float* kbar,
   if (absh_status st = check_shape(c, B, H, d)) return st;
   if (!qbar || !kbar || !s) return fail(ABSH_EINVAL, "qbar, kbar or s is NULL");
   if (!aligned16(qbar) || !aligned16(kbar)) return fail(ABSH_EINVAL, "qbar and kbar must be 16-byte aligned");
-  if (absh_status st = use_device(c)) return st;
+  DeviceScope dev;
+  if (absh_status st = dev.enter(c->device)) return st;
   ABSH_HIP(absh::launch_scores(c, qbar, kbar, s, B * H, d, reinterpret_cast<hipStream_t>(stream)),
            "absh_block_scores");
   return ABSH_OK;
@@ -482,7 +508,8 @@ absh_status route_impl(absh_ctx* c, const void* qh, const void* kh, absh_dtype q
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
     return fail(ABSH_EINVAL, "workspace must be %zu-byte aligned", kAlign);
   if (check_only) return ABSH_OK;
-  if (absh_status st = use_device(c)) return st;
+  DeviceScope dev;
+  if (absh_status st = dev.enter(c->device)) return st;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = reinterpret_cast<char*>(ws);
@@ -644,7 +671,8 @@ absh_status absh_sparse_attn(absh_ctx* c, const void* qh, const void* kh, const 
     return fail(ABSH_EINVAL, "qh, kh, vt and oh must be 16-byte aligned");
   absh::AttnLists L;
   if (absh_status st = attn_lists(c, lists, &L)) return st;
-  if (absh_status st = use_device(c)) return st;
+  DeviceScope dev;
+  if (absh_status st = dev.enter(c->device)) return st;
   ABSH_HIP(absh::launch_attention(c, qh, kh, vt, oh, B, H, d, lists ? &L : nullptr,
                                   reinterpret_cast<hipStream_t>(stream)),
            "absh_sparse_attn");
@@ -662,7 +690,8 @@ absh_status absh_quantize_v(absh_ctx* c, const void* vh, int B, int H, int d, vo
   if (!aligned16(vh) || !aligned16(vt8) || !aligned16(vscale))
     return fail(ABSH_EINVAL, "vh, vt8 and vscale must be 16-byte aligned");
   if ((double)B * H * (c->n_pad / 64) >= 2147483647.0) return fail(ABSH_EINVAL, "B*H*n_pad/64 must fit in int32");
-  if (absh_status st = use_device(c)) return st;
+  DeviceScope dev;
+  if (absh_status st = dev.enter(c->device)) return st;
   ABSH_HIP(absh::launch_quantize_v(c, vh, vt8, vscale, B * H, d, reinterpret_cast<hipStream_t>(stream)),
            "absh_quantize_v");
   return ABSH_OK;
@@ -681,7 +710,8 @@ absh_status absh_sparse_attn_v8(absh_ctx* c, const void* qh, const void* kh, con
   const int members = lists ? L.members : (c->block >= 128 ? 2 : 4);
   if (!absh::union_attention_supported(d, c->block, members))
     return fail(ABSH_EUNSUPPORTED, "8-bit values need block 64 or 128");
-  if (absh_status st = use_device(c)) return st;
+  DeviceScope dev;
+  if (absh_status st = dev.enter(c->device)) return st;
   ABSH_HIP(absh::launch_union_attention(c, qh, kh, vt8, vscale, oh, B, H, d, lists ? &L : nullptr,
                                         reinterpret_cast<hipStream_t>(stream)),
            "absh_sparse_attn_v8");
@@ -701,7 +731,8 @@ absh_status absh_sparse_attn_grid(absh_ctx* c, const void* qh, const void* kh, c
   const int members = lists ? L.members : (c->block >= 128 ? 2 : 4);
   if (vscale && !absh::union_attention_supported(d, c->block, members))
     return fail(ABSH_EUNSUPPORTED, "8-bit values need block 64 or 128");
-  if (absh_status st = use_device(c)) return st;
+  DeviceScope dev;
+  if (absh_status st = dev.enter(c->device)) return st;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (vscale)
     ABSH_HIP(absh::launch_union_attention(c, qh, kh, vt, vscale, o, B, H, d, lists ? &L : nullptr, s, true),

@@ -17,6 +17,8 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
  *    call except absh_create/absh_destroy only enqueues work on it: no host
  *    synchronisation, no device allocation.
+ *  - Each call makes the context's device current while it runs and makes the
+ *    caller's current device current again before it returns.
  *  - Grid order: token n = (t*Y + y)*X + x of the (T, Y, X) latent grid; caller
  *    tensors are [B, N, H, d], row-major.
  *  - Hilbert order: the library's own tensors hold tokens sorted along a 3-D
