@@ -1,0 +1,88 @@
+"""The whole path (absh_forward) captured in a HIP graph and replayed.
+
+Inside absh_forward the library allocates nothing and does not synchronise with the
+host. It clears its counters and scratch with kernels of its own, not memset nodes,
+and the attention leaves its pull counters at zero. So each replay of the captured
+graph must reproduce the eager call's lists and output bit for bit. The test runs
+eager work and a host synchronisation between the replays, and checks every replay
+against the eager call."""
+import numpy as np
+import pytest
+import torch
+
+import adaptive_block_sparse_hilbert_amd as absh
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def routing_tensors(r):
+    names = ["counts", "kv_idx", "work", "L", "queue", "sched", "unit_list", "unit_cnt"]
+    if r.unit_queue is not None and r.unit_queue.numel():
+        names.append("unit_queue")
+    return {n: getattr(r, n) for n in names}
+
+
+def written(name, t, r):
+    """The part of a routing tensor the call writes: lists are row-padded, and only the
+    first counts[tile] (kv_idx) or unit_cnt[unit] (unit_list) entries of a row are set."""
+    if name == "kv_idx":
+        nb = t.shape[-1]
+        return t[torch.arange(nb, device=t.device) < r.counts[..., None]]
+    if name == "unit_list":
+        nb = t.shape[-1]
+        return t[torch.arange(nb, device=t.device) < r.unit_cnt[:, None]]
+    return t
+
+
+@pytest.mark.parametrize("index,schedule", [(1, "xcd"), (3, "lpt")])
+def test_forward_graph_replays_equal_the_eager_call(index, schedule):
+    w = W.workload(index)
+    print(f"[graph] {w.name} {schedule}", flush=True)
+    d = W.generate(w)
+    q, k, v = (bf16_dev(d[n]) for n in ("q16", "k16", "v16"))
+    ctx = absh.create(w.T, w.Y, w.X, w.block)
+    B, _, H, hd = q.shape
+    args = dict(slack_frac=w.slack_frac, schedule=schedule)
+
+    # the eager reference (its own routing, output and workspace)
+    o_ref, r_ref = absh.forward(ctx, q, k, v, w.p, w.k_floor, **args)
+    torch.cuda.synchronize()
+    want = {n: written(n, t, r_ref).clone() for n, t in routing_tensors(r_ref).items()}
+
+    # everything the captured call touches is allocated before the capture
+    ws = torch.empty(absh.forward_workspace_bytes(ctx, B, H, hd), dtype=torch.uint8, device=DEV)
+    routing = absh.alloc_routing(ctx, B, H)
+    out = torch.empty_like(o_ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one call on a side stream before capturing
+        absh.forward(ctx, q, k, v, w.p, w.k_floor, routing=routing, out=out, workspace=ws, **args)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        absh.forward(ctx, q, k, v, w.p, w.k_floor, routing=routing, out=out, workspace=ws, **args)
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        # eager work between the replays: clear every output of the captured call
+        out.zero_()
+        for t in routing_tensors(routing).values():
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), o_ref.view(torch.int16)), f"output, replay {rep}"
+        for n, t in routing_tensors(routing).items():
+            assert torch.equal(written(n, t, routing), want[n]), f"{n}, replay {rep}"
+        print(f"[graph] replay {rep} identical", flush=True)
+    del graph
+    ctx.close()
