@@ -22,26 +22,29 @@ def bf16_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
 
 
-def routing_tensors(r):
-    names = ["counts", "kv_idx", "work", "L", "queue", "sched", "unit_list", "unit_cnt"]
-    if r.unit_queue is not None and r.unit_queue.numel():
-        names.append("unit_queue")
-    return {n: getattr(r, n) for n in names}
-
-
-def written(name, t, r):
-    """The part of a routing tensor the call writes: lists are row-padded, and only the
-    first counts[tile] (kv_idx) or unit_cnt[unit] (unit_list) entries of a row are set."""
-    if name == "kv_idx":
-        nb = t.shape[-1]
-        return t[torch.arange(nb, device=t.device) < r.counts[..., None]]
-    if name == "unit_list":
-        nb = t.shape[-1]
-        return t[torch.arange(nb, device=t.device) < r.unit_cnt[:, None]]
+def routing_tensors(r, units, schedule):
+    """The routing outputs the call writes for this schedule (units: its work units)."""
+    t = dict(counts=r.counts, kv_idx=r.kv_idx, work=r.work, L=r.L, queue=r.queue, sched=r.sched,
+             unit_list=r.unit_list[:units], unit_cnt=r.unit_cnt[:units])
+    if schedule == "lpt":
+        t["unit_queue"] = r.unit_queue[:units]
+    if schedule == "ranks":
+        t["head_order"] = r.head_order
     return t
 
 
-@pytest.mark.parametrize("index,schedule", [(1, "xcd"), (3, "lpt")])
+def written(name, t, r, units):
+    """The part of a routing tensor the call writes: lists are row-padded, and only the
+    first counts[tile] (kv_idx) or unit_cnt[unit] (unit_list) entries of a row are set."""
+    nb = t.shape[-1]
+    if name == "kv_idx":
+        return t[torch.arange(nb, device=t.device) < r.counts[..., None]]
+    if name == "unit_list":
+        return t[torch.arange(nb, device=t.device) < r.unit_cnt[:units, None]]
+    return t
+
+
+@pytest.mark.parametrize("index,schedule", [(1, "xcd"), (3, "lpt"), (2, "ranks"), (4, "xcd")])
 def test_forward_graph_replays_equal_the_eager_call(index, schedule):
     w = W.workload(index)
     print(f"[graph] {w.name} {schedule}", flush=True)
@@ -54,7 +57,9 @@ def test_forward_graph_replays_equal_the_eager_call(index, schedule):
     # the eager reference (its own routing, output and workspace)
     o_ref, r_ref = absh.forward(ctx, q, k, v, w.p, w.k_floor, **args)
     torch.cuda.synchronize()
-    want = {n: written(n, t, r_ref).clone() for n, t in routing_tensors(r_ref).items()}
+    units = absh.lists_units(ctx, B, H, schedule)
+    assert units > 0
+    want = {n: written(n, t, r_ref, units).clone() for n, t in routing_tensors(r_ref, units, schedule).items()}
 
     # everything the captured call touches is allocated before the capture
     ws = torch.empty(absh.forward_workspace_bytes(ctx, B, H, hd), dtype=torch.uint8, device=DEV)
@@ -75,14 +80,14 @@ def test_forward_graph_replays_equal_the_eager_call(index, schedule):
     for rep in range(3):
         # eager work between the replays: clear every output of the captured call
         out.zero_()
-        for t in routing_tensors(routing).values():
+        for t in routing_tensors(routing, units, schedule).values():
             t.zero_()
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), o_ref.view(torch.int16)), f"output, replay {rep}"
-        for n, t in routing_tensors(routing).items():
-            assert torch.equal(written(n, t, routing), want[n]), f"{n}, replay {rep}"
+        for n, t in routing_tensors(routing, units, schedule).items():
+            assert torch.equal(written(n, t, routing, units), want[n]), f"{n}, replay {rep}"
         print(f"[graph] replay {rep} identical", flush=True)
     del graph
     ctx.close()
