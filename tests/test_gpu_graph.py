@@ -91,3 +91,63 @@ def test_forward_graph_replays_equal_the_eager_call(index, schedule):
         print(f"[graph] replay {rep} identical", flush=True)
     del graph
     ctx.close()
+
+
+def test_separate_calls_graph_replays_equal_the_eager_calls():
+    """The same with the calls made one by one (permute with pooling of q and k, permute
+    of v, routing from the block means, attention writing grid order), 480p, xcd."""
+    w = W.workload(1)
+    schedule = "xcd"
+    print(f"[graph] {w.name} separate calls", flush=True)
+    d = W.generate(w)
+    q, k, v = (bf16_dev(d[n]) for n in ("q16", "k16", "v16"))
+    ctx = absh.create(w.T, w.Y, w.X, w.block)
+    B, _, H, hd = q.shape
+    units = absh.lists_units(ctx, B, H, schedule)
+
+    def path(bufs=None):
+        b = bufs or {}
+        qh, qbar = absh.permute_pool(ctx, q, out=b.get("qh"), means=b.get("qbar"))
+        kh, kbar = absh.permute_pool(ctx, k, out=b.get("kh"), means=b.get("kbar"))
+        vt = absh.permute(ctx, v, layout=absh.ABSH_VT, out=b.get("vt"))
+        r = absh.route(ctx, None, None, w.p, w.k_floor, schedule=schedule, qbar=qbar, kbar=kbar,
+                       out=b.get("routing"), workspace=b.get("ws"))
+        o = absh.sparse_attn_grid(ctx, qh, kh, vt, r, out=b.get("o"))
+        return dict(qh=qh, qbar=qbar, kh=kh, kbar=kbar, vt=vt, routing=r, o=o)
+
+    ref = path()
+    torch.cuda.synchronize()
+    want = {n: written(n, t, ref["routing"], units).clone()
+            for n, t in routing_tensors(ref["routing"], units, schedule).items()}
+    # every buffer of the captured calls, allocated before the capture
+    bufs = {n: torch.empty_like(t) for n, t in ref.items() if n != "routing"}
+    bufs["routing"] = absh.alloc_routing(ctx, B, H)
+    bufs["ws"] = torch.empty(absh.route_workspace_bytes(ctx, B, H, hd), dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        path(bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path(bufs)
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        for n in ("qh", "qbar", "kh", "kbar", "vt", "o"):
+            bufs[n].zero_()
+        for t in routing_tensors(bufs["routing"], units, schedule).values():
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in ("qh", "kh", "vt", "o"):
+            assert torch.equal(bufs[n].view(torch.int16), ref[n].view(torch.int16)), f"{n}, replay {rep}"
+        for n in ("qbar", "kbar"):
+            assert torch.equal(bufs[n].view(torch.int32), ref[n].view(torch.int32)), f"{n}, replay {rep}"
+        for n, t in routing_tensors(bufs["routing"], units, schedule).items():
+            assert torch.equal(written(n, t, bufs["routing"], units), want[n]), f"{n}, replay {rep}"
+        print(f"[graph] separate calls: replay {rep} identical", flush=True)
+    del graph
+    ctx.close()
